@@ -71,14 +71,14 @@ def srs_shuffle(partials, dest, G):
     range (a stable sort by predicted cluster).
 
     The sum is the output's quantised code, so it follows the kernel's
-    precision: binary32, partials added in order p = 0..P-1, rounded once to
-    bf16 (nearest even).
+    precision: binary32, a left fold p_0 + p_1 + ... + p_{P-1} (so a sum of
+    negative zeros stays -0.0), rounded once to bf16 (nearest even).
     """
     partials = np.asarray(partials, dtype=np.uint16)
     _check(partials.ndim == 3, "partials must be [P][N][d]")
     P, N, d = partials.shape
-    acc = np.zeros((N, d), dtype=np.float32)
-    for p in range(P):
+    acc = bf16_to_f64(partials[0]).astype(np.float32)
+    for p in range(1, P):
         acc = acc + bf16_to_f64(partials[p]).astype(np.float32)
     x = round_bf16(acc.astype(np.float64))
     if dest is None:

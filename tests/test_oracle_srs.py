@@ -98,3 +98,11 @@ def test_bad_dest_raises():
     parts = _parts(1, 10, 8, 0)
     with pytest.raises(ValueError):
         srs_shuffle(parts, np.full(10, 3), 3)
+
+
+def test_signed_zero_sum_is_ieee_fold():
+    # -0 + -0 = -0 under IEEE addition; the sum starts at the first partial
+    parts = np.full((2, 1, 8), 0x8000, dtype=np.uint16)
+    assert np.all(srs_shuffle(parts, None, 1)["out"] == 0x8000)
+    parts[1] = 0x0000
+    assert np.all(srs_shuffle(parts, None, 1)["out"] == 0x0000)
