@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE routing/dispatch path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input,
+already resident in HBM: predict -> SRS (reduce P partials + shuffle into G
+cluster ranges) -> gate -> top-K -> LAR -> expert-contiguous dispatch ->
+weighted combine with the unshuffle (identity experts). Default workload:
+DeepSeek-V2-shaped (N=16384 tokens, d=5120, E=160, K=6, P=2, G=8).
+
+Prints ONE JSON line: routed tokens/s, the per-stage times, the HBM roofline
+fraction of the pass and of its dominant kernel, and the CPU oracle timed on
+a bounded sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12            # MI355X HBM3E, bytes/s (AMD spec sheet)
+METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofline"
+
+ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
+
+
+def route_bytes(N, d, E, K, P, G, fallback):
+    """Algorithmic HBM bytes per pass: every call reads its inputs once and
+    writes its outputs once (bf16 rows = 2 bytes per element)."""
+    b = 2
+    st = {
+        "predict": (9 if fallback else 6) * N,
+        "srs": P * N * d * b + N * d * b + 10 * N + 4 * (G + 1),
+        "gate": N * d * b + E * d * b + 4 * N * E,
+        "topk": 4 * N * E + 8 * N * K,
+        "lar": 4 * N * K + N + E,
+        "permute": 12 * N * K + 4 * (E + 1) + N * d * b + N * K * d * b,
+        "combine": N * K * d * b + 8 * N * K + 4 * N + N * d * b,
+    }
+    return st
+
+
+def foe_bytes(N, d, E, K, H):
+    b = 2
+    return {
+        "reduce": H * N * d * b + N * d * b + 8,
+        "gate": N * d * b + E * d * b + 4 * N * E,
+        "topk": 4 * N * E + 8 * N * K,
+        "lar": 4 * N * K + N * H + E,
+        "permute": 12 * N * K + 4 * (E + 1) + H * N * d * b + N * K * d * b,
+        "combine": N * K * d * b + 8 * N * K + N * d * b,
+    }
+
+
+def cpu_baseline(name: str, n_sample: int):
+    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
+    same workload: n_sample tokens drawn with the workload's recipe."""
+    from threadpoolctl import threadpool_info
+    from synth import make_config_inputs
+    import oracle.pipeline as op
+
+    inp = make_config_inputs(name, N=n_sample)
+    if name == "foe":
+        t0 = time.perf_counter()
+        op.foe_pass(inp)
+        dt = time.perf_counter() - t0
+    else:
+        lut, conf = op.build_tables(inp)
+        t0 = time.perf_counter()
+        op.route_pass(inp, lut, conf)
+        dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_sample} tokens of the {name} workload, one full pass (float64 NumPy; "
+                      f"BLAS on {threads} threads, elementwise steps single-threaded); {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="deepseek", choices=["tiny", "mixtral", "deepseek", "foe"])
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    from synth import make_config_inputs, get_config
+    from token_routing_speculation_amd.pipeline import RoutePass, FoEPass
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 3
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    inp = make_config_inputs(args.config)
+    if args.config == "foe":
+        p = FoEPass(inp)
+        bytes_st = foe_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.H)
+        conf = {"workload": "foe-grouped", "N": cfg.N, "d": cfg.d, "E": cfg.E, "H": cfg.H,
+                "K": cfg.K, "G": cfg.G}
+    else:
+        p = RoutePass(inp)
+        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback)
+        conf = {"workload": ROUTE_WORKLOADS[args.config], "N": cfg.N, "d": cfg.d, "E": cfg.E,
+                "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
+                "fallback": "2-gram" if p.fallback else "none"}
+    stages = p.STAGES
+    stream = torch.cuda.current_stream()
+
+    # a plain copy of known size, untimed: the calibration kernel for the
+    # FETCH_SIZE / WRITE_SIZE counters of a profiled run
+    calib = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+
+    for _ in range(args.warmup):
+        p.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(K):
+        for s, name in enumerate(stages):
+            ev[k][s].record(stream)
+            getattr(p, name)()
+        ev[k][len(stages)].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / K
+    st_us = {name: 1e3 * sum(ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)) / K
+             for s, name in enumerate(stages)}
+
+    N = cfg.N
+    tokens_per_s = N / (ms * 1e-3)
+    total_bytes = sum(bytes_st.values())
+    # dominant single-kernel stage: the combine (one launch per pass)
+    dom = "combine"
+    dom_bytes = bytes_st[dom]
+    achieved = dom_bytes / (st_us[dom] * 1e-6)
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": conf,
+        "hbm_frac_pass": total_bytes / (ms * 1e-3) / HBM_PEAK,
+        "alg_bytes_pass": total_bytes,
+        "stages_us": {k: round(v, 2) for k, v in st_us.items()},
+        "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
+        "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine)",
+                     "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None},
+        "lar": int(p.local.item()) / (K + args.warmup) / (N * cfg.K),
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline and args.config != "tiny":
+        out["cpu_baseline"] = cpu_baseline(args.config, min(args.cpu_sample, N))
+    elif not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, N)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,260 @@
+/*
+ * route.h - C ABI of libroute.so: the MoE token-routing and dispatch path on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (web pages; sections as the pages number them):
+ *   [SMOE]  "Speculative MoE" notes, research-notes-783.pages.dev/p/speculative-moe/
+ *   [SPEC]  "Speculating Experts Accelerates Inference for Mixture-of-Experts",
+ *           gist.science/ko/paper/2603.19289 (technical summary items)
+ *   [FOE]   "Federation of Experts (FoE)", aitrends.kr/articles/58129
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is a DEVICE pointer unless marked "host". bf16 values are
+ *    passed as uint16_t bit patterns (upper half of an IEEE binary32).
+ *  - Row-data tensors (marked "rows") are row-major and contiguous, their
+ *    row length d is a multiple of 8 and their base pointer is 16-byte
+ *    aligned, so every row is a whole number of 16-byte vectors.
+ *  - The caller owns every buffer. The library never allocates, frees or
+ *    synchronises, keeps no global state and is safe to call on several
+ *    streams at once for disjoint buffers. Every call only enqueues work on
+ *    stream `s` (a hipStream_t; NULL is the default stream) and returns.
+ *  - Scratch space ("ws") is caller-provided; its size comes from the
+ *    matching *_workspace_size() call. Its contents need no initialisation
+ *    and are meaningless after the call.
+ *  - Host-checkable errors (null required pointer, bad shape, misalignment,
+ *    unsupported size, workspace too small) are returned as a status before
+ *    anything is enqueued; nothing is written then. ROUTE_ERR_HIP means a
+ *    kernel launch failed.
+ *  - Data-dependent violations (a token id outside the vocabulary, a cluster
+ *    id >= G, an expert id >= E, a slot or row index out of range) cannot be
+ *    seen by the host: kernels OR the ROUTE_EBIT_* bits into the optional
+ *    device word `err` (never cleared by the library) and skip the offending
+ *    element; the affected outputs are then unspecified, but no access goes
+ *    out of bounds.
+ *  - n = 0 is a valid no-op (offset arrays are still written, all zero).
+ *  - All outputs are bitwise reproducible run to run: no float atomics, and a
+ *    fixed accumulation order per output element.
+ *  - Counters (lar_count, hit_count) ADD into a caller-zeroed device uint64.
+ */
+#ifndef ROUTE_H_
+#define ROUTE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  ROUTE_OK = 0,
+  ROUTE_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  ROUTE_ERR_SHAPE = 2,        /* n < 0, d % 8 != 0, E % H != 0, K > E/H, ...    */
+  ROUTE_ERR_ALIGN = 3,        /* a rows pointer is not 16-byte aligned          */
+  ROUTE_ERR_UNSUPPORTED = 4,  /* E > 1024, K > 16, G > 256, P > 16, d too big   */
+  ROUTE_ERR_WORKSPACE = 5,    /* ws NULL or ws_bytes below the required size    */
+  ROUTE_ERR_HIP = 6           /* a kernel launch failed                         */
+};
+
+enum {
+  ROUTE_EBIT_TOKEN_RANGE = 1u,   /* token id < 0 or >= vocab                    */
+  ROUTE_EBIT_DEST_RANGE = 2u,    /* cluster id >= G                             */
+  ROUTE_EBIT_EXPERT_RANGE = 4u,  /* expert id < 0 or >= E                       */
+  ROUTE_EBIT_INDEX_RANGE = 8u    /* slot / row / pair index out of range        */
+};
+
+/* Readable name of a status code (host; static string). */
+const char* route_status_str(int status);
+
+/*
+ * route_predict - speculative destination cluster of each token.
+ * [SMOE] section 4.1 (route-path prediction with lookup tables): the
+ * intra-layer token table lut[id] gives the cluster; when the fallback is
+ * enabled (conf != NULL) and the table's confidence byte conf[id] is below
+ * conf_thr (128 ~ 0.5), the inter-layer 2-gram table
+ * ngram[prev2[i] * G + prev1[i]] over the token's clusters at the two
+ * preceding layers gives it instead.
+ *   tok   int32[n]          token ids, 0 <= id < vocab
+ *   lut   uint8[vocab]      token -> cluster
+ *   conf  uint8[vocab]      confidence bytes (q/255), NULL disables the fallback
+ *   prev2, prev1 uint8[n]   previous-layer clusters; ngram uint8[G*G]
+ *                           (all three required iff conf != NULL)
+ *   dest  uint8[n]          output cluster, written for every valid token
+ * Errors: ROUTE_ERR_NULL, ROUTE_ERR_SHAPE (n < 0, vocab < 1, G < 1),
+ * ROUTE_ERR_UNSUPPORTED (G > 256). Device bits: TOKEN_RANGE (dest[i] = 0),
+ * DEST_RANGE (a table entry or prev cluster >= G; the entry is written as is).
+ */
+int route_predict(const int32_t* tok, int64_t n, const uint8_t* lut, const uint8_t* conf,
+                  int32_t vocab, const uint8_t* prev2, const uint8_t* prev1,
+                  const uint8_t* ngram, int32_t G, int32_t conf_thr, uint8_t* dest,
+                  uint32_t* err, hipStream_t s);
+
+/*
+ * route_lut_build - offline table builder for route_predict.
+ * [SMOE] section 4.1: the token-expert confidence table is reduced to a
+ * token -> cluster table. For row i (id ids[i], routing idx[i][K] with
+ * weights w[i][K]) the share of cluster c is the binary32 sum over
+ * k = 0..K-1 of the w[i][k] whose expert sits on c (expert_cluster[]);
+ * lut[ids[i]] = the cluster with the largest share (lower cluster on ties),
+ * conf[ids[i]] = floor(fl(fl(255 * share) + 0.5)), clamped to [0, 255].
+ *   ids int32[n] (distinct), idx int32[n][K], w float[n][K],
+ *   expert_cluster uint8[E], lut uint8[vocab], conf uint8[vocab] (nullable)
+ * Errors: ROUTE_ERR_NULL, ROUTE_ERR_SHAPE, ROUTE_ERR_UNSUPPORTED (G > 256,
+ * K > 16, E > 1024). Device bits: TOKEN_RANGE, EXPERT_RANGE, DEST_RANGE.
+ * Rows whose ids repeat race; ids must be distinct.
+ */
+int route_lut_build(const int32_t* ids, int64_t n, const int32_t* idx, const float* w,
+                    int32_t K, const uint8_t* expert_cluster, int32_t E, int32_t G,
+                    uint8_t* lut, uint8_t* conf, int32_t vocab, uint32_t* err,
+                    hipStream_t s);
+
+/*
+ * srs_shuffle - shuffled reduce-scatter on one GPU.
+ * [SMOE] section 3.1 (s-TS): the tensor-parallel all-reduce becomes a
+ * reduce-scatter fused with a token shuffle that delivers each token's
+ * reduced activation to its predicted cluster. Here the G clusters are G
+ * contiguous row ranges of `out`:
+ *   X[i]  = bf16_rne( sum_{p=0..P-1} partials[p][i] )  (binary32, in p order)
+ *   rows are stably sorted by dest[i]: cluster c owns rows
+ *   [cluster_offsets[c], cluster_offsets[c+1]), tokens in original order;
+ *   out[row_of_src[i]] = X[i], src_of_row[row] = i, row_cluster[row] = dest[i].
+ *   partials bf16 rows [P][n][d]; dest uint8[n] (NULL only when G == 1:
+ *   pure reduce, identity order); out bf16 rows [n][d]; cluster_offsets
+ *   int32[G+1]; row_of_src, src_of_row int32[n] and row_cluster uint8[n]
+ *   are optional outputs (NULL = not written).
+ *   ws: srs_shuffle_workspace_size(n, G) bytes.
+ * Errors: NULL, SHAPE (n < 0, P < 1, d < 8 or d % 8, G < 1, n >= 2^31),
+ * ALIGN, UNSUPPORTED (P > 16, G > 256), WORKSPACE. Device bit: DEST_RANGE.
+ */
+int srs_shuffle(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                const uint8_t* dest, int32_t G, uint16_t* out, int32_t* cluster_offsets,
+                int32_t* row_of_src, int32_t* src_of_row, uint8_t* row_cluster,
+                void* ws, size_t ws_bytes, uint32_t* err, hipStream_t s);
+size_t srs_shuffle_workspace_size(int64_t n, int32_t G);
+
+/*
+ * route_gate - router logits = x . w^T.
+ * [FOE] per-layer comparison (router scores g[i]); [SPEC] item 2.A (the
+ * next layer's gate applied to q_l). bf16 operands, binary32 accumulation
+ * on the MFMA units.
+ *   x bf16 rows [n][d]; w bf16 rows [E][d]; logits float[n][E] (row-major).
+ * Errors: NULL, SHAPE (n < 0, d % 8, E < 1), ALIGN, UNSUPPORTED (E > 1024).
+ */
+int route_gate(const uint16_t* x, int64_t n, int32_t d, const uint16_t* w, int32_t E,
+               float* logits, hipStream_t s);
+
+/*
+ * route_topk - softmax + top-K, plain (H = 1) or FoE-grouped (H > 1).
+ * [SMOE] section 1 and glossary (top-K experts per token); [FOE] grouped MoE
+ * block: group h owns experts [h*E/H, (h+1)*E/H) and picks its top K/H.
+ * Ranking is on the binary32 logits: larger first, lower expert index first
+ * on equal values, -0.0 equal to +0.0. Slots are group-major, descending
+ * inside a group. weights: renorm = 1 -> softmax over each group's chosen
+ * logits (sums to 1 per group); renorm = 0 -> softmax over all E logits,
+ * read at the chosen experts.
+ *   logits float[n][E]; idx int32[n][K]; weights float[n][K] (nullable).
+ * NaN logits are outside the contract (no fault, unspecified choice).
+ * Errors: NULL, SHAPE (E % H, K % H, K/H > E/H, K < 1, H < 1), UNSUPPORTED
+ * (E > 1024, K > 16).
+ */
+int route_topk(const float* logits, int64_t n, int32_t E, int32_t K, int32_t H, int32_t renorm,
+               int32_t* idx, float* weights, hipStream_t s);
+
+/*
+ * lar_count - local activation counter.
+ * [SMOE] glossary (local activation rate: the share of activations routed
+ * to an expert on the token's own device); [FOE] rho. Adds to *local the
+ * number of (i, k) with expert_cluster[idx[i][k]] == row_cluster[i*H + k/(K/H)].
+ *   idx int32[n][K]; row_cluster uint8[n*H]; expert_cluster uint8[E];
+ *   local: device uint64, accumulated. Out-of-range experts count as remote.
+ * Errors: NULL, SHAPE, UNSUPPORTED (K > 16).
+ */
+int lar_count(const int32_t* idx, int64_t n, int32_t K, int32_t H, const uint8_t* row_cluster,
+              const uint8_t* expert_cluster, int32_t E, unsigned long long* local,
+              hipStream_t s);
+
+/*
+ * moe_permute - expert-contiguous dispatch.
+ * [SMOE] section 1 (dispatch sends each token's activation to its K
+ * experts); [FOE] grouped block (experts of group h read the group-h
+ * activation). Pairs p = i*K + k are stably counting-sorted by idx[i][k]:
+ * expert e owns slots [expert_offsets[e], expert_offsets[e+1]), pairs in
+ * increasing p; slot_of_pair[p] = slot, pair_of_slot[slot] = p;
+ * disp[slot] = src[(k / (K/H)) * n + i] (each source row read once, written
+ * K/H times).
+ *   idx int32[n][K]; src bf16 rows [H][n][d] (NULL = indices only; then
+ *   disp must be NULL too); expert_offsets int32[E+1]; slot_of_pair,
+ *   pair_of_slot int32[n*K]; disp bf16 rows [n*K][d].
+ *   ws: moe_permute_workspace_size(n, K, E) bytes.
+ * Errors: NULL, SHAPE (K % H, n*K >= 2^31, d % 8 when src given), ALIGN,
+ * UNSUPPORTED (E > 1024, K > 16), WORKSPACE. Device bit: EXPERT_RANGE.
+ */
+int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                const uint16_t* src, int32_t d, int32_t* expert_offsets, int32_t* slot_of_pair,
+                int32_t* pair_of_slot, uint16_t* disp, void* ws, size_t ws_bytes,
+                uint32_t* err, hipStream_t s);
+size_t moe_permute_workspace_size(int64_t n, int32_t K, int32_t E);
+
+/*
+ * moe_combine - weighted combine of the expert outputs, with the SAG unshuffle.
+ * [SMOE] section 1 (combine returns expert outputs to the token and sums
+ * them) and section 3.1 (SAG, the inverse shuffle: out_row); [FOE] (the K
+ * slots span the H groups, so the sum is also the cross-group sum).
+ *   o[j] = sum_{k=0..K-1} weights[j][k] * y[slot_of_pair[j*K + k]]  (binary32, k order)
+ *   out[out_row ? out_row[j] : j] = o[j]
+ *   y bf16 rows [n*K][d]; weights float[n][K]; slot_of_pair int32[n*K];
+ *   out_row int32[n] (nullable, must be a permutation of 0..n-1);
+ *   out rows [n][d]: out_dtype 0 = bf16 (nearest even), 1 = float32.
+ * Errors: NULL, SHAPE (d % 8, out_dtype), ALIGN, UNSUPPORTED (K > 16).
+ * Device bit: INDEX_RANGE (slot >= n*K or out_row >= n; the term / row is skipped).
+ */
+int moe_combine(const uint16_t* y, const float* weights, const int32_t* slot_of_pair,
+                int64_t n, int32_t K, int32_t d, const int32_t* out_row, void* out,
+                int32_t out_dtype, uint32_t* err, hipStream_t s);
+
+/*
+ * route_qhidden - quasi-hidden state q_l = LN_{l+1}(d_l + r_l).
+ * [SPEC] item 2.A: default vector plus residual, normalised with the next
+ * layer's LayerNorm (biased variance over d, binary32 statistics).
+ *   r bf16 rows [n][d]; dvec float[d]; gamma, beta float[d] (nullable =>
+ *   1 and 0); q bf16 rows [n][d] (nearest even).
+ * Errors: NULL, SHAPE (d % 8, eps < 0), ALIGN, UNSUPPORTED (d > 8192).
+ */
+int route_qhidden(const uint16_t* r, const float* dvec, const float* gamma, const float* beta,
+                  int64_t n, int32_t d, float eps, uint16_t* q, hipStream_t s);
+
+/*
+ * route_estimator - lightweight neural estimator of next-layer logits.
+ * [SPEC] item 2.C: logits = GELU(q . w1^T + b1) . w2^T + b2 (GELU with erf).
+ * The hidden activation is kept in bf16 (nearest even) in the workspace
+ * between the two MFMA products.
+ *   q bf16 rows [n][d]; w1 bf16 rows [hd][d]; b1 float[hd]; w2 bf16 rows
+ *   [E][hd]; b2 float[E]; logits float[n][E].
+ *   ws: route_estimator_workspace_size(n, hd) bytes.
+ * Errors: NULL, SHAPE (d % 8, hd % 8), ALIGN, UNSUPPORTED (hd > 4096,
+ * E > 1024), WORKSPACE.
+ */
+int route_estimator(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1, const float* b1,
+                    int32_t hd, const uint16_t* w2, const float* b2, int32_t E, float* logits,
+                    void* ws, size_t ws_bytes, hipStream_t s);
+size_t route_estimator_workspace_size(int64_t n, int32_t hd);
+
+/*
+ * hit_count - prefetch hit counter.
+ * [SPEC] item 4 (hit rate of predicted experts). Adds to *hits the sum over
+ * tokens of |set(pred[i]) intersect set(truth[i])|.
+ *   pred, truth int32[n][K]; hits: device uint64, accumulated.
+ * Errors: NULL, SHAPE, UNSUPPORTED (K > 16).
+ */
+int hit_count(const int32_t* pred, const int32_t* truth, int64_t n, int32_t K,
+              unsigned long long* hits, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTE_H_ */

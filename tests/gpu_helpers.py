@@ -1,0 +1,68 @@
+"""Helpers for the GPU parity tests: host<->device copies and the tolerance
+checks the tests assert."""
+import numpy as np
+import torch
+
+from oracle.bf16 import bf16_to_f64, round_bf16
+
+DEV = "cuda"
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def rel_err_rowfloor(got: np.ndarray, ref: np.ndarray) -> float:
+    """max_ij |got - ref| / max(|ref_ij|, rms(ref_i)): elementwise relative
+    error with each row's rms as the floor near zero."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.abs(got - ref) / den)) if got.size else 0.0
+
+
+def assert_rel(got, ref, tol, what):
+    e = rel_err_rowfloor(got, ref)
+    assert e <= tol, f"{what}: max relative error {e:.3e} > {tol:.1e}"
+    return e
+
+
+def bf16_ulps(got_bits: np.ndarray, ref: np.ndarray) -> int:
+    """Max distance in bf16 ulps between bf16 results and the nearest-even
+    bf16 rounding of the float64 reference (same sign assumed away from 0)."""
+    want = round_bf16(ref).astype(np.int64)
+    got = np.asarray(got_bits).astype(np.int64)
+    # map sign-magnitude bit patterns onto a monotone integer line
+    def line(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return int(np.max(np.abs(line(got) - line(want)))) if got.size else 0
+
+
+def assert_bf16(got_bits, ref, what, floor=1e-3):
+    """bf16 outputs against a float64 reference: each element within one bf16
+    ulp of the reference's nearest-even rounding, or within floor * rms(row of
+    the reference) where the sum cancels (near zero one bf16 ulp is smaller
+    than the binary32 accumulation error)."""
+    want = round_bf16(ref).astype(np.int64)
+    got = np.asarray(got_bits).astype(np.int64)
+    line = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    ulps = np.abs(line(got) - line(want))
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    near = np.abs(bf16_to_f64(got_bits) - ref) <= floor * rms
+    bad = (ulps > 1) & ~near
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp / {floor} rms; max ulps {int(ulps.max())}"
+
+
+def sync():
+    torch.cuda.synchronize()

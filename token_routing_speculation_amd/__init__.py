@@ -1,0 +1,290 @@
+"""MI355X-native MoE token routing and dispatch.
+
+A thin ctypes binding over ``libroute.so`` (declared in ``include/route.h``).
+Every function here only marshals arguments: it checks dtypes, devices and
+contiguity of torch tensors, passes their device pointers and the current
+HIP stream to the C entry point of the same name, and raises ``RouteError``
+on a non-zero status. All arithmetic runs in the library's HIP kernels; there
+is no fallback path. PyTorch is used only for device memory and streams.
+
+Outputs may be passed in (``out=``-style keyword arguments) or are allocated
+with ``torch.empty`` on the input's device. Workspaces likewise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RouteError", "lib", "library_path",
+    "route_predict", "route_lut_build", "srs_shuffle", "route_gate", "route_topk",
+    "lar_count", "moe_permute", "moe_combine", "route_qhidden", "route_estimator",
+    "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
+    "route_estimator_workspace_size", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libroute.so")
+
+# status codes and device error bits (include/route.h)
+ROUTE_OK = 0
+EBIT_TOKEN_RANGE, EBIT_DEST_RANGE, EBIT_EXPERT_RANGE, EBIT_INDEX_RANGE = 1, 2, 4, 8
+
+_p, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+# name -> (restype, argtypes), in the header's order
+EXPORTS = {
+    "route_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "route_predict": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _p]),
+    "route_lut_build": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _p]),
+    "srs_shuffle": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
+    "route_gate": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _p]),
+    "route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "lar_count": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
+    "moe_permute": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
+    "route_qhidden": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p]),
+    "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
+    "route_estimator_workspace_size": (_sz, [_i64, _i32]),
+    "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
+}
+
+
+class RouteError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({_status_str(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libroute.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m token_routing_speculation_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return lib().route_status_str(status).decode()
+    except Exception:  # pragma: no cover - only while the library is unusable
+        return "?"
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != ROUTE_OK:
+        raise RouteError(name, st)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str, numel: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, has {t.numel()}")
+    return t.data_ptr()
+
+
+def _opt(t, dtype, name, numel=None):
+    return None if t is None else _dev(t, dtype, name, numel)
+
+
+def _empty(shape, dtype, like: torch.Tensor):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def _bf16(t: torch.Tensor) -> torch.dtype:
+    # bf16 rows may be given as torch.bfloat16 or as their int16 bit patterns
+    return t.dtype if t.dtype in (torch.bfloat16, torch.int16) else torch.bfloat16
+
+
+# ------------------------------------------------------------------ entry points
+
+def route_predict(tok, lut, G, conf=None, prev2=None, prev1=None, ngram=None, conf_thr=128,
+                  dest=None, err=None, stream=None):
+    n = tok.numel()
+    dest = _empty((n,), torch.uint8, tok) if dest is None else dest
+    fb = conf is not None
+    _call("route_predict", _dev(tok, torch.int32, "tok"), n, _dev(lut, torch.uint8, "lut"),
+          _opt(conf, torch.uint8, "conf"), lut.numel(),
+          _opt(prev2, torch.uint8, "prev2", n if fb else None),
+          _opt(prev1, torch.uint8, "prev1", n if fb else None),
+          _opt(ngram, torch.uint8, "ngram", G * G if fb else None), G, conf_thr,
+          _dev(dest, torch.uint8, "dest", n), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return dest
+
+
+def route_lut_build(ids, idx, w, expert_cluster, G, lut, conf=None, err=None, stream=None):
+    n, K = idx.shape
+    _call("route_lut_build", _dev(ids, torch.int32, "ids", n), n, _dev(idx, torch.int32, "idx"),
+          _dev(w, torch.float32, "w", n * K), K, _dev(expert_cluster, torch.uint8, "expert_cluster"),
+          expert_cluster.numel(), G, _dev(lut, torch.uint8, "lut"),
+          _opt(conf, torch.uint8, "conf", lut.numel()), lut.numel(),
+          _opt(err, torch.int32, "err", 1), _stream(stream))
+    return lut, conf
+
+
+def srs_shuffle_workspace_size(n: int, G: int) -> int:
+    return int(lib().srs_shuffle_workspace_size(n, G))
+
+
+def srs_shuffle(partials, dest, G, out=None, offsets=None, row_of_src=None, src_of_row=None,
+                row_cluster=None, maps=True, ws=None, err=None, stream=None):
+    """partials [P][n][d] bf16 -> (out [n][d], offsets [G+1], row_of_src, src_of_row, row_cluster)."""
+    P, n, d = partials.shape
+    bt = _bf16(partials)
+    out = _empty((n, d), bt, partials) if out is None else out
+    offsets = _empty((G + 1,), torch.int32, partials) if offsets is None else offsets
+    if maps:
+        row_of_src = _empty((n,), torch.int32, partials) if row_of_src is None else row_of_src
+        src_of_row = _empty((n,), torch.int32, partials) if src_of_row is None else src_of_row
+        row_cluster = _empty((n,), torch.uint8, partials) if row_cluster is None else row_cluster
+    need = srs_shuffle_workspace_size(n, G)
+    ws = _empty((max(need, 1),), torch.uint8, partials) if ws is None else ws
+    _call("srs_shuffle", _dev(partials, bt, "partials"), P, n, d,
+          _opt(dest, torch.uint8, "dest", n), G, _dev(out, bt, "out", n * d),
+          _dev(offsets, torch.int32, "offsets", G + 1), _opt(row_of_src, torch.int32, "row_of_src", n),
+          _opt(src_of_row, torch.int32, "src_of_row", n), _opt(row_cluster, torch.uint8, "row_cluster", n),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return out, offsets, row_of_src, src_of_row, row_cluster
+
+
+def route_gate(x, w, logits=None, stream=None):
+    n, d = x.shape
+    E = w.shape[0]
+    logits = _empty((n, E), torch.float32, x) if logits is None else logits
+    _call("route_gate", _dev(x, _bf16(x), "x"), n, d, _dev(w, _bf16(w), "w", E * d), E,
+          _dev(logits, torch.float32, "logits", n * E), _stream(stream))
+    return logits
+
+
+def route_topk(logits, K, H=1, renorm=1, idx=None, weights=None, want_weights=True, stream=None):
+    n, E = logits.shape
+    idx = _empty((n, K), torch.int32, logits) if idx is None else idx
+    if want_weights and weights is None:
+        weights = _empty((n, K), torch.float32, logits)
+    _call("route_topk", _dev(logits, torch.float32, "logits"), n, E, K, H, renorm,
+          _dev(idx, torch.int32, "idx", n * K), _opt(weights, torch.float32, "weights", n * K),
+          _stream(stream))
+    return idx, weights
+
+
+def lar_count(idx, H, row_cluster, expert_cluster, local, stream=None):
+    n, K = idx.shape
+    _call("lar_count", _dev(idx, torch.int32, "idx"), n, K, H,
+          _dev(row_cluster, torch.uint8, "row_cluster", n * H),
+          _dev(expert_cluster, torch.uint8, "expert_cluster"), expert_cluster.numel(),
+          _dev(local, torch.int64, "local", 1), _stream(stream))
+    return local
+
+
+def moe_permute_workspace_size(n: int, K: int, E: int) -> int:
+    return int(lib().moe_permute_workspace_size(n, K, E))
+
+
+def moe_permute(idx, E, src=None, H=1, expert_offsets=None, slot_of_pair=None, pair_of_slot=None,
+                disp=None, ws=None, err=None, stream=None):
+    """idx [n][K]; src [H][n][d] bf16 (optional) -> offsets, slot_of_pair, pair_of_slot, disp."""
+    n, K = idx.shape
+    expert_offsets = _empty((E + 1,), torch.int32, idx) if expert_offsets is None else expert_offsets
+    slot_of_pair = _empty((n * K,), torch.int32, idx) if slot_of_pair is None else slot_of_pair
+    pair_of_slot = _empty((n * K,), torch.int32, idx) if pair_of_slot is None else pair_of_slot
+    d = 0
+    if src is not None:
+        if src.dim() == 2:
+            src = src.unsqueeze(0)
+        if src.shape[0] != H or src.shape[1] != n:
+            raise ValueError("src must be [H][n][d]")
+        d = src.shape[2]
+        disp = _empty((n * K, d), _bf16(src), idx) if disp is None else disp
+    need = moe_permute_workspace_size(n, K, E)
+    ws = _empty((max(need, 1),), torch.uint8, idx) if ws is None else ws
+    bt = _bf16(src) if src is not None else torch.bfloat16
+    _call("moe_permute", _dev(idx, torch.int32, "idx"), n, K, E, H, _opt(src, bt, "src"), d,
+          _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+          _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K),
+          _dev(pair_of_slot, torch.int32, "pair_of_slot", n * K),
+          _opt(disp, bt, "disp", n * K * d if src is not None else None),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return expert_offsets, slot_of_pair, pair_of_slot, disp
+
+
+def moe_combine(y, weights, slot_of_pair, out_row=None, out=None, out_dtype=torch.bfloat16,
+                err=None, stream=None):
+    n, K = weights.shape
+    d = y.shape[1]
+    code = {torch.bfloat16: 0, torch.int16: 0, torch.float32: 1}[out.dtype if out is not None else out_dtype]
+    if out is None:
+        out = _empty((n, d), out_dtype, y)
+    _call("moe_combine", _dev(y, _bf16(y), "y", n * K * d), _dev(weights, torch.float32, "weights"),
+          _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K), n, K, d,
+          _opt(out_row, torch.int32, "out_row", n), _dev(out, out.dtype, "out", n * d), code,
+          _opt(err, torch.int32, "err", 1), _stream(stream))
+    return out
+
+
+def route_qhidden(r, dvec, gamma=None, beta=None, eps=1e-5, q=None, stream=None):
+    n, d = r.shape
+    q = _empty((n, d), _bf16(r), r) if q is None else q
+    _call("route_qhidden", _dev(r, _bf16(r), "r"), _dev(dvec, torch.float32, "dvec", d),
+          _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
+          float(eps), _dev(q, _bf16(r), "q", n * d), _stream(stream))
+    return q
+
+
+def route_estimator_workspace_size(n: int, hd: int) -> int:
+    return int(lib().route_estimator_workspace_size(n, hd))
+
+
+def route_estimator(q, w1, b1, w2, b2, logits=None, ws=None, stream=None):
+    n, d = q.shape
+    hd = w1.shape[0]
+    E = w2.shape[0]
+    logits = _empty((n, E), torch.float32, q) if logits is None else logits
+    need = route_estimator_workspace_size(n, hd)
+    ws = _empty((max(need, 16),), torch.uint8, q) if ws is None else ws
+    _call("route_estimator", _dev(q, _bf16(q), "q"), n, d, _dev(w1, _bf16(w1), "w1", hd * d),
+          _dev(b1, torch.float32, "b1", hd), hd, _dev(w2, _bf16(w2), "w2", E * hd),
+          _dev(b2, torch.float32, "b2", E), E, _dev(logits, torch.float32, "logits", n * E),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+    return logits
+
+
+def hit_count(pred, truth, hits, stream=None):
+    n, K = pred.shape
+    _call("hit_count", _dev(pred, torch.int32, "pred"), _dev(truth, torch.int32, "truth", n * K),
+          n, K, _dev(hits, torch.int64, "hits", 1), _stream(stream))
+    return hits

@@ -1,0 +1,113 @@
+// lar_count and hit_count: the two quality counters of the path.
+// Local activation rate: "Speculative MoE" notes, section 7 glossary, and
+// the rho of the "Federation of Experts (FoE)" article. Prefetch hit rate:
+// "Speculating Experts Accelerates Inference for Mixture-of-Experts",
+// technical summary item 4. Integer counts, block-reduced, one 64-bit atomic
+// add per block over a capped grid-stride grid.
+#include "common.hpp"
+
+namespace route {
+
+constexpr int kCntThreads = 256;
+constexpr unsigned kCntMaxBlocks = 128;  // few blocks: few atomics on one address
+
+// Block-wide sum of one count per thread; thread 0 adds it to *dst.
+__device__ __forceinline__ void block_add(unsigned v, unsigned long long* dst) {
+  __shared__ unsigned part[kCntThreads / kWave];
+  v = wave_sum_u32(v);
+  if (lane_id() == 0) part[threadIdx.x / kWave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned t = 0;
+#pragma unroll
+    for (int w = 0; w < kCntThreads / kWave; ++w) t += part[w];
+    if (t) atomicAdd(dst, static_cast<unsigned long long>(t));
+  }
+}
+
+__global__ __launch_bounds__(kCntThreads) void lar_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int K, int H,
+    const uint8_t* __restrict__ row_cluster, const uint8_t* __restrict__ expert_cluster, int E,
+    unsigned long long* __restrict__ local) {
+  const int kg = K / H;
+  unsigned hit = 0;
+  for (int64_t p = static_cast<int64_t>(blockIdx.x) * kCntThreads + threadIdx.x; p < n * K;
+       p += static_cast<int64_t>(gridDim.x) * kCntThreads) {
+    const int64_t i = p / K;
+    const int k = static_cast<int>(p - i * K);
+    const int e = idx[p];
+    if (e >= 0 && e < E) hit += expert_cluster[e] == row_cluster[i * H + k / kg] ? 1u : 0u;
+  }
+  block_add(hit, local);
+}
+
+__global__ __launch_bounds__(kCntThreads) void hit_kernel(const int32_t* __restrict__ pred,
+                                                          const int32_t* __restrict__ truth,
+                                                          int64_t n, int K,
+                                                          unsigned long long* __restrict__ hits) {
+  unsigned cnt = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCntThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kCntThreads) {
+    int t[kMaxK];
+    int p[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      t[k] = k < K ? truth[i * K + k] : 0;
+      p[k] = k < K ? pred[i * K + k] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      if (k >= K) break;
+      bool in_truth = false, seen = false;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < K && t[j] == p[k]) in_truth = true;
+        if (j < k && p[j] == p[k]) seen = true;
+      }
+      cnt += (in_truth && !seen) ? 1u : 0u;
+    }
+  }
+  block_add(cnt, hits);
+}
+
+}  // namespace route
+
+using namespace route;
+
+ROUTE_API int lar_count(const int32_t* idx, int64_t n, int32_t K, int32_t H,
+                        const uint8_t* row_cluster, const uint8_t* expert_cluster, int32_t E,
+                        unsigned long long* local, hipStream_t s) {
+  if (n < 0 || K < 1 || H < 1 || K % H != 0 || E < 1) return ROUTE_ERR_SHAPE;
+  if (K > kMaxK || E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!idx || !row_cluster || !expert_cluster || !local) return ROUTE_ERR_NULL;
+  const unsigned grid = ceil_div(n * K, kCntThreads) < kCntMaxBlocks ? ceil_div(n * K, kCntThreads)
+                                                                      : kCntMaxBlocks;
+  lar_kernel<<<grid, kCntThreads, 0, s>>>(idx, n, K, H, row_cluster, expert_cluster, E, local);
+  return launch_status();
+}
+
+ROUTE_API int hit_count(const int32_t* pred, const int32_t* truth, int64_t n, int32_t K,
+                        unsigned long long* hits, hipStream_t s) {
+  if (n < 0 || K < 1) return ROUTE_ERR_SHAPE;
+  if (K > kMaxK) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!pred || !truth || !hits) return ROUTE_ERR_NULL;
+  const unsigned grid = ceil_div(n, kCntThreads) < kCntMaxBlocks ? ceil_div(n, kCntThreads)
+                                                                 : kCntMaxBlocks;
+  hit_kernel<<<grid, kCntThreads, 0, s>>>(pred, truth, n, K, hits);
+  return launch_status();
+}
+
+ROUTE_API const char* route_status_str(int status) {
+  switch (status) {
+    case ROUTE_OK: return "ok";
+    case ROUTE_ERR_NULL: return "a required pointer is NULL";
+    case ROUTE_ERR_SHAPE: return "invalid shape or argument";
+    case ROUTE_ERR_ALIGN: return "row data pointer not 16-byte aligned";
+    case ROUTE_ERR_UNSUPPORTED: return "size beyond the supported maximum";
+    case ROUTE_ERR_WORKSPACE: return "workspace missing or too small";
+    case ROUTE_ERR_HIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}

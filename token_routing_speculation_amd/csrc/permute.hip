@@ -1,0 +1,80 @@
+// moe_permute: expert-contiguous dispatch on one GPU. "Speculative MoE"
+// notes, section 1: dispatch sends each token's activation to its K experts;
+// on one device that is a stable counting sort of the (token, expert) pairs
+// by expert (csort.hpp) followed by a row scatter. With H groups ("Federation
+// of Experts (FoE)" article) pair (i, k) reads the group-(k / (K/H)) row of
+// token i, so each source row is read once and written K/H times.
+#include "common.hpp"
+#include "csort.hpp"
+
+namespace route {
+
+constexpr int kPermThreads = 256;
+
+// One wave per (token i, group h): read src[h][i], write it to the slots of
+// the K/H pairs (i, h*kg .. h*kg + kg - 1).
+__global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __restrict__ src,
+                                                             int64_t n, int K, int H, int d,
+                                                             const int* __restrict__ slot_of_pair,
+                                                             uint16_t* __restrict__ disp) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + threadIdx.x / kWave;
+  if (g >= n * H) return;
+  const int64_t i = g / H;
+  const int h = static_cast<int>(g - i * H);
+  const int kg = K / H;
+  const int64_t nslots = n * K;
+  int slot[kMaxK];
+#pragma unroll
+  for (int t = 0; t < kMaxK; ++t) {
+    slot[t] = -1;
+    if (t < kg) {
+      const int sl = slot_of_pair[i * K + h * kg + t];
+      slot[t] = (sl >= 0 && sl < nslots) ? sl : -1;
+    }
+  }
+  const int lane = lane_id();
+  const int nv = d >> 3;
+  const uint16_t* row = src + (static_cast<size_t>(h) * n + i) * d;
+  for (int v = lane; v < nv; v += kWave) {
+    const u32x4 x = ld16_stream(row + 8 * v);
+#pragma unroll
+    for (int t = 0; t < kMaxK; ++t)
+      if (t < kg && slot[t] >= 0) st16_stream(disp + static_cast<size_t>(slot[t]) * d + 8 * v, x);
+  }
+}
+
+}  // namespace route
+
+using namespace route;
+
+ROUTE_API size_t moe_permute_workspace_size(int64_t n, int32_t K, int32_t E) {
+  if (n < 0 || K < 1 || E < 1 || E > kMaxExperts) return 0;
+  return csort_ws_bytes(n * K, E);
+}
+
+ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                          const uint16_t* src, int32_t d, int32_t* expert_offsets,
+                          int32_t* slot_of_pair, int32_t* pair_of_slot, uint16_t* disp,
+                          void* ws, size_t ws_bytes, uint32_t* err, hipStream_t s) {
+  if (n < 0 || K < 1 || E < 1 || H < 1 || K % H != 0) return ROUTE_ERR_SHAPE;
+  if (n * static_cast<int64_t>(K) >= (int64_t(1) << 31)) return ROUTE_ERR_SHAPE;
+  if (E > kMaxExperts || K > kMaxK) return ROUTE_ERR_UNSUPPORTED;
+  if (!expert_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(E + 1, 256), 256, 0, s>>>(expert_offsets, E + 1, 0);
+    return launch_status();
+  }
+  if (!idx || !slot_of_pair || !pair_of_slot) return ROUTE_ERR_NULL;
+  if ((src == nullptr) != (disp == nullptr)) return ROUTE_ERR_NULL;
+  if (src) {
+    if (d < 8 || d % 8 != 0) return ROUTE_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(disp)) return ROUTE_ERR_ALIGN;
+  }
+  if (!ws || ws_bytes < moe_permute_workspace_size(n, K, E)) return ROUTE_ERR_WORKSPACE;
+  int st = csort_launch<int32_t>(idx, n * K, E, expert_offsets, slot_of_pair, pair_of_slot,
+                                 nullptr, ws, err, ROUTE_EBIT_EXPERT_RANGE, s);
+  if (st != ROUTE_OK || !src || n == 0) return st;
+  const unsigned grid = ceil_div(n * H, kPermThreads / kWave);
+  permute_move<<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair, disp);
+  return launch_status();
+}

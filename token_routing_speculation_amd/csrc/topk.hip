@@ -1,0 +1,221 @@
+// route_topk: softmax + top-K of each token's router logits, plain or
+// grouped ("Federation of Experts (FoE)" article, grouped MoE block: group h
+// takes its own top k/H among experts [h*E/H, (h+1)*E/H)).
+//
+// A token is handled by a segment of S lanes of one wave (S = 4..64, a power
+// of two >= E up to 64; for E > 64, S = 64 and lane s holds the V = E/64
+// logits of columns s, s+64, ...). Logits become 32-bit orderable keys (the
+// float bits with the sign folded so unsigned order is float order; -0.0 is
+// folded onto +0.0 first). Each of the K rounds takes a segment-wide max of
+// the keys with DPP row operations (quad permutes and row mirrors, no LDS
+// traffic), then resolves equal keys to the lowest expert index with a
+// ballot; the chosen key is then removed (set to 0, below every logit).
+#include "common.hpp"
+
+namespace route {
+
+constexpr int kTopkThreads = 256;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i inside each 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i inside each 16
+
+// Max over each aligned segment of S lanes; every lane of the segment gets it.
+template <int S>
+__device__ __forceinline__ uint32_t seg_max(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  if (S >= 8) v = max(v, dpp<kDppHalfMirror>(v));
+  if (S >= 16) v = max(v, dpp<kDppMirror>(v));
+  if (S == 32) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 16, kWave)));
+  if (S == 64) {
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    v = max(max(a, b), max(c, d));
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+template <int S, int V>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ logits,
+                                                            int64_t n, int E, int K, int H,
+                                                            int renorm, int* __restrict__ idx,
+                                                            float* __restrict__ wout) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = lane & (S - 1);
+  const int seg_base = lane & ~(S - 1);
+  const int64_t tok = (static_cast<int64_t>(blockIdx.x) * kTopkThreads + threadIdx.x) / S;
+  const bool active = tok < n;  // inactive lanes still join the cross-lane steps
+  const float* row = logits + (active ? tok : 0) * static_cast<int64_t>(E);
+
+  uint32_t key[V];
+  float val[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = s + S * v;
+    val[v] = (active && c < E) ? row[c] : 0.f;
+    key[v] = (active && c < E) ? order_key(val[v]) : 0u;  // 0: never chosen
+  }
+
+  const int eg = E / H;
+  const int kg = K / H;
+  float selv[kMaxK];
+  int selc[kMaxK];
+#pragma unroll
+  for (int r = 0; r < kMaxK; ++r) {
+    if (r < K) {
+      const int lo = (r / kg) * eg;
+      const int hi = lo + eg;
+      uint32_t best = 0u;
+      int bcol = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int c = s + S * v;
+        if (c >= lo && c < hi && key[v] > best) {  // strict: lowest v on equal keys
+          best = key[v];
+          bcol = c;
+        }
+      }
+      const uint32_t m = seg_max<S>(best);
+      const uint64_t tie = __ballot(best == m && best != 0u);
+      int col;
+      if (V == 1) {
+        // one column per lane: the lowest tied lane of the segment holds the
+        // lowest column
+        const uint64_t mine = (tie >> seg_base) & (S == 64 ? ~0ull : ((1ull << S) - 1));
+        col = __builtin_ctzll(mine);
+      } else {
+        // S == 64: one tied lane is the common case; otherwise take the
+        // smallest column among the tied lanes
+        if (__popcll(tie) == 1)
+          col = __builtin_amdgcn_readlane(bcol, __builtin_ctzll(tie));
+        else
+          col = static_cast<int>(wave_min(best == m ? static_cast<uint32_t>(bcol) : 0xffffffffu));
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (s + S * v == col) key[v] = 0u;
+      selc[r] = col;
+      selv[r] = key_float(m);
+    }
+  }
+
+  float wt[kMaxK];
+  if (renorm) {
+    // softmax over each group's chosen logits; the group's first pick is its max
+    float mg = 0.f, z = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+      if (r < K) {
+        if (r % kg == 0) {
+          mg = selv[r];
+          z = 0.f;
+        }
+        wt[r] = expf(selv[r] - mg);
+        z += wt[r];
+        if (r % kg == kg - 1) {
+          // close the group: r - kg + 1 .. r share z
+#pragma unroll
+          for (int q = 0; q < kMaxK; ++q)
+            if (q <= r && q > r - kg) wt[q] = wt[q] / z;
+        }
+      }
+    }
+  } else {
+    float mall = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r)
+      if (r < K && r % kg == 0) mall = fmaxf(mall, selv[r]);
+    float zl = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c = s + S * v;
+      if (active && c < E) zl += expf(val[v] - mall);
+    }
+#pragma unroll
+    for (int o = S / 2; o > 0; o >>= 1) zl += __shfl_xor(zl, o, kWave);
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r)
+      if (r < K) wt[r] = expf(selv[r] - mall) / zl;
+  }
+
+  if (active && s == 0) {
+    int* io = idx + tok * K;
+    float* wo = wout ? wout + tok * K : nullptr;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+      if (r < K) {
+        io[r] = selc[r];
+        if (wo) wo[r] = wt[r];
+      }
+    }
+  }
+}
+
+template <int S, int V>
+static void launch_topk(const float* logits, int64_t n, int E, int K, int H, int renorm,
+                        int* idx, float* w, hipStream_t s) {
+  const unsigned grid = ceil_div(n * S, kTopkThreads);
+  topk_kernel<S, V><<<grid, kTopkThreads, 0, s>>>(logits, n, E, K, H, renorm, idx, w);
+}
+
+}  // namespace route
+
+using namespace route;
+
+ROUTE_API int route_topk(const float* logits, int64_t n, int32_t E, int32_t K, int32_t H,
+                         int32_t renorm, int32_t* idx, float* weights, hipStream_t s) {
+  if (n < 0 || E < 1 || K < 1 || H < 1 || E % H != 0 || K % H != 0 || K / H > E / H)
+    return ROUTE_ERR_SHAPE;
+  if (E > kMaxExperts || K > kMaxK) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!logits || !idx) return ROUTE_ERR_NULL;
+  if (E <= 4)
+    launch_topk<4, 1>(logits, n, E, K, H, renorm, idx, weights, s);
+  else if (E <= 8)
+    launch_topk<8, 1>(logits, n, E, K, H, renorm, idx, weights, s);
+  else if (E <= 16)
+    launch_topk<16, 1>(logits, n, E, K, H, renorm, idx, weights, s);
+  else if (E <= 32)
+    launch_topk<32, 1>(logits, n, E, K, H, renorm, idx, weights, s);
+  else {
+    switch ((E + 63) / 64) {
+#define ROUTE_V_CASE(v) \
+  case v: launch_topk<64, v>(logits, n, E, K, H, renorm, idx, weights, s); break;
+      ROUTE_V_CASE(1) ROUTE_V_CASE(2) ROUTE_V_CASE(3) ROUTE_V_CASE(4) ROUTE_V_CASE(5)
+      ROUTE_V_CASE(6) ROUTE_V_CASE(7) ROUTE_V_CASE(8) ROUTE_V_CASE(9) ROUTE_V_CASE(10)
+      ROUTE_V_CASE(11) ROUTE_V_CASE(12) ROUTE_V_CASE(13) ROUTE_V_CASE(14) ROUTE_V_CASE(15)
+      ROUTE_V_CASE(16)
+#undef ROUTE_V_CASE
+      default: return ROUTE_ERR_UNSUPPORTED;
+    }
+  }
+  return launch_status();
+}

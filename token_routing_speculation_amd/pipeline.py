@@ -1,0 +1,232 @@
+"""Whole passes of the routing path, with every buffer allocated up front.
+
+``RoutePass``: predict -> SRS -> gate -> top-K -> LAR -> permute -> combine
+(identity experts: the combine reads the dispatched rows themselves), the
+s-MoE layer of the "Speculative MoE" notes (section 3.1 and Figure 3's online
+path) on one GPU.
+
+``FoEPass``: cross-group reduce of the H group activations -> gate ->
+grouped top-k/H -> LAR -> permute from the group activations -> combine
+(cross-group sum), the grouped block of the "Federation of Experts (FoE)"
+article.
+
+``PredictorPass``: q_l -> next gate (or the estimator on early layers) ->
+top-K, and the next layer's true top-K -> hit count ("Speculating Experts
+Accelerates Inference for Mixture-of-Experts", items 2.A, 2.C and 4).
+
+Inputs are host numpy arrays from the ``synth`` generator; they are copied to
+the device once, in the constructor. ``step()`` enqueues one pass on the
+current stream and allocates nothing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (route_predict, route_lut_build, srs_shuffle, route_gate, route_topk, lar_count,
+               moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
+               srs_shuffle_workspace_size, moe_permute_workspace_size,
+               route_estimator_workspace_size)
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """device bf16 tensor -> host uint16 bit patterns."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def build_tables_device(inp: dict, device="cuda"):
+    """Token -> cluster table (and confidence) from each occurring id's
+    noiseless routing: gate + top-K of bf16(base[id]) reduced per cluster by
+    route_lut_build ("Speculative MoE" notes, section 4.1)."""
+    lut = to_device(inp["lut"], device)
+    conf = to_device(inp["conf"], device) if "conf" in inp else None
+    if inp.get("lut_mode") != "routing":
+        return lut, conf
+    base = to_device(inp["base_present"], device)
+    w = to_device(inp["w"], device)
+    logits = route_gate(base, w)
+    idx, wt = route_topk(logits, inp["K"], 1, 1)
+    ids = to_device(inp["ids_present"], device)
+    ec = to_device(inp["expert_cluster"], device)
+    route_lut_build(ids, idx, wt, ec, inp["G"], lut, conf)
+    return lut, conf
+
+
+class RoutePass:
+    def __init__(self, inp: dict, lut=None, conf=None, device="cuda", out_dtype=torch.bfloat16):
+        self.N, self.d, self.E, self.K = inp["N"], inp["d"], inp["E"], inp["K"]
+        self.P, self.G = inp["P"], inp["G"]
+        N, d, E, K, P, G = self.N, self.d, self.E, self.K, self.P, self.G
+        dev = device
+        self.tok = to_device(inp["tok"], dev)
+        self.partials = to_device(inp["partials"], dev)
+        self.w = to_device(inp["w"], dev)
+        self.expert_cluster = to_device(inp["expert_cluster"], dev)
+        if lut is None:
+            lut, conf = build_tables_device(inp, dev)
+        self.lut = lut if isinstance(lut, torch.Tensor) else to_device(lut, dev)
+        self.conf = None
+        self.fallback = conf is not None and "ngram" in inp
+        if self.fallback:
+            self.conf = conf if isinstance(conf, torch.Tensor) else to_device(conf, dev)
+            self.prev2 = to_device(inp["prev2"], dev)
+            self.prev1 = to_device(inp["prev1"], dev)
+            self.ngram = to_device(inp["ngram"].reshape(-1), dev)
+        self.conf_thr = 128
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.dest = e((N,), torch.uint8)
+        self.x = e((N, d), torch.bfloat16)
+        self.cluster_offsets = e((G + 1,), torch.int32)
+        self.row_of_src = e((N,), torch.int32)
+        self.src_of_row = e((N,), torch.int32)
+        self.row_cluster = e((N,), torch.uint8)
+        self.ws_srs = e((max(srs_shuffle_workspace_size(N, G), 1),), torch.uint8)
+        self.logits = e((N, E), torch.float32)
+        self.idx = e((N, K), torch.int32)
+        self.weights = e((N, K), torch.float32)
+        self.local = torch.zeros((1,), dtype=torch.int64, device=dev)
+        self.expert_offsets = e((E + 1,), torch.int32)
+        self.slot_of_pair = e((N * K,), torch.int32)
+        self.pair_of_slot = e((N * K,), torch.int32)
+        self.disp = e((N * K, d), torch.bfloat16)
+        self.ws_perm = e((max(moe_permute_workspace_size(N, K, E), 1),), torch.uint8)
+        self.out = e((N, d), out_dtype)
+        self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def predict(self):
+        if self.fallback:
+            route_predict(self.tok, self.lut, self.G, self.conf, self.prev2, self.prev1, self.ngram,
+                          self.conf_thr, dest=self.dest, err=self.err)
+        else:
+            route_predict(self.tok, self.lut, self.G, dest=self.dest, err=self.err)
+
+    def srs(self):
+        srs_shuffle(self.partials, self.dest, self.G, out=self.x, offsets=self.cluster_offsets,
+                    row_of_src=self.row_of_src, src_of_row=self.src_of_row,
+                    row_cluster=self.row_cluster, ws=self.ws_srs, err=self.err)
+
+    def gate(self):
+        route_gate(self.x, self.w, logits=self.logits)
+
+    def topk(self):
+        route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
+
+    def lar(self):
+        lar_count(self.idx, 1, self.row_cluster, self.expert_cluster, self.local)
+
+    def permute(self):
+        moe_permute(self.idx, self.E, self.x, 1, expert_offsets=self.expert_offsets,
+                    slot_of_pair=self.slot_of_pair, pair_of_slot=self.pair_of_slot,
+                    disp=self.disp, ws=self.ws_perm, err=self.err)
+
+    def combine(self):
+        moe_combine(self.disp, self.weights, self.slot_of_pair, out_row=self.src_of_row,
+                    out=self.out, err=self.err)
+
+    STAGES = ("predict", "srs", "gate", "topk", "lar", "permute", "combine")
+
+    def step(self):
+        for s in self.STAGES:
+            getattr(self, s)()
+
+
+class FoEPass:
+    def __init__(self, inp: dict, device="cuda", out_dtype=torch.bfloat16):
+        self.N, self.d, self.E, self.K, self.H, self.G = (inp["N"], inp["d"], inp["E"], inp["K"],
+                                                          inp["H"], inp["G"])
+        N, d, E, K, H = self.N, self.d, self.E, self.K, self.H
+        dev = device
+        self.xg = to_device(inp["x"], dev)
+        self.w = to_device(inp["w"], dev)
+        self.expert_cluster = to_device(inp["expert_cluster"], dev)
+        self.row_cluster = to_device(inp["row_cluster"], dev)
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.r_full = e((N, d), torch.bfloat16)
+        self.cluster_offsets = e((2,), torch.int32)
+        self.ws_srs = e((16,), torch.uint8)
+        self.logits = e((N, E), torch.float32)
+        self.idx = e((N, K), torch.int32)
+        self.weights = e((N, K), torch.float32)
+        self.local = torch.zeros((1,), dtype=torch.int64, device=dev)
+        self.expert_offsets = e((E + 1,), torch.int32)
+        self.slot_of_pair = e((N * K,), torch.int32)
+        self.pair_of_slot = e((N * K,), torch.int32)
+        self.disp = e((N * K, d), torch.bfloat16)
+        self.ws_perm = e((max(moe_permute_workspace_size(N, K, E), 1),), torch.uint8)
+        self.out = e((N, d), out_dtype)
+        self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def reduce(self):
+        srs_shuffle(self.xg, None, 1, out=self.r_full, offsets=self.cluster_offsets, maps=False,
+                    ws=self.ws_srs, err=self.err)
+
+    def gate(self):
+        route_gate(self.r_full, self.w, logits=self.logits)
+
+    def topk(self):
+        route_topk(self.logits, self.K, self.H, 1, idx=self.idx, weights=self.weights)
+
+    def lar(self):
+        lar_count(self.idx, self.H, self.row_cluster, self.expert_cluster, self.local)
+
+    def permute(self):
+        moe_permute(self.idx, self.E, self.xg, self.H, expert_offsets=self.expert_offsets,
+                    slot_of_pair=self.slot_of_pair, pair_of_slot=self.pair_of_slot,
+                    disp=self.disp, ws=self.ws_perm, err=self.err)
+
+    def combine(self):
+        moe_combine(self.disp, self.weights, self.slot_of_pair, out=self.out, err=self.err)
+
+    STAGES = ("reduce", "gate", "topk", "lar", "permute", "combine")
+
+    def step(self):
+        for s in self.STAGES:
+            getattr(self, s)()
+
+
+class PredictorPass:
+    """One source layer of the q_l predictor; ``load(layer)`` swaps inputs."""
+
+    def __init__(self, N, d, E, K, hd, device="cuda"):
+        self.N, self.d, self.E, self.K, self.hd = N, d, E, K, hd
+        dev = device
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.q = e((N, d), torch.bfloat16)
+        self.logits = e((N, E), torch.float32)
+        self.true_logits = e((N, E), torch.float32)
+        self.pred = e((N, K), torch.int32)
+        self.truth = e((N, K), torch.int32)
+        self.hits = torch.zeros((1,), dtype=torch.int64, device=dev)
+        self.ws = e((max(route_estimator_workspace_size(N, hd), 16),), torch.uint8)
+        self.device = dev
+        self.layer = None
+
+    def load(self, layer: dict):
+        dev = self.device
+        self.layer = {k: (to_device(v, dev) if isinstance(v, np.ndarray) else v)
+                      for k, v in layer.items()}
+        return self
+
+    def truth_step(self):
+        """Layer l+1's own routing (not part of the predictor's pass)."""
+        L = self.layer
+        route_gate(L["s_next"], L["w_next"], logits=self.true_logits)
+        route_topk(self.true_logits, self.K, 1, 1, idx=self.truth, want_weights=False)
+
+    def step(self):
+        L = self.layer
+        route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
+        if L["estimator"]:
+            route_estimator(self.q, L["w1"], L["b1"], L["w2"], L["b2"], logits=self.logits, ws=self.ws)
+        else:
+            route_gate(self.q, L["w_next"], logits=self.logits)
+        route_topk(self.logits, self.K, 1, 1, idx=self.pred, want_weights=False)
+        hit_count(self.pred, self.truth, self.hits)
