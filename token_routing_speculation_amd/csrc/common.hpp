@@ -76,7 +76,25 @@ __device__ __forceinline__ unsigned wave_sum_u32(unsigned v) {
   return v;
 }
 
+// Wave-wide integer sum, returned to every lane (DPP row reductions, then
+// the four row sums combined through scalar reads).
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot prove threadIdx.x / 64 uniform by itself, and control flow
+// or addresses derived from it would otherwise be treated as divergent.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
 
 __device__ __forceinline__ void set_err(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);

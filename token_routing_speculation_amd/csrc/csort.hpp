@@ -1,12 +1,13 @@
-// Stable counting sort of small integer keys, in three launches:
-//   1. csort_hist:  per-chunk histograms in LDS, written bin-major [B][nchunks];
-//   2. csort_scan:  one workgroup scans the bin-major table (exclusive), so
-//                   base[b][c] is where chunk c's first key of bin b lands, and
-//                   writes the bin offsets [B+1];
-//   3. csort_rank:  per chunk, keys are ranked in order (256 at a time) with a
-//                   ballot-based match of equal keys inside each wave, a prefix
-//                   over the block's waves and a running per-bin count, giving
-//                   each key its stable position.
+// Stable counting sort of small integer keys, in two launches:
+//   1. csort_hist:  per-chunk histograms in LDS, written chunk-major
+//                   [nchunks][B] (at most 64 chunks);
+//   2. csort_rank:  each chunk's block derives where its keys of each bin
+//                   start (all earlier bins, plus this bin's count in earlier
+//                   chunks): one thread per bin loads the bin's count in
+//                   every chunk at once and sums them; block 0 also writes
+//                   the bin offsets [B+1]. Each wave then ranks one quarter
+//                   of the chunk (ballot-matched equal keys, wave-private
+//                   running counts), giving each key its stable position.
 // Keys >= B (or negative) are skipped: flagged in err, position -1.
 #pragma once
 
@@ -17,13 +18,14 @@ namespace {  // internal linkage: each translation unit gets its own copy
 
 constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kScanThreads = 1024;
-constexpr int kMaxScanEntries = 65536;
+constexpr int kMaxChunks = 64;
+constexpr int kBatch = 8;  // keys per thread loaded ahead of use (histogram)  // one lane per chunk when summing a bin's counts
 
-// Keys per chunk: 1024, doubled until the bin-major table fits one scan block.
+// Keys per chunk: a power of two >= 1024 giving at most kMaxChunks chunks.
 inline int64_t csort_chunk(int64_t n, int B) {
+  (void)B;
   int64_t chunk = 1024;
-  while (static_cast<int64_t>(B) * ((n + chunk - 1) / chunk) > kMaxScanEntries) chunk *= 2;
+  while ((n + chunk - 1) / chunk > kMaxChunks) chunk *= 2;
   return chunk;
 }
 
@@ -32,10 +34,10 @@ inline int64_t csort_nchunks(int64_t n, int B) {
   return n == 0 ? 0 : (n + c - 1) / c;
 }
 
-// Bytes of scratch: hist and base tables, 256-byte aligned each.
+// Bytes of scratch: the chunk-major histogram table, 256-byte aligned.
 inline size_t csort_ws_bytes(int64_t n, int B) {
   size_t t = static_cast<size_t>(B) * static_cast<size_t>(csort_nchunks(n, B)) * sizeof(int);
-  return 2 * align_up(t, 256);
+  return align_up(t, 256);
 }
 
 template <typename KeyT>
@@ -59,111 +61,199 @@ __global__ __launch_bounds__(kSortThreads) void csort_hist(const KeyT* __restric
   const int64_t lo = c * chunk;
   const int64_t hi = lo + chunk < n ? lo + chunk : n;
   bool bad = false;
-  for (int64_t j = lo + threadIdx.x; j < hi; j += kSortThreads) {
-    uint32_t k = key_u32<KeyT>(keys[j]);
-    if (k < static_cast<uint32_t>(B))
-      atomicAdd(&h[k], 1);
-    else
-      bad = true;
+  // keys are loaded kBatch at a time before any is counted, so the loads
+  // overlap instead of each waiting behind the previous count
+  for (int64_t j0 = lo + threadIdx.x; j0 < hi; j0 += kBatch * kSortThreads) {
+    uint32_t k[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t j = j0 + q * kSortThreads;
+      k[q] = j < hi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (k[q] < static_cast<uint32_t>(B))
+        atomicAdd(&h[k[q]], 1);
+      else if (j0 + q * kSortThreads < hi)
+        bad = true;
+    }
   }
   if (bad) set_err(err, ebit);
   __syncthreads();
-  for (int b = threadIdx.x; b < B; b += kSortThreads)
-    hist[static_cast<int64_t>(b) * nchunks + c] = h[b];
+  for (int b = threadIdx.x; b < B; b += kSortThreads) hist[c * B + b] = h[b];
 }
 
-// Exclusive scan of the bin-major table (M = B * nchunks entries) by one
-// workgroup; also writes offsets[b] = first slot of bin b, offsets[B] = total.
-__global__ __launch_bounds__(kScanThreads) void csort_scan(const int* __restrict__ hist, int M,
-                                                           int B, int nchunks,
-                                                           int* __restrict__ base,
-                                                           int* __restrict__ offsets) {
-  __shared__ int part[kScanThreads];
-  const int t = threadIdx.x;
-  const int per = (M + kScanThreads - 1) / kScanThreads;
-  const int lo = t * per;
-  const int hi = lo + per < M ? lo + per : M;
-  int s = 0;
-  for (int j = lo; j < hi; ++j) s += hist[j];
-  part[t] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int o = 1; o < kScanThreads; o <<= 1) {
-    int v = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+// Lanes of this wave holding the same valid key as this lane (match by
+// ballots over the key bits), and this lane's rank among them.
+__device__ __forceinline__ uint64_t match_key(uint32_t k, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = valid && ((k >> bit) & 1u);
+    const uint64_t bs = __ballot(set);
+    m &= set ? bs : ~bs;
   }
-  int run = t == 0 ? 0 : part[t - 1];
-  for (int j = lo; j < hi; ++j) {
-    base[j] = run;
-    if (nchunks > 0 && j % nchunks == 0) offsets[j / nchunks] = run;
-    run += hist[j];
-  }
-  if (t == kScanThreads - 1) offsets[B] = part[kScanThreads - 1];
+  return m;
 }
 
 // Ranks the keys of chunk blockIdx.x. fwd[j] = position of key j,
 // inv[pos] = j, inv_key[pos] = key (inv_key nullable).
+//
+// The chunk is split into four contiguous quarters, one per wave. Pass 1:
+// each wave counts its quarter per bin into its own LDS row (per 64-key
+// tile, the lowest lane of each key's match adds the match size). After one
+// barrier the four rows become per-wave starting positions (the chunk's base
+// for the bin plus the counts of the earlier quarters). Pass 2: each wave
+// walks its quarter again in order; a key's position is its wave's running
+// start for the bin plus its rank among equal keys in the tile, then the
+// lowest lane advances the start. Waves touch only their own LDS row, in
+// program order, so pass 2 needs no barriers.
 template <typename KeyT>
 __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restrict__ keys,
                                                            int64_t n, int B, int nbits,
                                                            int64_t chunk, int nchunks,
-                                                           const int* __restrict__ base,
+                                                           const int* __restrict__ hist,
+                                                           int* __restrict__ offsets,
                                                            int* __restrict__ fwd,
                                                            int* __restrict__ inv,
                                                            uint8_t* __restrict__ inv_key) {
   __shared__ int sbase[kMaxExperts];
-  __shared__ int srun[kMaxExperts];
-  __shared__ int wcnt[kSortWaves][kMaxExperts];
+  __shared__ int stot[kMaxExperts];
+  __shared__ int wrow[kSortWaves][kMaxExperts];
+  __shared__ int stotal;
   const int t = threadIdx.x;
-  const int w = t / kWave;
+  const int w = wave_id();
   const int lane = t & (kWave - 1);
-  const int64_t c = blockIdx.x;
+  const int c = blockIdx.x;
   for (int b = t; b < B; b += kSortThreads) {
-    sbase[b] = base[static_cast<int64_t>(b) * nchunks + c];
-    srun[b] = 0;
 #pragma unroll
-    for (int v = 0; v < kSortWaves; ++v) wcnt[v][b] = 0;
+    for (int v = 0; v < kSortWaves; ++v) wrow[v][b] = 0;
+  }
+  // per bin: total count, and the count in chunks before this one. One bin
+  // per thread; its (at most kMaxChunks) counts are all loaded before any is
+  // added, so the loads overlap.
+  for (int b = t; b < B; b += kSortThreads) {
+    int v[kMaxChunks];
+#pragma unroll
+    for (int q = 0; q < kMaxChunks; ++q) v[q] = q < nchunks ? hist[q * B + b] : 0;
+    int tot = 0, pre = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxChunks; ++q) {
+      tot += v[q];
+      pre += q < c ? v[q] : 0;
+    }
+    sbase[b] = pre;
+    stot[b] = tot;
   }
   __syncthreads();
-  const int64_t lo = c * chunk;
-  const int64_t hi = lo + chunk < n ? lo + chunk : n;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t j0 = lo; j0 < hi; j0 += kSortThreads) {
-    const int64_t j = j0 + t;
-    uint32_t k = 0xffffffffu;
-    if (j < hi) k = key_u32<KeyT>(keys[j]);
-    const bool valid = k < static_cast<uint32_t>(B);
-    // lanes of this wave holding the same valid key
-    uint64_t m = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((k >> bit) & 1u);
-      const uint64_t bs = __ballot(set);
-      m &= set ? bs : ~bs;
-    }
-    const int rank = __popcll(m & below);
-    const int total = __popcll(m);
-    const bool leader = valid && rank == 0;
-    if (leader) wcnt[w][k] = total;
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
+  // exclusive scan of the bin totals by wave 0 (each lane a contiguous run)
+  if (w == 0) {
+    const int per = (B + kWave - 1) / kWave;
+    const int lo = lane * per;
+    const int hi = lo + per < B ? lo + per : B;
+    int local = 0;
+    for (int b = lo; b < hi; ++b) local += stot[b];
+    int incl = local;
 #pragma unroll
-      for (int v = 0; v < kSortWaves; ++v) pre += v < w ? wcnt[v][k] : 0;
-      const int pos = sbase[k] + srun[k] + pre + rank;
-      fwd[j] = pos;
-      inv[pos] = static_cast<int>(j);
-      if (inv_key) inv_key[pos] = static_cast<uint8_t>(k);
-    } else if (j < hi) {
-      fwd[j] = -1;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
     }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&srun[k], total);
-      wcnt[w][k] = 0;
+    int run = incl - local;
+    for (int b = lo; b < hi; ++b) {
+      const int v = stot[b];
+      stot[b] = run;
+      run += v;
     }
-    __syncthreads();
+    if (lane == kWave - 1) stotal = incl;
+  }
+  __syncthreads();
+  for (int b = t; b < B; b += kSortThreads) {
+    if (c == 0) offsets[b] = stot[b];
+    sbase[b] += stot[b];
+  }
+  if (c == 0 && t == 0) offsets[B] = stotal;
+
+  // this wave's quarter of the chunk
+  const int64_t clo = static_cast<int64_t>(c) * chunk;
+  const int64_t chi = clo + chunk < n ? clo + chunk : n;
+  const int64_t quarter = chunk / kSortWaves;
+  const int64_t qlo = clo + w * quarter;
+  const int64_t qhi = qlo + quarter < chi ? qlo + quarter : chi;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // keys are read kBatch tiles (of 64) at a time, all loads issued before
+  // any tile is processed; the first batch stays in registers for pass 2
+  auto load_batch = [&](uint32_t (&kb)[kBatch], int64_t base) {
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t j = base + q * kWave + lane;
+      kb[q] = j < qhi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
+    }
+  };
+  constexpr int64_t kSpan = static_cast<int64_t>(kBatch) * kWave;
+  uint32_t first[kBatch];
+  load_batch(first, qlo);
+
+  // pass 1: per-bin counts of the quarter
+  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
+    uint32_t kb[kBatch];
+    if (jb == qlo) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+    } else {
+      load_batch(kb, jb);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (jb + q * kWave >= qhi) break;
+      const uint32_t k = kb[q];
+      const bool valid = k < static_cast<uint32_t>(B);
+      const uint64_t m = match_key(k, valid, nbits);
+      if (valid && __popcll(m & below) == 0) wrow[w][k] += __popcll(m);
+    }
+  }
+  __syncthreads();
+  // counts -> per-wave starting positions
+  for (int b = t; b < B; b += kSortThreads) {
+    int run = sbase[b];
+#pragma unroll
+    for (int v = 0; v < kSortWaves; ++v) {
+      const int cnt = wrow[v][b];
+      wrow[v][b] = run;
+      run += cnt;
+    }
+  }
+  __syncthreads();
+  // pass 2: positions
+  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
+    uint32_t kb[kBatch];
+    if (jb == qlo) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+    } else {
+      load_batch(kb, jb);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t j0 = jb + q * kWave;
+      if (j0 >= qhi) break;
+      const int64_t j = j0 + lane;
+      const uint32_t k = kb[q];
+      const bool valid = k < static_cast<uint32_t>(B);
+      const uint64_t m = match_key(k, valid, nbits);
+      const int rank = __popcll(m & below);
+      int start = 0;
+      if (valid) start = wrow[w][k];
+      if (valid) {
+        const int pos = start + rank;
+        fwd[j] = pos;
+        inv[pos] = static_cast<int>(j);
+        if (inv_key) inv_key[pos] = static_cast<uint8_t>(k);
+      } else if (j < qhi) {
+        fwd[j] = -1;
+      }
+      if (valid && rank == 0) wrow[w][k] = start + __popcll(m);
+    }
   }
 }
 
@@ -188,7 +278,7 @@ inline int bits_for(int B) {
   return nb;
 }
 
-// Enqueues the three sort launches. ws holds the two tables.
+// Enqueues the two sort launches. ws holds the histogram table.
 template <typename KeyT>
 int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int* inv,
                  uint8_t* inv_key, void* ws, uint32_t* err, uint32_t ebit, hipStream_t s) {
@@ -198,13 +288,10 @@ int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int
   }
   const int64_t chunk = csort_chunk(n, B);
   const int nch = static_cast<int>(csort_nchunks(n, B));
-  const size_t t = align_up(static_cast<size_t>(B) * nch * sizeof(int), 256);
   int* hist = static_cast<int*>(ws);
-  int* base = reinterpret_cast<int*>(static_cast<char*>(ws) + t);
   csort_hist<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, chunk, nch, hist, err, ebit);
-  csort_scan<<<1, kScanThreads, 0, s>>>(hist, B * nch, B, nch, base, offsets);
-  csort_rank<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, bits_for(B), chunk, nch, base, fwd,
-                                                 inv, inv_key);
+  csort_rank<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, bits_for(B), chunk, nch, hist,
+                                                 offsets, fwd, inv, inv_key);
   return launch_status();
 }
 

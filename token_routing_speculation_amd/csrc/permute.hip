@@ -12,17 +12,27 @@ namespace route {
 constexpr int kPermThreads = 256;
 
 // One wave per (token i, group h): read src[h][i], write it to the slots of
-// the K/H pairs (i, h*kg .. h*kg + kg - 1).
+// the K/H pairs (i, h*kg .. h*kg + kg - 1). The row is loaded whole into
+// registers (CPL 16-byte vectors per lane) before any store is issued.
+// Cache policy, measured on MI355X for this 1-read : K-write pattern: plain
+// loads with streaming (nontemporal) stores move about 6.0 TB/s, against
+// 4.9 TB/s with both streaming.
+template <int CPL>
 __global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __restrict__ src,
                                                              int64_t n, int K, int H, int d,
                                                              const int* __restrict__ slot_of_pair,
                                                              uint16_t* __restrict__ disp) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + threadIdx.x / kWave;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * (kPermThreads / kWave) + wave_id();
   if (g >= n * H) return;
   const int64_t i = g / H;
   const int h = static_cast<int>(g - i * H);
   const int kg = K / H;
   const int64_t nslots = n * K;
+  const int lane = lane_id();
+  const int nv = d >> 3;
+  const uint16_t* row = src + (static_cast<size_t>(h) * n + i) * d;
+  // vectors past the row end load vector 0 again (in bounds) and are never stored
+  // the K/H destination slots first (scalar loads, all issued together)
   int slot[kMaxK];
 #pragma unroll
   for (int t = 0; t < kMaxK; ++t) {
@@ -32,15 +42,28 @@ __global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __r
       slot[t] = (sl >= 0 && sl < nslots) ? sl : -1;
     }
   }
-  const int lane = lane_id();
-  const int nv = d >> 3;
-  const uint16_t* row = src + (static_cast<size_t>(h) * n + i) * d;
-  for (int v = lane; v < nv; v += kWave) {
-    const u32x4 x = ld16_stream(row + 8 * v);
+  u32x4 x[CPL];
 #pragma unroll
-    for (int t = 0; t < kMaxK; ++t)
-      if (t < kg && slot[t] >= 0) st16_stream(disp + static_cast<size_t>(slot[t]) * d + 8 * v, x);
+  for (int c = 0; c < CPL; ++c) {
+    const int v = lane + c * kWave;
+    x[c] = ld16(row + 8 * (v < nv ? v : 0));
   }
+#pragma unroll
+  for (int t = 0; t < kMaxK; ++t) {
+    if (t >= kg || slot[t] < 0) continue;
+    uint16_t* dst = disp + static_cast<size_t>(slot[t]) * d;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int v = lane + c * kWave;
+      if (v < nv) st16_stream(dst + 8 * v, x[c]);
+    }
+  }
+}
+
+// vectors per lane for a row of nv 16-byte vectors: one of the instantiated sizes
+inline int cpl_for(int nv) {
+  const int need = (nv + kWave - 1) / kWave;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 10 ? 10 : 16;
 }
 
 }  // namespace route
@@ -68,13 +91,22 @@ ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, i
   if ((src == nullptr) != (disp == nullptr)) return ROUTE_ERR_NULL;
   if (src) {
     if (d < 8 || d % 8 != 0) return ROUTE_ERR_SHAPE;
+    if (d > 16 * 8 * kWave) return ROUTE_ERR_UNSUPPORTED;
     if (!aligned16(src) || !aligned16(disp)) return ROUTE_ERR_ALIGN;
   }
   if (!ws || ws_bytes < moe_permute_workspace_size(n, K, E)) return ROUTE_ERR_WORKSPACE;
   int st = csort_launch<int32_t>(idx, n * K, E, expert_offsets, slot_of_pair, pair_of_slot,
                                  nullptr, ws, err, ROUTE_EBIT_EXPERT_RANGE, s);
   if (st != ROUTE_OK || !src || n == 0) return st;
+  if (d > 16 * 8 * kWave) return ROUTE_ERR_UNSUPPORTED;
   const unsigned grid = ceil_div(n * H, kPermThreads / kWave);
-  permute_move<<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair, disp);
+  switch (cpl_for(d / 8)) {
+#define ROUTE_CPL_CASE(c) \
+  case c: permute_move<c><<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair, disp); break;
+    ROUTE_CPL_CASE(1) ROUTE_CPL_CASE(2) ROUTE_CPL_CASE(4) ROUTE_CPL_CASE(8) ROUTE_CPL_CASE(10)
+    ROUTE_CPL_CASE(16)
+#undef ROUTE_CPL_CASE
+    default: return ROUTE_ERR_UNSUPPORTED;
+  }
   return launch_status();
 }

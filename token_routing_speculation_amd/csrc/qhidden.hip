@@ -14,7 +14,7 @@ __global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, int d,
     float eps, uint16_t* __restrict__ q) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kLnThreads / kWave) + threadIdx.x / kWave;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kLnThreads / kWave) + wave_id();
   if (i >= n) return;
   const int lane = lane_id();
   const int nv = d >> 3;

@@ -14,14 +14,17 @@ namespace route {
 
 constexpr int kMoveThreads = 256;
 
-// One wave per source row: out[dst(i)] = bf16(sum_p partials[p][i]).
-template <int PT>
+// One wave per source row: out[dst(i)] = bf16(sum_p partials[p][i]). Every
+// lane first loads all P x CPL of its 16-byte vectors, then sums and stores.
+// Cache policy, measured on MI355X for this pattern: streaming (nontemporal)
+// loads with plain stores move about 6.5 TB/s, against 5.4 TB/s with both
+// streaming.
+template <int PT, int CPL>
 __global__ __launch_bounds__(kMoveThreads) void srs_move(const uint16_t* __restrict__ partials,
-                                                         int P_dyn, int64_t n, int d,
+                                                         int64_t n, int d,
                                                          const int* __restrict__ row_of_src,
                                                          uint16_t* __restrict__ out) {
-  const int P = PT > 0 ? PT : P_dyn;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kMoveThreads / kWave) + threadIdx.x / kWave;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kMoveThreads / kWave) + wave_id();
   if (i >= n) return;
   const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
   if (dst < 0 || dst >= n) return;
@@ -30,27 +33,72 @@ __global__ __launch_bounds__(kMoveThreads) void srs_move(const uint16_t* __restr
   const size_t plane = static_cast<size_t>(n) * d;
   const uint16_t* src = partials + static_cast<size_t>(i) * d;
   uint16_t* o = out + static_cast<size_t>(dst) * d;
-#pragma unroll 2
-  for (int v = lane; v < nv; v += kWave) {
+  // vectors past the row end load vector 0 again (in bounds) and are never stored
+  u32x4 x[PT][CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int v = lane + c * kWave;
+    const int vv = v < nv ? v : 0;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) x[p][c] = ld16_stream(src + p * plane + 8 * vv);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int v = lane + c * kWave;
+    float acc[8];
+    unpack8(x[0][c], acc);
+#pragma unroll
+    for (int p = 1; p < PT; ++p) {
+      float f[8];
+      unpack8(x[p][c], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += f[e];
+    }
+    if (v < nv) st16(o + 8 * v, pack8(acc));
+  }
+}
+
+// Any P and row length: a plain loop over the row, partial by partial.
+__global__ __launch_bounds__(kMoveThreads) void srs_move_any(const uint16_t* __restrict__ partials,
+                                                             int P, int64_t n, int d,
+                                                             const int* __restrict__ row_of_src,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kMoveThreads / kWave) + wave_id();
+  if (i >= n) return;
+  const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
+  if (dst < 0 || dst >= n) return;
+  const int nv = d >> 3;
+  const size_t plane = static_cast<size_t>(n) * d;
+  const uint16_t* src = partials + static_cast<size_t>(i) * d;
+  uint16_t* o = out + static_cast<size_t>(dst) * d;
+  for (int v = lane_id(); v < nv; v += kWave) {
     float acc[8];
     unpack8(ld16_stream(src + 8 * v), acc);
-    if (PT > 0) {
+    for (int p = 1; p < P; ++p) {
+      float f[8];
+      unpack8(ld16_stream(src + p * plane + 8 * v), f);
 #pragma unroll
-      for (int p = 1; p < PT; ++p) {
-        float f[8];
-        unpack8(ld16_stream(src + p * plane + 8 * v), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += f[e];
-      }
-    } else {
-      for (int p = 1; p < P; ++p) {
-        float f[8];
-        unpack8(ld16_stream(src + p * plane + 8 * v), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += f[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += f[e];
     }
-    st16_stream(o + 8 * v, pack8(acc));
+    st16(o + 8 * v, pack8(acc));
+  }
+}
+
+// vectors per lane for a row of nv 16-byte vectors (0: no instantiated size)
+static int srs_cpl(int nv) {
+  const int need = (nv + kWave - 1) / kWave;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 10 ? 10 : 0;
+}
+
+template <int PT>
+static bool launch_srs_move(int cpl, unsigned grid, hipStream_t s, const uint16_t* partials,
+                            int64_t n, int d, const int* fwd, uint16_t* out) {
+  switch (cpl) {
+#define ROUTE_SRS_CASE(c) \
+  case c: srs_move<PT, c><<<grid, kMoveThreads, 0, s>>>(partials, n, d, fwd, out); return true;
+    ROUTE_SRS_CASE(1) ROUTE_SRS_CASE(2) ROUTE_SRS_CASE(4) ROUTE_SRS_CASE(8) ROUTE_SRS_CASE(10)
+#undef ROUTE_SRS_CASE
+    default: return false;
   }
 }
 
@@ -110,12 +158,11 @@ ROUTE_API int srs_shuffle(const uint16_t* partials, int32_t P, int64_t n, int32_
     if (row_cluster) fill_u8<<<ceil_div(n, 256), 256, 0, s>>>(row_cluster, n, 0);
   }
   const unsigned grid = ceil_div(n, kMoveThreads / kWave);
-  switch (P) {
-    case 1: srs_move<1><<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out); break;
-    case 2: srs_move<2><<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out); break;
-    case 3: srs_move<3><<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out); break;
-    case 4: srs_move<4><<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out); break;
-    default: srs_move<0><<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out); break;
-  }
+  const int cpl = srs_cpl(d / 8);
+  bool done = false;
+  if (P == 1) done = launch_srs_move<1>(cpl, grid, s, partials, n, d, fwd, out);
+  if (P == 2) done = launch_srs_move<2>(cpl, grid, s, partials, n, d, fwd, out);
+  if (P == 4 && cpl <= 4) done = launch_srs_move<4>(cpl, grid, s, partials, n, d, fwd, out);
+  if (!done) srs_move_any<<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out);
   return launch_status();
 }

@@ -2,9 +2,10 @@
 // grouped ("Federation of Experts (FoE)" article, grouped MoE block: group h
 // takes its own top k/H among experts [h*E/H, (h+1)*E/H)).
 //
-// A token is handled by a segment of S lanes of one wave (S = 4..64, a power
-// of two >= E up to 64; for E > 64, S = 64 and lane s holds the V = E/64
-// logits of columns s, s+64, ...). Logits become 32-bit orderable keys (the
+// A token is handled by a segment of S lanes of one wave (S = 4..32, a power
+// of two >= E, for E <= 32; S = 16 for E <= 256 and 64 beyond, lane s holding
+// the V = E/S logits of columns s, s+S, ...: the work per token is about
+// K (V + log S) lane steps, so small segments keep every lane busy). Logits become 32-bit orderable keys (the
 // float bits with the sign folded so unsigned order is float order; -0.0 is
 // folded onto +0.0 first). Each of the K rounds takes a segment-wide max of
 // the keys with DPP row operations (quad permutes and row mirrors, no LDS
@@ -53,14 +54,20 @@ __device__ __forceinline__ uint32_t seg_max(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+// Min over each aligned segment of S >= 16 lanes; every lane of the segment gets it.
+template <int S>
+__device__ __forceinline__ uint32_t seg_min(uint32_t v) {
   v = min(v, dpp<kDppXor1>(v));
   v = min(v, dpp<kDppXor2>(v));
   v = min(v, dpp<kDppHalfMirror>(v));
   v = min(v, dpp<kDppMirror>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return min(min(a, b), min(c, d));
+  if (S == 32) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 16, kWave)));
+  if (S == 64) {
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    v = min(min(a, b), min(c, d));
+  }
+  return v;
 }
 
 template <int S, int V>
@@ -112,12 +119,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         const uint64_t mine = (tie >> seg_base) & (S == 64 ? ~0ull : ((1ull << S) - 1));
         col = __builtin_ctzll(mine);
       } else {
-        // S == 64: one tied lane is the common case; otherwise take the
-        // smallest column among the tied lanes
-        if (__popcll(tie) == 1)
-          col = __builtin_amdgcn_readlane(bcol, __builtin_ctzll(tie));
-        else
-          col = static_cast<int>(wave_min(best == m ? static_cast<uint32_t>(bcol) : 0xffffffffu));
+        // several columns per lane: the smallest column among the tied lanes
+        col = static_cast<int>(seg_min<S>(best == m ? static_cast<uint32_t>(bcol) : 0xffffffffu));
       }
 #pragma unroll
       for (int v = 0; v < V; ++v)
@@ -205,14 +208,24 @@ ROUTE_API int route_topk(const float* logits, int64_t n, int32_t E, int32_t K, i
     launch_topk<16, 1>(logits, n, E, K, H, renorm, idx, weights, s);
   else if (E <= 32)
     launch_topk<32, 1>(logits, n, E, K, H, renorm, idx, weights, s);
-  else {
+  else if (E <= 256) {
+    switch ((E + 15) / 16) {
+#define ROUTE_V16_CASE(v) \
+  case v: launch_topk<16, v>(logits, n, E, K, H, renorm, idx, weights, s); break;
+      ROUTE_V16_CASE(3) ROUTE_V16_CASE(4) ROUTE_V16_CASE(5) ROUTE_V16_CASE(6) ROUTE_V16_CASE(7)
+      ROUTE_V16_CASE(8) ROUTE_V16_CASE(9) ROUTE_V16_CASE(10) ROUTE_V16_CASE(11)
+      ROUTE_V16_CASE(12) ROUTE_V16_CASE(13) ROUTE_V16_CASE(14) ROUTE_V16_CASE(15)
+      ROUTE_V16_CASE(16)
+#undef ROUTE_V16_CASE
+      default: return ROUTE_ERR_UNSUPPORTED;
+    }
+  } else {
     switch ((E + 63) / 64) {
 #define ROUTE_V_CASE(v) \
   case v: launch_topk<64, v>(logits, n, E, K, H, renorm, idx, weights, s); break;
-      ROUTE_V_CASE(1) ROUTE_V_CASE(2) ROUTE_V_CASE(3) ROUTE_V_CASE(4) ROUTE_V_CASE(5)
-      ROUTE_V_CASE(6) ROUTE_V_CASE(7) ROUTE_V_CASE(8) ROUTE_V_CASE(9) ROUTE_V_CASE(10)
-      ROUTE_V_CASE(11) ROUTE_V_CASE(12) ROUTE_V_CASE(13) ROUTE_V_CASE(14) ROUTE_V_CASE(15)
-      ROUTE_V_CASE(16)
+      ROUTE_V_CASE(5) ROUTE_V_CASE(6) ROUTE_V_CASE(7) ROUTE_V_CASE(8) ROUTE_V_CASE(9)
+      ROUTE_V_CASE(10) ROUTE_V_CASE(11) ROUTE_V_CASE(12) ROUTE_V_CASE(13) ROUTE_V_CASE(14)
+      ROUTE_V_CASE(15) ROUTE_V_CASE(16)
 #undef ROUTE_V_CASE
       default: return ROUTE_ERR_UNSUPPORTED;
     }
