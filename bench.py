@@ -15,6 +15,7 @@ a bounded sample of the same workload on this host.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -56,27 +57,67 @@ def foe_bytes(N, d, E, K, H):
     }
 
 
-def cpu_baseline(name: str, n_sample: int):
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_combine_deepseek.json")
+TRAFFIC_SOURCES = ("token_routing_speculation_amd/csrc/combine.hip",
+                   "token_routing_speculation_amd/csrc/common.hpp")
+
+
+def sources_digest(paths) -> str:
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the combine kernel from the committed counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None when the kernel's sources have changed
+    since they were taken or the workload differs."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("sha256") != sources_digest(TRAFFIC_SOURCES):
+        return None
+    return (rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
+
+
+def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
     """The oracle (float64 NumPy, as it stands) on a bounded sample of the
-    same workload: n_sample tokens drawn with the workload's recipe."""
+    same workload: n_sample tokens drawn with the workload's recipe, full
+    passes repeated until min_seconds of host time have been spent."""
     from threadpoolctl import threadpool_info
     from synth import make_config_inputs
     import oracle.pipeline as op
 
     inp = make_config_inputs(name, N=n_sample)
-    if name == "foe":
+    tables = None if name == "foe" else op.build_tables(inp)
+    passes, dt = 0, 0.0
+    while dt < min_seconds:
         t0 = time.perf_counter()
-        op.foe_pass(inp)
-        dt = time.perf_counter() - t0
-    else:
-        lut, conf = op.build_tables(inp)
-        t0 = time.perf_counter()
-        op.route_pass(inp, lut, conf)
-        dt = time.perf_counter() - t0
+        if name == "foe":
+            op.foe_pass(inp)
+        else:
+            op.route_pass(inp, *tables)
+        dt += time.perf_counter() - t0
+        passes += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_sample} tokens of the {name} workload, one full pass (float64 NumPy; "
-                      f"BLAS on {threads} threads, elementwise steps single-threaded); {dt:.1f} s"}
+    return {"value": passes * n_sample / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{passes} full passes over {n_sample} tokens of the {name} workload "
+                      f"(float64 NumPy; BLAS on {threads} threads, elementwise steps "
+                      f"single-threaded); {dt:.1f} s"}
+
+
+def lar_rate(p, pairs):
+    """Local activation rate of one pass (the counter accumulates)."""
+    p.local.zero_()
+    p.step()
+    return int(p.local.item()) / pairs
 
 
 def main(argv=None):
@@ -85,8 +126,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="deepseek", choices=["tiny", "mixtral", "deepseek", "foe"])
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the pass replayed as a HIP graph)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -96,7 +139,7 @@ def main(argv=None):
 
     import torch
     from synth import make_config_inputs, get_config
-    from token_routing_speculation_amd.pipeline import RoutePass, FoEPass
+    from token_routing_speculation_amd.pipeline import RoutePass, FoEPass, capture_graph
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -129,6 +172,7 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     K = args.steps
+    # eager steps, with events around every stage (per-stage and dominant-kernel times)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -143,9 +187,27 @@ def main(argv=None):
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / K
+    ms_eager = t_start.elapsed_time(t_end) / K
     st_us = {name: 1e3 * sum(ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)) / K
              for s, name in enumerate(stages)}
+    ms = ms_eager
+    if not args.no_graph:
+        # the same pass captured once and replayed: identical kernels, no
+        # per-launch host gaps
+        graph = capture_graph(p.step)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        g0.record(stream)
+        for _ in range(K):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = g0.elapsed_time(g1) / K
 
     N = cfg.N
     tokens_per_s = N / (ms * 1e-3)
@@ -162,6 +224,8 @@ def main(argv=None):
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "launch": "eager" if args.no_graph else "hip graph replay",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -174,8 +238,9 @@ def main(argv=None):
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
         "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None},
-        "lar": int(p.local.item()) / (K + args.warmup) / (N * cfg.K),
+                     "frac": achieved / HBM_PEAK,
+                     "traffic": measured_traffic(conf["workload"])},
+        "lar": lar_rate(p, N * cfg.K),
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline and args.config != "tiny":

@@ -301,3 +301,25 @@ def test_run_twice_bitwise():
     p.step()
     for k, v in first.items():
         assert np.array_equal(host(getattr(p, k)), v), k
+
+
+# ------------------------------------------------------------ graph replay
+def test_graph_replay_matches_eager():
+    """The benchmark replays the pass as a captured graph: every replay, with
+    eager work and synchronisations in between, must equal the eager pass."""
+    from token_routing_speculation_amd.pipeline import RoutePass, capture_graph
+    inp = make_route_inputs(2000, 512, 160, 6, 2, 8, 5000, 91, ngram=True)
+    p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
+    keys = ("dest", "x", "row_of_src", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
+    p.step()
+    sync()
+    eager = {k: host(getattr(p, k)).copy() for k in keys}
+    g = capture_graph(p.step)
+    for rep in range(4):
+        for k in keys:                      # scribble over the outputs eagerly
+            getattr(p, k).view(torch.uint8).fill_(0xA5)
+        sync()
+        g.replay()
+        sync()
+        for k in keys:
+            assert np.array_equal(host(getattr(p, k)), eager[k]), (rep, k)

@@ -16,7 +16,9 @@ Accelerates Inference for Mixture-of-Experts", items 2.A, 2.C and 4).
 
 Inputs are host numpy arrays from the ``synth`` generator; they are copied to
 the device once, in the constructor. ``step()`` enqueues one pass on the
-current stream and allocates nothing.
+current stream and allocates nothing, so it can be captured once into a HIP
+graph (``capture_graph``) and replayed: the same kernels, launched without
+per-kernel host overhead.
 """
 
 from __future__ import annotations
@@ -40,6 +42,22 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """device bf16 tensor -> host uint16 bit patterns."""
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def capture_graph(step, warmup: int = 2):
+    """Capture one call of ``step`` (a pass that allocates nothing and records
+    no memset) into a graph; returns the graph, replayed with ``.replay()``."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
 
 
 def build_tables_device(inp: dict, device="cuda"):
