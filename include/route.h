@@ -142,7 +142,8 @@ size_t srs_shuffle_workspace_size(int64_t n, int32_t G);
  * next layer's gate applied to q_l). bf16 operands, binary32 accumulation
  * on the MFMA units.
  *   x bf16 rows [n][d]; w bf16 rows [E][d]; logits float[n][E] (row-major).
- * Errors: NULL, SHAPE (n < 0, d % 8, E < 1), ALIGN, UNSUPPORTED (E > 1024).
+ * Errors: NULL, SHAPE (n < 0, d % 8, E < 1), ALIGN, UNSUPPORTED (E > 1024,
+ * or d > 4194304 with E > 32).
  */
 int route_gate(const uint16_t* x, int64_t n, int32_t d, const uint16_t* w, int32_t E,
                float* logits, hipStream_t s);
@@ -236,7 +237,7 @@ int route_qhidden(const uint16_t* r, const float* dvec, const float* gamma, cons
  *   [E][hd]; b2 float[E]; logits float[n][E].
  *   ws: route_estimator_workspace_size(n, hd) bytes.
  * Errors: NULL, SHAPE (d % 8, hd % 8), ALIGN, UNSUPPORTED (hd > 4096,
- * E > 1024), WORKSPACE.
+ * E > 1024, d > 4194304), WORKSPACE.
  */
 int route_estimator(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1, const float* b1,
                     int32_t hd, const uint16_t* w2, const float* b2, int32_t E, float* logits,

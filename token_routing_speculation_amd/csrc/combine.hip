@@ -6,10 +6,13 @@
 // cross-group sum ("Federation of Experts (FoE)" article).
 //
 // One wave per token: K row gathers of 16-byte vectors, binary32 FMA in slot
-// order k = 0..K-1, one row store (bf16 nearest-even or float32). Cache
-// policy, measured on MI355X for this K-read : 1-write pattern: streaming
-// (nontemporal) loads with plain stores move about 5.6 TB/s, against
-// 5.1 TB/s the other way round.
+// order k = 0..K-1, one row store (bf16 nearest-even or float32). Both the
+// gathers and the row stores are streaming (nontemporal): neither is re-read
+// within the pass, and a streaming store leaves MI355X's memory-side cache to
+// the activations that the shuffle writes and the gate and the dispatch read
+// back. Measured on whole DeepSeek-V2-shaped passes, that keeps about 40 us
+// of HBM reads per pass out of the following stages; with plain stores the
+// combine alone moves the same bytes as fast (5.6 TB/s), but the pass does not.
 #include "common.hpp"
 
 namespace route {
@@ -21,13 +24,13 @@ template <int OUT_F32>
 __device__ __forceinline__ void store_out(void* out, int64_t dst, int d, int v, const float* acc) {
   if (OUT_F32) {
     float* o = static_cast<float*>(out) + static_cast<size_t>(dst) * d + 8 * v;
-    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                  __float_as_uint(acc[3])});
-    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
-                      __float_as_uint(acc[7])});
+    st16_stream(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                         __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+    st16_stream(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                             __float_as_uint(acc[6]), __float_as_uint(acc[7])});
   } else {
     uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(dst) * d + 8 * v;
-    st16(o, pack8(acc));
+    st16_stream(o, pack8(acc));
   }
 }
 

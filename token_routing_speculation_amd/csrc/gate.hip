@@ -8,14 +8,21 @@
 // the K dimension (wave w takes the 32-wide K steps w, w+4, ...), so each
 // operand byte is fetched by exactly one wave, straight into registers in
 // the MFMA operand layout (8 contiguous bf16 per lane and row). The A stream
-// (from HBM) is prefetched kPfa steps ahead, the small B (L2-resident) one
-// step ahead. Partial tiles are summed through LDS at the end; each wave
-// finishes a quarter of the tiles.
+// is prefetched kPfa steps ahead, the small B (L2-resident) one step ahead.
+// Partial tiles are summed through LDS at the end; each wave finishes a
+// quarter of the tiles.
+//
+// A is read with plain (not streaming) loads in both kernels: in the routing
+// pass the activations were just written by the shuffle and are read again by
+// the dispatch, and plain loads leave them resident in MI355X's memory-side
+// cache for that second read (about 40 us of HBM reads per DeepSeek-V2-shaped
+// pass, measured against streaming loads here).
 //
 // Used by the "Federation of Experts (FoE)" article's router scores g[i]
 // and by "Speculating Experts Accelerates Inference for Mixture-of-Experts"
 // (item 2.A: next gate on q_l; item 2.C: the estimator MLP).
 #include "common.hpp"
+#include <type_traits>
 
 namespace route {
 
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt(const uint16_t* __res
   auto load_a = [&](u32x4 (&a)[MT], int st) {
     const int k = koff(st);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a[m] = ld16_stream(ap[m] + k);
+    for (int m = 0; m < MT; ++m) a[m] = ld16(ap[m] + k);
   };
   // zero the lanes of a partial last step (applied at use, not at load, so
   // the select never waits for a load still in flight)
@@ -202,96 +209,183 @@ static void launch_nt(int NT, dim3 grid, hipStream_t s, const uint16_t* A, int64
 // ---------------------------------------------------------------------------
 // LDS-staged product for wider outputs (E > 32). A workgroup owns a BM x BN
 // tile (BM = 16 MTW WR rows, BN = 16 NTW WC columns) and walks K in 64-wide
-// steps. Each step's A and B slabs are fetched by all 256 threads as whole
-// 128-byte lines (16 bytes per thread and load), kept in a four-deep register
-// ring, written to one of two LDS buffers (row stride 144 bytes, so the MFMA
-// fragment reads of 16 consecutive rows spread over the banks) and consumed
-// by the four waves, laid out WR x WC over the tile, each owning a
-// 16 MTW x 16 NTW block of accumulators. The register ring is written out
-// over four statically named slots so no slot is ever copied (a copy would
-// wait for its load): the loads of step s+3 are in flight while step s runs.
+// steps. Each step's slabs are fetched as whole 128-byte lines (16 bytes per
+// lane and load), written to one of two LDS buffers and consumed by four
+// waves laid out WR x WC over the tile, each owning a 16 MTW x 16 NTW block
+// of accumulators. Slab rows are 128 bytes with the 16-byte piece index
+// XORed with the row's low three bits, so neither the row-wise stores nor
+// the MFMA fragment reads (16 consecutive rows, one piece) pile onto a few
+// LDS banks; on gfx950 this measured as fast as the best padded stride
+// (160 bytes) in less LDS.
+//
+// Staging is split by operand: waves 0-1 fetch the A slab, waves 2-3 the B
+// slab. Loads retire in issue order per wave, so a wave that fetched both
+// would wait on its long-latency A stream whenever it needs B; with the
+// roles split, A runs further ahead than B (small, L2-resident). Each role's
+// register ring is indexed with compile-time slots only, so no slot is ever
+// copied (a copy would wait for its load).
 // ---------------------------------------------------------------------------
-constexpr int kLdsRowBytes = 144;  // 128 data bytes + 16 pad
+constexpr bool kLdsSwizzle = true;
+constexpr int kLdsRowBytes = 160;  // row stride when not swizzled: 128 data bytes + 32 pad
 
-template <int BM, int BN>
-struct StageRegs {
-  static constexpr int A_CH = BM * 8 / kGemmThreads;  // 16-byte chunks per thread
-  static constexpr int B_CH = BN * 8 / kGemmThreads;
-  u32x4 a[A_CH];
-  u32x4 b[B_CH];
+// LDS byte offset of 16-byte piece `piece` (0..7) of slab row rbase + r16,
+// where rbase is a multiple of 16.
+__device__ __forceinline__ int lds_off(int rbase, int r16, int piece) {
+  if (kLdsSwizzle) return (rbase + r16) * 128 + ((piece ^ (r16 & 7)) << 4);
+  return (rbase + r16) * kLdsRowBytes + (piece << 4);
+}
+constexpr int kLdsRow = kLdsSwizzle ? 128 : kLdsRowBytes;
+
+// Prefetch leads (steps in flight ahead of the one consumed) for KG K groups
+// per workgroup: with two groups sharing a CU each needs half the lead, and
+// the smaller rings keep both groups' waves within 256 registers.
+template <int KG>
+struct Leads;
+template <>
+struct Leads<1> {
+  static constexpr int A = 7, B = 3;
+};
+template <>
+struct Leads<2> {
+  static constexpr int A = 3, B = 1;
 };
 
-template <int MTW, int NTW, int WR>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds(const uint16_t* __restrict__ A,
-                                                            int64_t M, int Kd,
-                                                            const uint16_t* __restrict__ B,
-                                                            int N, const float* __restrict__ bias,
-                                                            void* __restrict__ C, int epi) {
+// Operand loads of the staged kernel: a wave-uniform base and a 32-bit byte
+// offset per lane. POL < 0 is a plain global load; POL >= 0 a buffer load
+// whose cache-policy bits are POL (bit 0 sc0, bit 1 nt, bit 4 sc1); buffer
+// loads also return zeros for any offset past the descriptor's extent.
+constexpr int kLdGlobal = -1;
+
+struct Operand {
+  const char* base;  // wave-uniform
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+
+__device__ __forceinline__ Operand make_operand(const void* base, uint32_t extent_bytes) {
+  Operand o;
+  o.base = static_cast<const char*>(base);
+  // dword 3: the raw (untyped) buffer format of gfx9-family descriptors
+  o.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(extent_bytes), 0x00020000);
+  return o;
+}
+
+template <int POL>
+__device__ __forceinline__ u32x4 ld_operand(const Operand& o, uint32_t off) {
+  if constexpr (POL < 0) {
+    return *reinterpret_cast<const u32x4*>(o.base + off);
+  } else {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         o.rsrc, static_cast<int>(off), 0, POL));
+  }
+}
+
+// One role's K loop over nsteps 64-wide steps starting at k0: NCH 16-byte
+// chunks per lane and step (byte offsets off[] from the operand base), a ring
+// of LEAD + 1 slots. Each step prefetches step st + LEAD, publishes step st
+// to LDS buffer st % 2, waits at the barrier and multiplies that buffer.
+// Steps, or pieces of a step, at k >= Kd are published as zeros (their loads
+// are redirected in bounds to k = 0).
+template <int NCH, int LEAD, int POL, class Compute>
+__device__ __forceinline__ void stage_loop(const Operand& op, const uint32_t (&off)[NCH],
+                                           const int (&lo)[NCH], char* lds, int buf_bytes, int k0,
+                                           int nsteps, int Kd, int kpiece, Compute&& compute) {
+  constexpr int NSLOT = LEAD + 1;
+  static_assert(8 % NSLOT == 0, "a group of eight steps must cycle the ring whole");
+  auto koff = [&](int st) {
+    st = st < nsteps ? st : nsteps - 1;
+    const int k = k0 + 64 * st;
+    return static_cast<uint32_t>(k + kpiece < Kd ? k : 0) * 2u;
+  };
+  u32x4 r[NSLOT][NCH];
+  auto load = [&](u32x4 (&d)[NCH], int st) {
+    const uint32_t ko = koff(st);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) d[i] = ld_operand<POL>(op, off[i] + ko);
+  };
+  auto store = [&](const u32x4 (&v)[NCH], int st, int buf) {
+    char* base = lds + buf * buf_bytes;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(base + lo[i]) = v[i];
+    // a second store behind a branch, so no select on the loaded data can be
+    // hoisted ahead of its load
+    const int k = k0 + 64 * st;
+    if (k + 64 > Kd && k + kpiece >= Kd) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(base + lo[i]) = zero;
+    }
+  };
+  // step st at ring slot j (j = st mod 8, a compile-time constant)
+  auto step = [&](auto jc, int st) {
+    constexpr int j = decltype(jc)::value;
+    load(r[(j + LEAD) % NSLOT], st + LEAD);
+    store(r[j % NSLOT], st, j & 1);
+    __syncthreads();
+    compute(j & 1);
+  };
+#pragma unroll
+  for (int j = 0; j < LEAD; ++j) load(r[j], j);
+  int st = 0;
+  for (int g = 0; g < nsteps / 8; ++g, st += 8) {
+    step(std::integral_constant<int, 0>{}, st);
+    step(std::integral_constant<int, 1>{}, st + 1);
+    step(std::integral_constant<int, 2>{}, st + 2);
+    step(std::integral_constant<int, 3>{}, st + 3);
+    step(std::integral_constant<int, 4>{}, st + 4);
+    step(std::integral_constant<int, 5>{}, st + 5);
+    step(std::integral_constant<int, 6>{}, st + 6);
+    step(std::integral_constant<int, 7>{}, st + 7);
+  }
+  const int rest = nsteps % 8;
+  if (rest > 0) step(std::integral_constant<int, 0>{}, st);
+  if (rest > 1) step(std::integral_constant<int, 1>{}, st + 1);
+  if (rest > 2) step(std::integral_constant<int, 2>{}, st + 2);
+  if (rest > 3) step(std::integral_constant<int, 3>{}, st + 3);
+  if (rest > 4) step(std::integral_constant<int, 4>{}, st + 4);
+  if (rest > 5) step(std::integral_constant<int, 5>{}, st + 5);
+  if (rest > 6) step(std::integral_constant<int, 6>{}, st + 6);
+}
+
+constexpr int kPolA = kLdGlobal;  // cache policy of the A (activation) slabs
+constexpr int kPolB = kLdGlobal;  // and of the B (weight) slabs
+
+// KG groups of four waves per workgroup split K in KG contiguous ranges of
+// equal step count (the last padded with zero steps, so every wave meets the
+// same barriers); each group stages and multiplies its own range in its own
+// pair of LDS buffers, and the groups' partial tiles are summed in group
+// order at the end. Two groups on one CU overlap one group's LDS phase with
+// the other's matrix-core phase.
+template <int MTW, int NTW, int WR, int KG>
+__global__ __launch_bounds__(kGemmThreads * KG, 1) void gemm_lds(
+    const uint16_t* __restrict__ A, int64_t M, int Kd, const uint16_t* __restrict__ B, int N,
+    const float* __restrict__ bias, void* __restrict__ C, int epi) {
   constexpr int WC = 4 / WR;
   constexpr int BM = 16 * MTW * WR;
   constexpr int BN = 16 * NTW * WC;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "slabs must split evenly over 256 threads");
-  using Regs = StageRegs<BM, BN>;
-  constexpr int ABYTES = BM * kLdsRowBytes;
-  constexpr int BBYTES = BN * kLdsRowBytes;
-  __shared__ __attribute__((aligned(16))) char lds[2 * (ABYTES + BBYTES)];
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "slabs must split evenly over two waves");
+  constexpr int A_CH = BM * 8 / 128;  // 16-byte chunks per lane and step, A role
+  constexpr int B_CH = BN * 8 / 128;
+  constexpr int ABYTES = BM * kLdsRow;
+  constexpr int BBYTES = BN * kLdsRow;
+  constexpr int BUF = ABYTES + BBYTES;
+  static_assert(KG == 1 || (KG - 1) * 4 * MTW * NTW * kWave * 16 <= KG * 2 * BUF,
+                "partial tiles must fit in the staging buffers");
+  __shared__ __attribute__((aligned(16))) char lds[KG * 2 * BUF];
 
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  const int lane = tid & (kWave - 1);
+  const int wave = wave_id();
+  const int grp = wave / 4;  // K group
+  const int w = wave % 4;    // wave inside its group
+  const int lane = threadIdx.x & (kWave - 1);
   const int wr = w % WR;
   const int wc = w / WR;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int col0 = blockIdx.y * BN;
-
-  // global chunk c of a slab: row c / 8, 16-byte piece c % 8 of its 128 bytes
-  const uint16_t* agp[Regs::A_CH];
-  int alds[Regs::A_CH];
-#pragma unroll
-  for (int i = 0; i < Regs::A_CH; ++i) {
-    const int c = tid + i * kGemmThreads;
-    const int64_t row = row0 + c / 8;
-    agp[i] = A + (row < M ? row : M - 1) * static_cast<int64_t>(Kd) + (c % 8) * 8;
-    alds[i] = (c / 8) * kLdsRowBytes + (c % 8) * 16;
-  }
-  const uint16_t* bgp[Regs::B_CH];
-  int blds[Regs::B_CH];
-#pragma unroll
-  for (int i = 0; i < Regs::B_CH; ++i) {
-    const int c = tid + i * kGemmThreads;
-    const int col = col0 + c / 8;
-    bgp[i] = B + static_cast<int64_t>(col < N ? col : N - 1) * Kd + (c % 8) * 8;
-    blds[i] = ABYTES + (c / 8) * kLdsRowBytes + (c % 8) * 16;
-  }
-  const int kpiece = tid % 8 * 8;  // this thread's k offset inside a step (same for all chunks)
-
-  const int nsteps = (Kd + 63) / 64;
-  auto load = [&](Regs& r, int st) {
-    st = st < nsteps ? st : nsteps - 1;  // past the end: reload the last step (unused)
-    const int k = 64 * st;
-    const int ko = k + kpiece < Kd ? k : 0;  // a partial last step reads in bounds
-#pragma unroll
-    for (int i = 0; i < Regs::A_CH; ++i) r.a[i] = ld16_stream(agp[i] + ko);
-#pragma unroll
-    for (int i = 0; i < Regs::B_CH; ++i) r.b[i] = ld16(bgp[i] + ko);
-  };
-  auto store = [&](const Regs& r, int st, int buf) {
-    char* base = lds + buf * (ABYTES + BBYTES);
-#pragma unroll
-    for (int i = 0; i < Regs::A_CH; ++i) *reinterpret_cast<u32x4*>(base + alds[i]) = r.a[i];
-#pragma unroll
-    for (int i = 0; i < Regs::B_CH; ++i) *reinterpret_cast<u32x4*>(base + blds[i]) = r.b[i];
-    // a partial last step: the pieces past Kd (read from k = 0) become zeros.
-    // Done as a second store behind a branch, so no select on the loaded data
-    // can be hoisted ahead of its load.
-    if (64 * st + 64 > Kd && 64 * st + kpiece >= Kd) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < Regs::A_CH; ++i) *reinterpret_cast<u32x4*>(base + alds[i]) = zero;
-#pragma unroll
-      for (int i = 0; i < Regs::B_CH; ++i) *reinterpret_cast<u32x4*>(base + blds[i]) = zero;
-    }
-  };
+  const int sub = (w & 1) * kWave + lane;  // lane index inside its role's two waves
+  const int kpiece = lane % 8 * 8;         // k offset of this lane's piece inside a step
+  char* glds = lds + grp * 2 * BUF;
+  const int per = ((Kd + 63) / 64 + KG - 1) / KG;  // steps per group
+  const int k0 = grp * per * 64;
 
   f32x4 acc[MTW][NTW];
 #pragma unroll
@@ -299,20 +393,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds(const uint16_t* __re
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment addresses: A tile m, k half h -> row 16 m + (lane & 15), piece 4 h + lane / 16
-  const int afrag = (wr * 16 * MTW + (lane & 15)) * kLdsRowBytes + (lane >> 4) * 16;
-  const int bfrag = ABYTES + (wc * 16 * NTW + (lane & 15)) * kLdsRowBytes + (lane >> 4) * 16;
+  // fragments: A tile m, k half h -> slab row 16 m + (lane & 15), piece 4 h + lane / 16
   auto compute = [&](int buf) {
-    const char* base = lds + buf * (ABYTES + BBYTES);
+    const char* base = glds + buf * BUF;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 af[MTW], bf[NTW];
 #pragma unroll
       for (int m = 0; m < MTW; ++m)
-        af[m] = *reinterpret_cast<const u32x4*>(base + afrag + m * 16 * kLdsRowBytes + h * 64);
+        af[m] = *reinterpret_cast<const u32x4*>(
+            base + lds_off(wr * 16 * MTW + 16 * m, lane & 15, 4 * h + (lane >> 4)));
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
-        bf[t] = *reinterpret_cast<const u32x4*>(base + bfrag + t * 16 * kLdsRowBytes + h * 64);
+        bf[t] = *reinterpret_cast<const u32x4*>(
+            base + ABYTES + lds_off(wc * 16 * NTW + 16 * t, lane & 15, 4 * h + (lane >> 4)));
 #pragma unroll
       for (int m = 0; m < MTW; ++m)
 #pragma unroll
@@ -320,29 +414,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds(const uint16_t* __re
     }
   };
 
-  Regs r0, r1, r2, r3;
-  load(r0, 0);
-  load(r1, 1);
-  load(r2, 2);
-  int st = 0;
-// one K step: prefetch step st+3, publish step st to LDS, multiply it
-#define ROUTE_LDS_STEP(RU, RL, BUF) \
-  load(RL, st + 3);                 \
-  store(RU, st, BUF);               \
-  __syncthreads();                  \
-  compute(BUF);                     \
-  ++st;
-  for (int g = 0; g < nsteps / 4; ++g) {
-    ROUTE_LDS_STEP(r0, r3, 0)
-    ROUTE_LDS_STEP(r1, r0, 1)
-    ROUTE_LDS_STEP(r2, r1, 0)
-    ROUTE_LDS_STEP(r3, r2, 1)
+  // chunk c of a slab: row c / 8, 16-byte piece c % 8 of the row's 128 bytes.
+  // Offsets are in bytes from this tile's first row (first column) and stay
+  // below BM * Kd * 2 (BN * Kd * 2); rows past M and columns past N are
+  // clamped onto the last valid one (their results are never stored).
+  if (w < 2) {
+    const int64_t rows = M - row0 < BM ? M - row0 : BM;
+    const Operand op = make_operand(A + row0 * Kd, static_cast<uint32_t>(rows * Kd * 2));
+    uint32_t off[A_CH];
+    int lo[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = sub + i * 128;
+      const int r = c / 8 < rows ? c / 8 : static_cast<int>(rows) - 1;
+      off[i] = static_cast<uint32_t>(r * Kd + (c % 8) * 8) * 2u;
+      lo[i] = lds_off(c / 128 * 16, c / 8 % 16, c % 8);
+    }
+    stage_loop<A_CH, Leads<KG>::A, kPolA>(op, off, lo, glds, BUF, k0, per, Kd, kpiece, compute);
+  } else {
+    const int cols = N - col0 < BN ? N - col0 : BN;
+    const Operand op = make_operand(B + static_cast<int64_t>(col0) * Kd,
+                                    static_cast<uint32_t>(static_cast<int64_t>(cols) * Kd * 2));
+    uint32_t off[B_CH];
+    int lo[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = sub + i * 128;
+      const int r = c / 8 < cols ? c / 8 : cols - 1;
+      off[i] = static_cast<uint32_t>(r * Kd + (c % 8) * 8) * 2u;
+      lo[i] = ABYTES + lds_off(c / 128 * 16, c / 8 % 16, c % 8);
+    }
+    stage_loop<B_CH, Leads<KG>::B, kPolB>(op, off, lo, glds, BUF, k0, per, Kd, kpiece, compute);
   }
-  const int rest = nsteps % 4;
-  if (rest > 0) { ROUTE_LDS_STEP(r0, r3, 0) }
-  if (rest > 1) { ROUTE_LDS_STEP(r1, r0, 1) }
-  if (rest > 2) { ROUTE_LDS_STEP(r2, r1, 0) }
-#undef ROUTE_LDS_STEP
+
+  if (KG > 1) {
+    // groups 1.. park their partial tiles in LDS; group 0 adds them in order
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          red[(((grp - 1) * 4 + w) * MTW * NTW + m * NTW + t) * kWave + lane] = acc[m][t];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g)
+#pragma unroll
+      for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          acc[m][t] += red[(((g - 1) * 4 + w) * MTW * NTW + m * NTW + t) * kWave + lane];
+  }
 
 #pragma unroll
   for (int m = 0; m < MTW; ++m)
@@ -365,15 +490,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds(const uint16_t* __re
     }
 }
 
-// Picks the tile shape: all columns in one block when E <= 160 (A streamed
-// once), else blocks of 128 columns; rows per block shrink until the grid
-// has at least one workgroup per CU, and to 32 when a 64-row tile would not
-// fit in registers.
+template <int MTW, int NTW, int WR>
+static void launch_lds(int kg, dim3 grid, hipStream_t s, const uint16_t* A, int64_t M, int Kd,
+                       const uint16_t* B, int N, const float* bias, void* C, int epi) {
+  if (kg == 2)
+    gemm_lds<MTW, NTW, WR, 2><<<grid, kGemmThreads * 2, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+  else
+    gemm_lds<MTW, NTW, WR, 1><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+}
+
 static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N,
                        const float* bias, void* C, int epi, hipStream_t s) {
   if (M == 0) return ROUTE_OK;
   const int ntiles = (N + 15) / 16;
   if (N > 32) {
+    if (Kd > (1 << 22)) return ROUTE_ERR_UNSUPPORTED;  // tile byte offsets are 32-bit
     // LDS-staged tiles: 64 x 160 for E <= 160 (one pass over A), else 64 x 128
     // blocks of columns; 32-row tiles when 64-row ones would leave CUs idle
     const bool wide = ntiles > 8;
@@ -381,18 +512,21 @@ static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, 
     const int bn = gy > 1 ? 128 : (ntiles <= 4 ? 64 : (ntiles <= 8 ? 128 : 160));
     const bool tall = static_cast<int64_t>(ceil_div(M, 64)) * gy >= 256;
     dim3 grid(ceil_div(M, tall ? 64 : 32), gy);
+    // two K groups per workgroup when one workgroup per CU is all the grid
+    // gives (the groups then share the CU's SIMDs); one group otherwise
+    const int kg = static_cast<int64_t>(grid.x) * grid.y <= 256 ? 2 : 1;
     if (bn == 160 && tall)
-      gemm_lds<2, 5, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<2, 5, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     else if (bn == 160)
-      gemm_lds<1, 5, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<1, 5, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     else if (bn == 128 && tall)
-      gemm_lds<2, 4, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<2, 4, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     else if (bn == 128)
-      gemm_lds<1, 4, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<1, 4, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     else if (tall)
-      gemm_lds<2, 2, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<2, 2, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     else
-      gemm_lds<1, 2, 2><<<grid, kGemmThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+      launch_lds<1, 2, 2>(kg, grid, s, A, M, Kd, B, N, bias, C, epi);
     return launch_status();
   }
   // skinny outputs (E <= 32): split-K register kernel, 16..64-row tiles
