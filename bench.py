@@ -24,6 +24,7 @@ import time
 import numpy as np
 
 HBM_PEAK = 8.0e12            # MI355X HBM3E, bytes/s (AMD spec sheet)
+MFMA_BF16_PEAK = 2.5e15      # MI355X dense bf16 matrix throughput, FLOP/s
 METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofline"
 
 ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
@@ -113,6 +114,12 @@ def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
                       f"single-threaded); {dt:.1f} s"}
 
 
+def pct(xs):
+    """10th, 50th and 90th percentile of a list of per-pass times (ms)."""
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return [round(float(v), 4) for v in q]
+
+
 def lar_rate(p, pairs):
     """Local activation rate of one pass (the counter accumulates)."""
     p.local.zero_()
@@ -191,6 +198,7 @@ def main(argv=None):
     st_us = {name: 1e3 * sum(ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)) / K
              for s, name in enumerate(stages)}
     ms = ms_eager
+    per_pass = cold = None
     if not args.no_graph:
         # the same pass captured once and replayed: identical kernels, no
         # per-launch host gaps
@@ -198,16 +206,34 @@ def main(argv=None):
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         wall0 = time.perf_counter()
-        g0.record(stream)
-        for _ in range(K):
+        ge[0].record(stream)
+        for k in range(K):
             graph.replay()
-        g1.record(stream)
+            ge[k + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        ms = g0.elapsed_time(g1) / K
+        ms = ge[0].elapsed_time(ge[K]) / K
+        per_pass = [ge[k].elapsed_time(ge[k + 1]) for k in range(K)]
+        # cold protocol: a 512 MiB read before every timed pass, so nothing a
+        # previous pass left in the 256 MB memory-side cache helps. The scrub
+        # only reads (the cache then holds clean lines): a writing scrub would
+        # charge the write-back of its own dirty lines to the pass.
+        scrub = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+        sink = torch.zeros((), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            torch.sum(scrub, dim=0, out=sink)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for k in range(K):
+            torch.sum(scrub, dim=0, out=sink)
+            ce[k][0].record(stream)
+            graph.replay()
+            ce[k][1].record(stream)
+        torch.cuda.synchronize()
+        cold = [a.elapsed_time(b) for a, b in ce]
+        del scrub, sink
 
     N = cfg.N
     tokens_per_s = N / (ms * 1e-3)
@@ -234,7 +260,10 @@ def main(argv=None):
         "config": conf,
         "hbm_frac_pass": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_pass": total_bytes,
+        "pass_ms_p10_p50_p90": pct(per_pass) if per_pass else None,
+        "cold_pass_ms_p10_p50_p90": pct(cold) if cold else None,
         "stages_us": {k: round(v, 2) for k, v in st_us.items()},
+        "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us["gate"] * 1e-6) / MFMA_BF16_PEAK,
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
         "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
