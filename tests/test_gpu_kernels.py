@@ -136,7 +136,11 @@ def test_gate_empty_is_noop():
 TOPK_CASES = [(1, 2, 1, 1), (500, 4, 2, 1), (333, 5, 3, 1), (1000, 8, 2, 1), (257, 16, 4, 2),
               (700, 33, 5, 1), (1000, 64, 8, 4), (1000, 64, 2, 1), (999, 128, 8, 1),
               (2048, 160, 6, 1), (400, 160, 6, 2), (100, 1024, 16, 4), (300, 200, 10, 5),
-              (64, 7, 7, 1)]
+              (64, 7, 7, 1),
+              # compile-time-shaped kernels on ragged token counts, and the
+              # general kernel on the same E with other K
+              (1, 160, 6, 1), (77, 64, 8, 4), (17, 128, 8, 1), (5, 4, 2, 1), (3, 8, 2, 1),
+              (300, 160, 4, 1), (129, 128, 4, 1)]
 
 
 def _tie_logits(n, E, seed):

@@ -1,13 +1,13 @@
 // Stable counting sort of small integer keys, in two launches:
 //   1. csort_hist:  per-chunk histograms in LDS, written chunk-major
-//                   [nchunks][B] (at most 64 chunks);
+//                   [nchunks][B] (at most 128 chunks);
 //   2. csort_rank:  each chunk's block derives where its keys of each bin
 //                   start (all earlier bins, plus this bin's count in earlier
-//                   chunks): one thread per bin loads the bin's count in
-//                   every chunk at once and sums them; block 0 also writes
-//                   the bin offsets [B+1]. Each wave then ranks one quarter
-//                   of the chunk (ballot-matched equal keys, wave-private
-//                   running counts), giving each key its stable position.
+//                   chunks), summing the table over all of its threads;
+//                   block 0 also writes the bin offsets [B+1]. Each wave
+//                   then ranks a contiguous share of the chunk (ballot-
+//                   matched equal keys, wave-private running counts), giving
+//                   each key its stable position.
 // Keys >= B (or negative) are skipped: flagged in err, position -1.
 #pragma once
 
@@ -17,9 +17,8 @@ namespace route {
 namespace {  // internal linkage: each translation unit gets its own copy
 
 constexpr int kSortThreads = 256;
-constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kMaxChunks = 64;
-constexpr int kBatch = 8;  // keys per thread loaded ahead of use (histogram)  // one lane per chunk when summing a bin's counts
+constexpr int kMaxChunks = 128;
+constexpr int kBatch = 8;  // keys (tiles) per thread loaded ahead of use
 
 // Keys per chunk: a power of two >= 1024 giving at most kMaxChunks chunks.
 inline int64_t csort_chunk(int64_t n, int B) {
@@ -96,50 +95,68 @@ __device__ __forceinline__ uint64_t match_key(uint32_t k, bool valid, int nbits)
 }
 
 // Ranks the keys of chunk blockIdx.x. fwd[j] = position of key j,
-// inv[pos] = j, inv_key[pos] = key (inv_key nullable).
+// inv[pos] = j, inv_key[pos] = key (inv_key nullable). THREADS / 64 waves.
 //
-// The chunk is split into four contiguous quarters, one per wave. Pass 1:
-// each wave counts its quarter per bin into its own LDS row (per 64-key
-// tile, the lowest lane of each key's match adds the match size). After one
-// barrier the four rows become per-wave starting positions (the chunk's base
-// for the bin plus the counts of the earlier quarters). Pass 2: each wave
-// walks its quarter again in order; a key's position is its wave's running
-// start for the bin plus its rank among equal keys in the tile, then the
-// lowest lane advances the start. Waves touch only their own LDS row, in
-// program order, so pass 2 needs no barriers.
-template <typename KeyT>
-__global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restrict__ keys,
-                                                           int64_t n, int B, int nbits,
-                                                           int64_t chunk, int nchunks,
-                                                           const int* __restrict__ hist,
-                                                           int* __restrict__ offsets,
-                                                           int* __restrict__ fwd,
-                                                           int* __restrict__ inv,
-                                                           uint8_t* __restrict__ inv_key) {
+// Prologue: per bin, the total count and the count in earlier chunks. The
+// threads form R = min(THREADS / B, nchunks) groups of B; group r sums chunks
+// r, r + R, ... so the loads spread over all threads, and the R partial sums
+// meet in LDS.
+//
+// The chunk is split into NW contiguous shares, one per wave. Pass 1: each
+// wave counts its share per bin into its own LDS row (per 64-key tile, the
+// lowest lane of each key's match adds the match size). After one barrier the
+// rows become per-wave starting positions (the chunk's base for the bin plus
+// the counts of the earlier shares). Pass 2: each wave walks its share again
+// in order; a key's position is its wave's running start for the bin plus its
+// rank among equal keys in the tile, then the lowest lane advances the start.
+// Waves touch only their own LDS row, in program order, so pass 2 needs no
+// barriers. More waves make each wave's serial walk shorter: the kernel is
+// bound by that walk's latency, not by throughput.
+template <typename KeyT, int THREADS>
+__global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ keys, int64_t n,
+                                                      int B, int nbits, int64_t chunk,
+                                                      int nchunks, const int* __restrict__ hist,
+                                                      int* __restrict__ offsets,
+                                                      int* __restrict__ fwd,
+                                                      int* __restrict__ inv,
+                                                      uint8_t* __restrict__ inv_key) {
+  constexpr int NW = THREADS / kWave;
+  // one LDS row of B counters per wave: the launch uses sixteen waves only for
+  // B <= kMaxExperts / 4, and four waves for any B <= kMaxExperts
+  constexpr int kMaxB = NW > 4 ? kMaxExperts / 4 : kMaxExperts;
+  constexpr int kRowInts = NW * kMaxB;
+  static_assert(NW == 4 || NW == 16, "launched with 256 or 1024 threads");
   __shared__ int sbase[kMaxExperts];
   __shared__ int stot[kMaxExperts];
-  __shared__ int wrow[kSortWaves][kMaxExperts];
+  __shared__ int wrow[kRowInts];
+  __shared__ int ppre[THREADS > kMaxExperts ? THREADS : kMaxExperts];  // R * B entries
+  __shared__ int ptot[THREADS > kMaxExperts ? THREADS : kMaxExperts];
   __shared__ int stotal;
   const int t = threadIdx.x;
   const int w = wave_id();
   const int lane = t & (kWave - 1);
   const int c = blockIdx.x;
-  for (int b = t; b < B; b += kSortThreads) {
-#pragma unroll
-    for (int v = 0; v < kSortWaves; ++v) wrow[v][b] = 0;
-  }
-  // per bin: total count, and the count in chunks before this one. One bin
-  // per thread; its (at most kMaxChunks) counts are all loaded before any is
-  // added, so the loads overlap.
-  for (int b = t; b < B; b += kSortThreads) {
-    int v[kMaxChunks];
-#pragma unroll
-    for (int q = 0; q < kMaxChunks; ++q) v[q] = q < nchunks ? hist[q * B + b] : 0;
+  for (int i = t; i < NW * B; i += THREADS) wrow[i] = 0;
+
+  const int R = THREADS / B < nchunks ? (THREADS / B > 0 ? THREADS / B : 1) : nchunks;
+  for (int i = t; i < R * B; i += THREADS) {  // one pass when B <= THREADS
+    const int r = i / B, b = i - r * B;
     int tot = 0, pre = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxChunks; ++q) {
-      tot += v[q];
-      pre += q < c ? v[q] : 0;
+#pragma unroll 4
+    for (int q = r; q < nchunks; q += R) {
+      const int v = hist[q * B + b];
+      tot += v;
+      pre += q < c ? v : 0;
+    }
+    ppre[i] = pre;
+    ptot[i] = tot;
+  }
+  __syncthreads();
+  for (int b = t; b < B; b += THREADS) {
+    int tot = 0, pre = 0;
+    for (int r = 0; r < R; ++r) {
+      tot += ptot[r * B + b];
+      pre += ppre[r * B + b];
     }
     sbase[b] = pre;
     stot[b] = tot;
@@ -167,19 +184,20 @@ __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restric
     if (lane == kWave - 1) stotal = incl;
   }
   __syncthreads();
-  for (int b = t; b < B; b += kSortThreads) {
+  for (int b = t; b < B; b += THREADS) {
     if (c == 0) offsets[b] = stot[b];
     sbase[b] += stot[b];
   }
   if (c == 0 && t == 0) offsets[B] = stotal;
 
-  // this wave's quarter of the chunk
+  // this wave's share of the chunk
   const int64_t clo = static_cast<int64_t>(c) * chunk;
   const int64_t chi = clo + chunk < n ? clo + chunk : n;
-  const int64_t quarter = chunk / kSortWaves;
-  const int64_t qlo = clo + w * quarter;
-  const int64_t qhi = qlo + quarter < chi ? qlo + quarter : chi;
+  const int64_t share = chunk / NW;
+  const int64_t qlo = clo + w * share;
+  const int64_t qhi = qlo + share < chi ? qlo + share : chi;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int* myrow = wrow + w * B;
 
   // keys are read kBatch tiles (of 64) at a time, all loads issued before
   // any tile is processed; the first batch stays in registers for pass 2
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restric
   uint32_t first[kBatch];
   load_batch(first, qlo);
 
-  // pass 1: per-bin counts of the quarter
+  // pass 1: per-bin counts of the share
   for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
     uint32_t kb[kBatch];
     if (jb == qlo) {
@@ -209,17 +227,17 @@ __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restric
       const uint32_t k = kb[q];
       const bool valid = k < static_cast<uint32_t>(B);
       const uint64_t m = match_key(k, valid, nbits);
-      if (valid && __popcll(m & below) == 0) wrow[w][k] += __popcll(m);
+      if (valid && __popcll(m & below) == 0) myrow[k] += __popcll(m);
     }
   }
   __syncthreads();
   // counts -> per-wave starting positions
-  for (int b = t; b < B; b += kSortThreads) {
+  for (int b = t; b < B; b += THREADS) {
     int run = sbase[b];
 #pragma unroll
-    for (int v = 0; v < kSortWaves; ++v) {
-      const int cnt = wrow[v][b];
-      wrow[v][b] = run;
+    for (int v = 0; v < NW; ++v) {
+      const int cnt = wrow[v * B + b];
+      wrow[v * B + b] = run;
       run += cnt;
     }
   }
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restric
       const uint64_t m = match_key(k, valid, nbits);
       const int rank = __popcll(m & below);
       int start = 0;
-      if (valid) start = wrow[w][k];
+      if (valid) start = myrow[k];
       if (valid) {
         const int pos = start + rank;
         fwd[j] = pos;
@@ -252,7 +270,7 @@ __global__ __launch_bounds__(kSortThreads) void csort_rank(const KeyT* __restric
       } else if (j < qhi) {
         fwd[j] = -1;
       }
-      if (valid && rank == 0) wrow[w][k] = start + __popcll(m);
+      if (valid && rank == 0) myrow[k] = start + __popcll(m);
     }
   }
 }
@@ -290,8 +308,14 @@ int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int
   const int nch = static_cast<int>(csort_nchunks(n, B));
   int* hist = static_cast<int*>(ws);
   csort_hist<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, chunk, nch, hist, err, ebit);
-  csort_rank<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, bits_for(B), chunk, nch, hist,
+  // sixteen waves per chunk where their LDS rows fit (B <= 256), else four
+  if (B <= kMaxExperts / 4)
+    csort_rank<KeyT, 1024><<<nch, 1024, 0, s>>>(keys, n, B, bits_for(B), chunk, nch, hist,
                                                  offsets, fwd, inv, inv_key);
+  else
+    csort_rank<KeyT, kSortThreads><<<nch, kSortThreads, 0, s>>>(keys, n, B, bits_for(B), chunk,
+                                                                nch, hist, offsets, fwd, inv,
+                                                                inv_key);
   return launch_status();
 }
 

@@ -27,10 +27,12 @@ __device__ __forceinline__ float key_float(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
 }
 
+// Lane permutation inside rows of 16 (every lane reads a lane of its own row,
+// so the bound control never applies; it lets the move fold into the max/min).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf, false));
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, true));
 }
 
 constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]
@@ -182,6 +184,117 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
+// The same selection with the shape fixed at compile time: E = S * V exactly,
+// K picks, H groups. Group h owns columns [h E/H, (h+1) E/H); when that range
+// is a multiple of S, lane s's value v (column s + S v) belongs to group
+// S v / (E/H) for every lane, so each round scans only its group's values and
+// no bound is checked.
+template <int S, int V, int K, int H>
+__global__ __launch_bounds__(kTopkThreads) void topk_fixed(const float* __restrict__ logits,
+                                                           int64_t n, int renorm,
+                                                           int* __restrict__ idx,
+                                                           float* __restrict__ wout) {
+  constexpr int E = S * V;
+  constexpr int EG = E / H;
+  constexpr int KG = K / H;
+  static_assert(E % H == 0 && K % H == 0 && EG % S == 0 && KG <= EG, "fixed top-K shape");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = lane & (S - 1);
+  const int seg_base = lane & ~(S - 1);
+  const int64_t tok = (static_cast<int64_t>(blockIdx.x) * kTopkThreads + threadIdx.x) / S;
+  const bool active = tok < n;  // inactive lanes read row 0 and still join the cross-lane steps
+  const float* row = logits + (active ? tok : 0) * static_cast<int64_t>(E);
+
+  float val[V];
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) val[v] = row[s + S * v];
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = order_key(val[v]);
+
+  float selv[K];
+  int selc[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int g = r / KG;
+    uint32_t best = 0u;
+    int bv = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if ((S * v) / EG != g) continue;  // compile-time after unrolling
+      if (key[v] > best) {  // strict: lowest v on equal keys
+        best = key[v];
+        bv = v;
+      }
+    }
+    const uint32_t m = seg_max<S>(best);
+    int col;
+    if (V == 1) {
+      const uint64_t tie = __ballot(best == m);
+      const uint64_t mine = (tie >> seg_base) & (S == 64 ? ~0ull : ((1ull << S) - 1));
+      col = __builtin_ctzll(mine);
+    } else {
+      col = static_cast<int>(
+          seg_min<S>(best == m ? static_cast<uint32_t>(s + S * bv) : 0xffffffffu));
+    }
+    // remove the pick: the winning lane (col % S) drops its best value,
+    // which is the pick itself (value bv, the lowest v on equal keys)
+    const bool mine = s == (col & (S - 1));
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((S * v) / EG == g) key[v] = (mine && bv == v) ? 0u : key[v];
+    selc[r] = col;
+    selv[r] = key_float(m);
+  }
+
+  // Lane s < K of the segment finishes pick s: its weight is one exponential
+  // and one division, the softmax sum a segment reduction (over the group's
+  // KG lanes when KG is a power of two, else over the whole segment, H = 1).
+  static_assert(K <= S, "one lane per pick");
+  static_assert(H == 1 || (KG & (KG - 1)) == 0, "groups reduce over aligned lane groups");
+  float mysel = selv[0];
+  int mycol = selc[0];
+#pragma unroll
+  for (int r = 1; r < K; ++r) {
+    if (s == r) {
+      mysel = selv[r];
+      mycol = selc[r];
+    }
+  }
+  const int g = s / KG;
+  float w;
+  if (renorm) {
+    float gmax = selv[0];  // a group's first pick is its max
+#pragma unroll
+    for (int q = 1; q < H; ++q)
+      if (g == q) gmax = selv[q * KG];
+    const float e = s < K ? __expf(mysel - gmax) : 0.f;
+    float z = e;
+    if (H == 1) {
+#pragma unroll
+      for (int o = S / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+    } else {
+#pragma unroll
+      for (int o = KG / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+    }
+    w = __fdividef(e, z);
+  } else {
+    float mall = selv[0];
+#pragma unroll
+    for (int q = 1; q < H; ++q) mall = fmaxf(mall, selv[q * KG]);
+    float zl = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) zl += __expf(val[v] - mall);
+#pragma unroll
+    for (int o = S / 2; o > 0; o >>= 1) zl += __shfl_xor(zl, o, kWave);
+    w = __fdividef(__expf(mysel - mall), zl);
+  }
+  if (active && s < K) {
+    idx[tok * K + s] = mycol;
+    if (wout) wout[tok * K + s] = w;
+  }
+}
+
 template <int S, int V>
 static void launch_topk(const float* logits, int64_t n, int E, int K, int H, int renorm,
                         int* idx, float* w, hipStream_t s) {
@@ -200,6 +313,19 @@ ROUTE_API int route_topk(const float* logits, int64_t n, int32_t E, int32_t K, i
   if (E > kMaxExperts || K > kMaxK) return ROUTE_ERR_UNSUPPORTED;
   if (n == 0) return ROUTE_OK;
   if (!logits || !idx) return ROUTE_ERR_NULL;
+  // shapes of the routing workloads, fixed at compile time
+#define ROUTE_FIXED(s_, v_, k_, h_)                                                       \
+  if (E == s_ * v_ && K == k_ && H == h_) {                                               \
+    topk_fixed<s_, v_, k_, h_><<<ceil_div(n * s_, kTopkThreads), kTopkThreads, 0, s>>>(   \
+        logits, n, renorm, idx, weights);                                                 \
+    return launch_status();                                                               \
+  }
+  ROUTE_FIXED(16, 10, 6, 1)
+  ROUTE_FIXED(16, 8, 8, 1)
+  ROUTE_FIXED(16, 4, 8, 4)
+  ROUTE_FIXED(8, 1, 2, 1)
+  ROUTE_FIXED(4, 1, 2, 1)
+#undef ROUTE_FIXED
   if (E <= 4)
     launch_topk<4, 1>(logits, n, E, K, H, renorm, idx, weights, s);
   else if (E <= 8)
