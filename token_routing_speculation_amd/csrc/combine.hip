@@ -18,6 +18,8 @@
 namespace route {
 
 constexpr int kCombThreads = 256;
+constexpr int kCombGroup = 2;         // 16-byte vectors per lane gathered per step
+constexpr bool kCombPingPong = true;  // next step's gathers issued before this step's stores
 
 // Stores the combined vector v of a row (bf16 or float32 output).
 template <int OUT_F32>
@@ -68,8 +70,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ weights,
     const int* __restrict__ slot_of_pair, int64_t n, int d, const int* __restrict__ out_row,
     void* __restrict__ out, uint32_t* err) {
-  constexpr int GV = 2;                       // vectors per group
-  constexpr int NG = (CPL + GV - 1) / GV;     // groups per lane
+  constexpr int GV = kCombGroup < CPL ? kCombGroup : CPL;  // vectors per group
+  constexpr int NG = (CPL + GV - 1) / GV;                   // groups per lane
   const int64_t j = static_cast<int64_t>(blockIdx.x) * (kCombThreads / kWave) + wave_id();
   if (j >= n) return;
   int slot[KT];
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   if (bad && lane_id() == 0) set_err(err, ROUTE_EBIT_INDEX_RANGE);
   const int lane = lane_id();
   const int nv = d >> 3;
-  u32x4 buf[2][KT][GV];
+  u32x4 buf[kCombPingPong ? 2 : 1][KT][GV];
   auto gather = [&](u32x4 (&b)[KT][GV], int g) {
 #pragma unroll
     for (int q = 0; q < GV; ++q) {
@@ -112,11 +114,19 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
       if (v < nv) store_out<OUT_F32>(out, dst, d, v, acc);
     }
   };
-  gather(buf[0], 0);
+  if (kCombPingPong) {
+    gather(buf[0], 0);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (g + 1 < NG) gather(buf[(g + 1) & 1], g + 1);
-    finish(buf[g & 1], g);
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) gather(buf[(g + 1) & 1], g + 1);
+      finish(buf[g & 1], g);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      gather(buf[0], g);
+      finish(buf[0], g);
+    }
   }
 }
 
