@@ -6,7 +6,8 @@ links this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 helper with the HIP library.
 
 Every function is a plain, slow, obviously correct definition written from
-three web pages on the subject:
+three web pages on the subject (``oracle.eg`` holds the s-EG expert
+placement of the "Speculative MoE" notes, sections 3.2 and 4.2):
 
 * "Speculative MoE" notes (research-notes-783.pages.dev/p/speculative-moe/):
   route prediction tables (section 4.1), the shuffled reduce-scatter SRS and
@@ -59,4 +60,11 @@ PINS = {
     "route_estimator": "math.erf GELU; torch linear in float64",
     "hit_count": "pred == truth gives N*K; disjoint gives 0; random gives about K/E",
     "route_lut_build": "per-id brute force over cluster shares",
+    "eg.splitmix64": "first three published outputs of the reference generator (seed 0)",
+    "eg.coact_profile": "conservation: counts sum to n*K, rows to K*freq",
+    "eg.eg_score": "G=1 gives all local; T/G <= local <= T; relabelling; planted all-local",
+    "eg.eg_objective": "closed forms (all local + balanced = 0; nothing local + one full cluster)",
+    "eg.eg_sample": "equal capacity always; a one-hot table is reproduced; first-draw frequencies",
+    "eg.eg_update": "one elite with alpha=1 gives its one-hot; tie to lower index; incumbent kept",
+    "eg.ceo_place": "finds the planted block placement (every activation local)",
 }
