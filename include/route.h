@@ -64,7 +64,8 @@ enum {
   ROUTE_EBIT_TOKEN_RANGE = 1u,   /* token id < 0 or >= vocab                    */
   ROUTE_EBIT_DEST_RANGE = 2u,    /* cluster id >= G                             */
   ROUTE_EBIT_EXPERT_RANGE = 4u,  /* expert id < 0 or >= E                       */
-  ROUTE_EBIT_INDEX_RANGE = 8u    /* slot / row / pair index out of range        */
+  ROUTE_EBIT_INDEX_RANGE = 8u,   /* slot / row / pair index out of range        */
+  ROUTE_EBIT_VALUE_RANGE = 16u   /* a count or placement entry out of its range */
 };
 
 /* Readable name of a status code (host; static string). */
@@ -253,6 +254,83 @@ size_t route_estimator_workspace_size(int64_t n, int32_t hd);
  */
 int hit_count(const int32_t* pred, const int32_t* truth, int64_t n, int32_t K,
               unsigned long long* hits, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Speculative expert grouping (s-EG): [SMOE] section 3.2 (co-activated
+ * experts placed in one cluster, offline, with the gate's columns permuted)
+ * and section 4.2 (balanced token-expert co-clustering, a theta-weighted
+ * sum of token-load imbalance and cross-cluster activations with equal
+ * experts per cluster, solved by a two-stage cross-entropy method).
+ *
+ * Readings (the pages give the terms, not their normalisation or the
+ * method's steps): a token goes to the cluster holding most of its
+ * activations (lowest cluster on ties); a placement x scores
+ *   J = (1 - theta) * (1 - local / total) + theta * (G * max_g load[g] / tokens - 1)
+ * with local = sum over tokens of that best cluster's activations and
+ * load[g] the token count sent to g; the cross-entropy stage keeps a table
+ * P[E][G] of placement probabilities. One solver iteration is
+ * eg_sample -> eg_score -> eg_update, all enqueued (no host round trip).
+ * Limits: E % 4 == 0, E % G == 0, E <= 1024, G <= 32, B <= 1024.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * eg_profile - token-id x expert activation counts of a routed batch.
+ *   tok int32[n]; idx int32[n][K] (a route_topk output); row_of_id int32
+ *   [vocab]: the profile row of each id, -1 for ids not profiled; counts
+ *   int32[U][E] and freq int32[U] are ADDED to (caller-zeroed):
+ *   counts[u][idx[i][k]] += 1 and freq[u] += 1 for u = row_of_id[tok[i]].
+ * Device bits: TOKEN_RANGE, INDEX_RANGE (row_of_id < 0 or >= U), EXPERT_RANGE;
+ * the offending pair is skipped. Integer atomics: exact in any order.
+ */
+int eg_profile(const int32_t* tok, const int32_t* idx, int64_t n, int32_t K,
+               const int32_t* row_of_id, int32_t vocab, int32_t U, int32_t E, int32_t* counts,
+               int32_t* freq, uint32_t* err, hipStream_t s);
+
+/*
+ * eg_init - solver state: P[e][g] = 1/G (float64 [E][G]) and *best_J = +inf.
+ */
+int eg_init(double* P, int32_t E, int32_t G, double* best_J, hipStream_t s);
+
+/*
+ * eg_sample - B candidate placements place uint8[B][E]. Candidate b takes
+ * experts in index order; expert e goes to the first cluster g whose running
+ * sum of P[e][g'] over clusters with room left (E/G experts each) exceeds
+ * u * W, W that total and u = (SplitMix64 output n >> 11) * 2^-53 for the
+ * generator seeded with `seed` and n = (iter * B + b) * E + e + 1. When
+ * rounding leaves no such g, the last open cluster of positive weight; when
+ * W = 0, the first open cluster.
+ */
+int eg_sample(const double* P, int32_t E, int32_t G, int32_t B, uint64_t seed, int32_t iter,
+              uint8_t* place, hipStream_t s);
+
+/*
+ * eg_score - scores of B placements against a profile.
+ *   counts int32[U][E] (each entry <= 65535, each row summing below 2^24,
+ *   else VALUE_RANGE), freq int32[U], place uint8[B][E] (entries < G, else
+ *   VALUE_RANGE) -> local int64[B], load int64[B][G] (overwritten).
+ *   ws: eg_score_workspace_size(U, E, G, B) bytes, 16-byte aligned.
+ * Exact integer results (bf16 matrix-core product of the counts' high and
+ * low bytes against one-hot placements; every partial sum an integer below
+ * 2^24).
+ */
+size_t eg_score_workspace_size(int32_t U, int32_t E, int32_t G, int32_t B);
+int eg_score(const int32_t* counts, const int32_t* freq, int32_t U, int32_t E, int32_t G,
+             const uint8_t* place, int32_t B, long long* local, long long* load, void* ws,
+             size_t ws_bytes, uint32_t* err, hipStream_t s);
+
+/*
+ * eg_update - one cross-entropy step. J[b] (float64, nullable output) as
+ * above from local, load, total (activations in the profile) and tokens
+ * (sum of freq); candidate b is elite when fewer than n_elite candidates
+ * precede it (lower J, or equal J and lower index); then
+ *   P[e][g] = alpha * (#elite with place[b][e] == g) / n_elite + (1 - alpha) * P[e][g]
+ * and, if the lowest J is below *best_J, *best_J and best_place uint8[E]
+ * take that candidate's. Float64 in exactly this operation order.
+ */
+int eg_update(const long long* local, const long long* load, const uint8_t* place, int32_t B,
+              int32_t E, int32_t G, long long total, long long tokens, double theta,
+              int32_t n_elite, double alpha, double* P, double* best_J, uint8_t* best_place,
+              double* J, hipStream_t s);
 
 #ifdef __cplusplus
 }

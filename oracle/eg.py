@@ -94,9 +94,8 @@ def eg_score(counts, freq, place, G):
     local = np.zeros(B, dtype=np.int64)
     load = np.zeros((B, G), dtype=np.int64)
     for b in range(B):
-        onehot = np.zeros((counts.shape[1], G), dtype=np.int64)
-        onehot[np.arange(counts.shape[1]), place[b]] = 1
-        S = counts @ onehot                       # [U][G]
+        # S[u][g]: token u's activations of the experts placed in cluster g
+        S = np.stack([counts[:, place[b] == g].sum(axis=1) for g in range(G)], axis=1)
         best = np.argmax(S, axis=1)               # first maximum: lowest g on ties
         local[b] = S[np.arange(S.shape[0]), best].sum()
         load[b] = np.bincount(best, weights=freq, minlength=G).astype(np.int64)

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -137,3 +137,36 @@ def test_workspace_sizes_monotone(L):
     assert L.srs_shuffle_workspace_size(-1, 8) == 0
     assert L.moe_permute_workspace_size(16384, 6, 160) < L.moe_permute_workspace_size(32768, 8, 160)
     assert L.moe_permute_workspace_size(10, 2, 2000) == 0
+
+
+def test_eg_errors(L):
+    # eg_profile(tok, idx, n, K, row_of_id, vocab, U, E, counts, freq, err, s)
+    f = L.eg_profile
+    assert f(A, A, -1, 2, A, 10, 4, 8, A, A, None, None) == SHAPE
+    assert f(A, A, 10, 2, A, 10, 4, 2000, A, A, None, None) == UNSUP
+    assert f(None, A, 10, 2, A, 10, 4, 8, A, A, None, None) == NULL
+    assert f(None, None, 0, 2, None, 10, 4, 8, None, None, None, None) == OK
+    # eg_sample(P, E, G, B, seed, iter, place, s)
+    f = L.eg_sample
+    assert f(A, 10, 4, 8, 0, 0, A, None) == SHAPE      # E % 4
+    assert f(A, 16, 3, 8, 0, 0, A, None) == SHAPE      # E % G
+    assert f(A, 64, 64, 8, 0, 0, A, None) == UNSUP     # G > 32
+    assert f(A, 16, 4, 2000, 0, 0, A, None) == UNSUP   # B > 1024
+    assert f(None, 16, 4, 8, 0, 0, A, None) == NULL
+    # eg_score(counts, freq, U, E, G, place, B, local, load, ws, ws_bytes, err, s)
+    f = L.eg_score
+    need = L.eg_score_workspace_size(100, 16, 4, 8)
+    assert need > 0 and L.eg_score_workspace_size(100, 15, 4, 8) == 0
+    assert f(A, A, 100, 16, 4, A, 8, A, A, A, need - 1, None, None) == WS
+    assert f(A, A, 100, 16, 4, A, 8, A, A, MIS, need, None, None) == WS
+    assert f(A, A, 100, 16, 4, None, 8, A, A, A, need, None, None) == NULL
+    assert f(A, A, 100, 18, 4, A, 8, A, A, A, need, None, None) == SHAPE
+    # eg_update(local, load, place, B, E, G, total, tokens, theta, n_elite, alpha, P, bJ, bp, J, s)
+    f = L.eg_update
+    assert f(A, A, A, 8, 16, 4, 100, 50, 0.0, 0, 0.5, A, A, A, None, None) == SHAPE
+    assert f(A, A, A, 8, 16, 4, 100, 50, 0.0, 9, 0.5, A, A, A, None, None) == SHAPE
+    assert f(A, A, A, 8, 16, 4, 0, 50, 0.0, 1, 0.5, A, A, A, None, None) == SHAPE
+    assert f(A, A, None, 8, 16, 4, 100, 50, 0.0, 1, 0.5, A, A, A, None, None) == NULL
+    # eg_init(P, E, G, best_J, s)
+    assert L.eg_init(A, 16, 5, A, None) == SHAPE
+    assert L.eg_init(None, 16, 4, A, None) == NULL

@@ -23,7 +23,8 @@ __all__ = [
     "route_predict", "route_lut_build", "srs_shuffle", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_combine", "route_qhidden", "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
-    "route_estimator_workspace_size", "EXPORTS",
+    "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
+    "eg_score_workspace_size", "eg_score", "eg_update", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,8 +33,10 @@ _LIB_PATH = os.path.join(_HERE, "libroute.so")
 # status codes and device error bits (include/route.h)
 ROUTE_OK = 0
 EBIT_TOKEN_RANGE, EBIT_DEST_RANGE, EBIT_EXPERT_RANGE, EBIT_INDEX_RANGE = 1, 2, 4, 8
+EBIT_VALUE_RANGE = 16
 
 _p, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_u64, _f64 = ctypes.c_uint64, ctypes.c_double
 
 # name -> (restype, argtypes), in the header's order
 EXPORTS = {
@@ -52,6 +55,13 @@ EXPORTS = {
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
+    "eg_profile": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "eg_init": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
+    "eg_sample": (ctypes.c_int, [_p, _i32, _i32, _i32, _u64, _i32, _p, _p]),
+    "eg_score_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "eg_score": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _sz, _p, _p]),
+    "eg_update": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i64, _i64, _f64, _i32, _f64,
+                                 _p, _p, _p, _p, _p]),
 }
 
 
@@ -288,3 +298,63 @@ def hit_count(pred, truth, hits, stream=None):
     _call("hit_count", _dev(pred, torch.int32, "pred"), _dev(truth, torch.int32, "truth", n * K),
           n, K, _dev(hits, torch.int64, "hits", 1), _stream(stream))
     return hits
+
+
+# ------------------------------------------------------------ s-EG placement
+
+def eg_profile(tok, idx, row_of_id, counts, freq, err=None, stream=None):
+    """counts [U][E] += activations of tok[n] routed to idx[n][K]; freq [U] += occurrences."""
+    n, K = idx.shape
+    U, E = counts.shape
+    _call("eg_profile", _dev(tok, torch.int32, "tok", n), _dev(idx, torch.int32, "idx"), n, K,
+          _dev(row_of_id, torch.int32, "row_of_id"), row_of_id.numel(), U, E,
+          _dev(counts, torch.int32, "counts"), _dev(freq, torch.int32, "freq", U),
+          _opt(err, torch.int32, "err", 1), _stream(stream))
+    return counts, freq
+
+
+def eg_init(P, best_J, stream=None):
+    E, G = P.shape
+    _call("eg_init", _dev(P, torch.float64, "P"), E, G, _dev(best_J, torch.float64, "best_J", 1),
+          _stream(stream))
+    return P, best_J
+
+
+def eg_sample(P, B, seed, it, place=None, stream=None):
+    E, G = P.shape
+    place = _empty((B, E), torch.uint8, P) if place is None else place
+    _call("eg_sample", _dev(P, torch.float64, "P"), E, G, B, int(seed) & ((1 << 64) - 1), it,
+          _dev(place, torch.uint8, "place", B * E), _stream(stream))
+    return place
+
+
+def eg_score_workspace_size(U: int, E: int, G: int, B: int) -> int:
+    return int(lib().eg_score_workspace_size(U, E, G, B))
+
+
+def eg_score(counts, freq, place, G, local=None, load=None, ws=None, err=None, stream=None):
+    """local [B] and load [B][G] (int64) of placements place [B][E] against a profile."""
+    U, E = counts.shape
+    B = place.shape[0]
+    local = _empty((B,), torch.int64, place) if local is None else local
+    load = _empty((B, G), torch.int64, place) if load is None else load
+    need = eg_score_workspace_size(U, E, G, B)
+    ws = _empty((max(need, 16),), torch.uint8, place) if ws is None else ws
+    _call("eg_score", _dev(counts, torch.int32, "counts"), _dev(freq, torch.int32, "freq", U),
+          U, E, G, _dev(place, torch.uint8, "place", B * E), B,
+          _dev(local, torch.int64, "local", B), _dev(load, torch.int64, "load", B * G),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1),
+          _stream(stream))
+    return local, load
+
+
+def eg_update(local, load, place, total, tokens, theta, n_elite, alpha, P, best_J, best_place,
+              J=None, stream=None):
+    B, E = place.shape
+    G = P.shape[1]
+    _call("eg_update", _dev(local, torch.int64, "local", B), _dev(load, torch.int64, "load", B * G),
+          _dev(place, torch.uint8, "place"), B, E, G, int(total), int(tokens), float(theta),
+          int(n_elite), float(alpha), _dev(P, torch.float64, "P", E * G),
+          _dev(best_J, torch.float64, "best_J", 1), _dev(best_place, torch.uint8, "best_place", E),
+          _opt(J, torch.float64, "J", B), _stream(stream))
+    return P, best_J, best_place

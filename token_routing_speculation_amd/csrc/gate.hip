@@ -22,6 +22,7 @@
 // and by "Speculating Experts Accelerates Inference for Mixture-of-Experts"
 // (item 2.A: next gate on q_l; item 2.C: the estimator MLP).
 #include "common.hpp"
+#include "gemm.hpp"
 #include <type_traits>
 
 namespace route {
@@ -541,6 +542,11 @@ static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, 
   else
     launch_nt<1>(NT, grid, s, A, M, Kd, B, N, bias, C, epi);
   return launch_status();
+}
+
+int gemm_f32(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, float* C,
+             hipStream_t s) {
+  return gemm_launch(A, M, Kd, B, N, nullptr, C, EPI_F32, s);
 }
 
 }  // namespace route

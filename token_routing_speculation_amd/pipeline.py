@@ -10,6 +10,11 @@ grouped top-k/H -> LAR -> permute from the group activations -> combine
 (cross-group sum), the grouped block of the "Federation of Experts (FoE)"
 article.
 
+``ExpertGrouping``: the s-EG expert placement of the "Speculative MoE" notes
+(sections 3.2 and 4.2): a token-expert activation profile, then cross-entropy
+iterations (sample -> score -> update), all enqueued, and ``grouped_gate`` to
+regroup the gate's rows by cluster.
+
 ``PredictorPass``: q_l -> next gate (or the estimator on early layers) ->
 top-K, and the next layer's true top-K -> hit count ("Speculating Experts
 Accelerates Inference for Mixture-of-Experts", items 2.A, 2.C and 4).
@@ -29,7 +34,8 @@ import torch
 from . import (route_predict, route_lut_build, srs_shuffle, route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
-               route_estimator_workspace_size)
+               route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
+               eg_update, eg_score_workspace_size)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -248,3 +254,62 @@ class PredictorPass:
             route_gate(self.q, L["w_next"], logits=self.logits)
         route_topk(self.logits, self.K, 1, 1, idx=self.pred, want_weights=False)
         hit_count(self.pred, self.truth, self.hits)
+
+
+class ExpertGrouping:
+    """Cross-entropy placement of E experts in G equal clusters from a
+    token-expert activation profile. Every step is a library call; ``step``
+    and ``solve`` allocate nothing, so an iteration can be captured."""
+
+    def __init__(self, U, E, G, B=256, theta=0.0, rho=0.1, alpha=0.7, seed=0, device="cuda"):
+        self.U, self.E, self.G, self.B = U, E, G, B
+        self.theta, self.alpha, self.seed = theta, alpha, seed
+        self.n_elite = max(1, int(np.ceil(rho * B)))
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.counts = z((U, E), torch.int32)
+        self.freq = z((U,), torch.int32)
+        self.P = z((E, G), torch.float64)
+        self.best_J = z((1,), torch.float64)
+        self.best_place = z((E,), torch.uint8)
+        self.place = z((B, E), torch.uint8)
+        self.local = z((B,), torch.int64)
+        self.load = z((B, G), torch.int64)
+        self.J = z((B,), torch.float64)
+        self.ws = z((max(eg_score_workspace_size(U, E, G, B), 16),), torch.uint8)
+        self.err = z((1,), torch.int32)
+        self.total = 0
+        self.tokens = 0
+
+    def profile(self, tok, idx, row_of_id):
+        """Adds a routed batch (tok [n] ids, idx [n][K] experts) to the profile."""
+        eg_profile(tok, idx, row_of_id, self.counts, self.freq, err=self.err)
+        self.total += idx.numel()
+        self.tokens += idx.shape[0]
+
+    def reset(self):
+        eg_init(self.P, self.best_J)
+        self.best_place.zero_()
+
+    def step(self, it):
+        eg_sample(self.P, self.B, self.seed, it, place=self.place)
+        eg_score(self.counts, self.freq, self.place, self.G, local=self.local, load=self.load,
+                 ws=self.ws, err=self.err)
+        eg_update(self.local, self.load, self.place, self.total, self.tokens, self.theta,
+                  self.n_elite, self.alpha, self.P, self.best_J, self.best_place, J=self.J)
+
+    def solve(self, iters):
+        self.reset()
+        for it in range(iters):
+            self.step(it)
+        return self.best_place
+
+
+def grouped_gate(w, place, G):
+    """The gate's rows regrouped by cluster (stable within a cluster): returns
+    (w_grouped [E][d], expert_offsets [G+1], new_of_old [E], old_of_new [E]).
+    Expert e of the old numbering is row new_of_old[e] of w_grouped, and the
+    experts of cluster g are rows expert_offsets[g] .. expert_offsets[g+1]-1."""
+    E = w.shape[0]
+    keys = place.to(torch.int32).view(E, 1)
+    offs, new_of_old, old_of_new, wg = moe_permute(keys, G, w.view(1, E, -1), 1)
+    return wg, offs, new_of_old, old_of_new
