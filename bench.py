@@ -127,6 +127,102 @@ def lar_rate(p, pairs):
     return int(p.local.item()) / pairs
 
 
+def eg_bench(args):
+    """s-EG expert placement ("Speculative MoE" notes, sections 3.2 and 4.2) on
+    the DeepSeek-V2-shaped model: profile a held-out routed batch, solve the
+    placement by cross-entropy iterations, then route the benchmark batch with
+    the default contiguous placement and with the solved one and compare the
+    local activation rate and the cluster load balance."""
+    import torch
+    from synth import make_config_inputs, get_config
+    from token_routing_speculation_amd.pipeline import RoutePass, ExpertGrouping
+
+    cfg = get_config(args.config)
+    torch.cuda.set_device(0)
+    # profile: a held-out batch of the same model, routed by the library
+    prof = make_config_inputs(args.config, sample=1)
+    pp = RoutePass(prof)
+    pp.predict(); pp.srs(); pp.gate(); pp.topk()
+    tok_rows = torch.from_numpy(prof["tok"]).cuda()[pp.src_of_row.long()].to(torch.int32)
+    ids = np.unique(prof["tok"])
+    row_of_id = np.full(cfg.V, -1, np.int32)
+    row_of_id[ids] = np.arange(len(ids), dtype=np.int32)
+    U = len(ids)
+    g = ExpertGrouping(U, cfg.E, cfg.G, B=args.eg_candidates, theta=args.eg_theta, seed=7)
+    g.profile(tok_rows, pp.idx, torch.from_numpy(row_of_id).cuda())
+    torch.cuda.synchronize()
+    del pp
+    stream = torch.cuda.current_stream()
+    iters = args.eg_iters
+    # per-stage times over a few iterations, then the whole solve
+    g.reset()
+    from token_routing_speculation_amd import eg_sample, eg_score, eg_update
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
+    for it in range(5):
+        ev[it][0].record(stream)
+        eg_sample(g.P, g.B, g.seed, it, place=g.place)
+        ev[it][1].record(stream)
+        eg_score(g.counts, g.freq, g.place, g.G, local=g.local, load=g.load, ws=g.ws, err=g.err)
+        ev[it][2].record(stream)
+        eg_update(g.local, g.load, g.place, g.total, g.tokens, g.theta, g.n_elite, g.alpha,
+                  g.P, g.best_J, g.best_place, J=g.J)
+        ev[it][3].record(stream)
+    torch.cuda.synchronize()
+    stage = {n: 1e3 * np.median([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(1, 5)])
+             for k, n in enumerate(("sample", "score", "update"))}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    best = g.solve(iters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    solve_ms = e0.elapsed_time(e1)
+    place = best.cpu().numpy()
+
+    eval_inp = make_config_inputs(args.config)
+
+    def route_with(expert_cluster):
+        inp = dict(eval_inp, expert_cluster=expert_cluster)
+        p = RoutePass(inp)
+        lar = lar_rate(p, cfg.N * cfg.K)
+        offs = p.cluster_offsets.cpu().numpy()
+        sizes = np.diff(offs)
+        return lar, float(sizes.max() / sizes.mean())
+
+    from synth.gen import default_expert_cluster
+    lar0, imb0 = route_with(default_expert_cluster(cfg.E, cfg.G))
+    lar1, imb1 = route_with(place.astype(np.uint8))
+    # score-stage roofline: the matrix-core product (exact integer counts)
+    flops = 2.0 * U * (2 * cfg.E) * g.B * cfg.G
+    out = {
+        "metric": "s-EG cross-entropy placement: solve time and local activation rate gain",
+        "value": iters / (solve_ms * 1e-3), "unit": "solver iterations/s",
+        "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": ROUTE_WORKLOADS[args.config], "profile_tokens": cfg.N,
+                   "profiled_ids": U, "E": cfg.E, "G": cfg.G, "candidates": g.B,
+                   "iterations": iters, "theta": g.theta, "elite": g.n_elite, "alpha": g.alpha},
+        "solve_ms": solve_ms, "stage_us": {k: round(v, 2) for k, v in stage.items()},
+        "score_gemm_tflops_at_stage_time": flops / (stage["score"] * 1e-6) / 1e12,
+        "best_J": float(g.best_J.item()),
+        "lar_default_placement": lar0, "lar_eg_placement": lar1,
+        "lar_gain": lar1 / lar0 - 1.0,
+        "cluster_load_max_over_mean": {"default": imb0, "eg": imb1},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import eg as oeg
+        counts = g.counts.cpu().numpy().astype(np.int64)
+        freq = g.freq.cpu().numpy().astype(np.int64)
+        t0 = time.perf_counter()
+        total_its = 2
+        oeg.ceo_place(counts, freq, cfg.G, theta=g.theta, B=g.B, iters=total_its, seed=7)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": total_its / dt, "unit": "solver iterations/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{total_its} oracle iterations (float64 NumPy) on the "
+                                         f"same profile; {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +233,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the pass replayed as a HIP graph)")
+    ap.add_argument("--eg", action="store_true",
+                    help="measure the s-EG expert placement instead of the routing pass")
+    ap.add_argument("--eg-iters", type=int, default=40)
+    ap.add_argument("--eg-candidates", type=int, default=256)
+    ap.add_argument("--eg-theta", type=float, default=0.0)
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -148,6 +249,14 @@ def main(argv=None):
     from synth import make_config_inputs, get_config
     from token_routing_speculation_amd.pipeline import RoutePass, FoEPass, capture_graph
 
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 3
+    if args.eg:
+        if args.config == "foe":
+            print("--eg measures a routing workload (tiny, mixtral, deepseek)", file=sys.stderr)
+            return 2
+        return eg_bench(args)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3

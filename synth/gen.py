@@ -19,6 +19,9 @@ Recipe (all streams are ``numpy.random.default_rng([seed, stream, ...])``):
   ``A[G][G]`` uniform in [0, G) (stream 6), previous-layer clusters
   ``prev2, prev1`` uniform in [0, G) (stream 7).
 
+Another batch of the same model (``sample`` > 0, for profiling) keys the
+token, noise and split streams as ``[seed, stream, sample]``.
+
 Variance convention: ``N(0, v)`` names the variance, so W has std 1/sqrt(d).
 """
 
@@ -97,16 +100,21 @@ def foe_row_cluster(N: int, H: int, G: int) -> np.ndarray:
 
 
 def make_route_inputs(N, d, E, K, P, G, V, seed, *, lut_mode="random",
-                      ngram=False, zipf_s=1.1, noise=0.3):
-    """Inputs of the predict -> SRS -> gate -> top-K -> permute -> combine pass."""
-    tok = zipf_ids(_rng(seed, 0), N, V, zipf_s)
+                      ngram=False, zipf_s=1.1, noise=0.3, sample=0):
+    """Inputs of the predict -> SRS -> gate -> top-K -> permute -> combine pass.
+
+    ``sample`` > 0 draws another batch of the same model: new token ids,
+    noise and partial split (streams [seed, 0|2|3, sample]), the same per-id
+    base rows and gate weights."""
+    key = (lambda st: _rng(seed, st)) if sample == 0 else (lambda st: _rng(seed, st, sample))
+    tok = zipf_ids(key(0), N, V, zipf_s)
     ids_present = np.unique(tok).astype(np.int32)
     base = _base_rows(seed, ids_present, d)
     where = np.searchsorted(ids_present, tok)
-    hidden = _rng(seed, 2).standard_normal((N, d), dtype=np.float32)
+    hidden = key(2).standard_normal((N, d), dtype=np.float32)
     hidden *= np.float32(noise)
     hidden += base[where]
-    partials = _zero_sum_split(_rng(seed, 3), hidden, P)
+    partials = _zero_sum_split(key(3), hidden, P)
     del hidden
     w = to_bf16_bits(_rng(seed, 4).standard_normal((E, d), dtype=np.float32)
                      / np.float32(np.sqrt(d)))
@@ -176,14 +184,15 @@ def make_predictor_layer(cfg: PredictorConfig, l: int, N=None):
     return out
 
 
-def make_config_inputs(name: str, N=None):
-    """Inputs of a named workload (route or FoE); N overrides the token count."""
+def make_config_inputs(name: str, N=None, sample=0):
+    """Inputs of a named workload (route or FoE); N overrides the token count;
+    ``sample`` > 0 draws another batch of a routing workload's model."""
     cfg = get_config(name)
     n = cfg.N if N is None else N
     if isinstance(cfg, RouteConfig):
         return make_route_inputs(n, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, cfg.V, cfg.seed,
                                  lut_mode=cfg.lut_mode, ngram=cfg.ngram,
-                                 zipf_s=cfg.zipf_s, noise=cfg.noise)
+                                 zipf_s=cfg.zipf_s, noise=cfg.noise, sample=sample)
     if isinstance(cfg, FoEConfig):
         return make_foe_inputs(n, cfg.d, cfg.E, cfg.H, cfg.K, cfg.G, cfg.V, cfg.seed,
                                zipf_s=cfg.zipf_s, noise=cfg.noise)

@@ -35,8 +35,10 @@ namespace route {
 constexpr int kEgThreads = 256;
 constexpr int kEgMaxG = 32;
 constexpr int kEgMaxB = 1024;
-constexpr int kEgRowsPerBlock = 16;   // tokens per block in the score reduction
-constexpr int kEgSampleThreads = 64;  // candidates per block in the sampler
+constexpr int kEgRowsPerBlock = 8;    // tokens per block in the score reduction
+constexpr int kEgUpdateLdsBytes = 32768;  // elite placements staged in LDS up to this
+constexpr int kEgSampleThreads = 32;  // candidates per block in the sampler
+constexpr int kEgSampleLdsDoubles = 4096;  // P staged in LDS up to E * G of this
 
 // ------------------------------------------------------------------- profile
 __global__ __launch_bounds__(kEgThreads) void eg_profile_kernel(
@@ -77,42 +79,93 @@ __device__ __forceinline__ unsigned long long splitmix64(unsigned long long seed
 
 // One thread per candidate b: experts in index order; expert e goes to
 // cluster g with probability P[e][g] / W among the clusters with room left
-// (W their total): the first g whose running sum exceeds u * W.
+// (W their total): the first g whose running sum exceeds u * W. GM >= G is a
+// compile-time bound so the capacities live in registers; sums run over
+// g < G in index order. The table is staged in LDS when it fits (each step of
+// a walk reads one row of it).
+template <bool LDS_P, int GM, bool EXACT>
 __global__ __launch_bounds__(kEgSampleThreads) void eg_sample_kernel(
-    const double* __restrict__ P, int E, int G, int B, unsigned long long seed, int iter,
+    const double* __restrict__ P, int E, int G_, int B, unsigned long long seed, int iter,
     uint8_t* __restrict__ place) {
-  __shared__ int cap[kEgMaxG][kEgSampleThreads];
+  const int G = EXACT ? GM : G_;  // EXACT: G == GM, every bound below folds away
+  __shared__ double sP[LDS_P ? kEgSampleLdsDoubles : 1];
   const int t = threadIdx.x;
+  if (LDS_P) {
+    for (int i = t; i < E * G; i += kEgSampleThreads) sP[i] = P[i];
+    __syncthreads();
+  }
+  const double* Pt = LDS_P ? sP : P;
   const int b = blockIdx.x * kEgSampleThreads + t;
   if (b >= B) return;  // no barrier below: every thread works alone
-  for (int g = 0; g < G; ++g) cap[g][t] = E / G;
+  int cap[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) cap[g] = g < G ? E / G : 0;
   uint8_t* out = place + static_cast<int64_t>(b) * E;
+  // draw n for expert e of this candidate; the walk does not feed the
+  // generator, so each step computes the next draw alongside its own sums
+  const unsigned long long n0 =
+      (static_cast<unsigned long long>(iter) * B + b) * static_cast<unsigned long long>(E) + 1;
+  auto draw = [&](int e) {
+    return static_cast<double>(splitmix64(seed, n0 + e) >> 11) * 0x1.0p-53;
+  };
+  double u = draw(0);
   for (int e = 0; e < E; ++e) {
-    const double* pe = P + static_cast<int64_t>(e) * G;
+    const double u_next = draw(e + 1 < E ? e + 1 : e);
+    const double* pe = Pt + static_cast<int64_t>(e) * G;
+    double w[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) w[g] = g < G ? pe[g] : 0.0;
+#pragma unroll
+    for (int g = 0; g < GM; ++g) w[g] = cap[g] > 0 ? w[g] : 0.0;
     double W = 0.0;
-    for (int g = 0; g < G; ++g) {
-      const double w = cap[g][t] > 0 ? pe[g] : 0.0;
-      W = W + w;
-    }
-    const unsigned long long n =
-        (static_cast<unsigned long long>(iter) * B + b) * static_cast<unsigned long long>(E) +
-        e + 1;
-    const double u = static_cast<double>(splitmix64(seed, n) >> 11) * 0x1.0p-53;
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+      if (g < G) W = W + w[g];
     const double target = u * W;
     int pick = -1, last_pos = -1, first_open = -1;
     double c = 0.0;
-    for (int g = 0; g < G; ++g) {
-      const bool open = cap[g][t] > 0;
-      const double w = open ? pe[g] : 0.0;
-      c = c + w;
-      if (pick < 0 && w > 0.0 && c > target) pick = g;
-      if (w > 0.0) last_pos = g;
-      if (open && first_open < 0) first_open = g;
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      if (g < G) {
+        c = c + w[g];
+        if (pick < 0 && w[g] > 0.0 && c > target) pick = g;
+        if (w[g] > 0.0) last_pos = g;
+        if (cap[g] > 0 && first_open < 0) first_open = g;
+      }
     }
     if (pick < 0) pick = W > 0.0 ? last_pos : first_open;
     out[e] = static_cast<uint8_t>(pick);
-    cap[pick][t] -= 1;
+#pragma unroll
+    for (int g = 0; g < GM; ++g) cap[g] -= g == pick ? 1 : 0;
+    u = u_next;
   }
+}
+
+template <bool LDS_P, int GM>
+static void launch_sample_g(int E, int G, int B, unsigned long long seed, int iter,
+                            const double* P, uint8_t* place, hipStream_t s) {
+  const unsigned grid = ceil_div(B, kEgSampleThreads);
+  if (G == GM)
+    eg_sample_kernel<LDS_P, GM, true><<<grid, kEgSampleThreads, 0, s>>>(P, E, G, B, seed, iter,
+                                                                       place);
+  else
+    eg_sample_kernel<LDS_P, GM, false><<<grid, kEgSampleThreads, 0, s>>>(P, E, G, B, seed, iter,
+                                                                        place);
+}
+
+template <bool LDS_P>
+static void launch_sample(int E, int G, int B, unsigned long long seed, int iter, const double* P,
+                          uint8_t* place, hipStream_t s) {
+  if (G <= 2)
+    launch_sample_g<LDS_P, 2>(E, G, B, seed, iter, P, place, s);
+  else if (G <= 4)
+    launch_sample_g<LDS_P, 4>(E, G, B, seed, iter, P, place, s);
+  else if (G <= 8)
+    launch_sample_g<LDS_P, 8>(E, G, B, seed, iter, P, place, s);
+  else if (G <= 16)
+    launch_sample_g<LDS_P, 16>(E, G, B, seed, iter, P, place, s);
+  else
+    launch_sample_g<LDS_P, 32>(E, G, B, seed, iter, P, place, s);
 }
 
 // -------------------------------------------------------------------- score
@@ -170,8 +223,9 @@ __global__ __launch_bounds__(kEgThreads) void eg_onehot_kernel(const uint8_t* __
 }
 
 // Stage 1 of the reduction: thread = candidate b, block = kEgRowsPerBlock
-// tokens; each token's first maximum over its G cluster sums. Writes this
-// block's partial [local, load[0..G-1]] per candidate.
+// tokens (all their sums loaded before any is used); each token's first
+// maximum over its G cluster sums. Writes this block's partial
+// [local, load[0..G-1]] per candidate.
 template <int GM>
 __global__ __launch_bounds__(kEgThreads) void eg_reduce_kernel(const float* __restrict__ S,
                                                                const int* __restrict__ freq,
@@ -180,30 +234,36 @@ __global__ __launch_bounds__(kEgThreads) void eg_reduce_kernel(const float* __re
   const int b = blockIdx.y * kEgThreads + threadIdx.x;
   if (b >= B) return;
   const int u0 = blockIdx.x * kEgRowsPerBlock;
-  const int u1 = u0 + kEgRowsPerBlock < U ? u0 + kEgRowsPerBlock : U;
   const int64_t ld = static_cast<int64_t>(B) * G;
+  float v[kEgRowsPerBlock][GM];
+  long long f[kEgRowsPerBlock];
+#pragma unroll
+  for (int q = 0; q < kEgRowsPerBlock; ++q) {
+    const int u = u0 + q < U ? u0 + q : U - 1;  // past the end: reload the last row, unused
+    const float* s = S + u * ld + static_cast<int64_t>(b) * G;
+#pragma unroll
+    for (int g = 0; g < GM; ++g) v[q][g] = g < G ? s[g] : 0.f;
+    f[q] = freq[u];
+  }
   long long loc = 0;
   long long lo[GM];
 #pragma unroll
   for (int g = 0; g < GM; ++g) lo[g] = 0;
-  for (int u = u0; u < u1; ++u) {
-    const float* s = S + u * ld + static_cast<int64_t>(b) * G;
-    float best = s[0];
+#pragma unroll
+  for (int q = 0; q < kEgRowsPerBlock; ++q) {
+    if (u0 + q >= U) break;
+    float best = v[q][0];
     int bg = 0;
 #pragma unroll
     for (int g = 1; g < GM; ++g) {
-      if (g < G) {
-        const float v = s[g];
-        if (v > best) {  // strict: the lowest g on equal sums
-          best = v;
-          bg = g;
-        }
+      if (g < G && v[q][g] > best) {  // strict: the lowest g on equal sums
+        best = v[q][g];
+        bg = g;
       }
     }
     loc += static_cast<long long>(best);
-    const long long f = freq[u];
 #pragma unroll
-    for (int g = 0; g < GM; ++g) lo[g] += g == bg ? f : 0;
+    for (int g = 0; g < GM; ++g) lo[g] += g == bg ? f[q] : 0;
   }
   long long* out = part + (static_cast<int64_t>(blockIdx.x) * B + b) * (G + 1);
   out[0] = loc;
@@ -212,21 +272,27 @@ __global__ __launch_bounds__(kEgThreads) void eg_reduce_kernel(const float* __re
     if (g < G) out[1 + g] = lo[g];
 }
 
-// Stage 2: sums the blocks' partials in block order (one thread per output).
+// Stage 2: one wave per output sums the blocks' partials (integer sums: the
+// order does not change the result).
 __global__ __launch_bounds__(kEgThreads) void eg_finish_kernel(const long long* __restrict__ part,
                                                                int nblk, int G, int B,
                                                                long long* __restrict__ local,
                                                                long long* __restrict__ load) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kEgThreads + threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kEgThreads / kWave) + wave_id();
   if (t >= static_cast<int64_t>(B) * (G + 1)) return;
   const int b = static_cast<int>(t / (G + 1));
   const int q = static_cast<int>(t - static_cast<int64_t>(b) * (G + 1));
   long long acc = 0;
-  for (int k = 0; k < nblk; ++k) acc += part[(static_cast<int64_t>(k) * B + b) * (G + 1) + q];
-  if (q == 0)
-    local[b] = acc;
-  else
-    load[static_cast<int64_t>(b) * G + q - 1] = acc;
+  for (int k = lane_id(); k < nblk; k += kWave)
+    acc += part[(static_cast<int64_t>(k) * B + b) * (G + 1) + q];
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if (lane_id() == 0) {
+    if (q == 0)
+      local[b] = acc;
+    else
+      load[static_cast<int64_t>(b) * G + q - 1] = acc;
+  }
 }
 
 // ------------------------------------------------------------------- update
@@ -237,6 +303,8 @@ __global__ __launch_bounds__(kEgMaxB) void eg_update_kernel(
     uint8_t* __restrict__ best_place, double* __restrict__ Jout) {
   __shared__ double sJ[kEgMaxB];
   __shared__ unsigned char elite[kEgMaxB];
+  __shared__ int erank[kEgMaxB];  // elite rank -> candidate
+  __shared__ uint8_t eplace[kEgUpdateLdsBytes];
   __shared__ int sbmin;
   __shared__ int improved;
   const int t = threadIdx.x;
@@ -258,15 +326,29 @@ __global__ __launch_bounds__(kEgMaxB) void eg_update_kernel(
     int rank = 0;
     for (int c = 0; c < B; ++c) rank += (sJ[c] < Jb || (c < b && sJ[c] == Jb)) ? 1 : 0;
     elite[b] = rank < n_elite ? 1 : 0;
+    if (rank < n_elite) erank[rank] = b;
     if (rank == 0) sbmin = b;
+  }
+  __syncthreads();
+  // the elite placements, in rank order, staged in LDS when they fit
+  const bool staged = static_cast<int64_t>(n_elite) * E <= kEgUpdateLdsBytes;
+  if (staged) {
+    for (int i = t; i < n_elite * E; i += kEgMaxB) {
+      const int r = i / E;
+      eplace[i] = place[static_cast<int64_t>(erank[r]) * E + (i - r * E)];
+    }
   }
   __syncthreads();
   for (int i = t; i < E * G; i += kEgMaxB) {
     const int e = i / G;
     const int g = i - e * G;
     int cnt = 0;
-    for (int b = 0; b < B; ++b)
-      cnt += (elite[b] && place[static_cast<int64_t>(b) * E + e] == g) ? 1 : 0;
+    if (staged) {
+      for (int r = 0; r < n_elite; ++r) cnt += eplace[r * E + e] == g ? 1 : 0;
+    } else {
+      for (int b = 0; b < B; ++b)
+        cnt += (elite[b] && place[static_cast<int64_t>(b) * E + e] == g) ? 1 : 0;
+    }
     const double share = static_cast<double>(cnt) / static_cast<double>(n_elite);
     P[i] = alpha * share + (1.0 - alpha) * P[i];
   }
@@ -330,8 +412,10 @@ ROUTE_API int eg_sample(const double* P, int32_t E, int32_t G, int32_t B, uint64
   if (!eg_shape_ok(0, E, G) || B < 1 || iter < 0) return ROUTE_ERR_SHAPE;
   if (E > kMaxExperts || G > kEgMaxG || B > kEgMaxB) return ROUTE_ERR_UNSUPPORTED;
   if (!P || !place) return ROUTE_ERR_NULL;
-  eg_sample_kernel<<<ceil_div(B, kEgSampleThreads), kEgSampleThreads, 0, s>>>(P, E, G, B, seed,
-                                                                             iter, place);
+  if (E * G <= kEgSampleLdsDoubles)
+    launch_sample<true>(E, G, B, seed, iter, P, place, s);
+  else
+    launch_sample<false>(E, G, B, seed, iter, P, place, s);
   return launch_status();
 }
 
@@ -380,8 +464,8 @@ ROUTE_API int eg_score(const int32_t* counts, const int32_t* freq, int32_t U, in
     eg_reduce_kernel<16><<<grid, kEgThreads, 0, s>>>(S, freq, U, G, B, part);
   else
     eg_reduce_kernel<32><<<grid, kEgThreads, 0, s>>>(S, freq, U, G, B, part);
-  eg_finish_kernel<<<ceil_div(static_cast<int64_t>(B) * (G + 1), kEgThreads), kEgThreads, 0, s>>>(
-      part, nblk, G, B, local, load);
+  eg_finish_kernel<<<ceil_div(static_cast<int64_t>(B) * (G + 1), kEgThreads / kWave), kEgThreads,
+                     0, s>>>(part, nblk, G, B, local, load);
   return launch_status();
 }
 
