@@ -223,12 +223,139 @@ def eg_bench(args):
     return 0
 
 
+def predictor_bytes(N, d, E, K, hd, estimator):
+    """Algorithmic HBM bytes of one source layer's prediction (q_l -> logits ->
+    top-K -> hits), each call reading its inputs and writing its outputs once."""
+    b = 2
+    st = {"qhidden": 2 * N * d * b + 4 * d,
+          "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
+          if estimator else (N * d * b + E * d * b + 4 * N * E),
+          "topk": 4 * N * E + 4 * N * K,
+          "hits": 8 * N * K + 8}
+    return st
+
+
+def predictor_bench(args):
+    """The q_l predictor of "Speculating Experts Accelerates Inference for
+    Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
+    source layers of the Qwen3-30B-A3B-shaped workload: per layer q_l = LN(d_l
+    + r_l), the next gate on q_l (the MLP estimator on the early layers),
+    top-K and the hit count against the next layer's true top-K (computed
+    beforehand: it is layer l+1's own routing, not part of the prediction)."""
+    import torch
+    from synth import get_config
+    from synth.gen import make_predictor_layer
+    from token_routing_speculation_amd.pipeline import PredictorPass, capture_graph, to_device
+
+    cfg = get_config("qwen3")
+    torch.cuda.set_device(0)
+    N = cfg.N
+    p = PredictorPass(N, cfg.d, cfg.E, cfg.K, cfg.hd)
+    layers, truths, est = [], [], []
+    for l in range(cfg.L - 1):
+        lay = make_predictor_layer(cfg, l)
+        p.load(lay)
+        p.truth = torch.empty((N, cfg.K), dtype=torch.int32, device="cuda")
+        p.truth_step()
+        layers.append(p.layer)
+        truths.append(p.truth)
+        est.append(bool(lay["estimator"]))
+    torch.cuda.synchronize()
+
+    def sweep():
+        for L_, T_ in zip(layers, truths):
+            p.layer, p.truth = L_, T_
+            p.step()
+
+    for _ in range(args.warmup):
+        sweep()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = capture_graph(sweep)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(K):
+        graph.replay()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev[0].elapsed_time(ev[K]) / K
+    # per-stage times of one eager sweep, on an estimator layer and a gate layer
+    def stage_times(i):
+        p.layer, p.truth = layers[i], truths[i]
+        from token_routing_speculation_amd import route_qhidden, route_estimator, route_gate, route_topk, hit_count
+        L_ = p.layer
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        tt = {"qhidden": [], "logits": [], "topk": [], "hits": []}
+        for _ in range(10):
+            e[0].record(stream)
+            route_qhidden(L_["r"], L_["dvec"], eps=L_["eps"], q=p.q)
+            e[1].record(stream)
+            if L_["estimator"]:
+                route_estimator(p.q, L_["w1"], L_["b1"], L_["w2"], L_["b2"], logits=p.logits, ws=p.ws)
+            else:
+                route_gate(p.q, L_["w_next"], logits=p.logits)
+            e[2].record(stream)
+            route_topk(p.logits, p.K, 1, 1, idx=p.pred, want_weights=False)
+            e[3].record(stream)
+            hit_count(p.pred, p.truth, p.hits)
+            e[4].record(stream)
+            torch.cuda.synchronize()
+            for j, k_ in enumerate(tt):
+                tt[k_].append(1e3 * e[j].elapsed_time(e[j + 1]))
+        return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
+    st_est, st_gate = stage_times(0), stage_times(cfg.L - 2)
+    # hit rates per layer (one sweep from zeroed counters)
+    p.hits.zero_()
+    rates = []
+    for L_, T_ in zip(layers, truths):
+        before = int(p.hits.item())
+        p.layer, p.truth = L_, T_
+        p.step()
+        rates.append((int(p.hits.item()) - before) / (N * cfg.K))
+    nl = cfg.L - 1
+    byt_gate = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False)
+    byt_est = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, True)
+    ne = sum(est)
+    total_bytes = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_gate.values())
+    q_us = st_gate["qhidden"]
+    out = {
+        "metric": "q_l expert-prediction throughput over all source layers (token-predictions/s)",
+        "value": N * nl / (ms * 1e-3), "unit": "token-predictions/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": ms, "launch": "hip graph replay",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-30b-a3b-shaped predictor", "layers": nl, "N": N, "d": cfg.d,
+                   "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
+        "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
+        "alg_bytes_sweep": total_bytes,
+        "stages_us_gate_layer": st_gate, "stages_us_estimator_layer": st_est,
+        "roofline": {"bound": "hbm", "kernel": "qhidden_kernel (route_qhidden)",
+                     "achieved": byt_gate["qhidden"] / (q_us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": byt_gate["qhidden"] / (q_us * 1e-6) / HBM_PEAK,
+                     "traffic": None},
+        "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
+        / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
+        "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),
+        "hit_rate_gate_layers": float(np.mean([r for r, e_ in zip(rates, est) if not e_])),
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="deepseek", choices=["tiny", "mixtral", "deepseek", "foe"])
+    ap.add_argument("--config", default="deepseek",
+                    choices=["tiny", "mixtral", "deepseek", "foe", "qwen3"])
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -252,6 +379,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if args.config == "qwen3":
+        return predictor_bench(args)
     if args.eg:
         if args.config == "foe":
             print("--eg measures a routing workload (tiny, mixtral, deepseek)", file=sys.stderr)

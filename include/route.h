@@ -223,7 +223,8 @@ int moe_combine(const uint16_t* y, const float* weights, const int32_t* slot_of_
  * [SPEC] item 2.A: default vector plus residual, normalised with the next
  * layer's LayerNorm (biased variance over d, binary32 statistics).
  *   r bf16 rows [n][d]; dvec float[d]; gamma, beta float[d] (nullable =>
- *   1 and 0); q bf16 rows [n][d] (nearest even).
+ *   1 and 0); q bf16 rows [n][d] (nearest even). dvec, gamma and beta are
+ *   16-byte aligned like the rows.
  * Errors: NULL, SHAPE (d % 8, eps < 0), ALIGN, UNSUPPORTED (d > 8192).
  */
 int route_qhidden(const uint16_t* r, const float* dvec, const float* gamma, const float* beta,

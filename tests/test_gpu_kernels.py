@@ -251,6 +251,17 @@ def test_hit_count_duplicates_as_sets():
     assert int(hits.item()) == 4
 
 
+@pytest.mark.parametrize("K", [2, 4, 6, 8])
+def test_hit_count_duplicates_even_k(K):
+    # the vector-load kernels (even K) on rows with repeated and shared ids
+    rng = np.random.default_rng(K)
+    p = rng.integers(0, 5, (301, K)).astype(np.int32)
+    t = rng.integers(0, 5, (301, K)).astype(np.int32)
+    hits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tr.hit_count(dev(p), dev(t), hits)
+    assert int(hits.item()) == oracle.hit_count(p, t)
+
+
 # --------------------------------------------------------- q_l, estimator
 @pytest.mark.parametrize("n,d,affine", [(1, 8, False), (100, 128, True), (8192, 2048, False),
                                         (33, 8192, True), (257, 520, True)])

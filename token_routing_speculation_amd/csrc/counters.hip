@@ -70,6 +70,42 @@ __global__ __launch_bounds__(kCntThreads) void hit_kernel(const int32_t* __restr
   block_add(cnt, hits);
 }
 
+// K a compile-time even number: each row read as K/2 eight-byte vectors,
+// all issued before any compare.
+template <int KT>
+__global__ __launch_bounds__(kCntThreads) void hit_kernel_k(const int32_t* __restrict__ pred,
+                                                            const int32_t* __restrict__ truth,
+                                                            int64_t n,
+                                                            unsigned long long* __restrict__ hits) {
+  static_assert(KT % 2 == 0, "pairs of ids per load");
+  unsigned cnt = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCntThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kCntThreads) {
+    int t[KT], p[KT];
+    const int2* tr = reinterpret_cast<const int2*>(truth + i * KT);
+    const int2* pr = reinterpret_cast<const int2*>(pred + i * KT);
+#pragma unroll
+    for (int k = 0; k < KT / 2; ++k) {
+      const int2 a = tr[k], b = pr[k];
+      t[2 * k] = a.x;
+      t[2 * k + 1] = a.y;
+      p[2 * k] = b.x;
+      p[2 * k + 1] = b.y;
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      bool in_truth = false, seen = false;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        in_truth = in_truth || t[j] == p[k];
+        if (j < k) seen = seen || p[j] == p[k];
+      }
+      cnt += (in_truth && !seen) ? 1u : 0u;
+    }
+  }
+  block_add(cnt, hits);
+}
+
 }  // namespace route
 
 using namespace route;
@@ -95,7 +131,18 @@ ROUTE_API int hit_count(const int32_t* pred, const int32_t* truth, int64_t n, in
   if (!pred || !truth || !hits) return ROUTE_ERR_NULL;
   const unsigned grid = ceil_div(n, kCntThreads) < kCntMaxBlocks ? ceil_div(n, kCntThreads)
                                                                  : kCntMaxBlocks;
-  hit_kernel<<<grid, kCntThreads, 0, s>>>(pred, truth, n, K, hits);
+  const bool al8 = (reinterpret_cast<uintptr_t>(pred) & 7u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(truth) & 7u) == 0;
+  if (al8 && K == 8)
+    hit_kernel_k<8><<<grid, kCntThreads, 0, s>>>(pred, truth, n, hits);
+  else if (al8 && K == 6)
+    hit_kernel_k<6><<<grid, kCntThreads, 0, s>>>(pred, truth, n, hits);
+  else if (al8 && K == 4)
+    hit_kernel_k<4><<<grid, kCntThreads, 0, s>>>(pred, truth, n, hits);
+  else if (al8 && K == 2)
+    hit_kernel_k<2><<<grid, kCntThreads, 0, s>>>(pred, truth, n, hits);
+  else
+    hit_kernel<<<grid, kCntThreads, 0, s>>>(pred, truth, n, K, hits);
   return launch_status();
 }
 
