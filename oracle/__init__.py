@@ -7,7 +7,8 @@ helper with the HIP library.
 
 Every function is a plain, slow, obviously correct definition written from
 three web pages on the subject (``oracle.eg`` holds the s-EG expert
-placement of the "Speculative MoE" notes, sections 3.2 and 4.2):
+placement of the "Speculative MoE" notes, sections 3.2 and 4.2;
+``oracle.estfit`` the estimator fit of "Speculating Experts", item 2.C):
 
 * "Speculative MoE" notes (research-notes-783.pages.dev/p/speculative-moe/):
   route prediction tables (section 4.1), the shuffled reduce-scatter SRS and
@@ -67,4 +68,8 @@ PINS = {
     "eg.eg_sample": "equal capacity always; a one-hot table is reproduced; first-draw frequencies",
     "eg.eg_update": "one elite with alpha=1 gives its one-hot; tie to lower index; incumbent kept",
     "eg.ceo_place": "finds the planted block placement (every activation local)",
+    "estfit.est_gram": "Hadamard features give n*I; last row/diagonal are column sums and n",
+    "estfit.est_solve": "closed form on orthogonal features; exact linear target recovered; "
+                        "ridge residual identity",
+    "estfit.est_weights": "transpose and bf16 rounding of the recovered weights",
 }
