@@ -333,6 +333,52 @@ int eg_update(const long long* local, const long long* load, const uint8_t* plac
               int32_t n_elite, double alpha, double* P, double* best_J, uint8_t* best_place,
               double* J, hipStream_t s);
 
+/* ------------------------------------------------------------------------
+ * Estimator fit: [SPEC] item 2.C (a shallow network predicts the next
+ * layer's router logits from q_l) and item 4 (a few million training tokens
+ * suffice). Reading: the hidden layer GELU(q W1^T + b1) stays as drawn
+ * (random features, the estimator's own bf16 activations) and the output
+ * layer is the ridge fit (H'^T H' + lambda I) W' = H'^T Y with H' = [H | 1]
+ * and lambda = ridge * trace(H'^T H') / (hd + 1). Float64 throughout.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * route_est_hidden - the estimator's hidden layer alone: h bf16 rows [n][hd]
+ * = GELU(q W1^T + b1), exactly as route_estimator computes it.
+ * Errors: as route_estimator's first product (d % 8, hd % 8, hd > 4096).
+ */
+int route_est_hidden(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1,
+                     const float* b1, int32_t hd, uint16_t* h, hipStream_t s);
+
+/*
+ * est_fit_gram - gram float64[hd+1][hd+1] = H'^T H' and rhs float64[hd+1][E]
+ * = H'^T Y for features h bf16 [n][hd] and targets y float[n][E] (row-major).
+ * Products and sums in float64 (16 slices of the n rows, summed in order).
+ *   ws: est_fit_gram_workspace_size(n, hd, E) bytes.
+ * Errors: SHAPE (n < 1, hd < 1, E < 1), UNSUPPORTED (hd > 4096, E > 1024),
+ * WORKSPACE.
+ */
+size_t est_fit_gram_workspace_size(int64_t n, int32_t hd, int32_t E);
+int est_fit_gram(const uint16_t* h, const float* y, int64_t n, int32_t hd, int32_t E, double* gram,
+                 double* rhs, void* ws, size_t ws_bytes, hipStream_t s);
+
+/*
+ * est_fit_solve - in place: gram (m x m, m = hd + 1) gets lambda = ridge *
+ * trace / m added to its diagonal and is overwritten by its Cholesky factor
+ * (lower triangle; the upper is scratch); rhs (m x E) is overwritten by the
+ * solution W'. A non-positive pivot ORs 1 into the optional device *info.
+ * Errors: SHAPE (m < 1, E < 1, ridge < 0), UNSUPPORTED (m > 4097, E > 1024).
+ */
+int est_fit_solve(double* gram, double* rhs, int32_t m, int32_t E, double ridge, int32_t* info,
+                  hipStream_t s);
+
+/*
+ * est_fit_weights - w2 bf16 [E][hd] = W'[:hd]^T, each float64 value rounded
+ * once to the nearest bf16 (ties to even), and b2 float[E] = W'[hd].
+ */
+int est_fit_weights(const double* wsol, int32_t hd, int32_t E, uint16_t* w2, float* b2,
+                    hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

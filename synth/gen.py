@@ -154,7 +154,7 @@ def make_foe_inputs(N, d, E, H, K, G, V, seed, *, zipf_s=1.1, noise=0.3):
                 N=N, d=d, E=E, H=H, K=K, G=G, V=V)
 
 
-def make_predictor_layer(cfg: PredictorConfig, l: int, N=None):
+def make_predictor_layer(cfg: PredictorConfig, l: int, N=None, sample=0):
     """Inputs for source layer l (0 <= l < L-1) of the q_l predictor workload.
 
     r_l ~ N(0, 1) bf16; d_l ~ N(0, dvec_var) float32; the next layer's gate
@@ -166,12 +166,15 @@ def make_predictor_layer(cfg: PredictorConfig, l: int, N=None):
         raise ValueError("source layer out of range")
     N = cfg.N if N is None else N
     d, E, hd = cfg.d, cfg.E, cfg.hd
-    r = to_bf16_bits(_rng(cfg.seed, 10, l).standard_normal((N, d), dtype=np.float32))
+    # sample > 0: another batch of the same model (new r_l and drift noise)
+    key = (lambda st: _rng(cfg.seed, st, l)) if sample == 0 else \
+        (lambda st: _rng(cfg.seed, st, l, sample))
+    r = to_bf16_bits(key(10).standard_normal((N, d), dtype=np.float32))
     dvec = (_rng(cfg.seed, 11, l).standard_normal(d, dtype=np.float32)
             * np.float32(np.sqrt(cfg.dvec_var)))
     w_next = to_bf16_bits(_rng(cfg.seed, 12, l + 1).standard_normal((E, d), dtype=np.float32)
                           / np.float32(np.sqrt(d)))
-    s = from_bf16_bits(r) + np.float32(cfg.drift) * _rng(cfg.seed, 13, l).standard_normal(
+    s = from_bf16_bits(r) + np.float32(cfg.drift) * key(13).standard_normal(
         (N, d), dtype=np.float32)
     out = dict(r=r, dvec=dvec, w_next=w_next, s_next=to_bf16_bits(s),
                N=N, d=d, E=E, K=cfg.K, hd=hd, eps=cfg.eps, estimator=l in cfg.est_layers)

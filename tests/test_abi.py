@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -170,3 +170,26 @@ def test_eg_errors(L):
     # eg_init(P, E, G, best_J, s)
     assert L.eg_init(A, 16, 5, A, None) == SHAPE
     assert L.eg_init(None, 16, 4, A, None) == NULL
+
+
+def test_estfit_errors(L):
+    f = L.route_est_hidden
+    assert f(A, 10, 60, A, A, 64, A, None) == SHAPE
+    assert f(A, 10, 64, A, A, 8192, A, None) == UNSUP
+    assert f(None, 10, 64, A, A, 64, A, None) == NULL
+    assert f(MIS, 10, 64, A, A, 64, A, None) == ALIGN
+    assert f(None, 0, 64, None, None, 64, None, None) == OK
+    need = L.est_fit_gram_workspace_size(100, 64, 8)
+    assert need > 0 and L.est_fit_gram_workspace_size(100, 0, 8) == 0
+    f = L.est_fit_gram
+    assert f(A, A, 0, 64, 8, A, A, A, need, None) == SHAPE
+    assert f(A, A, 100, 64, 8, A, A, A, need - 1, None) == WS
+    assert f(A, A, 100, 5000, 8, A, A, A, need, None) == UNSUP
+    assert f(None, A, 100, 64, 8, A, A, A, need, None) == NULL
+    f = L.est_fit_solve
+    assert f(A, A, 0, 8, 0.1, None, None) == SHAPE
+    assert f(A, A, 65, 8, -1.0, None, None) == SHAPE
+    assert f(A, A, 5000, 8, 0.1, None, None) == UNSUP
+    assert f(None, A, 65, 8, 0.1, None, None) == NULL
+    assert L.est_fit_weights(A, 0, 8, A, A, None) == SHAPE
+    assert L.est_fit_weights(None, 64, 8, A, A, None) == NULL

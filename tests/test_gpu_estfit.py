@@ -1,0 +1,115 @@
+"""The estimator fit on the GPU against the oracle ("Speculating Experts
+Accelerates Inference for Mixture-of-Experts", item 2.C): Gram products,
+the regularised Cholesky solve, the weight rounding, the whole chain, and the
+hidden layer the estimator computes."""
+
+import numpy as np
+import pytest
+import torch
+
+import token_routing_speculation_amd as tr
+from oracle import estfit, gelu_erf
+from oracle.bf16 import round_bf16, bf16_to_f64
+
+from gpu_helpers import dev, host, assert_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(shape, seed, scale=1.0):
+    return round_bf16(np.random.default_rng(seed).standard_normal(shape) * scale)
+
+
+@pytest.mark.parametrize("n,hd,E", [(1, 1, 1), (37, 8, 3), (1000, 64, 16), (8192, 512, 128),
+                                    (300, 200, 77)])
+def test_gram(n, hd, E):
+    h = _bf16((n, hd), n + hd)
+    y = np.random.default_rng(E).standard_normal((n, E)).astype(np.float32)
+    G, R = tr.est_fit_gram(dev(h), dev(y))
+    wG, wR = estfit.est_gram(h, y)
+    np.testing.assert_allclose(host(G), wG, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(host(R), wR, rtol=1e-12, atol=1e-9)
+
+
+def _spd_case(m, E, seed):
+    rng = np.random.default_rng(seed)
+    X = round_bf16(rng.standard_normal((max(4 * m, 8), m - 1))) if m > 1 else np.zeros((8, 0), np.uint16)
+    y = rng.standard_normal((X.shape[0], E))
+    return estfit.est_gram(X, y)
+
+
+@pytest.mark.parametrize("m,E,ridge", [(1, 1, 0.1), (64, 8, 1e-3), (65, 1, 1e-2), (129, 33, 1e-4),
+                                       (513, 128, 1e-3)])
+def test_solve(m, E, ridge):
+    G, R = _spd_case(m, E, m + E)
+    Gd, Rd = dev(G.copy()), dev(R.copy())
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tr.est_fit_solve(Gd, Rd, ridge, info=info)
+    want = estfit.est_solve(G, R, ridge)
+    assert host(info)[0] == 0
+    np.testing.assert_allclose(host(Rd), want, rtol=1e-8, atol=1e-10 * np.abs(want).max())
+    # the factor: L L^T equals the regularised matrix
+    L = np.tril(host(Gd))
+    lam = ridge * np.trace(G) / m
+    np.testing.assert_allclose(L @ L.T, G + lam * np.eye(m), rtol=1e-10,
+                               atol=1e-10 * np.abs(G).max())
+
+
+def test_solve_flags_a_matrix_that_is_not_positive_definite():
+    G = -np.eye(70)
+    R = np.ones((70, 2))
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tr.est_fit_solve(dev(G), dev(R), 0.0, info=info)
+    assert host(info)[0] == 1
+
+
+def test_weights_rounding():
+    rng = np.random.default_rng(7)
+    hd, E = 40, 9
+    W = rng.standard_normal((hd + 1, E)) * 3.0
+    # exact ties between bf16 neighbours (to even), signed zero, huge, tiny
+    W[0, 0] = 1.0 + 2.0 ** -8
+    W[1, 0] = 1.0 + 3 * 2.0 ** -8
+    W[2, 0] = -0.0
+    W[3, 0] = 1e39
+    W[4, 0] = 3e-40
+    W[5, 0] = -(2.0 - 2.0 ** -9) * 2.0 ** 127
+    w2, b2 = tr.est_fit_weights(dev(W))
+    ww2, wb2 = estfit.est_weights(W)
+    assert np.array_equal(host(w2), ww2)
+    assert np.array_equal(host(b2), wb2)
+
+
+def test_fit_chain_matches_oracle():
+    n, hd, E, ridge = 4096, 256, 64, 1e-3
+    h = _bf16((n, hd), 11)
+    Wt = np.random.default_rng(12).standard_normal((hd + 1, E)) * 0.1
+    y = (np.concatenate([bf16_to_f64(h), np.ones((n, 1))], axis=1) @ Wt
+         + 0.05 * np.random.default_rng(13).standard_normal((n, E))).astype(np.float32)
+    G, R = tr.est_fit_gram(dev(h), dev(y))
+    tr.est_fit_solve(G, R, ridge)
+    w2, b2 = tr.est_fit_weights(R)
+    ww2, wb2, wW = estfit.est_fit(h, y, ridge)
+    np.testing.assert_allclose(host(R), wW, rtol=1e-8, atol=1e-12)
+    assert np.array_equal(host(b2), wb2)
+    # bf16 codes: equal unless the float64 solutions straddle a rounding
+    # boundary (their difference is ~1e-12 relative)
+    assert (host(w2) != ww2).mean() < 1e-4
+
+
+@pytest.mark.parametrize("n,d,hd", [(1, 64, 8), (999, 2048, 512), (64, 520, 40)])
+def test_est_hidden_is_the_estimators_hidden_layer(n, d, hd):
+    rng = np.random.default_rng(n + hd)
+    q = _bf16((n, d), 1)
+    w1 = _bf16((hd, d), 2, 1.0 / np.sqrt(d))
+    b1 = (rng.standard_normal(hd) * 0.1).astype(np.float32)
+    h = tr.route_est_hidden(dev(q), dev(w1), dev(b1))
+    ref = gelu_erf(bf16_to_f64(q) @ bf16_to_f64(w1).T + b1.astype(np.float64))
+    assert_bf16(host(h), ref, "hidden")
+    # and the estimator built on it: its logits use exactly this hidden layer
+    E = 16
+    w2 = _bf16((E, hd), 3, 1.0 / np.sqrt(hd))
+    b2 = np.zeros(E, np.float32)
+    lg = tr.route_estimator(dev(q), dev(w1), dev(b1), dev(w2), dev(b2))
+    lg2 = tr.route_gate(h, dev(w2))
+    assert np.array_equal(host(lg), host(lg2))

@@ -24,7 +24,8 @@ __all__ = [
     "lar_count", "moe_permute", "moe_combine", "route_qhidden", "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
-    "eg_score_workspace_size", "eg_score", "eg_update", "EXPORTS",
+    "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
+    "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,11 @@ EXPORTS = {
     "eg_score": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _sz, _p, _p]),
     "eg_update": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i64, _i64, _f64, _i32, _f64,
                                  _p, _p, _p, _p, _p]),
+    "route_est_hidden": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p]),
+    "est_fit_gram_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "est_fit_gram": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _p, _p, _p, _sz, _p]),
+    "est_fit_solve": (ctypes.c_int, [_p, _p, _i32, _i32, _f64, _p, _p]),
+    "est_fit_weights": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
 }
 
 
@@ -358,3 +364,54 @@ def eg_update(local, load, place, total, tokens, theta, n_elite, alpha, P, best_
           _dev(best_J, torch.float64, "best_J", 1), _dev(best_place, torch.uint8, "best_place", E),
           _opt(J, torch.float64, "J", B), _stream(stream))
     return P, best_J, best_place
+
+
+# ------------------------------------------------------------- estimator fit
+
+def route_est_hidden(q, w1, b1, h=None, stream=None):
+    """The estimator's hidden layer h [n][hd] = GELU(q W1^T + b1) (bf16)."""
+    n, d = q.shape
+    hd = w1.shape[0]
+    h = _empty((n, hd), _bf16(q), q) if h is None else h
+    _call("route_est_hidden", _dev(q, _bf16(q), "q"), n, d, _dev(w1, _bf16(w1), "w1", hd * d),
+          _dev(b1, torch.float32, "b1", hd), hd, _dev(h, _bf16(h), "h", n * hd), _stream(stream))
+    return h
+
+
+def est_fit_gram_workspace_size(n: int, hd: int, E: int) -> int:
+    return int(lib().est_fit_gram_workspace_size(n, hd, E))
+
+
+def est_fit_gram(h, y, gram=None, rhs=None, ws=None, stream=None):
+    """gram [hd+1][hd+1] = H'^T H', rhs [hd+1][E] = H'^T Y (float64)."""
+    n, hd = h.shape
+    E = y.shape[1]
+    gram = _empty((hd + 1, hd + 1), torch.float64, h) if gram is None else gram
+    rhs = _empty((hd + 1, E), torch.float64, h) if rhs is None else rhs
+    need = est_fit_gram_workspace_size(n, hd, E)
+    ws = _empty((max(need, 16),), torch.uint8, h) if ws is None else ws
+    _call("est_fit_gram", _dev(h, _bf16(h), "h"), _dev(y, torch.float32, "y", n * E), n, hd, E,
+          _dev(gram, torch.float64, "gram", (hd + 1) ** 2), _dev(rhs, torch.float64, "rhs", (hd + 1) * E),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+    return gram, rhs
+
+
+def est_fit_solve(gram, rhs, ridge, info=None, stream=None):
+    """In place: gram -> its Cholesky factor (after + lambda I), rhs -> W'."""
+    m = gram.shape[0]
+    E = rhs.shape[1]
+    _call("est_fit_solve", _dev(gram, torch.float64, "gram", m * m),
+          _dev(rhs, torch.float64, "rhs", m * E), m, E, float(ridge),
+          _opt(info, torch.int32, "info", 1), _stream(stream))
+    return rhs
+
+
+def est_fit_weights(wsol, w2=None, b2=None, stream=None):
+    """(w2 bf16 [E][hd], b2 float32 [E]) from W' [hd+1][E]."""
+    m, E = wsol.shape
+    hd = m - 1
+    w2 = _empty((E, hd), torch.bfloat16, wsol) if w2 is None else w2
+    b2 = _empty((E,), torch.float32, wsol) if b2 is None else b2
+    _call("est_fit_weights", _dev(wsol, torch.float64, "wsol", m * E), hd, E,
+          _dev(w2, _bf16(w2), "w2", E * hd), _dev(b2, torch.float32, "b2", E), _stream(stream))
+    return w2, b2

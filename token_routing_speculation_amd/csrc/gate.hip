@@ -563,6 +563,16 @@ ROUTE_API int route_gate(const uint16_t* x, int64_t n, int32_t d, const uint16_t
   return gemm_launch(x, n, d, w, E, nullptr, logits, EPI_F32, s);
 }
 
+ROUTE_API int route_est_hidden(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1,
+                              const float* b1, int32_t hd, uint16_t* h, hipStream_t s) {
+  if (n < 0 || d < 8 || d % 8 != 0 || hd < 8 || hd % 8 != 0) return ROUTE_ERR_SHAPE;
+  if (hd > 4096) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!q || !w1 || !b1 || !h) return ROUTE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(w1) || !aligned16(h)) return ROUTE_ERR_ALIGN;
+  return gemm_launch(q, n, d, w1, hd, b1, h, EPI_BIAS_GELU_BF16, s);
+}
+
 ROUTE_API size_t route_estimator_workspace_size(int64_t n, int32_t hd) {
   if (n < 0 || hd < 0) return 0;
   return align_up(static_cast<size_t>(n) * hd * sizeof(uint16_t), 256);
