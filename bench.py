@@ -235,6 +235,47 @@ def predictor_bytes(N, d, E, K, hd, estimator):
     return st
 
 
+def fit_estimator(cfg, l, lay, n_train, ridge):
+    """Fits layer l's estimator output weights on a held-out batch of the same
+    model ("Speculating Experts", item 2.C; ridge regression on the
+    estimator's own features) and stores them in ``lay``. Returns timings and
+    the hit rate of the gate on q_l for the same layer (the alternative the
+    estimator replaces)."""
+    import torch
+    import token_routing_speculation_amd as tr
+    from synth.gen import make_predictor_layer
+    from token_routing_speculation_amd.pipeline import to_device
+
+    tr_l = make_predictor_layer(cfg, l, N=n_train, sample=1)
+    dev_ = {k: to_device(v) for k, v in tr_l.items() if isinstance(v, np.ndarray)}
+    q = tr.route_qhidden(dev_["r"], dev_["dvec"], eps=cfg.eps)
+    y = tr.route_gate(dev_["s_next"], dev_["w_next"])
+    gram = torch.empty((cfg.hd + 1, cfg.hd + 1), dtype=torch.float64, device="cuda")
+    rhs = torch.empty((cfg.hd + 1, cfg.E), dtype=torch.float64, device="cuda")
+    ws = torch.empty(tr.est_fit_gram_workspace_size(n_train, cfg.hd, cfg.E), dtype=torch.uint8,
+                     device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    h = tr.route_est_hidden(q, dev_["w1"], dev_["b1"])
+    ev[1].record()
+    tr.est_fit_gram(h, y, gram=gram, rhs=rhs, ws=ws)
+    ev[2].record()
+    tr.est_fit_solve(gram, rhs, ridge, info=info)
+    ev[3].record()
+    w2, b2 = tr.est_fit_weights(rhs)
+    ev[4].record()
+    torch.cuda.synchronize()
+    if int(info.item()):
+        raise RuntimeError(f"estimator fit of layer {l}: matrix not positive definite")
+    lay["w2"] = w2.view(torch.int16).cpu().numpy().view(np.uint16)
+    lay["b2"] = b2.cpu().numpy()
+    t = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    return {"train_tokens": n_train, "ridge": ridge, "hidden_ms": t[0], "gram_ms": t[1],
+            "solve_ms": t[2], "weights_ms": t[3]}
+
+
 def predictor_bench(args):
     """The q_l predictor of "Speculating Experts Accelerates Inference for
     Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
@@ -252,8 +293,11 @@ def predictor_bench(args):
     N = cfg.N
     p = PredictorPass(N, cfg.d, cfg.E, cfg.K, cfg.hd)
     layers, truths, est = [], [], []
+    fit_info = {}
     for l in range(cfg.L - 1):
         lay = make_predictor_layer(cfg, l)
+        if args.fit and lay["estimator"]:
+            fit_info[l] = fit_estimator(cfg, l, lay, args.fit_tokens, args.fit_ridge)
         p.load(lay)
         p.truth = torch.empty((N, cfg.K), dtype=torch.int32, device="cuda")
         p.truth_step()
@@ -318,6 +362,15 @@ def predictor_bench(args):
         p.layer, p.truth = L_, T_
         p.step()
         rates.append((int(p.hits.item()) - before) / (N * cfg.K))
+    # the same estimator layers predicted by the next gate on q_l instead
+    gate_on_est = []
+    for L_, T_, e_ in zip(layers, truths, est):
+        if not e_:
+            continue
+        p.layer, p.truth = dict(L_, estimator=False), T_
+        before = int(p.hits.item())
+        p.step()
+        gate_on_est.append((int(p.hits.item()) - before) / (N * cfg.K))
     nl = cfg.L - 1
     byt_gate = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False)
     byt_est = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, True)
@@ -342,7 +395,12 @@ def predictor_bench(args):
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
         "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),
+        "estimator_weights": ("fitted (ridge on a held-out batch of %d tokens)" % args.fit_tokens)
+        if args.fit else "random (as drawn)",
+        "fit": fit_info or None,
         "hit_rate_gate_layers": float(np.mean([r for r, e_ in zip(rates, est) if not e_])),
+        "hit_rate_estimator_layers_by_gate_on_q": float(np.mean(gate_on_est)),
+        "hit_rate_per_estimator_layer": [round(r, 4) for r, e_ in zip(rates, est) if e_],
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
@@ -365,6 +423,10 @@ def main(argv=None):
     ap.add_argument("--eg-iters", type=int, default=40)
     ap.add_argument("--eg-candidates", type=int, default=256)
     ap.add_argument("--eg-theta", type=float, default=0.0)
+    ap.add_argument("--fit", action="store_true",
+                    help="qwen3: fit the estimator layers' output weights before timing")
+    ap.add_argument("--fit-tokens", type=int, default=32768)
+    ap.add_argument("--fit-ridge", type=float, default=1e-3)
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

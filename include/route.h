@@ -365,8 +365,9 @@ int est_fit_gram(const uint16_t* h, const float* y, int64_t n, int32_t hd, int32
 /*
  * est_fit_solve - in place: gram (m x m, m = hd + 1) gets lambda = ridge *
  * trace / m added to its diagonal and is overwritten by its Cholesky factor
- * (lower triangle; the upper is scratch); rhs (m x E) is overwritten by the
- * solution W'. A non-positive pivot ORs 1 into the optional device *info.
+ * L (lower triangle and diagonal) and L^T (strict upper triangle); rhs
+ * (m x E) is overwritten by the solution W'. A non-positive pivot ORs 1 into
+ * the optional device *info (that pivot is taken as 1 and the solve goes on).
  * Errors: SHAPE (m < 1, E < 1, ridge < 0), UNSUPPORTED (m > 4097, E > 1024).
  */
 int est_fit_solve(double* gram, double* rhs, int32_t m, int32_t E, double ridge, int32_t* info,

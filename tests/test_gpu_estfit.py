@@ -39,7 +39,7 @@ def _spd_case(m, E, seed):
 
 
 @pytest.mark.parametrize("m,E,ridge", [(1, 1, 0.1), (64, 8, 1e-3), (65, 1, 1e-2), (129, 33, 1e-4),
-                                       (513, 128, 1e-3)])
+                                       (200, 3, 1e-3), (513, 128, 1e-3), (1100, 5, 1e-2)])
 def test_solve(m, E, ridge):
     G, R = _spd_case(m, E, m + E)
     Gd, Rd = dev(G.copy()), dev(R.copy())
@@ -48,8 +48,10 @@ def test_solve(m, E, ridge):
     want = estfit.est_solve(G, R, ridge)
     assert host(info)[0] == 0
     np.testing.assert_allclose(host(Rd), want, rtol=1e-8, atol=1e-10 * np.abs(want).max())
-    # the factor: L L^T equals the regularised matrix
-    L = np.tril(host(Gd))
+    # the factor: L L^T equals the regularised matrix; L^T fills the upper triangle
+    F = host(Gd)
+    L = np.tril(F)
+    assert np.array_equal(np.triu(F, 1), np.tril(F, -1).T)
     lam = ridge * np.trace(G) / m
     np.testing.assert_allclose(L @ L.T, G + lam * np.eye(m), rtol=1e-10,
                                atol=1e-10 * np.abs(G).max())

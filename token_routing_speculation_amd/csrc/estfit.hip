@@ -11,15 +11,19 @@
 //       slices (float64 products of bf16 and binary32 values are exact),
 //       slices summed in slice order;
 //   chol_diag / chol_panel / chol_update : blocked right-looking Cholesky,
-//       64-wide blocks, in place in the lower triangle;
-//   tri_solve_fwd / tri_solve_bwd : L Z = R (row dot products) and
-//       L^T W = Z (row updates), one workgroup per right-hand side;
+//       64-wide blocks, L in place in the lower triangle and L^T written to
+//       the strict upper one (so both solves read rows of 64 contiguous
+//       values); the diagonal block and the panel rows one wave each, a lane
+//       per row, the row in registers;
+//   tri_solve : L Z = R, then L^T W = Z, one workgroup per right-hand side,
+//       64-row blocks solved by one wave, the rest updated by all;
 //   est_weights_kernel : W2 = W'[:hd]^T rounded once to bf16 (float64 ->
 //       bf16 directly, nearest even), b2 = W'[hd].
-// Every step has a fixed operation order, so results are reproducible.
+// Every step has a fixed operation order, so results are reproducible. Fused
+// multiply-adds are allowed: in the Gram products they change nothing (each
+// product is exact in float64), and the factor and solves are accurate to
+// float64 rounding either way.
 #include "common.hpp"
-
-#pragma clang fp contract(off)
 
 namespace route {
 
@@ -114,70 +118,125 @@ __global__ __launch_bounds__(kFitThreads) void est_gram_reduce(const double* __r
     rhs[static_cast<int64_t>(i) * E + (j - m)] = acc;
 }
 
-// lambda = ridge * trace / m added to the diagonal (one thread: the trace in
-// index order).
-__global__ void fit_regularise(double* __restrict__ A, int m, double ridge) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double tr = 0.0;
-  for (int i = 0; i < m; ++i) tr = tr + A[static_cast<int64_t>(i) * m + i];
-  const double lam = ridge * tr / static_cast<double>(m);
-  for (int i = 0; i < m; ++i) A[static_cast<int64_t>(i) * m + i] = A[static_cast<int64_t>(i) * m + i] + lam;
+// lambda = ridge * trace / m added to the diagonal: the diagonal loaded in
+// parallel into LDS, summed by one thread in index order.
+__global__ __launch_bounds__(kFitThreads) void fit_regularise(double* __restrict__ A, int m,
+                                                              double ridge) {
+  extern __shared__ double dg[];
+  __shared__ double lam;
+  for (int i = threadIdx.x; i < m; i += kFitThreads) dg[i] = A[static_cast<int64_t>(i) * m + i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < m; ++i) tr = tr + dg[i];
+    lam = ridge * tr / static_cast<double>(m);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += kFitThreads)
+    A[static_cast<int64_t>(i) * m + i] = dg[i] + lam;
 }
 
-// Factor of the diagonal block at k0 (b = min(64, m - k0) rows), in LDS.
-__global__ __launch_bounds__(kFitThreads) void chol_diag(double* __restrict__ A, int m, int k0,
-                                                         int* __restrict__ info) {
+// v of lane `lane` (wave-uniform) to every lane.
+__device__ __forceinline__ double lane_bcast(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
+
+// Factor of the diagonal block at k0 (b = min(64, m - k0) rows): one wave,
+// lane r holds row r in registers. Step j: L[j][j] = sqrt(a[j][j]),
+// L[r][j] = a[r][j] / L[j][j] (r > j), then a[r][c] -= L[r][j] L[c][j] for
+// j < c <= r, with column j shared through LDS. Writes L (lower) and L^T
+// (strict upper) of the block; info |= 1 where a pivot is not positive.
+__global__ __launch_bounds__(kWave) void chol_diag(double* __restrict__ A, int m, int k0,
+                                                   int* __restrict__ info) {
   __shared__ double T[kFitTile][kFitTile + 1];
+  __shared__ double colv[kFitTile];
   const int b = m - k0 < kFitTile ? m - k0 : kFitTile;
-  const int t = threadIdx.x;
-  for (int e = t; e < b * b; e += kFitThreads) {
-    const int r = e / b, c = e - r * b;
-    T[r][c] = A[static_cast<int64_t>(k0 + r) * m + k0 + c];
+  const int r = threadIdx.x;
+  // the block's lower triangle, row i read across the lanes (coalesced), all
+  // 64 loads issued before the first is used
+  {
+    double v[kFitTile];
+#pragma unroll
+    for (int i = 0; i < kFitTile; ++i)
+      v[i] = (i < b && r <= i) ? A[static_cast<int64_t>(k0 + i) * m + k0 + r] : 0.0;
+#pragma unroll
+    for (int i = 0; i < kFitTile; ++i) T[i][r] = v[i];
   }
   __syncthreads();
-  for (int j = 0; j < b; ++j) {
-    if (t == 0) {
-      const double d = T[j][j];
-      if (!(d > 0.0) && info) atomicOr(info, 1);
-      T[j][j] = sqrt(d > 0.0 ? d : 1.0);
+  double a[kFitTile];
+#pragma unroll
+  for (int c = 0; c < kFitTile; ++c) a[c] = r < b ? T[r][c] : 0.0;
+#pragma unroll
+  for (int j = 0; j < kFitTile; ++j) {
+    if (j < b) {
+      const double d = lane_bcast(a[j], j);
+      if (r == 0 && !(d > 0.0) && info) atomicOr(info, 1);
+      const double sd = sqrt(d > 0.0 ? d : 1.0);
+      const double l = r > j ? a[j] * (1.0 / sd) : (r == j ? sd : 0.0);
+      a[j] = l;
+      colv[r] = r > j ? l : 0.0;
+      __syncthreads();
+#pragma unroll
+      for (int c = j + 1; c < kFitTile; ++c) a[c] = a[c] - l * colv[c];
+      __syncthreads();
     }
-    __syncthreads();
-    for (int r = j + 1 + t; r < b; r += kFitThreads) T[r][j] = T[r][j] / T[j][j];
-    __syncthreads();
-    const int w = b - j - 1;  // trailing block (j < c <= r < b), row-major pairs
-    for (int e = t; e < w * w; e += kFitThreads) {
-      const int r = j + 1 + e / w, c = j + 1 + e % w;
-      if (c <= r) T[r][c] = T[r][c] - T[r][j] * T[c][j];
-    }
-    __syncthreads();
   }
-  for (int e = t; e < b * b; e += kFitThreads) {
-    const int r = e / b, c = e - r * b;
-    if (c <= r) A[static_cast<int64_t>(k0 + r) * m + k0 + c] = T[r][c];
-  }
+#pragma unroll
+  for (int c = 0; c < kFitTile; ++c) T[r][c] = a[c];
+  __syncthreads();
+  if (r < b)
+    for (int i = 0; i < b; ++i)  // row i: L[i][r] for r <= i, L^T[i][r] = L[r][i] for r > i
+      A[static_cast<int64_t>(k0 + i) * m + k0 + r] = r <= i ? T[i][r] : T[r][i];
 }
 
-// Panel below the diagonal block: rows x of A21 become x L11^{-T} (forward
-// substitution along the row). One thread per row of a 64-row block.
-__global__ __launch_bounds__(kFitTile) void chol_panel(double* __restrict__ A, int m, int k0) {
-  __shared__ double L[kFitTile][kFitTile + 1];
+// Panel below the diagonal block: each row x of A21 becomes x L11^{-T}:
+// x[j] *= 1 / L[j][j], then x[c] -= x[j] L[c][j] for c > j, j ascending
+// (forward substitution along the row, by columns). One wave per 64 rows, a
+// lane per row held in registers; L11^T (the block's upper triangle) and the
+// pivots' reciprocals are read from LDS by broadcast. Launched only while
+// rows remain below a full 64-wide diagonal block. Writes the rows (lower)
+// and their transpose (upper).
+__global__ __launch_bounds__(kWave) void chol_panel(double* __restrict__ A, int m, int k0) {
+  __shared__ double U[kFitTile][kFitTile + 1];  // U[j][c] = L[c][j], c >= j
   __shared__ double X[kFitTile][kFitTile + 1];
-  const int b = m - k0 < kFitTile ? m - k0 : kFitTile;
-  const int t = threadIdx.x;
-  for (int e = t; e < b * b; e += kFitTile) {
-    const int r = e / b, c = e - r * b;
-    L[r][c] = A[static_cast<int64_t>(k0 + r) * m + k0 + c];
+  __shared__ double rpiv[kFitTile];
+  const int lane = threadIdx.x;
+  const int row0 = k0 + kFitTile + blockIdx.x * kFitTile;
+  const int nr = m - row0 < kFitTile ? m - row0 : kFitTile;
+  {
+    double v[kFitTile], u[kFitTile];  // all loads in flight together
+    const int64_t rl = row0 + (lane < nr ? lane : 0);
+#pragma unroll
+    for (int j = 0; j < kFitTile; ++j) u[j] = A[static_cast<int64_t>(k0 + j) * m + k0 + lane];
+#pragma unroll
+    for (int c = 0; c < kFitTile; ++c) v[c] = A[rl * m + k0 + c];
+#pragma unroll
+    for (int j = 0; j < kFitTile; ++j) U[j][lane] = u[j];
+#pragma unroll
+    for (int c = 0; c < kFitTile; ++c) X[lane][c] = v[c];
   }
-  const int row = k0 + b + blockIdx.x * kFitTile + t;
   __syncthreads();
-  if (row >= m) return;  // no barrier below
-  double* a = A + static_cast<int64_t>(row) * m + k0;
-  for (int j = 0; j < b; ++j) {
-    double v = a[j];
-    for (int l = 0; l < j; ++l) v = v - X[t][l] * L[j][l];
-    X[t][j] = v / L[j][j];
+  rpiv[lane] = 1.0 / U[lane][lane];
+  __syncthreads();
+  double x[kFitTile];
+#pragma unroll
+  for (int c = 0; c < kFitTile; ++c) x[c] = X[lane][c];
+#pragma unroll
+  for (int j = 0; j < kFitTile; ++j) {
+    x[j] = x[j] * rpiv[j];
+#pragma unroll
+    for (int c = j + 1; c < kFitTile; ++c) x[c] = x[c] - x[j] * U[j][c];
   }
-  for (int j = 0; j < b; ++j) a[j] = X[t][j];
+  if (lane < nr) {
+    double* arow = A + static_cast<int64_t>(row0 + lane) * m + k0;
+#pragma unroll
+    for (int c = 0; c < kFitTile; ++c) {
+      arow[c] = x[c];                                              // lower
+      A[static_cast<int64_t>(k0 + c) * m + row0 + lane] = x[c];  // upper, coalesced
+    }
+  }
 }
 
 // Trailing update A22 -= L21 L21^T for the 64 x 64 tile (bi, bj), bj <= bi,
@@ -190,10 +249,21 @@ __global__ __launch_bounds__(kFitThreads) void chol_update(double* __restrict__ 
   const int base = k0 + kFitTile;
   const int r0 = base + bi * kFitTile, c0 = base + bj * kFitTile;
   const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  for (int e = t; e < kFitTile * kFitTile; e += kFitThreads) {
-    const int r = e / kFitTile, c = e % kFitTile;
-    Li[r][c] = r0 + r < m ? A[static_cast<int64_t>(r0 + r) * m + k0 + c] : 0.0;
-    Lj[r][c] = c0 + r < m ? A[static_cast<int64_t>(c0 + r) * m + k0 + c] : 0.0;
+  {
+    constexpr int kPer = kFitTile * kFitTile / kFitThreads;
+    double vi[kPer], vj[kPer];  // all loads in flight together
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + q * kFitThreads, r = e / kFitTile, c = e % kFitTile;
+      vi[q] = r0 + r < m ? A[static_cast<int64_t>(r0 + r) * m + k0 + c] : 0.0;
+      vj[q] = c0 + r < m ? A[static_cast<int64_t>(c0 + r) * m + k0 + c] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + q * kFitThreads, r = e / kFitTile, c = e % kFitTile;
+      Li[r][c] = vi[q];
+      Lj[r][c] = vj[q];
+    }
   }
   __syncthreads();
   double acc[4][4];
@@ -222,48 +292,107 @@ __global__ __launch_bounds__(kFitThreads) void chol_update(double* __restrict__ 
   }
 }
 
-// L z = r for right-hand side column e (blockIdx.x): z[i] = (r[i] - sum_{j<i}
-// L[i][j] z[j]) / L[i][i]; the dot product reduced wave by wave in a fixed
-// tree, the waves' partials in wave order.
-__global__ __launch_bounds__(kFitThreads) void tri_solve_fwd(const double* __restrict__ L, int m,
-                                                             double* __restrict__ R, int E) {
-  extern __shared__ double z[];
-  __shared__ double wpart[kFitThreads / kWave];
-  const int e = blockIdx.x, t = threadIdx.x, w = wave_id();
-  for (int i = 0; i < m; ++i) {
-    const double* li = L + static_cast<int64_t>(i) * m;
-    double p = 0.0;
-    for (int j = t; j < i; j += kFitThreads) p = p + li[j] * z[j];
+// L Z = R, then L^T W = Z, for right-hand side column e (blockIdx.x); the
+// vector sits in LDS and is solved 64 rows at a time. Wave 0 solves the
+// block's triangle one row per step (lane = row, the solved value broadcast
+// from its lane, each pivot applied as its reciprocal); then all threads
+// subtract the block's contribution from the rows still unsolved, a thread
+// per row, its 64 values loaded together. Forward: z[r] -= L[r][j] z[j],
+// j ascending; backward: w[r] -= L[j][r] w[j], j descending. Row j of the
+// factor as stored (L below the diagonal, L^T above) holds L[r][j] (r > j)
+// and L[j][r] (r < j) contiguous in r, so every load is coalesced.
+constexpr int kFitMaxM = 4097;  // hd <= 4096 features plus the bias column
+
+// One 64-row block of the triangle by wave 0 (lane = row): forward
+// z[k0 + i] = acc_i / L_ii, then acc_r -= L[r][i] z_i (r > i), i ascending;
+// backward the same with L^T, i descending. FULL: b == 64 (no row guards).
+template <bool FULL>
+__device__ __forceinline__ void solve_block(const double* __restrict__ A, int m, int k0, int b,
+                                            int pass, double* __restrict__ z) {
+  const int lane = lane_id();
+  const bool live = FULL || lane < b;
+  const int64_t cl = k0 + (live ? lane : 0);
+  double col[kFitTile];  // col[i] = stored (k0 + i, k0 + lane)
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) p = p + __shfl_xor(p, o, kWave);
-    if (lane_id() == 0) wpart[w] = p;
-    __syncthreads();
-    if (t == 0) {
-      double s = 0.0;
+  for (int i = 0; i < kFitTile; ++i)
+    col[i] = (FULL || i < b) ? A[static_cast<int64_t>(k0 + (FULL || i < b ? i : 0)) * m + cl] : 0.0;
+  const double rinv = 1.0 / A[cl * m + cl];
+  double acc = live ? z[k0 + lane] : 0.0;
+  double mine = 0.0;
+  if (pass == 0) {
 #pragma unroll
-      for (int q = 0; q < kFitThreads / kWave; ++q) s = s + wpart[q];
-      z[i] = (R[static_cast<int64_t>(i) * E + e] - s) / li[i];
+    for (int i = 0; i < kFitTile; ++i) {
+      if (FULL || i < b) {
+        const double zi = lane_bcast(acc * rinv, i);
+        mine = lane == i ? zi : mine;
+        acc = acc - col[i] * zi;  // lanes > i: L[lane][i]
+      }
     }
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = kFitTile - 1; i >= 0; --i) {
+      if (FULL || i < b) {
+        const double wi = lane_bcast(acc * rinv, i);
+        mine = lane == i ? wi : mine;
+        acc = acc - col[i] * wi;  // lanes < i: L[i][lane]
+      }
+    }
   }
-  for (int i = t; i < m; i += kFitThreads) R[static_cast<int64_t>(i) * E + e] = z[i];
+  if (live) z[k0 + lane] = mine;
 }
 
-// L^T w = z for column e: for i = m-1 .. 0, w[i] = z[i] / L[i][i], then
-// z[j] -= L[i][j] w[i] for j < i (row i of L, read contiguously).
-__global__ __launch_bounds__(kFitThreads) void tri_solve_bwd(const double* __restrict__ L, int m,
-                                                             double* __restrict__ R, int E) {
+// The solved block's contribution to the unsolved rows [lo, hi), a thread
+// per row: forward z[r] -= L[r][j] z[j] (j ascending), backward
+// w[r] -= L[j][r] w[j] (j descending), j over the block.
+template <bool FULL>
+__device__ __forceinline__ void update_rows(const double* __restrict__ A, int m, int k0, int b,
+                                            int pass, int lo, int hi, double* __restrict__ z) {
+  for (int r = lo + static_cast<int>(threadIdx.x); r < hi; r += kFitThreads) {
+    double v[kFitTile];
+#pragma unroll
+    for (int jj = 0; jj < kFitTile; ++jj)
+      v[jj] = (FULL || jj < b) ? A[static_cast<int64_t>(k0 + jj) * m + r] : 0.0;
+    double acc = z[r];
+    if (pass == 0) {
+#pragma unroll
+      for (int jj = 0; jj < kFitTile; ++jj)
+        if (FULL || jj < b) acc = acc - v[jj] * z[k0 + jj];
+    } else {
+#pragma unroll
+      for (int jj = kFitTile - 1; jj >= 0; --jj)
+        if (FULL || jj < b) acc = acc - v[jj] * z[k0 + jj];
+    }
+    z[r] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kFitThreads) void tri_solve(const double* __restrict__ A, int m,
+                                                         double* __restrict__ R, int E) {
   extern __shared__ double z[];
   const int e = blockIdx.x, t = threadIdx.x;
+  const bool lead = t < kWave;
   for (int i = t; i < m; i += kFitThreads) z[i] = R[static_cast<int64_t>(i) * E + e];
   __syncthreads();
-  for (int i = m - 1; i >= 0; --i) {
-    const double* li = L + static_cast<int64_t>(i) * m;
-    const double wi = z[i] / li[i];
-    for (int j = t; j < i; j += kFitThreads) z[j] = z[j] - li[j] * wi;
-    __syncthreads();
-    if (t == 0) z[i] = wi;
-    __syncthreads();
+  const int nblk = (m + kFitTile - 1) / kFitTile;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int q = 0; q < nblk; ++q) {
+      const int kb = pass == 0 ? q : nblk - 1 - q;
+      const int k0 = kb * kFitTile;
+      const int b = m - k0 < kFitTile ? m - k0 : kFitTile;
+      if (lead) {
+        if (b == kFitTile)
+          solve_block<true>(A, m, k0, b, pass, z);
+        else
+          solve_block<false>(A, m, k0, b, pass, z);
+      }
+      __syncthreads();
+      const int lo = pass == 0 ? k0 + b : 0, hi = pass == 0 ? m : k0;
+      if (b == kFitTile)
+        update_rows<true>(A, m, k0, b, pass, lo, hi, z);
+      else
+        update_rows<false>(A, m, k0, b, pass, lo, hi, z);
+      __syncthreads();
+    }
   }
   for (int i = t; i < m; i += kFitThreads) R[static_cast<int64_t>(i) * E + e] = z[i];
 }
@@ -307,7 +436,7 @@ ROUTE_API size_t est_fit_gram_workspace_size(int64_t n, int32_t hd, int32_t E) {
 ROUTE_API int est_fit_gram(const uint16_t* h, const float* y, int64_t n, int32_t hd, int32_t E,
                            double* gram, double* rhs, void* ws, size_t ws_bytes, hipStream_t s) {
   if (n < 1 || hd < 1 || E < 1) return ROUTE_ERR_SHAPE;
-  if (hd > 4096 || E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
+  if (hd + 1 > kFitMaxM || E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
   if (!h || !y || !gram || !rhs) return ROUTE_ERR_NULL;
   if (!ws || ws_bytes < est_fit_gram_workspace_size(n, hd, E)) return ROUTE_ERR_WORKSPACE;
   const int m = hd + 1, mc = hd + 1 + E;
@@ -322,21 +451,19 @@ ROUTE_API int est_fit_gram(const uint16_t* h, const float* y, int64_t n, int32_t
 ROUTE_API int est_fit_solve(double* gram, double* rhs, int32_t m, int32_t E, double ridge,
                             int32_t* info, hipStream_t s) {
   if (m < 1 || E < 1 || !(ridge >= 0.0)) return ROUTE_ERR_SHAPE;
-  if (m > 4097 || E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
+  if (m > kFitMaxM || E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
   if (!gram || !rhs) return ROUTE_ERR_NULL;
-  fit_regularise<<<1, 64, 0, s>>>(gram, m, ridge);
+  fit_regularise<<<1, kFitThreads, static_cast<size_t>(m) * sizeof(double), s>>>(gram, m, ridge);
   for (int k0 = 0; k0 < m; k0 += kFitTile) {
-    chol_diag<<<1, kFitThreads, 0, s>>>(gram, m, k0, info);
+    chol_diag<<<1, kWave, 0, s>>>(gram, m, k0, info);
     const int rest = m - k0 - kFitTile;
     if (rest > 0) {
       const unsigned nb = ceil_div(rest, kFitTile);
-      chol_panel<<<nb, kFitTile, 0, s>>>(gram, m, k0);
+      chol_panel<<<nb, kWave, 0, s>>>(gram, m, k0);
       chol_update<<<dim3(nb, nb), kFitThreads, 0, s>>>(gram, m, k0);
     }
   }
-  const size_t zb = static_cast<size_t>(m) * sizeof(double);
-  tri_solve_fwd<<<E, kFitThreads, zb, s>>>(gram, m, rhs, E);
-  tri_solve_bwd<<<E, kFitThreads, zb, s>>>(gram, m, rhs, E);
+  tri_solve<<<E, kFitThreads, static_cast<size_t>(m) * sizeof(double), s>>>(gram, m, rhs, E);
   return launch_status();
 }
 
