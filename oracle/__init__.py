@@ -8,7 +8,9 @@ helper with the HIP library.
 Every function is a plain, slow, obviously correct definition written from
 three web pages on the subject (``oracle.eg`` holds the s-EG expert
 placement of the "Speculative MoE" notes, sections 3.2 and 4.2;
-``oracle.estfit`` the estimator fit of "Speculating Experts", item 2.C):
+``oracle.estfit`` the estimator fit of "Speculating Experts", item 2.C;
+``oracle.prefetch`` the expert prefetch plan of "Speculating Experts",
+items 1, 2 and 4):
 
 * "Speculative MoE" notes (research-notes-783.pages.dev/p/speculative-moe/):
   route prediction tables (section 4.1), the shuffled reduce-scatter SRS and
@@ -72,4 +74,9 @@ PINS = {
     "estfit.est_solve": "closed form on orthogonal features; exact linear target recovered; "
                         "ridge residual identity",
     "estfit.est_weights": "transpose and bf16 rounding of the recovered weights",
+    "prefetch.prefetch_plan": "hand-worked example; one token gives its predicted set; "
+                              "brute-force best C-subset with the stated order",
+    "prefetch.prefetch_coverage": "hand-worked example; set intersection for one token; "
+                                  "covered + missed picks = n*K; prediction = truth covers all",
+    "prefetch.prefetch_copy": "listed slots equal their bank rows, unlisted slots unchanged",
 }
