@@ -35,7 +35,8 @@
  *  - n = 0 is a valid no-op (offset arrays are still written, all zero).
  *  - All outputs are bitwise reproducible run to run: no float atomics, and a
  *    fixed accumulation order per output element.
- *  - Counters (lar_count, hit_count) ADD into a caller-zeroed device uint64.
+ *  - Counters (lar_count, hit_count, prefetch_coverage's covered) ADD into a
+ *    caller-zeroed device uint64.
  */
 #ifndef ROUTE_H_
 #define ROUTE_H_
@@ -57,7 +58,9 @@ enum {
   ROUTE_ERR_ALIGN = 3,        /* a rows pointer is not 16-byte aligned          */
   ROUTE_ERR_UNSUPPORTED = 4,  /* E > 1024, K > 16, G > 256, P > 16, d too big   */
   ROUTE_ERR_WORKSPACE = 5,    /* ws NULL or ws_bytes below the required size    */
-  ROUTE_ERR_HIP = 6           /* a kernel launch failed                         */
+  ROUTE_ERR_HIP = 6,          /* a kernel launch failed                         */
+  ROUTE_ERR_NOT_MAPPED = 7    /* a buffer the GPU must read is not device-      */
+                              /* accessible at its own address                  */
 };
 
 enum {
@@ -379,6 +382,61 @@ int est_fit_solve(double* gram, double* rhs, int32_t m, int32_t E, double ridge,
  */
 int est_fit_weights(const double* wsol, int32_t hd, int32_t E, uint16_t* w2, float* b2,
                     hipStream_t s);
+
+/* ------------------------------------------------ speculative expert prefetch
+ * [SPEC] items 1, 2 and 4: with expert weights offloaded to host memory,
+ * on-demand loading copies a layer's selected experts after its router runs;
+ * prefetching copies the next layer's predicted experts while the current
+ * layer computes, and speculative execution runs them without waiting for
+ * the true router. The page describes one decoding request (its K predicted
+ * experts); for a batch of n tokens and C staging slots the prefetched set is
+ * the distinct predicted experts ranked by how many picks name them.
+ */
+
+/*
+ * prefetch_plan - list[C]: the distinct experts named by pred int32[n][K],
+ * ordered by pick count (descending), equal counts by expert index
+ * (ascending), the first C of them; unused slots hold -1. *nlist = the
+ * number listed (min(distinct, C)).
+ *   list: device int32[C]; nlist: device int32[1].
+ * Errors: SHAPE (n < 0, K < 1, E < 1, C < 1, C > E), UNSUPPORTED (E > 1024),
+ * NULL. Device bits: EXPERT_RANGE (a pick outside [0, E): not counted).
+ */
+int prefetch_plan(const int32_t* pred, int64_t n, int32_t K, int32_t E, int32_t C, int32_t* list,
+                  int32_t* nlist, uint32_t* err, hipStream_t s);
+
+/*
+ * prefetch_copy - slot i (expert_bytes bytes at slots + i * expert_bytes)
+ * receives expert list[i]'s block (bank + list[i] * expert_bytes) for each
+ * i < C with list[i] >= 0; slots with -1 are left as they are.
+ *   bank: E blocks of expert_bytes, either device memory or pinned host
+ *   memory mapped for the device at the same address (hipHostMalloc, or a
+ *   pinned torch tensor): the copy runs as a kernel of 64 workgroups that
+ *   reads it over PCIe, so `list` can be produced on the GPU by
+ *   prefetch_plan in the same stream. slots: device memory, C blocks.
+ *   Calls on one slot buffer in different streams must be ordered by the
+ *   caller.
+ * Errors: SHAPE (E < 1, C < 1, expert_bytes < 0), UNSUPPORTED (E > 1024),
+ * ALIGN (expert_bytes % 16, bank or slots not 16-byte aligned), NULL,
+ * NOT_MAPPED (hipPointerGetAttributes does not report bank as accessible
+ * at its own address). Device bits: EXPERT_RANGE (list[i] >= E: skipped).
+ */
+int prefetch_copy(const void* bank, int32_t E, int64_t expert_bytes, const int32_t* list,
+                  int32_t C, void* slots, uint32_t* err, hipStream_t s);
+
+/*
+ * prefetch_coverage - for the true picks truth int32[n][K] and the slot
+ * list[C] (-1 = empty): *covered += the number of picks whose expert is
+ * listed; miss int32[E] = the true experts listed in no slot, in index order,
+ * padded with -1; *nmiss = their number (the blocks an on-demand load still
+ * copies: prefetch_copy with list = miss, C = E).
+ *   covered: device uint64, accumulated; miss: device int32[E]; nmiss: int32[1].
+ * Errors: SHAPE (n < 0, K < 1, E < 1, C < 1), UNSUPPORTED (E > 1024), NULL.
+ * Device bits: EXPERT_RANGE (a pick or list entry >= E, or a pick < 0: ignored).
+ */
+int prefetch_coverage(const int32_t* truth, int64_t n, int32_t K, int32_t E, const int32_t* list,
+                      int32_t C, unsigned long long* covered, int32_t* miss, int32_t* nmiss,
+                      uint32_t* err, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 26, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_status_strings(L):
     assert L.route_status_str(0) == b"ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert L.route_status_str(s) not in (b"ok", b"unknown status")
     assert L.route_status_str(99) == b"unknown status"
 
@@ -193,3 +193,27 @@ def test_estfit_errors(L):
     assert f(None, A, 65, 8, 0.1, None, None) == NULL
     assert L.est_fit_weights(A, 0, 8, A, A, None) == SHAPE
     assert L.est_fit_weights(None, 64, 8, A, A, None) == NULL
+
+
+def test_prefetch_errors(L):
+    p, c, v = L.prefetch_plan, L.prefetch_copy, L.prefetch_coverage
+    assert p(A, -1, 8, 128, 8, A, A, None, None) == SHAPE
+    assert p(A, 4, 0, 128, 8, A, A, None, None) == SHAPE
+    assert p(A, 4, 8, 128, 0, A, A, None, None) == SHAPE
+    assert p(A, 4, 8, 128, 129, A, A, None, None) == SHAPE     # C > E
+    assert p(A, 4, 8, 1025, 8, A, A, None, None) == UNSUP
+    assert p(None, 4, 8, 128, 8, A, A, None, None) == NULL
+    assert p(A, 4, 8, 128, 8, None, A, None, None) == NULL
+    assert c(A, 0, 4096, A, 8, A, None, None) == SHAPE
+    assert c(A, 128, -16, A, 8, A, None, None) == SHAPE
+    assert c(A, 2048, 4096, A, 8, A, None, None) == UNSUP
+    assert c(A, 128, 4100, A, 8, A, None, None) == ALIGN
+    assert c(MIS, 128, 4096, A, 8, A, None, None) == ALIGN
+    assert c(A, 128, 4096, A, 8, MIS, None, None) == ALIGN
+    assert c(None, 128, 4096, A, 8, A, None, None) == NULL
+    assert c(A, 128, 0, A, 8, A, None, None) == OK           # nothing to copy
+    assert v(A, -1, 8, 128, A, 8, A, A, A, None, None) == SHAPE
+    assert v(A, 4, 8, 2048, A, 8, A, A, A, None, None) == UNSUP
+    assert v(A, 4, 8, 128, A, 8, None, A, A, None, None) == NULL
+    assert v(A, 4, 8, 128, A, 8, A, None, A, None, None) == NULL
+

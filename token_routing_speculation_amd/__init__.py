@@ -25,7 +25,8 @@ __all__ = [
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
     "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
-    "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights", "EXPORTS",
+    "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
+    "prefetch_plan", "prefetch_copy", "prefetch_coverage", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,9 @@ EXPORTS = {
     "est_fit_gram": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _p, _p, _p, _sz, _p]),
     "est_fit_solve": (ctypes.c_int, [_p, _p, _i32, _i32, _f64, _p, _p]),
     "est_fit_weights": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "prefetch_plan": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "prefetch_copy": (ctypes.c_int, [_p, _i32, _i64, _p, _i32, _p, _p, _p]),
+    "prefetch_coverage": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p]),
 }
 
 
@@ -415,3 +419,50 @@ def est_fit_weights(wsol, w2=None, b2=None, stream=None):
     _call("est_fit_weights", _dev(wsol, torch.float64, "wsol", m * E), hd, E,
           _dev(w2, _bf16(w2), "w2", E * hd), _dev(b2, torch.float32, "b2", E), _stream(stream))
     return w2, b2
+
+
+# ------------------------------------------------- speculative expert prefetch
+
+def prefetch_plan(pred, E, C, lst=None, nlist=None, err=None, stream=None):
+    """list [C] int32: the distinct experts of pred [n][K] by pick count (ties to the
+    lower index), -1 padded; nlist [1] int32: how many are listed."""
+    n, K = pred.shape
+    dev = pred.device
+    lst = torch.empty(C, dtype=torch.int32, device=dev) if lst is None else lst
+    nlist = torch.empty(1, dtype=torch.int32, device=dev) if nlist is None else nlist
+    _call("prefetch_plan", _dev(pred, torch.int32, "pred"), n, K, E, C,
+          _dev(lst, torch.int32, "list", C), _dev(nlist, torch.int32, "nlist", 1),
+          _opt(err, torch.int32, "err", 1), _stream(stream))
+    return lst, nlist
+
+
+def prefetch_copy(bank, lst, slots, err=None, stream=None):
+    """slots [C][B] uint8 <- bank [E][B] rows named by lst [C] (-1: left as is). bank may
+    be a pinned host tensor (read by the GPU over PCIe) or a device tensor."""
+    if not isinstance(bank, torch.Tensor) or bank.dtype != torch.uint8 or bank.dim() != 2:
+        raise TypeError("bank must be a 2-D uint8 tensor [E][expert_bytes]")
+    if not bank.is_contiguous():
+        raise ValueError("bank must be contiguous")
+    if bank.device.type != "cuda" and not bank.is_pinned():
+        raise ValueError("bank must be a GPU tensor or pinned host memory")
+    E, B = bank.shape
+    C = lst.numel()
+    _call("prefetch_copy", bank.data_ptr(), E, B, _dev(lst, torch.int32, "list"), C,
+          _dev(slots, torch.uint8, "slots", C * B), _opt(err, torch.int32, "err", 1),
+          _stream(stream))
+    return slots
+
+
+def prefetch_coverage(truth, lst, E, covered, miss=None, nmiss=None, err=None, stream=None):
+    """covered [1] += true picks whose expert is listed; miss [E]: the true experts
+    listed nowhere, in index order, -1 padded; nmiss [1]: their number."""
+    n, K = truth.shape
+    dev = truth.device
+    miss = torch.empty(E, dtype=torch.int32, device=dev) if miss is None else miss
+    nmiss = torch.empty(1, dtype=torch.int32, device=dev) if nmiss is None else nmiss
+    _call("prefetch_coverage", _dev(truth, torch.int32, "truth"), n, K, E,
+          _dev(lst, torch.int32, "list"), lst.numel(), _dev(covered, torch.int64, "covered", 1),
+          _dev(miss, torch.int32, "miss", E), _dev(nmiss, torch.int32, "nmiss", 1),
+          _opt(err, torch.int32, "err", 1), _stream(stream))
+    return miss, nmiss
+

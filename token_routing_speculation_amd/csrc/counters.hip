@@ -155,6 +155,7 @@ ROUTE_API const char* route_status_str(int status) {
     case ROUTE_ERR_UNSUPPORTED: return "size beyond the supported maximum";
     case ROUTE_ERR_WORKSPACE: return "workspace missing or too small";
     case ROUTE_ERR_HIP: return "kernel launch failed";
+    case ROUTE_ERR_NOT_MAPPED: return "buffer not device-accessible at its own address";
     default: return "unknown status";
   }
 }
