@@ -276,20 +276,14 @@ def fit_estimator(cfg, l, lay, n_train, ridge):
             "solve_ms": t[2], "weights_ms": t[3]}
 
 
-def predictor_bench(args):
-    """The q_l predictor of "Speculating Experts Accelerates Inference for
-    Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
-    source layers of the Qwen3-30B-A3B-shaped workload: per layer q_l = LN(d_l
-    + r_l), the next gate on q_l (the MLP estimator on the early layers),
-    top-K and the hit count against the next layer's true top-K (computed
-    beforehand: it is layer l+1's own routing, not part of the prediction)."""
+def predictor_setup(cfg, args):
+    """The predictor pass and every source layer's device inputs, with layer
+    l+1's true top-K (its own routing) computed once; optionally the
+    estimator layers' output weights fitted first."""
     import torch
-    from synth import get_config
     from synth.gen import make_predictor_layer
-    from token_routing_speculation_amd.pipeline import PredictorPass, capture_graph, to_device
+    from token_routing_speculation_amd.pipeline import PredictorPass
 
-    cfg = get_config("qwen3")
-    torch.cuda.set_device(0)
     N = cfg.N
     p = PredictorPass(N, cfg.d, cfg.E, cfg.K, cfg.hd)
     layers, truths, est = [], [], []
@@ -305,6 +299,25 @@ def predictor_bench(args):
         truths.append(p.truth)
         est.append(bool(lay["estimator"]))
     torch.cuda.synchronize()
+    return p, layers, truths, est, fit_info
+
+
+def predictor_bench(args):
+    """The q_l predictor of "Speculating Experts Accelerates Inference for
+    Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
+    source layers of the Qwen3-30B-A3B-shaped workload: per layer q_l = LN(d_l
+    + r_l), the next gate on q_l (the MLP estimator on the early layers),
+    top-K and the hit count against the next layer's true top-K (computed
+    beforehand: it is layer l+1's own routing, not part of the prediction)."""
+    import torch
+    from synth import get_config
+    from synth.gen import make_predictor_layer
+    from token_routing_speculation_amd.pipeline import PredictorPass, capture_graph, to_device
+
+    cfg = get_config("qwen3")
+    torch.cuda.set_device(0)
+    N = cfg.N
+    p, layers, truths, est, fit_info = predictor_setup(cfg, args)
 
     def sweep():
         for L_, T_ in zip(layers, truths):
@@ -407,6 +420,216 @@ def predictor_bench(args):
     return 0
 
 
+PCIE_PEAK = 64.0e9           # PCIe 5.0 x16 host link, bytes/s per direction (32 GT/s x 16 lanes)
+
+
+def prefetch_bench(args):
+    """Speculative expert prefetch ("Speculating Experts Accelerates Inference
+    for Mixture-of-Experts", items 1, 2 and 4) for decoding a
+    Qwen3-30B-A3B-shaped model whose expert weights sit in pinned host memory.
+    For each decoded token and source layer l, layer l+1's experts are
+    predicted from q_l (the predictor pass) and planned into C = K * batch
+    staging slots. Three schedules of the transfers are timed per token:
+      on_demand:   after layer l+1's routing, its true experts are copied
+                   (prefetch_copy: the list stays on the GPU, which waits);
+      speculative: the predicted list comes back to pinned host memory and
+                   prefetch_issue copies those experts on a second stream
+                   (DMA engines); layer l+1 waits only for that copy
+                   (speculative execution runs the prefetched experts);
+      prefetch_then_misses: the same, then the true experts that were not
+                   prefetched are copied after routing (no speculative execution).
+    The layers' own compute (attention, expert FFNs) is not built, so the
+    schedules differ only by what they transfer and when. The overlap leg
+    runs the N-row predictor sweep (compute) beside the transfers, through
+    the DMA path and through the copy kernel."""
+    import torch
+    import token_routing_speculation_amd as tr
+    from synth import get_config
+    from token_routing_speculation_amd.pipeline import capture_graph
+
+    cfg = get_config("qwen3")
+    torch.cuda.set_device(0)
+    E, K = cfg.E, cfg.K
+    nl = cfg.L - 1
+    B = args.prefetch_batch
+    T = args.prefetch_tokens
+    C = min(E, K * B)
+    EB = 3 * cfg.d * cfg.ffn * 2
+    W = min(2, T)                                  # warm-up tokens per schedule
+    p, layers, truths, est, _ = predictor_setup(cfg, args)
+    # layer l+1's predicted top-K for all N rows, from the predictor pass
+    preds = []
+    for L_, T_ in zip(layers, truths):
+        p.layer, p.truth = L_, T_
+        p.step()
+        preds.append(p.pred.clone())
+    torch.cuda.synchronize()
+    assert T * B <= cfg.N
+    bank = torch.empty((E, EB), dtype=torch.uint8, pin_memory=True)   # 1.2 GB, content irrelevant
+    slots = torch.empty((2, C, EB), dtype=torch.uint8, device="cuda")
+    miss_slots = torch.empty((E, EB), dtype=torch.uint8, device="cuda")
+    lists = torch.empty((T, nl, C), dtype=torch.int32, device="cuda")
+    lists_h = torch.empty((T, nl, C), dtype=torch.int32, pin_memory=True)
+    nlists = torch.zeros((T, nl), dtype=torch.int32, device="cuda")
+    tlists = torch.empty((T, nl, C), dtype=torch.int32, device="cuda")
+    ntlists = torch.zeros((T, nl), dtype=torch.int32, device="cuda")
+    misses = torch.empty((T, nl, E), dtype=torch.int32, device="cuda")
+    nmisses = torch.zeros((T, nl), dtype=torch.int32, device="cuda")
+    covered = torch.zeros((nl,), dtype=torch.int64, device="cuda")
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()                     # default priority
+    rows = lambda t: slice(t * B, (t + 1) * B)
+    ev_plan = [torch.cuda.Event() for _ in range(nl)]
+    ev_copy = [torch.cuda.Event() for _ in range(nl)]
+
+    def token_on_demand(t):
+        for l in range(nl):
+            tr.prefetch_plan(truths[l][rows(t)], E, C, lst=tlists[t, l], nlist=ntlists[t, l:l + 1])
+            tr.prefetch_copy(bank, tlists[t, l], slots[l % 2])
+
+    def token_speculative(t, with_misses):
+        for l in range(nl):
+            # during layer l: plan layer l+1 from q_l's prediction, list back to the host
+            tr.prefetch_plan(preds[l][rows(t)], E, C, lst=lists[t, l], nlist=nlists[t, l:l + 1])
+            lists_h[t, l].copy_(lists[t, l], non_blocking=True)
+            ev_plan[l].record(comp)
+            ev_plan[l].synchronize()
+            tr.prefetch_issue(bank, lists_h[t, l], slots[l % 2], stream=copy)
+            ev_copy[l].record(copy)
+            # layer l+1 starts once its experts are in (speculative execution)
+            comp.wait_event(ev_copy[l])
+            tr.prefetch_coverage(truths[l][rows(t)], lists[t, l], E, covered[l:l + 1],
+                                 miss=misses[t, l], nmiss=nmisses[t, l:l + 1])
+            if with_misses:
+                tr.prefetch_copy(bank, misses[t, l], miss_slots)
+
+    def timed(fn):
+        for t in range(W):
+            fn(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        for t in range(T):
+            fn(t)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / T
+
+    ms_od = timed(token_on_demand)
+    ms_sp = timed(lambda t: token_speculative(t, False))
+    covered.zero_()
+    ms_pm = timed(lambda t: token_speculative(t, True))
+    cov_by_layer = covered.cpu().numpy() / ((T + W) * B * K)
+    byt_od = int(ntlists.sum()) * EB / T
+    byt_sp = int(nlists.sum()) * EB / T
+    byt_pm = byt_sp + int(nmisses.sum()) * EB / T
+
+    # the copy kernel alone: one layer's C experts per launch, HIP events on its stream
+    lst0, lst0_h = lists[0, 0], lists_h[0, 0]
+    n_copied = int(nlists[0, 0])
+    reps = args.steps
+    for _ in range(3):
+        tr.prefetch_copy(bank, lst0, slots[0])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(comp)
+    for r in range(reps):
+        tr.prefetch_copy(bank, lst0, slots[0])
+        ev[r + 1].record(comp)
+    torch.cuda.synchronize()
+    copy_us = [1e3 * ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+    copy_gbs = n_copied * EB / (np.mean(copy_us) * 1e-6) / 1e9
+    # the same layer's experts through the DMA engines
+    for _ in range(3):
+        tr.prefetch_issue(bank, lst0_h, slots[0])
+    torch.cuda.synchronize()
+    ev[0].record(comp)
+    for r in range(reps):
+        tr.prefetch_issue(bank, lst0_h, slots[0])
+        ev[r + 1].record(comp)
+    torch.cuda.synchronize()
+    dma_us = [1e3 * ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+    dma_gbs = n_copied * EB / (np.mean(dma_us) * 1e-6) / 1e9
+
+    # overlap: the N-row predictor sweep (compute) beside one layer's transfer, repeated
+    def sweep():
+        for L_, T_ in zip(layers, truths):
+            p.layer, p.truth = L_, T_
+            p.step()
+    graph = capture_graph(sweep)
+    graph.replay()
+    torch.cuda.synchronize()
+    n_ov = 5
+
+    def sweeps_beside(xfer, n_x):
+        """(ms per sweep, total transfer ms) with n_x transfers on the copy
+        stream beside n_ov sweeps on the compute stream (n_x = 0: sweeps alone)."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        copy.wait_stream(comp)
+        if n_x:
+            c0.record(copy)
+            with torch.cuda.stream(copy):
+                for _ in range(n_x):
+                    xfer()
+            c1.record(copy)
+        a.record(comp)
+        for _ in range(n_ov):
+            graph.replay()
+        b.record(comp)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n_ov, (c0.elapsed_time(c1) if n_x else None)
+
+    sweep_alone, _ = sweeps_beside(None, 0)
+    n_x = max(1, int(round(n_ov * sweep_alone * 1e-3 / (np.mean(dma_us) * 1e-6))))
+    overlap = {"sweep_ms_alone": sweep_alone, "transfers": n_x}
+    for name, fn in (("dma", lambda: tr.prefetch_issue(bank, lst0_h, slots[1], stream=copy)),
+                     ("kernel", lambda: tr.prefetch_copy(bank, lst0, slots[1]))):
+        sw, xf = sweeps_beside(fn, n_x)
+        overlap[f"sweep_ms_with_{name}"] = sw
+        overlap[f"{name}_gbs_with_sweep"] = n_x * n_copied * EB / (xf * 1e-3) / 1e9
+
+    out = {
+        "metric": "speculative expert prefetch, host-to-GPU transfer rate (prefetch_issue, DMA)",
+        "value": dma_gbs, "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 3,
+        "ms_per_step": float(np.mean(dma_us)) / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "qwen3-30b-a3b-shaped decode, experts offloaded to pinned host memory",
+                   "layers": nl, "E": E, "K": K, "batch": B, "slots": C, "expert_bytes": EB,
+                   "tokens": T},
+        "roofline": {"bound": "pcie", "kernel": "prefetch_copy_kernel", "achieved": copy_gbs,
+                     "peak": PCIE_PEAK / 1e9, "unit": "GB/s", "frac": copy_gbs * 1e9 / PCIE_PEAK,
+                     "traffic": None},
+        "copy_kernel_us": {"mean": float(np.mean(copy_us)), "p50": float(np.median(copy_us)),
+                           "experts": n_copied},
+        "dma_us": {"mean": float(np.mean(dma_us)), "p50": float(np.median(dma_us))},
+        "dma_frac_of_pcie": dma_gbs * 1e9 / PCIE_PEAK,
+        "ms_per_token": {"on_demand": ms_od, "speculative": ms_sp, "prefetch_then_misses": ms_pm},
+        "bytes_per_token": {"on_demand": byt_od, "speculative": byt_sp,
+                            "prefetch_then_misses": byt_pm},
+        "coverage": {"gate_layers": float(np.mean([c for c, e_ in zip(cov_by_layer, est) if not e_])),
+                     "estimator_layers": float(np.mean([c for c, e_ in zip(cov_by_layer, est) if e_]))},
+        "overlap": overlap,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import prefetch as opf
+        lst_np = lst0_h.numpy().copy()
+        bank_np = bank.numpy()
+        sl = np.empty((C, EB), np.uint8)
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < 3.0:
+            sl = opf.prefetch_copy(bank_np, lst_np, sl)
+            k += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": k * n_copied * EB / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{k} copies of one layer's {n_copied} experts from the "
+                                         "pinned bank into host slots (numpy)"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +650,10 @@ def main(argv=None):
                     help="qwen3: fit the estimator layers' output weights before timing")
     ap.add_argument("--fit-tokens", type=int, default=32768)
     ap.add_argument("--fit-ridge", type=float, default=1e-3)
+    ap.add_argument("--prefetch", action="store_true",
+                    help="qwen3: measure speculative expert prefetch from pinned host memory")
+    ap.add_argument("--prefetch-tokens", type=int, default=16)
+    ap.add_argument("--prefetch-batch", type=int, default=1)
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -441,6 +668,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if args.prefetch:
+        return prefetch_bench(args)
     if args.config == "qwen3":
         return predictor_bench(args)
     if args.eg:

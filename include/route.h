@@ -406,6 +406,25 @@ int prefetch_plan(const int32_t* pred, int64_t n, int32_t K, int32_t E, int32_t 
                   int32_t* nlist, uint32_t* err, hipStream_t s);
 
 /*
+ * prefetch_issue - HOST function. For each i < C with list[i] >= 0, copies
+ * expert list[i]'s block (bank + list[i] * expert_bytes) to slot i (slots +
+ * i * expert_bytes) with hipMemcpyAsync on stream s (normally a copy stream
+ * beside the compute stream); runs of consecutive experts in consecutive
+ * slots go as one transfer. The DMA engines do the copy: no compute units
+ * are used and concurrent kernels keep their memory bandwidth, so this is
+ * the path that overlaps a prefetch with the current layer's compute.
+ *   bank: pinned host memory (or device memory), E blocks. list: HOST
+ *   int32[C] (-1 = empty slot), read during the call, e.g. prefetch_plan's
+ *   list copied back after an event. slots: device memory, C blocks.
+ * Errors: SHAPE (E < 1, C < 1, expert_bytes < 0, a list entry < -1 or
+ * >= E: nothing enqueued), NULL, NOT_MAPPED (bank not device memory or
+ * pinned host memory), HIP (an enqueue failed; earlier transfers of the
+ * call may be enqueued).
+ */
+int prefetch_issue(const void* bank, int32_t E, int64_t expert_bytes, const int32_t* list,
+                   int32_t C, void* slots, hipStream_t s);
+
+/*
  * prefetch_copy - slot i (expert_bytes bytes at slots + i * expert_bytes)
  * receives expert list[i]'s block (bank + list[i] * expert_bytes) for each
  * i < C with list[i] >= 0; slots with -1 are left as they are.
@@ -414,6 +433,10 @@ int prefetch_plan(const int32_t* pred, int64_t n, int32_t K, int32_t E, int32_t 
  *   pinned torch tensor): the copy runs as a kernel of 64 workgroups that
  *   reads it over PCIe, so `list` can be produced on the GPU by
  *   prefetch_plan in the same stream. slots: device memory, C blocks.
+ *   Measured on MI355X: the kernel reaches the same PCIe rate as the DMA
+ *   engines, but kernels running beside it that stream HBM slow down
+ *   several-fold; overlap a prefetch with compute through prefetch_issue,
+ *   and use this call where the GPU would otherwise wait (on-demand loads).
  *   Calls on one slot buffer in different streams must be ordered by the
  *   caller.
  * Errors: SHAPE (E < 1, C < 1, expert_bytes < 0), UNSUPPORTED (E > 1024),

@@ -61,6 +61,8 @@ class PredictorConfig:
     E: int
     K: int
     hd: int = 512                     # estimator hidden width
+    ffn: int = 768                    # expert FFN width: an expert's weights are gate, up
+                                      # and down projections, 3 * d * ffn bf16 values
     est_layers: tuple = (0, 1, 2, 3)  # source layers that use the MLP estimator
     dvec_var: float = 0.1
     drift: float = 0.5

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -216,4 +216,21 @@ def test_prefetch_errors(L):
     assert v(A, 4, 8, 2048, A, 8, A, A, A, None, None) == UNSUP
     assert v(A, 4, 8, 128, A, 8, None, A, A, None, None) == NULL
     assert v(A, 4, 8, 128, A, 8, A, None, A, None, None) == NULL
+
+
+def test_prefetch_issue_checks_the_host_list_first(L):
+    f = L.prefetch_issue
+    lst = (ctypes.c_int32 * 4)(0, 3, -1, 2)
+    bad_hi = (ctypes.c_int32 * 4)(0, 3, 4, 2)     # 4 >= E
+    bad_lo = (ctypes.c_int32 * 4)(0, -2, 1, 2)    # only -1 marks an empty slot
+    addr = lambda a: ctypes.cast(a, ctypes.c_void_p).value
+    assert f(A, 4, 4096, addr(bad_hi), 4, A, None) == SHAPE
+    assert f(A, 4, 4096, addr(bad_lo), 4, A, None) == SHAPE
+    assert f(A, 0, 4096, addr(lst), 4, A, None) == SHAPE
+    assert f(A, 4, -1, addr(lst), 4, A, None) == SHAPE
+    assert f(A, 4, 4096, addr(lst), 0, A, None) == SHAPE
+    assert f(None, 4, 4096, addr(lst), 4, A, None) == NULL
+    assert f(A, 4, 4096, None, 4, A, None) == NULL
+    assert f(A, 4, 4096, addr(lst), 4, None, None) == NULL
+    assert f(A, 4, 0, addr(lst), 4, A, None) == OK          # nothing to copy
 

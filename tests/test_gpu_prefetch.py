@@ -91,6 +91,46 @@ def test_copy(E, B, C, where):
     assert host(err)[0] == 0
 
 
+@pytest.mark.parametrize("lst,where", [([3, 4, 5, -1, 9, 10], "host"), ([7, 0, 1, 2, -1, -1], "host"),
+                                       ([11, 10, 9, 8, 7, 6], "device"), ([-1] * 6, "host")])
+def test_issue_dma(lst, where):
+    E, B = 12, 12288
+    bank = _pinned_bank(E, B, 77)
+    if where == "device":
+        bank = bank.cuda()
+    slots0 = np.random.default_rng(1).integers(0, 256, (len(lst), B), dtype=np.uint8)
+    slots = dev(slots0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    tr.prefetch_issue(bank, torch.tensor(lst, dtype=torch.int32), slots, stream=s)
+    s.synchronize()
+    want = opf.prefetch_copy(bank.cpu().numpy(), np.array(lst), slots0)
+    assert np.array_equal(host(slots), want)
+
+
+def test_issue_from_a_plan_copied_back():
+    """The plan runs on the GPU; its list comes back to pinned host memory;
+    the DMA copies run on a second stream and the compute stream waits."""
+    E, C = 12, 8
+    bank = _pinned_bank(E, QWEN3_EXPERT_BYTES, 6)
+    pred = _picks(1, 8, E, 10)
+    lst, nl = tr.prefetch_plan(dev(pred), E, C)
+    lst_h = torch.empty(C, dtype=torch.int32, pin_memory=True)
+    lst_h.copy_(lst, non_blocking=True)
+    done = torch.cuda.Event()
+    done.record()
+    done.synchronize()
+    slots = torch.zeros((C, QWEN3_EXPERT_BYTES), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    tr.prefetch_issue(bank, lst_h, slots, stream=cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    wl, _, _ = opf.prefetch_plan(pred, E, C)
+    assert np.array_equal(lst_h.numpy(), wl)
+    want = opf.prefetch_copy(bank.numpy(), wl, np.zeros((C, QWEN3_EXPERT_BYTES), np.uint8))
+    assert np.array_equal(host(slots), want)
+
+
 def test_copy_qwen3_experts_from_pinned_memory():
     E, C = 12, 8
     bank = _pinned_bank(E, QWEN3_EXPERT_BYTES, 5)
@@ -124,8 +164,15 @@ def test_copy_refuses_pageable_host_memory():
     st = tr.lib().prefetch_copy(ptr, 4, B, lst.data_ptr(), 2, slots.data_ptr(), None,
                                 torch.cuda.current_stream().cuda_stream)
     assert st == 7                                     # ROUTE_ERR_NOT_MAPPED
+    hl = np.array([0, 1], np.int32)
+    st = tr.lib().prefetch_issue(ptr, 4, B, hl.ctypes.data, 2, slots.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == 7
     with pytest.raises(ValueError):
         tr.prefetch_copy(torch.zeros((4, B), dtype=torch.uint8), lst, slots)
+    with pytest.raises(ValueError):
+        tr.prefetch_issue(torch.zeros((4, B), dtype=torch.uint8), torch.tensor([0, 1],
+                          dtype=torch.int32), slots)
     assert (host(slots) == 0).all()
 
 

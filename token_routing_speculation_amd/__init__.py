@@ -26,7 +26,7 @@ __all__ = [
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
     "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
     "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
-    "prefetch_plan", "prefetch_copy", "prefetch_coverage", "EXPORTS",
+    "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,7 @@ EXPORTS = {
     "est_fit_weights": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "prefetch_plan": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
     "prefetch_copy": (ctypes.c_int, [_p, _i32, _i64, _p, _i32, _p, _p, _p]),
+    "prefetch_issue": (ctypes.c_int, [_p, _i32, _i64, _p, _i32, _p, _p]),
     "prefetch_coverage": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p]),
 }
 
@@ -450,6 +451,26 @@ def prefetch_copy(bank, lst, slots, err=None, stream=None):
     _call("prefetch_copy", bank.data_ptr(), E, B, _dev(lst, torch.int32, "list"), C,
           _dev(slots, torch.uint8, "slots", C * B), _opt(err, torch.int32, "err", 1),
           _stream(stream))
+    return slots
+
+
+def prefetch_issue(bank, lst, slots, stream=None):
+    """DMA copies (hipMemcpyAsync on ``stream``) of the bank [E][B] rows named by the
+    HOST int32 list ``lst`` [C] (-1: skipped) into slots [C][B]; runs of consecutive
+    experts go as one transfer. bank: pinned host or device uint8 tensor."""
+    if not isinstance(bank, torch.Tensor) or bank.dtype != torch.uint8 or bank.dim() != 2:
+        raise TypeError("bank must be a 2-D uint8 tensor [E][expert_bytes]")
+    if not bank.is_contiguous():
+        raise ValueError("bank must be contiguous")
+    if bank.device.type != "cuda" and not bank.is_pinned():
+        raise ValueError("bank must be a GPU tensor or pinned host memory")
+    if not isinstance(lst, torch.Tensor) or lst.device.type != "cpu" or lst.dtype != torch.int32 \
+            or not lst.is_contiguous():
+        raise TypeError("lst must be a contiguous int32 host tensor")
+    E, B = bank.shape
+    C = lst.numel()
+    _call("prefetch_issue", bank.data_ptr(), E, B, lst.data_ptr(), C,
+          _dev(slots, torch.uint8, "slots", C * B), _stream(stream))
     return slots
 
 

@@ -6,10 +6,15 @@
 //   prefetch_plan_kernel  : the batch's predicted picks counted per expert in
 //       LDS; each named expert's rank (count descending, index ascending)
 //       places it in one of C staging slots;
-//   prefetch_copy_kernel  : slot i <- the weight block of expert list[i],
-//       read from pinned host memory over PCIe (or from device memory) by a
-//       fixed, small set of workgroups, so the plan never leaves the GPU and
-//       the remaining compute units stay with the layer's own work;
+//   prefetch_issue        : host side; the DMA engines copy the listed
+//       experts' blocks (hipMemcpyAsync on the caller's copy stream, runs of
+//       consecutive experts merged into one transfer). The engines use no
+//       compute units and leave concurrent kernels' memory traffic alone;
+//   prefetch_copy_kernel  : the same copy as a kernel that reads pinned host
+//       memory over PCIe, driven by a device-resident list. It reaches the
+//       same link rate, but while it runs concurrent HBM-bound kernels slow
+//       down several-fold, so it suits loads made while the GPU waits anyway
+//       (on-demand misses after routing), with no host round trip;
 //   prefetch_cover_kernel : the true picks whose expert sits in a slot, and
 //       the true experts that sit in none (what an on-demand load still
 //       copies), listed in index order.
@@ -185,3 +190,40 @@ ROUTE_API int prefetch_coverage(const int32_t* truth, int64_t n, int32_t K, int3
                                                  err);
   return launch_status();
 }
+
+ROUTE_API int prefetch_issue(const void* bank, int32_t E, int64_t expert_bytes,
+                             const int32_t* list, int32_t C, void* slots, hipStream_t s) {
+  if (E < 1 || C < 1 || expert_bytes < 0) return ROUTE_ERR_SHAPE;
+  if (!bank || !list || !slots) return ROUTE_ERR_NULL;
+  for (int i = 0; i < C; ++i)  // the host list is checked before anything is enqueued
+    if (list[i] < -1 || list[i] >= E) return ROUTE_ERR_SHAPE;
+  if (expert_bytes == 0) return ROUTE_OK;
+  // asynchronous DMA needs the bank in device memory or in pinned host memory
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, bank) != hipSuccess) {
+    (void)hipGetLastError();
+    return ROUTE_ERR_NOT_MAPPED;
+  }
+  if (at.devicePointer == nullptr) return ROUTE_ERR_NOT_MAPPED;
+  const char* src = static_cast<const char*>(bank);
+  char* dst = static_cast<char*>(slots);
+  int i = 0;
+  while (i < C) {
+    if (list[i] < 0) {
+      ++i;
+      continue;
+    }
+    int j = i + 1;  // a run of consecutive experts lands in consecutive slots
+    while (j < C && list[j] == list[j - 1] + 1) ++j;
+    const size_t bytes = static_cast<size_t>(j - i) * static_cast<size_t>(expert_bytes);
+    if (hipMemcpyAsync(dst + static_cast<int64_t>(i) * expert_bytes,
+                       src + static_cast<int64_t>(list[i]) * expert_bytes, bytes,
+                       hipMemcpyDefault, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return ROUTE_ERR_HIP;
+    }
+    i = j;
+  }
+  return ROUTE_OK;
+}
+
