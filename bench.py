@@ -87,16 +87,8 @@ def measured_traffic(workload: str):
     return (rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
 
 
-def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
-    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
-    same workload: n_sample tokens drawn with the workload's recipe, full
-    passes repeated until min_seconds of host time have been spent."""
-    from threadpoolctl import threadpool_info
-    from synth import make_config_inputs
+def _oracle_passes(name, inp, tables, n_sample, min_seconds):
     import oracle.pipeline as op
-
-    inp = make_config_inputs(name, N=n_sample)
-    tables = None if name == "foe" else op.build_tables(inp)
     passes, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
@@ -106,12 +98,33 @@ def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
             op.route_pass(inp, *tables)
         dt += time.perf_counter() - t0
         passes += 1
+    return passes, dt
+
+
+def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
+    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
+    same workload: n_sample tokens drawn with the workload's recipe, full
+    passes repeated until min_seconds of host time have been spent. Run with
+    the BLAS pool at its default size (the reported value) and again with
+    one thread (threadpoolctl limits the pool in-process)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from synth import make_config_inputs
+    import oracle.pipeline as op
+
+    inp = make_config_inputs(name, N=n_sample)
+    tables = None if name == "foe" else op.build_tables(inp)
+    passes, dt = _oracle_passes(name, inp, tables, n_sample, min_seconds)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    with threadpool_limits(limits=1):
+        passes1, dt1 = _oracle_passes(name, inp, tables, n_sample, min_seconds / 2)
     return {"value": passes * n_sample / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{passes} full passes over {n_sample} tokens of the {name} workload "
                       f"(float64 NumPy; BLAS on {threads} threads, elementwise steps "
-                      f"single-threaded); {dt:.1f} s"}
+                      f"single-threaded); {dt:.1f} s",
+            "value_1_thread": passes1 * n_sample / dt1,
+            "sample_1_thread": f"{passes1} passes with the BLAS pool limited to 1 thread; "
+                               f"{dt1:.1f} s"}
 
 
 def pct(xs):
