@@ -356,7 +356,7 @@ int route_est_hidden(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1
 /*
  * est_fit_gram - gram float64[hd+1][hd+1] = H'^T H' and rhs float64[hd+1][E]
  * = H'^T Y for features h bf16 [n][hd] and targets y float[n][E] (row-major).
- * Products and sums in float64 (16 slices of the n rows, summed in order).
+ * Products and sums in float64 (32 slices of the n rows, summed in order).
  *   ws: est_fit_gram_workspace_size(n, hd, E) bytes.
  * Errors: SHAPE (n < 1, hd < 1, E < 1), UNSUPPORTED (hd > 4096, E > 1024),
  * WORKSPACE.

@@ -8,8 +8,9 @@
 //     lambda = ridge * trace(H'^T H') / (hd + 1),
 // solved on the GPU in float64:
 //   est_gram_kernel / est_gram_reduce : H'^T [H' | Y] as 64 x 64 tiles over K
-//       slices (float64 products of bf16 and binary32 values are exact),
-//       slices summed in slice order;
+//       slices, one wave per tile with 8 x 8 accumulators per lane, tiles
+//       below the Gram block's diagonal skipped (float64 products of bf16
+//       and binary32 values are exact), slices summed in slice order;
 //   chol_diag / chol_panel / chol_update : blocked right-looking Cholesky,
 //       64-wide blocks, L in place in the lower triangle and L^T written to
 //       the strict upper one (so both solves read rows of 64 contiguous
@@ -29,79 +30,119 @@ namespace route {
 
 constexpr int kFitTile = 64;
 constexpr int kFitThreads = 256;
-constexpr int kFitKc = 16;        // rows of the K dimension staged per step
-constexpr int kFitSlices = 16;    // K slices of the Gram product
+constexpr int kFitKc = 8;         // rows of the K dimension staged per step
+constexpr int kFitSlices = 32;    // K slices of the Gram product
 
-// Element (n, c) of [H | 1 | Y] (c < hd: feature; c == hd: the bias column;
-// c < hd + 1 + E: target; beyond: zero padding).
-__device__ __forceinline__ double fit_col(const uint16_t* __restrict__ h,
-                                          const float* __restrict__ y, int64_t n, int c, int hd,
-                                          int E) {
-  if (c < hd) return static_cast<double>(__uint_as_float(static_cast<uint32_t>(h[n * hd + c]) << 16));
-  if (c == hd) return 1.0;
-  if (c < hd + 1 + E) return static_cast<double>(y[n * E + (c - hd - 1)]);
-  return 0.0;
+// Tiles of H'^T [H' | Y] below the diagonal of the Gram block (every column
+// j < m, tile column < tile row) are not computed: G is symmetric, and their
+// entries equal their mirror images bit for bit (the same exact products
+// summed in the same row order), which the mirror tiles write for them.
+__host__ __device__ __forceinline__ bool gram_tile_skipped(int bi, int bj, int m) {
+  return bj < bi && (bj + 1) * kFitTile <= m;
 }
 
 // part[s][i][j] = sum over rows of slice s of H'[n][i] * X[n][j], i < m = hd + 1,
-// j < m + E. A 64 x 64 output tile per workgroup, 4 x 4 per thread (rows
-// ty + 16 a, columns tx + 16 b), rows staged kFitKc at a time in LDS.
-__global__ __launch_bounds__(kFitThreads) void est_gram_kernel(const uint16_t* __restrict__ h,
-                                                               const float* __restrict__ y,
-                                                               int64_t n, int hd, int E,
-                                                               double* __restrict__ part) {
-  __shared__ double sa[kFitKc][kFitTile];
-  __shared__ double sb[kFitKc][kFitTile];
+// j < m + E. One wave per 64 x 64 output tile and slice, 8 x 8 accumulators
+// per lane (rows ty + 8 a, columns tx + 8 b); rows staged kFitKc at a time in
+// LDS as float64, the next chunk's loads issued before this chunk's FMAs.
+constexpr int kGramThreads = 64;
+
+__global__ __launch_bounds__(kGramThreads) void est_gram_kernel(const uint16_t* __restrict__ h,
+                                                                const float* __restrict__ y,
+                                                                int64_t n, int hd, int E,
+                                                                double* __restrict__ part) {
+  __shared__ double sa[2][kFitKc][kFitTile];
+  __shared__ double sb[2][kFitKc][kFitTile];
   const int m = hd + 1, mc = hd + 1 + E;
-  const int i0 = blockIdx.x * kFitTile, j0 = blockIdx.y * kFitTile;
+  const int nbj = (mc + kFitTile - 1) / kFitTile;
+  const int bi = blockIdx.x / nbj, bj = blockIdx.x % nbj;
+  if (gram_tile_skipped(bi, bj, m)) return;
+  const int i0 = bi * kFitTile, j0 = bj * kFitTile;
   const int s = blockIdx.z;
   const int64_t lo = n * s / kFitSlices, hi = n * (s + 1) / kFitSlices;
-  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  double acc[4][4];
+  const int t = threadIdx.x, tx = t % 8, ty = t / 8;
+  double acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int64_t k0 = lo; k0 < hi; k0 += kFitKc) {
-    // each thread stages 4 elements of each operand: row r = t / 16 ... ,
-    // column (t % 16) + 16 q
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = t / 16, c = t % 16 + 16 * q;
-      const int64_t nn = k0 + r;
-      const bool in = nn < hi;
-      sa[r][c] = (in && i0 + c < m) ? fit_col(h, y, nn, i0 + c, hd, E) : 0.0;
-      sb[r][c] = (in && j0 + c < mc) ? fit_col(h, y, nn, j0 + c, hd, E) : 0.0;
-    }
-    __syncthreads();
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
+  // lane t stages column t of both operands for the chunk's kFitKc rows. The
+  // column's kind is fixed per lane (0: feature h, 1: the bias column of
+  // ones, 2: target y, 3: padding); the loads keep raw bits so that none
+  // waits before the chunk's products, and rows past the slice are zeroed
+  // when published (their loads are clamped onto the last row, n >= 1).
+  const int ca = i0 + t, cb = j0 + t;
+  const int ka = ca < hd ? 0 : (ca == hd ? 1 : 3);
+  const int kb = cb < hd ? 0 : (cb == hd ? 1 : (cb < mc ? 2 : 3));
+  // every load is unconditional (indices clamped in bounds) so none waits
+  // behind a branch; the kind selects among them when publishing
+  const int64_t hca = ca < hd ? ca : hd - 1;
+  const int64_t hcb = cb < hd ? cb : hd - 1;
+  const int64_t ycb = cb - hd - 1 < 0 ? 0 : (cb - hd - 1 < E ? cb - hd - 1 : E - 1);
+  uint32_t ra[kFitKc], rbh[kFitKc], rby[kFitKc];
+  auto fetch = [&](int64_t k0) {
 #pragma unroll
     for (int r = 0; r < kFitKc; ++r) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = sa[r][ty + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = sb[r][tx + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = acc[a][b] + av[a] * bv[b];
+      const int64_t nn = k0 + r < n ? k0 + r : n - 1;  // n >= 1; rows past the slice zeroed
+      ra[r] = h[nn * hd + hca];
+      rbh[r] = h[nn * hd + hcb];
+      rby[r] = __float_as_uint(y[nn * E + ycb]);
     }
+  };
+  auto value = [&](int kind, uint32_t hbits, uint32_t ybits, bool in) -> double {
+    const float f = kind == 0 ? __uint_as_float(hbits << 16) : __uint_as_float(ybits);
+    const double v = kind == 1 ? 1.0 : (kind == 3 ? 0.0 : static_cast<double>(f));
+    return in ? v : 0.0;
+  };
+  auto publish = [&](int buf, int64_t k0) {
+#pragma unroll
+    for (int r = 0; r < kFitKc; ++r) {
+      const bool in = k0 + r < hi;
+      sa[buf][r][t] = value(ka, ra[r], 0u, in);
+      sb[buf][r][t] = value(kb, rbh[r], rby[r], in);
+    }
+  };
+  int buf = 0;
+  fetch(lo);
+  publish(0, lo);
+  __syncthreads();
+  for (int64_t k0 = lo; k0 < hi; k0 += kFitKc) {
+    const bool more = k0 + kFitKc < hi;
+    if (more) fetch(k0 + kFitKc);
+#pragma unroll 2
+    for (int r = 0; r < kFitKc; ++r) {
+      double av[8], bv[8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) av[a] = sa[buf][r][ty + 8 * a];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) bv[b] = sb[buf][r][tx + 8 * b];
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = acc[a][b] + av[a] * bv[b];
+    }
+    if (more) publish(buf ^ 1, k0 + kFitKc);
     __syncthreads();
+    buf ^= 1;
   }
   double* out = part + static_cast<int64_t>(s) * m * mc;
+  // a tile whose mirror image is skipped also writes its transpose there
+  const bool mirror = gram_tile_skipped(bj, bi, m);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + ty + 8 * a;
     if (i >= m) continue;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
+    for (int b = 0; b < 8; ++b) {
+      const int j = j0 + tx + 8 * b;
       if (j < mc) out[static_cast<int64_t>(i) * mc + j] = acc[a][b];
+      if (mirror && j < m) out[static_cast<int64_t>(j) * mc + i] = acc[a][b];
     }
   }
 }
 
-// gram[i][j] (j < m) and rhs[i][j - m] from the slices, summed in slice order.
+// gram = sum of the slices in slice order (entries of skipped tiles were
+// written by their mirror tiles), rhs likewise.
 __global__ __launch_bounds__(kFitThreads) void est_gram_reduce(const double* __restrict__ part,
                                                                int m, int E,
                                                                double* __restrict__ gram,
@@ -440,9 +481,9 @@ ROUTE_API int est_fit_gram(const uint16_t* h, const float* y, int64_t n, int32_t
   if (!h || !y || !gram || !rhs) return ROUTE_ERR_NULL;
   if (!ws || ws_bytes < est_fit_gram_workspace_size(n, hd, E)) return ROUTE_ERR_WORKSPACE;
   const int m = hd + 1, mc = hd + 1 + E;
-  dim3 grid(ceil_div(m, kFitTile), ceil_div(mc, kFitTile), kFitSlices);
+  dim3 grid(ceil_div(m, kFitTile) * ceil_div(mc, kFitTile), 1, kFitSlices);
   double* part = static_cast<double*>(ws);
-  est_gram_kernel<<<grid, kFitThreads, 0, s>>>(h, y, n, hd, E, part);
+  est_gram_kernel<<<grid, kGramThreads, 0, s>>>(h, y, n, hd, E, part);
   est_gram_reduce<<<ceil_div(static_cast<int64_t>(m) * mc, kFitThreads), kFitThreads, 0, s>>>(
       part, m, E, gram, rhs);
   return launch_status();
