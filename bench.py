@@ -236,10 +236,16 @@ def eg_bench(args):
     return 0
 
 
-def predictor_bytes(N, d, E, K, hd, estimator):
+def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     """Algorithmic HBM bytes of one source layer's prediction (q_l -> logits ->
-    top-K -> hits), each call reading its inputs and writing its outputs once."""
+    top-K -> hits), each call reading its inputs and writing its outputs once.
+    fused: the next gate as route_qgate (r, d_l and W read, logits written; q
+    never leaves the chip)."""
     b = 2
+    if fused and not estimator:
+        return {"qgate": N * d * b + 4 * d + E * d * b + 4 * N * E,
+                "topk": 4 * N * E + 4 * N * K,
+                "hits": 8 * N * K + 8}
     st = {"qhidden": 2 * N * d * b + 4 * d,
           "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
           if estimator else (N * d * b + E * d * b + 4 * N * E),
@@ -332,29 +338,33 @@ def predictor_bench(args):
     N = cfg.N
     p, layers, truths, est, fit_info = predictor_setup(cfg, args)
 
-    def sweep():
+    def sweep(fused=True):
         for L_, T_ in zip(layers, truths):
             p.layer, p.truth = L_, T_
-            p.step()
+            p.step(fused)
 
-    for _ in range(args.warmup):
-        sweep()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    graph = capture_graph(sweep)
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(K):
-        graph.replay()
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = ev[0].elapsed_time(ev[K]) / K
+
+    def timed(fused):
+        for _ in range(args.warmup):
+            sweep(fused)
+        torch.cuda.synchronize()
+        graph = capture_graph(lambda: sweep(fused))
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        wall0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(K):
+            graph.replay()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[K]) / K, time.perf_counter() - wall0
+
+    ms_unfused, _ = timed(False)
+    ms, wall = timed(True)
     # per-stage times of one eager sweep, on an estimator layer and a gate layer
     def stage_times(i):
         p.layer, p.truth = layers[i], truths[i]
@@ -379,7 +389,43 @@ def predictor_bench(args):
             for j, k_ in enumerate(tt):
                 tt[k_].append(1e3 * e[j].elapsed_time(e[j + 1]))
         return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
+
+    def fused_stage_times(i):
+        from token_routing_speculation_amd import route_qgate, route_topk, hit_count
+        p.layer, p.truth = layers[i], truths[i]
+        L_ = p.layer
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        tt = {"qgate": [], "topk": [], "hits": []}
+        for _ in range(10):
+            e[0].record(stream)
+            route_qgate(L_["r"], L_["dvec"], L_["w_next"], eps=L_["eps"], logits=p.logits)
+            e[1].record(stream)
+            route_topk(p.logits, p.K, 1, 1, idx=p.pred, want_weights=False)
+            e[2].record(stream)
+            hit_count(p.pred, p.truth, p.hits)
+            e[3].record(stream)
+            torch.cuda.synchronize()
+            for j, k_ in enumerate(tt):
+                tt[k_].append(1e3 * e[j].elapsed_time(e[j + 1]))
+        return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
     st_est, st_gate = stage_times(0), stage_times(cfg.L - 2)
+    st_fused = fused_stage_times(cfg.L - 2)
+
+    def back_to_back_us(fn, reps=20):
+        """Average duration of one launch over reps launches in a row."""
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / reps
+    from token_routing_speculation_amd import route_qgate
+    Lg = layers[cfg.L - 2]
+    qg_launch_us = back_to_back_us(
+        lambda: route_qgate(Lg["r"], Lg["dvec"], Lg["w_next"], eps=Lg["eps"], logits=p.logits))
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
     rates = []
@@ -399,10 +445,12 @@ def predictor_bench(args):
         gate_on_est.append((int(p.hits.item()) - before) / (N * cfg.K))
     nl = cfg.L - 1
     byt_gate = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False)
+    byt_fused = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False, fused=True)
     byt_est = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, True)
     ne = sum(est)
-    total_bytes = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_gate.values())
-    q_us = st_gate["qhidden"]
+    total_unfused = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_gate.values())
+    total_bytes = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_fused.values())
+    qg_us = qg_launch_us
     out = {
         "metric": "q_l expert-prediction throughput over all source layers (token-predictions/s)",
         "value": N * nl / (ms * 1e-3), "unit": "token-predictions/s", "n_gpus": 1,
@@ -413,10 +461,16 @@ def predictor_bench(args):
                    "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
         "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_sweep": total_bytes,
-        "stages_us_gate_layer": st_gate, "stages_us_estimator_layer": st_est,
-        "roofline": {"bound": "hbm", "kernel": "qhidden_kernel (route_qhidden)",
-                     "achieved": byt_gate["qhidden"] / (q_us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": byt_gate["qhidden"] / (q_us * 1e-6) / HBM_PEAK,
+        "gate_layers": "route_qgate (q_l kept on chip)",
+        "unfused": {"ms_per_step": ms_unfused, "value": N * nl / (ms_unfused * 1e-3),
+                    "alg_bytes_sweep": total_unfused,
+                    "hbm_frac_sweep": total_unfused / (ms_unfused * 1e-3) / HBM_PEAK,
+                    "stages_us_gate_layer": st_gate},
+        "stages_us_gate_layer": st_fused, "stages_us_estimator_layer": st_est,
+        "qgate_us_per_launch": qg_launch_us,
+        "roofline": {"bound": "hbm", "kernel": "qgate_kernel (route_qgate)",
+                     "achieved": byt_fused["qgate"] / (qg_us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": byt_fused["qgate"] / (qg_us * 1e-6) / HBM_PEAK,
                      "traffic": None},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,

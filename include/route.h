@@ -234,6 +234,23 @@ int route_qhidden(const uint16_t* r, const float* dvec, const float* gamma, cons
                   int64_t n, int32_t d, float eps, uint16_t* q, hipStream_t s);
 
 /*
+ * route_qgate - the next gate on q_l without writing q: logits float[n][E] =
+ * q . w^T, q = LN_{l+1}(d_l + r_l) rounded to bf16 exactly as route_qhidden
+ * stores it. [SPEC] item 2.A: q_l fed to layer l+1's router predicts its
+ * experts. The same result as route_qhidden followed by route_gate up to the
+ * order of the binary32 sums (route_gate splits K differently), in one pass
+ * that keeps each workgroup's q rows in LDS; use route_qhidden + route_gate
+ * where q itself is needed (the estimator layers) or d is another size.
+ *   r, dvec, gamma, beta, eps as route_qhidden; w bf16 rows [E][d] (16-byte
+ *   aligned); logits row-major.
+ * Errors: NULL, SHAPE (d % 8, eps < 0, E < 1), ALIGN, UNSUPPORTED (d not
+ * 1024, 2048 or 4096; E > 1024).
+ */
+int route_qgate(const uint16_t* r, const float* dvec, const float* gamma, const float* beta,
+                int64_t n, int32_t d, float eps, const uint16_t* w, int32_t E, float* logits,
+                hipStream_t s);
+
+/*
  * route_estimator - lightweight neural estimator of next-layer logits.
  * [SPEC] item 2.C: logits = GELU(q . w1^T + b1) . w2^T + b2 (GELU with erf).
  * The hidden activation is kept in bf16 (nearest even) in the workspace

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -233,4 +233,19 @@ def test_prefetch_issue_checks_the_host_list_first(L):
     assert f(A, 4, 4096, None, 4, A, None) == NULL
     assert f(A, 4, 4096, addr(lst), 4, None, None) == NULL
     assert f(A, 4, 0, addr(lst), 4, A, None) == OK          # nothing to copy
+
+
+def test_qgate_errors(L):
+    f = L.route_qgate
+    assert f(A, A, None, None, -1, 2048, 1e-5, A, 128, A, None) == SHAPE
+    assert f(A, A, None, None, 10, 2044, 1e-5, A, 128, A, None) == SHAPE
+    assert f(A, A, None, None, 10, 2048, -1.0, A, 128, A, None) == SHAPE
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 0, A, None) == SHAPE
+    assert f(A, A, None, None, 10, 512, 1e-5, A, 128, A, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 1025, A, None) == UNSUP
+    assert f(None, A, None, None, 10, 2048, 1e-5, A, 128, A, None) == NULL
+    assert f(A, A, None, None, 10, 2048, 1e-5, None, 128, A, None) == NULL
+    assert f(MIS, A, None, None, 10, 2048, 1e-5, A, 128, A, None) == ALIGN
+    assert f(A, A, MIS, None, 10, 2048, 1e-5, A, 128, A, None) == ALIGN
+    assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, A, None) == OK     # n = 0 is a no-op
 

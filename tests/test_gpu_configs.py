@@ -121,17 +121,22 @@ def test_predictor_workload(layer):
     lay = make_predictor_layer(cfg, layer)
     p = PredictorPass(cfg.N, cfg.d, cfg.E, cfg.K, cfg.hd).load(lay)
     p.truth_step()
-    p.step()
-    sync()
     S = _sample(cfg.N, 256, layer)
     q_ref = oracle.route_qhidden(lay["r"][S], lay["dvec"], eps=cfg.eps)
-    q_gpu = host(p.q)
-    assert_rel(oracle.bf16_to_f64(q_gpu[S]), q_ref, LOGIT_TOL, "q_l")
     qb = oracle.round_bf16(q_ref)
     if lay["estimator"]:
         ref = oracle.route_estimator(qb, lay["w1"], lay["b1"], lay["w2"], lay["b2"])
     else:
         ref = oracle.route_gate(qb, lay["w_next"])
+    # the two-call path materialises q_l; check it and its logits
+    p.step(fused=False)
+    sync()
+    assert_rel(oracle.bf16_to_f64(host(p.q)[S]), q_ref, LOGIT_TOL, "q_l")
+    assert_rel(host(p.logits)[S], ref, LOGIT_TOL, "predicted logits (two calls)")
+    # the pass as benchmarked (gate layers: route_qgate, q kept on chip)
+    p.hits.zero_()
+    p.step()
+    sync()
     lg = host(p.logits)
     assert_rel(lg[S], ref, LOGIT_TOL, "predicted logits")
     tl = host(p.true_logits)

@@ -1,0 +1,74 @@
+"""The fused next gate on q_l ("Speculating Experts Accelerates Inference
+for Mixture-of-Experts", item 2.A) against the oracle (float64 q_l and
+product, 1e-2 relative with the row floor) and against the two-call path
+route_qhidden + route_gate: the bf16 q rows are the same, so the logits may
+differ only by the order of the binary32 sums."""
+
+import numpy as np
+import pytest
+import torch
+
+import token_routing_speculation_amd as tr
+import oracle
+from oracle.bf16 import round_bf16
+
+from gpu_helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 1e-2
+
+
+def assert_rel(got, ref, tol, what):
+    """Elementwise |got - ref| <= tol * max(|ref|, rms of ref): the floor is
+    the whole matrix's rms, so rows of one or a few logits (E = 1) are judged
+    like the others."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref)))
+    e = float(np.max(np.abs(got - ref) / den))
+    assert e <= tol, f"{what}: max relative error {e:.3e} > {tol:.1e}"
+
+
+def _case(n, d, E, affine, seed):
+    rng = np.random.default_rng(seed)
+    r = round_bf16(rng.standard_normal((n, d)))
+    dv = (rng.standard_normal(d) * np.sqrt(0.1)).astype(np.float32)
+    g = rng.standard_normal(d).astype(np.float32) if affine else None
+    b = rng.standard_normal(d).astype(np.float32) if affine else None
+    w = round_bf16(rng.standard_normal((E, d)) / np.sqrt(d))
+    return r, dv, g, b, w
+
+
+@pytest.mark.parametrize("n,d,E,affine", [(1, 2048, 128, False), (8192, 2048, 128, False),
+                                          (37, 1024, 8, True), (1000, 4096, 160, True),
+                                          (100, 2048, 1, False), (33, 1024, 1024, False),
+                                          (77, 2048, 130, True), (16, 4096, 16, False)])
+def test_qgate(n, d, E, affine):
+    r, dv, g, b, w = _case(n, d, E, affine, n + d + E)
+    opt = lambda a: None if a is None else dev(a)
+    got = host(tr.route_qgate(dev(r), dev(dv), dev(w), opt(g), opt(b), 1e-5))
+    # against the oracle: float64 q_l (not rounded) and a float64 product
+    q64 = oracle.route_qhidden(r, dv, g, b, 1e-5)
+    want = q64 @ oracle.bf16_to_f64(w).T
+    assert_rel(got, want, LOGIT_TOL, "qgate logits")
+    # against the two-call path on the same device q
+    q = tr.route_qhidden(dev(r), dev(dv), opt(g), opt(b), 1e-5)
+    two = host(tr.route_gate(q, dev(w)))
+    ref = oracle.bf16_to_f64(host(q)) @ oracle.bf16_to_f64(w).T   # exact products of the bf16 q
+    assert_rel(got, ref, 1e-5, "qgate vs bf16 q")
+    assert_rel(two, ref, 1e-5, "two-call vs bf16 q")
+
+
+def test_qgate_top_k_matches_two_call_path():
+    """On the Qwen3-shaped next gate the fused and two-call logits pick the
+    same top-8 except where two logits sit within float32 rounding."""
+    n, d, E, K = 8192, 2048, 128, 8
+    r, dv, _, _, w = _case(n, d, E, False, 5)
+    a = tr.route_qgate(dev(r), dev(dv), dev(w))
+    q = tr.route_qhidden(dev(r), dev(dv))
+    bl = tr.route_gate(q, dev(w))
+    ia, _ = tr.route_topk(a, K, 1, 1)
+    ib, _ = tr.route_topk(bl, K, 1, 1)
+    same = (np.sort(host(ia), axis=1) == np.sort(host(ib), axis=1)).all(axis=1)
+    assert same.mean() > 0.999

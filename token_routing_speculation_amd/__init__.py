@@ -26,7 +26,8 @@ __all__ = [
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
     "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
     "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
-    "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "EXPORTS",
+    "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "route_qgate",
+    "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +55,7 @@ EXPORTS = {
     "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
     "route_qhidden": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p]),
+    "route_qgate": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _p, _p]),
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
@@ -284,6 +286,18 @@ def route_qhidden(r, dvec, gamma=None, beta=None, eps=1e-5, q=None, stream=None)
           _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
           float(eps), _dev(q, _bf16(r), "q", n * d), _stream(stream))
     return q
+
+
+def route_qgate(r, dvec, w, gamma=None, beta=None, eps=1e-5, logits=None, stream=None):
+    """logits [n][E] = bf16(LN(dvec + r)) . w^T without writing q (d in 1024, 2048, 4096)."""
+    n, d = r.shape
+    E = w.shape[0]
+    logits = _empty((n, E), torch.float32, r) if logits is None else logits
+    _call("route_qgate", _dev(r, _bf16(r), "r"), _dev(dvec, torch.float32, "dvec", d),
+          _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
+          float(eps), _dev(w, _bf16(w), "w", E * d), E, _dev(logits, torch.float32, "logits", n * E),
+          _stream(stream))
+    return logits
 
 
 def route_estimator_workspace_size(n: int, hd: int) -> int:

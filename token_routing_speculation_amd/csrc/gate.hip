@@ -23,21 +23,14 @@
 // (item 2.A: next gate on q_l; item 2.C: the estimator MLP).
 #include "common.hpp"
 #include "gemm.hpp"
+#include "mfma.hpp"
 #include <type_traits>
 
 namespace route {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kGemmThreads = 256;
 constexpr int kPfa = 3;  // A-operand prefetch depth, in K steps
 enum { EPI_F32 = 0, EPI_BIAS_GELU_BF16 = 1, EPI_BIAS_F32 = 2 };
-
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));

@@ -1,0 +1,19 @@
+// bf16 matrix-core product shared by the kernels that use it:
+// v_mfma_f32_16x16x32_bf16, D = A . B + C for a 16 x 32 A fragment and a
+// 32 x 16 B fragment. Lane l holds row (A) or column (B) l % 16, elements
+// k = 8 (l / 16) .. 8 (l / 16) + 7 as one 16-byte vector; the result holds
+// rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+#pragma once
+#include "common.hpp"
+
+namespace route {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+}  // namespace route

@@ -7,6 +7,7 @@
 // row's own bytes); the row loads are unconditional (vectors past the row
 // end reload vector 0 and are masked out), so they issue back to back.
 #include "common.hpp"
+#include "mfma.hpp"
 
 #include <type_traits>
 
@@ -33,26 +34,18 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (a + b) + (c + e);
 }
 
-template <int CPL>  // 16-byte vectors per lane
-__global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
-    const uint16_t* __restrict__ r, const float* __restrict__ dvec,
-    const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, int d,
-    float eps, uint16_t* __restrict__ q) {
-  __shared__ __attribute__((aligned(16))) float sd[kLnMaxD];
-  for (int j = threadIdx.x * 4; j < d; j += kLnThreads * 4)
-    *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
-  __syncthreads();
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kLnThreads / kWave) + wave_id();
-  if (i >= n) return;
-  const int lane = lane_id();
+// q for one row, held by one wave: lane `lane` owns 16-byte vectors
+// v = lane + c * 64 (c < CPL, v < nv = d / 8) of r + d_l (d_l staged in LDS
+// as sd), normalised with the row's binary32 mean and centred variance,
+// scaled and shifted (gamma, beta: nullable), rounded to bf16 (nearest
+// even) and packed eight to a vector in q[c]. raw[] holds the row's loads
+// (vectors past the row end were loaded from vector 0 and are ignored).
+template <int CPL>
+__device__ __forceinline__ void ln_row(const u32x4 (&raw)[CPL], const float* __restrict__ sd,
+                                       const float* __restrict__ gamma,
+                                       const float* __restrict__ beta, int d, float eps,
+                                       int lane, u32x4 (&q)[CPL]) {
   const int nv = d >> 3;
-  const uint16_t* row = r + static_cast<size_t>(i) * d;
-  u32x4 raw[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int v = lane + c * kWave;
-    raw[c] = ld16_stream(row + 8 * (v < nv ? v : 0));
-  }
   float x[CPL][8];
   float sum = 0.f;
 #pragma unroll
@@ -84,27 +77,183 @@ __global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
   }
   const float var = wave_sum_f32(ss) / static_cast<float>(d);
   const float inv = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int v = lane + c * kWave;
+    const int vv = v < nv ? v : 0;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * inv;
+    if (gamma) {
+      const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * vv);
+      const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * vv + 4);
+      y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
+      y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
+    }
+    if (beta) {
+      const float4 b0 = *reinterpret_cast<const float4*>(beta + 8 * vv);
+      const float4 b1 = *reinterpret_cast<const float4*>(beta + 8 * vv + 4);
+      y[0] += b0.x; y[1] += b0.y; y[2] += b0.z; y[3] += b0.w;
+      y[4] += b1.x; y[5] += b1.y; y[6] += b1.z; y[7] += b1.w;
+    }
+    q[c] = pack8(y);
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void load_row(const uint16_t* __restrict__ row, int nv, int lane,
+                                         u32x4 (&raw)[CPL]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int v = lane + c * kWave;
+    raw[c] = ld16_stream(row + 8 * (v < nv ? v : 0));
+  }
+}
+
+template <int CPL>  // 16-byte vectors per lane
+__global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
+    const uint16_t* __restrict__ r, const float* __restrict__ dvec,
+    const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, int d,
+    float eps, uint16_t* __restrict__ q) {
+  __shared__ __attribute__((aligned(16))) float sd[kLnMaxD];
+  for (int j = threadIdx.x * 4; j < d; j += kLnThreads * 4)
+    *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
+  __syncthreads();
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kLnThreads / kWave) + wave_id();
+  if (i >= n) return;
+  const int lane = lane_id();
+  const int nv = d >> 3;
+  u32x4 raw[CPL], y[CPL];
+  load_row<CPL>(r + static_cast<size_t>(i) * d, nv, lane, raw);
+  ln_row<CPL>(raw, sd, gamma, beta, d, eps, lane, y);
   uint16_t* out = q + static_cast<size_t>(i) * d;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int v = lane + c * kWave;
-    if (v < nv) {
-      float y[8];
+    if (v < nv) st16(out + 8 * v, y[c]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// route_qgate: the next gate applied to q_l without q leaving the chip. A
+// workgroup of eight waves owns BM rows: each row's q is computed by
+// ln_row (the same arithmetic as route_qhidden, so the bf16 values are the
+// same) and kept in LDS as a BM x D bf16 tile (128 KB of the CU's 160 KB);
+// then the waves take the 16-column groups of W in turn and multiply the
+// resident tile by W's rows, read from L2 as whole lines kQgLead pairs of K
+// steps ahead and turned into MFMA fragments through a small per-wave LDS
+// buffer. q is neither written nor read back.
+// ---------------------------------------------------------------------------
+constexpr int kQgThreads = 512;
+constexpr int kQgLead = 7;  // W line loads in flight, in pairs of K steps
+
+// LDS offset of 16-byte piece p of tile row rr: pieces XOR-swizzled by the
+// row's low three bits (within aligned groups of eight), so the sixteen rows
+// of an MFMA fragment read spread over the banks.
+template <int D>
+__device__ __forceinline__ int qg_off(int rr, int p) {
+  return rr * D * 2 + ((p ^ (rr & 7)) << 4);
+}
+
+template <int BM, int D>
+__global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
+    const uint16_t* __restrict__ r, const float* __restrict__ dvec,
+    const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
+    const uint16_t* __restrict__ w, int E, float* __restrict__ logits) {
+  constexpr int CPL = D / 8 / kWave;
+  constexpr int NV = D / 8;
+  constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
+  constexpr int MT = BM / 16;
+  constexpr int NPAIRS = D / 64;  // pairs of 32-wide K steps
+  static_assert(CPL * 8 * kWave == D && RPW >= 1 && BM % 16 == 0, "tile shape");
+  static_assert(NPAIRS % (kQgLead + 1) == 0, "the ring cycles whole");
+  __shared__ __attribute__((aligned(16))) float sd[D];
+  __shared__ __attribute__((aligned(16))) char tile[BM * D * 2];
+  __shared__ __attribute__((aligned(16))) char wstage[(kQgThreads / kWave) * 2048];
+  const int lane = lane_id(), wv = wave_id();
+  for (int j = threadIdx.x * 4; j < D; j += kQgThreads * 4)
+    *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
+  __syncthreads();
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  // q rows: wave wv takes tile rows wv, wv + 8, ...; all their loads are
+  // issued before the first is normalised. Rows past n repeat row n - 1
+  // (their logits are never stored).
+  u32x4 raw[RPW][CPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * inv;
-      if (gamma) {
-        const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * v);
-        const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * v + 4);
-        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
-        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
+  for (int k = 0; k < RPW; ++k) {
+    const int64_t i = row0 + wv + 8 * k;
+    load_row<CPL>(r + static_cast<size_t>(i < n ? i : n - 1) * D, NV, lane, raw[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    u32x4 y[CPL];
+    ln_row<CPL>(raw[k], sd, gamma, beta, D, eps, lane, y);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      *reinterpret_cast<u32x4*>(tile + qg_off<D>(wv + 8 * k, lane + c * kWave)) = y[c];
+  }
+  __syncthreads();
+  // W: wave wv takes the 16-column groups wv, wv + 8, ... Each pair of K
+  // steps (64 k) of its 16 rows is loaded as whole 128-byte lines (8 lanes
+  // per row, two loads), kQgLead pairs ahead, then passed through the wave's
+  // own 2 KB of LDS into the fragment layout (LDS operations of one wave
+  // complete in order, so no barrier is needed).
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int ngroups = (E + 15) / 16;
+  char* wst = wstage + wv * 2048;
+  const int lrow = lane >> 3, lchunk = lane & 7;  // line-load mapping: row, 16-byte chunk
+  for (int g = wv; g < ngroups; g += kQgThreads / kWave) {
+    const uint16_t* wq[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 16 * g + lrow + 8 * h;
+      wq[h] = w + static_cast<int64_t>(c < E ? c : E - 1) * D + 8 * lchunk;
+    }
+    f32x4 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 ring[kQgLead + 1][2];
+    auto ldw = [&](u32x4 (&dst)[2], int pp) {
+      pp = pp < NPAIRS ? pp : NPAIRS - 1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dst[h] = ld16(wq[h] + 64 * pp);
+    };
+#pragma unroll
+    for (int j = 0; j < kQgLead; ++j) ldw(ring[j], j);
+#pragma unroll 1
+    for (int p0 = 0; p0 < NPAIRS; p0 += kQgLead + 1) {
+#pragma unroll
+      for (int j = 0; j <= kQgLead; ++j) {
+        const int pp = p0 + j;
+        ldw(ring[(j + kQgLead) % (kQgLead + 1)], pp + kQgLead);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = lrow + 8 * h;
+          *reinterpret_cast<u32x4*>(wst + rr * 128 + ((lchunk ^ (rr & 7)) << 4)) = ring[j][h];
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const u32x4 bf = *reinterpret_cast<const u32x4*>(
+              wst + r16 * 128 + (((kq + 4 * half) ^ (r16 & 7)) << 4));
+          const int st = 2 * pp + half;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 af =
+                *reinterpret_cast<const u32x4*>(tile + qg_off<D>(16 * m + r16, 4 * st + kq));
+            acc[m] = mfma16x16x32(af, bf, acc[m]);
+          }
+        }
       }
-      if (beta) {
-        const float4 b0 = *reinterpret_cast<const float4*>(beta + 8 * v);
-        const float4 b1 = *reinterpret_cast<const float4*>(beta + 8 * v + 4);
-        y[0] += b0.x; y[1] += b0.y; y[2] += b0.z; y[3] += b0.w;
-        y[4] += b1.x; y[5] += b1.y; y[6] += b1.z; y[7] += b1.w;
-      }
-      st16(out + 8 * v, pack8(y));
+    }
+    const int colr = 16 * g + r16;
+    if (colr < E) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int64_t row = row0 + 16 * m + 4 * kq + jj;
+          if (row < n) logits[row * E + colr] = acc[m][jj];
+        }
     }
   }
 }
@@ -136,3 +285,25 @@ ROUTE_API int route_qhidden(const uint16_t* r, const float* dvec, const float* g
     qhidden_kernel<16><<<grid, kLnThreads, 0, s>>>(r, dvec, gamma, beta, n, d, eps, q);
   return launch_status();
 }
+
+ROUTE_API int route_qgate(const uint16_t* r, const float* dvec, const float* gamma,
+                          const float* beta, int64_t n, int32_t d, float eps, const uint16_t* w,
+                          int32_t E, float* logits, hipStream_t s) {
+  if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || E < 1) return ROUTE_ERR_SHAPE;
+  if (E > kMaxExperts || (d != 1024 && d != 2048 && d != 4096)) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!r || !dvec || !w || !logits) return ROUTE_ERR_NULL;
+  if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
+  if (d == 1024)
+    qgate_kernel<32, 1024><<<ceil_div(n, 32), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
+                                                                  E, logits);
+  else if (d == 2048)
+    qgate_kernel<32, 2048><<<ceil_div(n, 32), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
+                                                                  E, logits);
+  else
+    qgate_kernel<16, 4096><<<ceil_div(n, 16), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
+                                                                  E, logits);
+  return launch_status();
+}
+

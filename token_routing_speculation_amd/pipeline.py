@@ -35,7 +35,9 @@ from . import (route_predict, route_lut_build, srs_shuffle, route_gate, route_to
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
-               eg_update, eg_score_workspace_size)
+               eg_update, eg_score_workspace_size, route_qgate)
+
+QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -245,13 +247,20 @@ class PredictorPass:
         route_gate(L["s_next"], L["w_next"], logits=self.true_logits)
         route_topk(self.true_logits, self.K, 1, 1, idx=self.truth, want_weights=False)
 
-    def step(self):
+    def step(self, fused=True):
+        """One source layer: the next gate on q_l (route_qgate, q kept on chip,
+        when ``fused`` and d allows; else route_qhidden + route_gate) or the
+        estimator on q_l, then top-K and the hit count."""
         L = self.layer
-        route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
-        if L["estimator"]:
-            route_estimator(self.q, L["w1"], L["b1"], L["w2"], L["b2"], logits=self.logits, ws=self.ws)
+        if not L["estimator"] and fused and self.d in QGATE_D:
+            route_qgate(L["r"], L["dvec"], L["w_next"], eps=L["eps"], logits=self.logits)
         else:
-            route_gate(self.q, L["w_next"], logits=self.logits)
+            route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
+            if L["estimator"]:
+                route_estimator(self.q, L["w1"], L["b1"], L["w2"], L["b2"], logits=self.logits,
+                                ws=self.ws)
+            else:
+                route_gate(self.q, L["w_next"], logits=self.logits)
         route_topk(self.logits, self.K, 1, 1, idx=self.pred, want_weights=False)
         hit_count(self.pred, self.truth, self.hits)
 
