@@ -57,7 +57,8 @@ def test_predict_flags_out_of_vocabulary():
 
 # ------------------------------------------------------------------- SRS
 SRS_CASES = [(1, 8, 1, 1), (7, 136, 2, 2), (1000, 512, 2, 8), (3001, 64, 3, 5), (5000, 256, 4, 1),
-             (2049, 40, 5, 256), (4096, 4096, 2, 4), (300, 2048, 1, 7)]
+             (2049, 40, 5, 256), (4096, 4096, 2, 4), (300, 2048, 1, 7),
+             (257, 520, 16, 3), (64, 64, 9, 256)]   # the maximum P (16) and a P past the fast paths
 
 
 @pytest.mark.parametrize("n,d,P,G", SRS_CASES)
