@@ -239,12 +239,11 @@ def eg_bench(args):
 def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     """Algorithmic HBM bytes of one source layer's prediction (q_l -> logits ->
     top-K -> hits), each call reading its inputs and writing its outputs once.
-    fused: the next gate as route_qgate (r, d_l and W read, logits written; q
-    never leaves the chip)."""
+    fused: the next gate and its top-K as route_qgate_topk (r, d_l and W read,
+    the picks written; q and the logits never leave the chip)."""
     b = 2
     if fused and not estimator:
-        return {"qgate": N * d * b + 4 * d + E * d * b + 4 * N * E,
-                "topk": 4 * N * E + 4 * N * K,
+        return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K,
                 "hits": 8 * N * K + 8}
     st = {"qhidden": 2 * N * d * b + 4 * d,
           "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
@@ -391,19 +390,17 @@ def predictor_bench(args):
         return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
 
     def fused_stage_times(i):
-        from token_routing_speculation_amd import route_qgate, route_topk, hit_count
+        from token_routing_speculation_amd import route_qgate_topk, hit_count
         p.layer, p.truth = layers[i], truths[i]
         L_ = p.layer
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        tt = {"qgate": [], "topk": [], "hits": []}
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tt = {"qgate_topk": [], "hits": []}
         for _ in range(10):
             e[0].record(stream)
-            route_qgate(L_["r"], L_["dvec"], L_["w_next"], eps=L_["eps"], logits=p.logits)
+            route_qgate_topk(L_["r"], L_["dvec"], L_["w_next"], p.K, eps=L_["eps"], idx=p.pred)
             e[1].record(stream)
-            route_topk(p.logits, p.K, 1, 1, idx=p.pred, want_weights=False)
-            e[2].record(stream)
             hit_count(p.pred, p.truth, p.hits)
-            e[3].record(stream)
+            e[2].record(stream)
             torch.cuda.synchronize()
             for j, k_ in enumerate(tt):
                 tt[k_].append(1e3 * e[j].elapsed_time(e[j + 1]))
@@ -422,10 +419,10 @@ def predictor_bench(args):
         b.record(stream)
         torch.cuda.synchronize()
         return 1e3 * a.elapsed_time(b) / reps
-    from token_routing_speculation_amd import route_qgate
+    from token_routing_speculation_amd import route_qgate_topk
     Lg = layers[cfg.L - 2]
     qg_launch_us = back_to_back_us(
-        lambda: route_qgate(Lg["r"], Lg["dvec"], Lg["w_next"], eps=Lg["eps"], logits=p.logits))
+        lambda: route_qgate_topk(Lg["r"], Lg["dvec"], Lg["w_next"], p.K, eps=Lg["eps"], idx=p.pred))
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
     rates = []
@@ -461,17 +458,17 @@ def predictor_bench(args):
                    "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
         "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_sweep": total_bytes,
-        "gate_layers": "route_qgate (q_l kept on chip)",
+        "gate_layers": "route_qgate_topk (q_l and the logits kept on chip)",
         "unfused": {"ms_per_step": ms_unfused, "value": N * nl / (ms_unfused * 1e-3),
                     "alg_bytes_sweep": total_unfused,
                     "hbm_frac_sweep": total_unfused / (ms_unfused * 1e-3) / HBM_PEAK,
                     "stages_us_gate_layer": st_gate},
         "stages_us_gate_layer": st_fused, "stages_us_estimator_layer": st_est,
-        "qgate_us_per_launch": qg_launch_us,
-        "roofline": {"bound": "hbm", "kernel": "qgate_kernel (route_qgate)",
-                     "achieved": byt_fused["qgate"] / (qg_us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": byt_fused["qgate"] / (qg_us * 1e-6) / HBM_PEAK,
-                     "traffic": None},
+        "qgate_topk_us_per_launch": qg_launch_us,
+        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, true> (route_qgate_topk)",
+                     "achieved": byt_fused["qgate_topk"] / (qg_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK, "traffic": None},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
         "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),

@@ -251,6 +251,20 @@ int route_qgate(const uint16_t* r, const float* dvec, const float* gamma, const 
                 hipStream_t s);
 
 /*
+ * route_qgate_topk - route_qgate followed by each row's top K experts in the
+ * same kernel: idx int32[n][K] holds the K largest logits' columns, largest
+ * first, equal logits to the lower column, -0.0 == +0.0 (route_topk's order
+ * with H = 1; no weights). [SPEC] item 2.A (predicted top-K of layer l+1
+ * from q_l). logits float[n][E] is written too when not NULL; idx equals
+ * route_topk applied to those logits.
+ * Errors: as route_qgate, plus SHAPE (K < 1, K > E) and UNSUPPORTED (E > 256,
+ * K > 16).
+ */
+int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma, const float* beta,
+                     int64_t n, int32_t d, float eps, const uint16_t* w, int32_t E, int32_t K,
+                     float* logits, int32_t* idx, hipStream_t s);
+
+/*
  * route_estimator - lightweight neural estimator of next-layer logits.
  * [SPEC] item 2.C: logits = GELU(q . w1^T + b1) . w2^T + b2 (GELU with erf).
  * The hidden activation is kept in bf16 (nearest even) in the workspace

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -248,4 +248,15 @@ def test_qgate_errors(L):
     assert f(MIS, A, None, None, 10, 2048, 1e-5, A, 128, A, None) == ALIGN
     assert f(A, A, MIS, None, 10, 2048, 1e-5, A, 128, A, None) == ALIGN
     assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, A, None) == OK     # n = 0 is a no-op
+
+
+def test_qgate_topk_errors(L):
+    f = L.route_qgate_topk
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 0, None, A, None) == SHAPE
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 4, 5, None, A, None) == SHAPE     # K > E
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 257, 8, None, A, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 17, None, A, None) == UNSUP
+    assert f(A, A, None, None, 10, 512, 1e-5, A, 128, 8, None, A, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, None, None) == NULL
+    assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, 8, None, A, None) == OK
 

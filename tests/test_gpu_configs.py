@@ -133,9 +133,9 @@ def test_predictor_workload(layer):
     sync()
     assert_rel(oracle.bf16_to_f64(host(p.q)[S]), q_ref, LOGIT_TOL, "q_l")
     assert_rel(host(p.logits)[S], ref, LOGIT_TOL, "predicted logits (two calls)")
-    # the pass as benchmarked (gate layers: route_qgate, q kept on chip)
+    # the pass as benchmarked (gate layers: route_qgate_topk, q kept on chip)
     p.hits.zero_()
-    p.step()
+    p.step(keep_logits=True)
     sync()
     lg = host(p.logits)
     assert_rel(lg[S], ref, LOGIT_TOL, "predicted logits")

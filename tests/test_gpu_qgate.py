@@ -72,3 +72,37 @@ def test_qgate_top_k_matches_two_call_path():
     ib, _ = tr.route_topk(bl, K, 1, 1)
     same = (np.sort(host(ia), axis=1) == np.sort(host(ib), axis=1)).all(axis=1)
     assert same.mean() > 0.999
+
+
+@pytest.mark.parametrize("n,d,E,K,affine", [(1, 2048, 128, 8, False), (8192, 2048, 128, 8, False),
+                                            (37, 1024, 8, 2, True), (1000, 4096, 160, 6, True),
+                                            (77, 2048, 256, 16, False), (100, 2048, 1, 1, False),
+                                            (33, 1024, 200, 5, True), (16, 4096, 64, 8, False)])
+def test_qgate_topk_is_route_topk_of_its_logits(n, d, E, K, affine):
+    r, dv, g, b, w = _case(n, d, E, affine, n + d + E + K)
+    opt = lambda a: None if a is None else dev(a)
+    lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, opt(g), opt(b), 1e-5, logits=lg)
+    want, _ = tr.route_topk(lg, K, 1, 1)
+    assert np.array_equal(host(idx), host(want))              # the same picks, bit for bit
+    same = host(tr.route_qgate(dev(r), dev(dv), dev(w), opt(g), opt(b), 1e-5))
+    assert np.array_equal(host(lg), same)                     # the same logits as route_qgate
+    idx2 = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, opt(g), opt(b), 1e-5)   # no logits
+    assert np.array_equal(host(idx2), host(idx))
+
+
+def test_qgate_topk_ties_and_signed_zeros():
+    """W rows repeated and zeroed give equal logits and signed zeros; the
+    picks follow route_topk (lower column on equal logits, -0.0 == +0.0)."""
+    n, d, E, K = 64, 1024, 64, 8
+    r, dv, _, _, w = _case(n, d, E, False, 9)
+    w[10] = w[3]
+    w[40] = w[3]
+    w[20] = 0
+    w[21] = 0
+    w[22] = 0x8000                         # a row of -0.0: its logits are signed zeros
+    lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, logits=lg)
+    want, _ = tr.route_topk(lg, K, 1, 1)
+    assert np.array_equal(host(idx), host(want))
+

@@ -57,14 +57,13 @@ __global__ __launch_bounds__(kCntThreads) void hit_kernel(const int32_t* __restr
     }
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
-      if (k >= K) break;
       bool in_truth = false, seen = false;
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
         if (j < K && t[j] == p[k]) in_truth = true;
         if (j < k && p[j] == p[k]) seen = true;
       }
-      cnt += (in_truth && !seen) ? 1u : 0u;
+      cnt += (k < K && in_truth && !seen) ? 1u : 0u;
     }
   }
   block_add(cnt, hits);

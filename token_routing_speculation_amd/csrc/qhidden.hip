@@ -8,6 +8,7 @@
 // end reload vector 0 and are masked out), so they issue back to back.
 #include "common.hpp"
 #include "mfma.hpp"
+#include "topk.hpp"
 
 #include <type_traits>
 
@@ -155,11 +156,15 @@ __device__ __forceinline__ int qg_off(int rr, int p) {
   return rr * D * 2 + ((p ^ (rr & 7)) << 4);
 }
 
-template <int BM, int D>
+// TOPK: also pick each row's top K columns (E <= 256, K <= 16), in
+// route_topk's order (largest logit first, equal logits to the lower column,
+// -0.0 == +0.0), from the logits gathered in LDS; logits may then be NULL.
+template <int BM, int D, bool TOPK>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
-    const uint16_t* __restrict__ w, int E, float* __restrict__ logits) {
+    const uint16_t* __restrict__ w, int E, float* __restrict__ logits, int K,
+    int* __restrict__ idx) {
   constexpr int CPL = D / 8 / kWave;
   constexpr int NV = D / 8;
   constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
@@ -202,14 +207,13 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   const int ngroups = (E + 15) / 16;
   char* wst = wstage + wv * 2048;
   const int lrow = lane >> 3, lchunk = lane & 7;  // line-load mapping: row, 16-byte chunk
-  for (int g = wv; g < ngroups; g += kQgThreads / kWave) {
+  auto gemm_group = [&](int g, f32x4 (&acc)[MT]) {
     const uint16_t* wq[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = 16 * g + lrow + 8 * h;
       wq[h] = w + static_cast<int64_t>(c < E ? c : E - 1) * D + 8 * lchunk;
     }
-    f32x4 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 ring[kQgLead + 1][2];
@@ -245,6 +249,8 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
         }
       }
     }
+  };
+  auto store_logits = [&](int g, const f32x4 (&acc)[MT]) {
     const int colr = 16 * g + r16;
     if (colr < E) {
 #pragma unroll
@@ -254,6 +260,76 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
           const int64_t row = row0 + 16 * m + 4 * kq + jj;
           if (row < n) logits[row * E + colr] = acc[m][jj];
         }
+    }
+  };
+  if constexpr (!TOPK) {
+    for (int g = wv; g < ngroups; g += kQgThreads / kWave) {
+      f32x4 acc[MT];
+      gemm_group(g, acc);
+      store_logits(g, acc);
+    }
+  } else {
+    // at most two column groups per wave (E <= 256)
+    constexpr int NW = kQgThreads / kWave;
+    f32x4 accs[2][MT];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = wv + NW * gi;
+      if (g < ngroups) {
+        gemm_group(g, accs[gi]);
+        if (logits) store_logits(g, accs[gi]);
+      }
+    }
+    __syncthreads();  // every wave is done with the q tile: it now holds the logits
+    float* lt = reinterpret_cast<float*>(tile);  // BM x E
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = wv + NW * gi;
+      const int col = 16 * g + r16;
+      if (g < ngroups && col < E) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) lt[(16 * m + 4 * kq + jj) * E + col] = accs[gi][m][jj];
+      }
+    }
+    __syncthreads();
+    // a 16-lane segment per row, four rows per wave (rows 4 wv + seg): lane
+    // s of a segment holds columns s, s + 16, ...; K rounds of a segment max
+    // of the keys, equal keys resolved to the lowest column
+    const int seg = lane >> 4, sl = lane & 15;
+    const int rr = 4 * wv + seg;
+    if (4 * wv < BM) {
+      const int rrc = rr < BM ? rr : BM - 1;
+      uint32_t key[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int c = sl + 16 * v;
+        key[v] = c < E ? order_key(lt[rrc * E + c]) : 0u;
+      }
+      int myc = 0;
+#pragma unroll
+      for (int pick = 0; pick < kMaxK; ++pick) {
+        if (pick < K) {
+          uint32_t best = 0u;
+          int bv = 0;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (key[v] > best) {  // strict: the lowest v on equal keys
+              best = key[v];
+              bv = v;
+            }
+          const uint32_t mx = seg_max<16>(best);
+          const int col = static_cast<int>(
+              seg_min<16>(best == mx ? static_cast<uint32_t>(sl + 16 * bv) : 0xffffffffu));
+          const bool mine = sl == (col & 15);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) key[v] = (mine && bv == v) ? 0u : key[v];
+          if (sl == pick) myc = col;
+        }
+      }
+      const int64_t grow = row0 + rr;
+      if (rr < BM && grow < n && sl < K) idx[grow * K + sl] = myc;
     }
   }
 }
@@ -296,14 +372,36 @@ ROUTE_API int route_qgate(const uint16_t* r, const float* dvec, const float* gam
   if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
   if (d == 1024)
-    qgate_kernel<32, 1024><<<ceil_div(n, 32), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
-                                                                  E, logits);
+    qgate_kernel<32, 1024, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
   else if (d == 2048)
-    qgate_kernel<32, 2048><<<ceil_div(n, 32), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
-                                                                  E, logits);
+    qgate_kernel<32, 2048, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
   else
-    qgate_kernel<16, 4096><<<ceil_div(n, 16), kQgThreads, 0, s>>>(r, dvec, gamma, beta, n, eps, w,
-                                                                  E, logits);
+    qgate_kernel<16, 4096, false><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
   return launch_status();
 }
 
+ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma,
+                               const float* beta, int64_t n, int32_t d, float eps,
+                               const uint16_t* w, int32_t E, int32_t K, float* logits,
+                               int32_t* idx, hipStream_t s) {
+  if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || E < 1 || K < 1 || K > E)
+    return ROUTE_ERR_SHAPE;
+  if (E > 256 || K > kMaxK || (d != 1024 && d != 2048 && d != 4096)) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!r || !dvec || !w || !idx) return ROUTE_ERR_NULL;
+  if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
+  if (d == 1024)
+    qgate_kernel<32, 1024, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+  else if (d == 2048)
+    qgate_kernel<32, 2048, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+  else
+    qgate_kernel<16, 4096, true><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+  return launch_status();
+}

@@ -35,7 +35,7 @@ from . import (route_predict, route_lut_build, srs_shuffle, route_gate, route_to
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
-               eg_update, eg_score_workspace_size, route_qgate)
+               eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
@@ -247,13 +247,16 @@ class PredictorPass:
         route_gate(L["s_next"], L["w_next"], logits=self.true_logits)
         route_topk(self.true_logits, self.K, 1, 1, idx=self.truth, want_weights=False)
 
-    def step(self, fused=True):
-        """One source layer: the next gate on q_l (route_qgate, q kept on chip,
-        when ``fused`` and d allows; else route_qhidden + route_gate) or the
-        estimator on q_l, then top-K and the hit count."""
+    def step(self, fused=True, keep_logits=False):
+        """One source layer: on gate layers the next gate on q_l and its top-K
+        in one kernel (route_qgate_topk, q and the logits kept on chip; the
+        logits are written only if ``keep_logits``) when ``fused`` and the
+        shape allows, else route_qhidden + route_gate + route_topk; on
+        estimator layers q_l, the estimator and top-K. Then the hit count."""
         L = self.layer
-        if not L["estimator"] and fused and self.d in QGATE_D:
-            route_qgate(L["r"], L["dvec"], L["w_next"], eps=L["eps"], logits=self.logits)
+        if not L["estimator"] and fused and self.d in QGATE_D and self.E <= 256:
+            route_qgate_topk(L["r"], L["dvec"], L["w_next"], self.K, eps=L["eps"], idx=self.pred,
+                             logits=self.logits if keep_logits else None)
         else:
             route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
             if L["estimator"]:
@@ -261,7 +264,7 @@ class PredictorPass:
                                 ws=self.ws)
             else:
                 route_gate(self.q, L["w_next"], logits=self.logits)
-        route_topk(self.logits, self.K, 1, 1, idx=self.pred, want_weights=False)
+            route_topk(self.logits, self.K, 1, 1, idx=self.pred, want_weights=False)
         hit_count(self.pred, self.truth, self.hits)
 
 
