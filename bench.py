@@ -253,7 +253,7 @@ def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     return st
 
 
-def fit_estimator(cfg, l, lay, n_train, ridge):
+def fit_estimator(cfg, l, lay, n_train, ridge, time_oracle=False):
     """Fits layer l's estimator output weights on a held-out batch of the same
     model ("Speculating Experts", item 2.C; ridge regression on the
     estimator's own features) and stores them in ``lay``. Returns timings and
@@ -290,8 +290,22 @@ def fit_estimator(cfg, l, lay, n_train, ridge):
     lay["w2"] = w2.view(torch.int16).cpu().numpy().view(np.uint16)
     lay["b2"] = b2.cpu().numpy()
     t = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-    return {"train_tokens": n_train, "ridge": ridge, "hidden_ms": t[0], "gram_ms": t[1],
+    info = {"train_tokens": n_train, "ridge": ridge, "hidden_ms": t[0], "gram_ms": t[1],
             "solve_ms": t[2], "weights_ms": t[3]}
+    if time_oracle:
+        # the oracle's float64 fit (Gram, LAPACK solve, rounding) on the same features
+        from threadpoolctl import threadpool_info
+        from oracle import estfit as oest
+        h_np = h.view(torch.int16).cpu().numpy().view(np.uint16)
+        y_np = y.cpu().numpy()
+        t0 = time.perf_counter()
+        ow2, _, _ = oest.est_fit(h_np, y_np, ridge)
+        threads = max([p_.get("num_threads", 1) for p_ in threadpool_info()] or [1])
+        info["cpu_baseline"] = {"value": (time.perf_counter() - t0) * 1e3, "unit": "ms per fit",
+                                "cores": int(threads), "kind": "oracle",
+                                "sample": "the same layer's fit, once (float64 NumPy and LAPACK)",
+                                "bf16_codes_equal": float((ow2 == lay["w2"]).mean())}
+    return info
 
 
 def predictor_setup(cfg, args):
@@ -309,7 +323,8 @@ def predictor_setup(cfg, args):
     for l in range(cfg.L - 1):
         lay = make_predictor_layer(cfg, l)
         if args.fit and lay["estimator"]:
-            fit_info[l] = fit_estimator(cfg, l, lay, args.fit_tokens, args.fit_ridge)
+            fit_info[l] = fit_estimator(cfg, l, lay, args.fit_tokens, args.fit_ridge,
+                                        time_oracle=not args.no_cpu_baseline and not fit_info)
         p.load(lay)
         p.truth = torch.empty((N, cfg.K), dtype=torch.int32, device="cuda")
         p.truth_step()
@@ -318,6 +333,50 @@ def predictor_setup(cfg, args):
         est.append(bool(lay["estimator"]))
     torch.cuda.synchronize()
     return p, layers, truths, est, fit_info
+
+
+def predictor_cpu_baseline(cfg, n_sample, min_seconds=10.0):
+    """The oracle's prediction step (q_l, the next gate or the estimator,
+    top-K, hits against the precomputed truth) on n_sample tokens of one gate
+    layer and one estimator layer, weighted to the sweep's mix of layers."""
+    from threadpoolctl import threadpool_info
+    from synth.gen import make_predictor_layer
+    import oracle
+
+    def one(layer, truth):
+        q = oracle.route_qhidden(layer["r"], layer["dvec"], eps=layer["eps"])
+        qb = oracle.round_bf16(q)
+        if layer["estimator"]:
+            lg = oracle.route_estimator(qb, layer["w1"], layer["b1"], layer["w2"], layer["b2"])
+        else:
+            lg = oracle.route_gate(qb, layer["w_next"])
+        pred, _ = oracle.route_topk(lg, cfg.K, 1, 1)
+        return oracle.hit_count(pred, truth)
+
+    est_l, gate_l = cfg.est_layers[0], cfg.L - 2
+    lays = {l: make_predictor_layer(cfg, l, N=n_sample) for l in (est_l, gate_l)}
+    truths = {l: oracle.route_topk(oracle.route_gate(lay["s_next"], lay["w_next"]), cfg.K, 1, 1)[0]
+              for l, lay in lays.items()}
+    spent = {est_l: [0.0, 0], gate_l: [0.0, 0]}
+    t_all = 0.0
+    while t_all < min_seconds:
+        for l in (est_l, gate_l):
+            t0 = time.perf_counter()
+            one(lays[l], truths[l])
+            dt = time.perf_counter() - t0
+            spent[l][0] += dt
+            spent[l][1] += 1
+            t_all += dt
+    nl = cfg.L - 1
+    ne = len(cfg.est_layers)
+    per_layer = {l: spent[l][0] / spent[l][1] for l in spent}
+    per_token = (ne * per_layer[est_l] + (nl - ne) * per_layer[gate_l]) / nl / n_sample
+    threads = max([p_.get("num_threads", 1) for p_ in threadpool_info()] or [1])
+    return {"value": 1.0 / per_token, "unit": "token-predictions/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_sample} tokens of layer {gate_l} (gate) and layer {est_l} (estimator), "
+                      f"{spent[gate_l][1]} + {spent[est_l][1]} passes, weighted {nl - ne}:{ne}; "
+                      f"{t_all:.1f} s (float64 NumPy, BLAS on {threads} threads)"}
 
 
 def predictor_bench(args):
@@ -480,6 +539,8 @@ def predictor_bench(args):
         "hit_rate_per_estimator_layer": [round(r, 4) for r, e_ in zip(rates, est) if e_],
         "wall_s_timed": wall,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = predictor_cpu_baseline(cfg, min(args.cpu_sample, 1024))
     print(json.dumps(out), flush=True)
     return 0
 
