@@ -223,9 +223,14 @@ constexpr bool kLdsSwizzle = true;
 constexpr int kLdsRowBytes = 160;  // row stride when not swizzled: 128 data bytes + 32 pad
 
 // LDS byte offset of 16-byte piece `piece` (0..7) of slab row rbase + r16,
-// where rbase is a multiple of 16.
+// where rbase is a multiple of 16. gfx950's LDS serves a 16-byte read for 16
+// lanes at a time from a 256-byte window of banks, i.e. two 128-byte rows:
+// the piece is XOR-ed with (r16 / 2) % 8, so the 16 rows of a fragment read
+// (one piece each) fall on 16 distinct 16-byte bank groups. Swizzling by
+// r16 % 8 instead leaves rows r and r + 8 on the same banks (measured: half
+// of all LDS cycles were bank conflicts).
 __device__ __forceinline__ int lds_off(int rbase, int r16, int piece) {
-  if (kLdsSwizzle) return (rbase + r16) * 128 + ((piece ^ (r16 & 7)) << 4);
+  if (kLdsSwizzle) return (rbase + r16) * 128 + ((piece ^ ((r16 >> 1) & 7)) << 4);
   return (rbase + r16) * kLdsRowBytes + (piece << 4);
 }
 constexpr int kLdsRow = kLdsSwizzle ? 128 : kLdsRowBytes;

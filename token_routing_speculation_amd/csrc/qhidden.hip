@@ -148,13 +148,20 @@ __global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
 constexpr int kQgThreads = 512;
 constexpr int kQgLead = 7;  // W line loads in flight, in pairs of K steps
 
-// LDS offset of 16-byte piece p of tile row rr: pieces XOR-swizzled by the
-// row's low three bits (within aligned groups of eight), so the sixteen rows
-// of an MFMA fragment read spread over the banks.
+// LDS offset of 16-byte piece p of tile row rr. Rows are a multiple of 256
+// bytes long, so every row starts at the same bank; gfx950's LDS serves a
+// 16-byte read for 16 lanes at a time from a 256-byte window of banks, and
+// the piece is XOR-ed with the row's low four bits (within aligned groups of
+// sixteen pieces) so the sixteen rows of an MFMA fragment read fall on
+// sixteen distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int qg_off(int rr, int p) {
-  return rr * D * 2 + ((p ^ (rr & 7)) << 4);
+  return rr * D * 2 + ((p ^ (rr & 15)) << 4);
 }
+
+// The per-wave W staging rows are 128 bytes: two rows share a 256-byte bank
+// window, so the piece is XOR-ed with (row / 2) % 8.
+__device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ ((rr >> 1) & 7)) << 4); }
 
 // TOPK: also pick each row's top K columns (E <= 256, K <= 16), in
 // route_topk's order (largest logit first, equal logits to the lower column,
@@ -233,12 +240,11 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int rr = lrow + 8 * h;
-          *reinterpret_cast<u32x4*>(wst + rr * 128 + ((lchunk ^ (rr & 7)) << 4)) = ring[j][h];
+          *reinterpret_cast<u32x4*>(wst + wst_off(rr, lchunk)) = ring[j][h];
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const u32x4 bf = *reinterpret_cast<const u32x4*>(
-              wst + r16 * 128 + (((kq + 4 * half) ^ (r16 & 7)) << 4));
+          const u32x4 bf = *reinterpret_cast<const u32x4*>(wst + wst_off(r16, kq + 4 * half));
           const int st = 2 * pp + half;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
