@@ -114,7 +114,10 @@ def test_srs_flags_bad_cluster_and_stays_in_bounds():
 # ------------------------------------------------------------------- gate
 GATE_CASES = [(1, 8, 1), (17, 64, 4), (100, 136, 8), (1000, 520, 17), (4133, 2048, 64),
               (2000, 2048, 128), (1111, 5120, 160), (300, 1024, 200), (64, 256, 1024),
-              (4096, 4096, 8), (257, 72, 160)]
+              (4096, 4096, 8), (257, 72, 160),
+              # the matrix-core kernel: its shortest K (two steps), one row, a
+              # 33-column tile, and its 128 x 128 tiles with ragged rows and columns
+              (77, 128, 96), (1, 384, 40), (513, 256, 33), (8200, 1024, 520)]
 
 
 @pytest.mark.parametrize("n,d,E", GATE_CASES)

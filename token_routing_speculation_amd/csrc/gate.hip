@@ -21,6 +21,11 @@
 // Used by the "Federation of Experts (FoE)" article's router scores g[i]
 // and by "Speculating Experts Accelerates Inference for Mixture-of-Experts"
 // (item 2.A: next gate on q_l; item 2.C: the estimator MLP).
+//
+// gemm_launch picks the kernel per shape: the split-K register kernel for
+// E <= 32, the matrix-core kernel of mma.hip where it applies (K % 128 == 0
+// and 32 < E <= 128 or E > 160), and the staged kernel otherwise (among
+// them E = 160, whose one-pass 64 x 160 tiles read A exactly once).
 #include "common.hpp"
 #include "gemm.hpp"
 #include "mfma.hpp"
@@ -30,11 +35,6 @@ namespace route {
 
 constexpr int kGemmThreads = 256;
 constexpr int kPfa = 3;  // A-operand prefetch depth, in K steps
-enum { EPI_F32 = 0, EPI_BIAS_GELU_BF16 = 1, EPI_BIAS_F32 = 2 };
-
-__device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
-}
 
 template <int MT, int NT>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt(const uint16_t* __restrict__ A,
@@ -169,13 +169,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt(const uint16_t* __res
       for (int r = 0; r < 3; ++r) v += red[(i * 3 + r) * kWave + lane];
       const int col = col0 + 16 * t + r16;
       if (col >= N) continue;
-      const float bcol = epi != EPI_F32 ? bias[col] : 0.f;
+      const float bcol = epi != kEpiF32 ? bias[col] : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t row = row0 + 16 * m + 4 * (lane >> 4) + j;
         if (row >= M) continue;
         const int64_t o = row * N + col;
-        if (epi == EPI_BIAS_GELU_BF16) {
+        if (epi == kEpiBiasGeluBf16) {
           static_cast<uint16_t*>(C)[o] =
               static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(v[j] + bcol)));
         } else {
@@ -474,14 +474,14 @@ __global__ __launch_bounds__(kGemmThreads * KG, 1) void gemm_lds(
     for (int t = 0; t < NTW; ++t) {
       const int col = col0 + wc * 16 * NTW + 16 * t + (lane & 15);
       if (col >= N) continue;
-      const float bcol = epi != EPI_F32 ? bias[col] : 0.f;
+      const float bcol = epi != kEpiF32 ? bias[col] : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t row = row0 + wr * 16 * MTW + 16 * m + 4 * (lane >> 4) + j;
         if (row >= M) continue;
         const int64_t o = row * N + col;
         const float v = acc[m][t][j] + bcol;
-        if (epi == EPI_BIAS_GELU_BF16)
+        if (epi == kEpiBiasGeluBf16)
           static_cast<uint16_t*>(C)[o] = static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(v)));
         else
           static_cast<float*>(C)[o] = v;
@@ -501,6 +501,9 @@ static void launch_lds(int kg, dim3 grid, hipStream_t s, const uint16_t* A, int6
 static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N,
                        const float* bias, void* C, int epi, hipStream_t s) {
   if (M == 0) return ROUTE_OK;
+  // K a multiple of 128 and 32 < N <= 128 or N > 160: the matrix-core kernel
+  // of mma.hip (on MI355X 1.3-2.1x faster than the kernels below there)
+  if (mma_fits(M, Kd, N)) return mma_launch(A, M, Kd, B, N, bias, C, epi, s);
   const int ntiles = (N + 15) / 16;
   if (N > 32) {
     if (Kd > (1 << 22)) return ROUTE_ERR_UNSUPPORTED;  // tile byte offsets are 32-bit
@@ -544,7 +547,7 @@ static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, 
 
 int gemm_f32(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, float* C,
              hipStream_t s) {
-  return gemm_launch(A, M, Kd, B, N, nullptr, C, EPI_F32, s);
+  return gemm_launch(A, M, Kd, B, N, nullptr, C, kEpiF32, s);
 }
 
 }  // namespace route
@@ -558,7 +561,7 @@ ROUTE_API int route_gate(const uint16_t* x, int64_t n, int32_t d, const uint16_t
   if (n == 0) return ROUTE_OK;
   if (!x || !w || !logits) return ROUTE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w)) return ROUTE_ERR_ALIGN;
-  return gemm_launch(x, n, d, w, E, nullptr, logits, EPI_F32, s);
+  return gemm_launch(x, n, d, w, E, nullptr, logits, kEpiF32, s);
 }
 
 ROUTE_API int route_est_hidden(const uint16_t* q, int64_t n, int32_t d, const uint16_t* w1,
@@ -568,7 +571,7 @@ ROUTE_API int route_est_hidden(const uint16_t* q, int64_t n, int32_t d, const ui
   if (n == 0) return ROUTE_OK;
   if (!q || !w1 || !b1 || !h) return ROUTE_ERR_NULL;
   if (!aligned16(q) || !aligned16(w1) || !aligned16(h)) return ROUTE_ERR_ALIGN;
-  return gemm_launch(q, n, d, w1, hd, b1, h, EPI_BIAS_GELU_BF16, s);
+  return gemm_launch(q, n, d, w1, hd, b1, h, kEpiBiasGeluBf16, s);
 }
 
 ROUTE_API size_t route_estimator_workspace_size(int64_t n, int32_t hd) {
@@ -588,7 +591,7 @@ ROUTE_API int route_estimator(const uint16_t* q, int64_t n, int32_t d, const uin
   if (!ws || ws_bytes < route_estimator_workspace_size(n, hd)) return ROUTE_ERR_WORKSPACE;
   if (!aligned16(ws)) return ROUTE_ERR_ALIGN;
   uint16_t* h = static_cast<uint16_t*>(ws);
-  int st = gemm_launch(q, n, d, w1, hd, b1, h, EPI_BIAS_GELU_BF16, s);
+  int st = gemm_launch(q, n, d, w1, hd, b1, h, kEpiBiasGeluBf16, s);
   if (st != ROUTE_OK) return st;
-  return gemm_launch(h, n, hd, w2, E, b2, logits, EPI_BIAS_F32, s);
+  return gemm_launch(h, n, hd, w2, E, b2, logits, kEpiBiasF32, s);
 }

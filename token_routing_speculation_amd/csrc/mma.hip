@@ -1,0 +1,246 @@
+// Matrix-core product C = A . B^T (A [M][K], B [N][K], both K-contiguous bf16,
+// binary32 accumulation) for the shapes where the matrix cores and the
+// L2 -> CU operand stream, not HBM, set the pace: the estimator MLP of
+// "Speculating Experts Accelerates Inference for Mixture-of-Experts"
+// (item 2.C: 2048 -> 512 -> 128 for every token) and the router products
+// with E <= 128 columns (the "Federation of Experts (FoE)" article's router
+// scores g[i]; the next gate on q_l, item 2.A).
+//
+// gfx950 design (measured on MI355X, see the notes at each choice):
+//  - v_mfma_f32_32x32x16_bf16. With one wave per SIMD the 16x16x32 form
+//    reached 0.78 PFLOP/s and the 32x32x16 form 1.77 PFLOP/s (8 and 4
+//    independent accumulators per wave).
+//  - Operands go from global memory straight into LDS
+//    (global_load_lds_dwordx4: 64 lanes x 16 bytes land as 1 KB at the
+//    wave's LDS base), four stages deep, one barrier per 64-wide K step.
+//    No register ring, no LDS store instructions.
+//  - A workgroup of four waves owns BM x BN (2 x 2 waves); 128 x 128 when
+//    that still gives a workgroup per CU, 64 x 64 otherwise.
+//  - Slab rows are 128 bytes, 16-byte pieces XOR-swizzled by (row / 2) % 8:
+//    gfx950's LDS serves a 16-byte read for 16 lanes at a time from a
+//    256-byte window of banks, so the 32 rows of a fragment read are
+//    conflict-free (bank-conflict counter: zero).
+//  - All fragments of step s + 1 are read right after its barrier, before the
+//    MFMAs of step s are issued, so no MFMA waits on an LDS read; the loads of
+//    step s + 4 are interleaved with those MFMAs (two MFMAs, one load), which
+//    keeps a wave from stalling behind a full address queue.
+#include "common.hpp"
+#include "gemm.hpp"
+#include "mfma.hpp"
+
+namespace route {
+
+namespace {
+
+constexpr int kMmaThreads = 256;  // four waves, 2 x 2 over the tile
+constexpr int kMmaStages = 4;     // LDS stages (K steps of 64) in the ring
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D = A . B + C for a 32 x 16 A fragment and a 16 x 32 B fragment: lane l
+// holds row (A) or column (B) l % 32 and eight consecutive k, the halves
+// l / 32 = 0, 1 taking the two 8-wide k halves (any consistent assignment of
+// k to lanes gives the same product); the result holds column l % 32, rows
+// 8 (e / 4) + 4 (l / 32) + e % 4 for e = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One 16-byte piece per lane from global memory into LDS: lane i writes at
+// lds_base + 16 i (lds_base is wave-uniform). Completion is counted by vmcnt.
+__device__ __forceinline__ void lds_load16(const void* g, char* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+#endif
+}
+
+// Waits until at most N of this wave's vector-memory operations are pending
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until this wave's LDS reads have completed.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Byte offset of logical 16-byte piece p (0..7) of 128-byte slab row r.
+__device__ __forceinline__ int slab_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kMmaThreads, 1) void mma_nt_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int Kd, const uint16_t* __restrict__ B, int N,
+    const float* __restrict__ bias, void* __restrict__ C, int epi) {
+  constexpr int MT = BM / 64, NT = BN / 64;       // 32 x 32 tiles per wave
+  constexpr int STAGE = (BM + BN) * 128;          // one K step: BM + BN rows of 64 bf16
+  constexpr int NI = (BM + BN) / 8 / 4;           // 1 KB loads per wave and step
+  constexpr int NMF = 4 * MT * NT;                // MFMAs per wave and step
+  constexpr int PER = NMF / NI > 0 ? NMF / NI : 1;
+  static_assert(kMmaStages >= 3 && NI >= 1, "stage ring");
+  __shared__ __attribute__((aligned(1024))) char lds[kMmaStages * STAGE];
+  const int w = wave_id(), lane = lane_id();
+  const int wr = w & 1, wc = w >> 1;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int col0 = blockIdx.y * BN;
+  const int nsteps = Kd / 64;  // even, >= 2
+
+  // Load j of a stage (j = w + 4 i) fills slab rows 8 j .. 8 j + 7 (A rows
+  // first, then B rows): lane l fetches the piece that the swizzle stores at
+  // physical piece l % 8 of row 8 j + l / 8. Rows past M and columns past N
+  // re-read the last valid one (their results are never stored).
+  const char* src[NI];
+  int dst[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int j = w + 4 * i;
+    const int r = 8 * j + lane / 8;
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    if (r < BM) {
+      const int64_t gr = row0 + r < M ? row0 + r : M - 1;
+      src[i] = reinterpret_cast<const char*>(A + gr * Kd) + 16 * p;
+    } else {
+      const int gc = col0 + (r - BM) < N ? col0 + (r - BM) : N - 1;
+      src[i] = reinterpret_cast<const char*>(B + static_cast<int64_t>(gc) * Kd) + 16 * p;
+    }
+    dst[i] = 8 * j * 128;
+  }
+  // a step past the end re-loads the last step into its own buffer (the same
+  // bytes), which keeps every wave's count of pending loads uniform
+  auto load_one = [&](int i, int st) {
+    st = st < nsteps ? st : nsteps - 1;
+    lds_load16(src[i] + st * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
+  };
+  auto load_step = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_one(i, st);
+  };
+
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[m][t][e] = 0.f;
+
+  // fragments of one step: chunk c (16 k) is pieces 2c, 2c + 1 of each row
+  u32x4 fa[2][4][MT], fb[2][4][NT];
+  auto read_frags = [&](int set, int st) {
+    const char* base = lds + (st % kMmaStages) * STAGE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        fa[set][c][m] = *reinterpret_cast<const u32x4*>(
+            base + slab_off(wr * 32 * MT + 32 * m + (lane & 31), 2 * c + (lane >> 5)));
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        fb[set][c][t] = *reinterpret_cast<const u32x4*>(
+            base + BM * 128 + slab_off(wc * 32 * NT + 32 * t + (lane & 31), 2 * c + (lane >> 5)));
+    }
+  };
+  // the MFMAs of the step held in `set`, with the loads of step st_load
+  // (none if negative) spread between them
+  auto mfma_step = [&](int set, int st_load) {
+    int q = 0, i = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[m][t] = mfma32x32x16(fa[set][c][m], fb[set][c][t], acc[m][t]);
+          if (++q % PER == 0 && i < NI) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (st_load >= 0) load_one(i, st_load);
+            ++i;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+    for (; i < NI; ++i)
+      if (st_load >= 0) load_one(i, st_load);
+  };
+  // step st's data is in LDS for every wave, and every wave has finished
+  // reading step st - 1 (so its buffer may be refilled)
+  auto sync_step = [&]() {
+    wait_lgkm0();
+    wait_vmcnt<(kMmaStages - 2) * NI>();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+#pragma unroll
+  for (int s = 0; s < kMmaStages - 1; ++s) load_step(s);
+  sync_step();
+  load_step(kMmaStages - 1);
+  read_frags(0, 0);
+  for (int st = 0; st < nsteps - 2; st += 2) {
+    sync_step();
+    read_frags(1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0, st + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+    sync_step();
+    read_frags(0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(1, st + 1 + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sync_step();
+  read_frags(1, nsteps - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(0, -1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(1, -1);
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = col0 + wc * 32 * NT + 32 * t + (lane & 31);
+      if (col >= N) continue;
+      const float bcol = epi != kEpiF32 ? bias[col] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = row0 + wr * 32 * MT + 32 * m + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row >= M) continue;
+        const int64_t o = row * N + col;
+        const float v = acc[m][t][e] + bcol;
+        if (epi == kEpiBiasGeluBf16)
+          static_cast<uint16_t*>(C)[o] = static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(v)));
+        else
+          static_cast<float*>(C)[o] = v;
+      }
+    }
+}
+
+}  // namespace
+
+bool mma_fits(int64_t M, int Kd, int N) {
+  return M > 0 && N > 32 && Kd >= 128 && Kd % 128 == 0 && (N <= 128 || N > 160);
+}
+
+int mma_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, const float* bias,
+               void* C, int epi, hipStream_t s) {
+  if (!mma_fits(M, Kd, N)) return ROUTE_ERR_UNSUPPORTED;
+  const int64_t big = static_cast<int64_t>(ceil_div(M, 128)) * ceil_div(N, 128);
+  if (N >= 128 && big >= 256) {
+    dim3 grid(ceil_div(M, 128), ceil_div(N, 128));
+    mma_nt_kernel<128, 128><<<grid, kMmaThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+  } else {
+    dim3 grid(ceil_div(M, 64), ceil_div(N, 64));
+    mma_nt_kernel<64, 64><<<grid, kMmaThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+  }
+  return launch_status();
+}
+
+}  // namespace route
