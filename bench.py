@@ -239,12 +239,12 @@ def eg_bench(args):
 def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     """Algorithmic HBM bytes of one source layer's prediction (q_l -> logits ->
     top-K -> hits), each call reading its inputs and writing its outputs once.
-    fused: the next gate and its top-K as route_qgate_topk (r, d_l and W read,
-    the picks written; q and the logits never leave the chip)."""
+    fused: the next gate, its top-K and the hit count as one route_qgate_topk
+    (r, d_l, W and the true picks read, the picks written, the counter updated;
+    q and the logits never leave the chip)."""
     b = 2
     if fused and not estimator:
-        return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K,
-                "hits": 8 * N * K + 8}
+        return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K + 4 * N * K + 16}
     st = {"qhidden": 2 * N * d * b + 4 * d,
           "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
           if estimator else (N * d * b + E * d * b + 4 * N * E),
@@ -449,17 +449,16 @@ def predictor_bench(args):
         return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
 
     def fused_stage_times(i):
-        from token_routing_speculation_amd import route_qgate_topk, hit_count
+        from token_routing_speculation_amd import route_qgate_topk
         p.layer, p.truth = layers[i], truths[i]
         L_ = p.layer
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        tt = {"qgate_topk": [], "hits": []}
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        tt = {"qgate_topk_hits": []}
         for _ in range(10):
             e[0].record(stream)
-            route_qgate_topk(L_["r"], L_["dvec"], L_["w_next"], p.K, eps=L_["eps"], idx=p.pred)
+            route_qgate_topk(L_["r"], L_["dvec"], L_["w_next"], p.K, eps=L_["eps"], idx=p.pred,
+                             truth=p.truth, hits=p.hits)
             e[1].record(stream)
-            hit_count(p.pred, p.truth, p.hits)
-            e[2].record(stream)
             torch.cuda.synchronize()
             for j, k_ in enumerate(tt):
                 tt[k_].append(1e3 * e[j].elapsed_time(e[j + 1]))
@@ -481,7 +480,8 @@ def predictor_bench(args):
     from token_routing_speculation_amd import route_qgate_topk
     Lg = layers[cfg.L - 2]
     qg_launch_us = back_to_back_us(
-        lambda: route_qgate_topk(Lg["r"], Lg["dvec"], Lg["w_next"], p.K, eps=Lg["eps"], idx=p.pred))
+        lambda: route_qgate_topk(Lg["r"], Lg["dvec"], Lg["w_next"], p.K, eps=Lg["eps"], idx=p.pred,
+                                 truth=p.truth, hits=p.hits))
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
     rates = []
@@ -517,7 +517,7 @@ def predictor_bench(args):
                    "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
         "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_sweep": total_bytes,
-        "gate_layers": "route_qgate_topk (q_l and the logits kept on chip)",
+        "gate_layers": "route_qgate_topk with the hit count (q_l and the logits kept on chip)",
         "unfused": {"ms_per_step": ms_unfused, "value": N * nl / (ms_unfused * 1e-3),
                     "alg_bytes_sweep": total_unfused,
                     "hbm_frac_sweep": total_unfused / (ms_unfused * 1e-3) / HBM_PEAK,

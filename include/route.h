@@ -257,12 +257,17 @@ int route_qgate(const uint16_t* r, const float* dvec, const float* gamma, const 
  * with H = 1; no weights). [SPEC] item 2.A (predicted top-K of layer l+1
  * from q_l). logits float[n][E] is written too when not NULL; idx equals
  * route_topk applied to those logits.
- * Errors: as route_qgate, plus SHAPE (K < 1, K > E) and UNSUPPORTED (E > 256,
- * K > 16).
+ *   truth int32[n][K] and hits (device uint64, accumulated): when both are
+ *   given, the kernel also adds to *hits what hit_count(idx, truth) would
+ *   add ([SPEC] item 4), so the predicted picks need not be read back; both
+ *   NULL skips the count.
+ * Errors: as route_qgate, plus SHAPE (K < 1, K > E), UNSUPPORTED (E > 256,
+ * K > 16) and NULL (only one of truth, hits given).
  */
 int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma, const float* beta,
                      int64_t n, int32_t d, float eps, const uint16_t* w, int32_t E, int32_t K,
-                     float* logits, int32_t* idx, hipStream_t s);
+                     float* logits, int32_t* idx, const int32_t* truth, unsigned long long* hits,
+                     hipStream_t s);
 
 /*
  * route_estimator - lightweight neural estimator of next-layer logits.

@@ -252,11 +252,13 @@ def test_qgate_errors(L):
 
 def test_qgate_topk_errors(L):
     f = L.route_qgate_topk
-    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 0, None, A, None) == SHAPE
-    assert f(A, A, None, None, 10, 2048, 1e-5, A, 4, 5, None, A, None) == SHAPE     # K > E
-    assert f(A, A, None, None, 10, 2048, 1e-5, A, 257, 8, None, A, None) == UNSUP
-    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 17, None, A, None) == UNSUP
-    assert f(A, A, None, None, 10, 512, 1e-5, A, 128, 8, None, A, None) == UNSUP
-    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, None, None) == NULL
-    assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, 8, None, A, None) == OK
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 0, None, A, None, None, None) == SHAPE
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 4, 5, None, A, None, None, None) == SHAPE     # K > E
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 257, 8, None, A, None, None, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 17, None, A, None, None, None) == UNSUP
+    assert f(A, A, None, None, 10, 512, 1e-5, A, 128, 8, None, A, None, None, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, None, None, None, None) == NULL
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, A, A, None, None) == NULL  # truth without hits
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, A, None, A, None) == NULL  # hits without truth
+    assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, 8, None, A, None, None, None) == OK
 

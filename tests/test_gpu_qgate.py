@@ -106,3 +106,36 @@ def test_qgate_topk_ties_and_signed_zeros():
     want, _ = tr.route_topk(lg, K, 1, 1)
     assert np.array_equal(host(idx), host(want))
 
+
+
+@pytest.mark.parametrize("n,d,E,K", [(1, 2048, 128, 8), (8192, 2048, 128, 8), (37, 1024, 8, 2),
+                                     (1000, 4096, 160, 6), (77, 2048, 256, 16), (100, 2048, 1, 1),
+                                     (45, 4096, 64, 3)])
+def test_qgate_topk_counts_hits_like_hit_count(n, d, E, K):
+    """The fused hit count adds exactly the oracle's |picks & truth| summed
+    over rows (integer, bit-exact), computed on the picks the kernel wrote;
+    truth rows hold repeats and ids outside 0..E-1 (a repeat counts once, a
+    foreign id never), and the counter accumulates."""
+    r, dv, _, _, w = _case(n, d, E, False, 3 * n + d + E + K)
+    rng = np.random.default_rng(n + K)
+    truth = rng.integers(0, E, (n, K)).astype(np.int32)        # repeats allowed
+    truth[::7, 0] = E + 3                                       # never a pick
+    truth[::5, -1] = -1
+    hits = torch.full((1,), 1000, dtype=torch.int64, device="cuda")
+    idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, truth=dev(truth), hits=hits)
+    picks = host(idx)
+    assert int(host(hits)[0]) == 1000 + oracle.hit_count(picks, truth)
+    # the picks are those of the call without the count, and hit_count agrees
+    assert np.array_equal(host(tr.route_qgate_topk(dev(r), dev(dv), dev(w), K)), picks)
+    h2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tr.hit_count(idx, dev(truth), h2)
+    assert int(host(h2)[0]) == oracle.hit_count(picks, truth)
+
+
+def test_qgate_topk_hits_when_truth_is_the_prediction():
+    n, d, E, K = 300, 2048, 128, 8
+    r, dv, _, _, w = _case(n, d, E, False, 11)
+    idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K)
+    hits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, truth=idx.clone(), hits=hits)
+    assert int(host(hits)[0]) == n * K

@@ -57,7 +57,7 @@ EXPORTS = {
     "route_qhidden": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p]),
     "route_qgate": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _p, _p]),
     "route_qgate_topk": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _i32, _p, _p,
-                                        _p]),
+                                        _p, _p, _p]),
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
@@ -303,16 +303,21 @@ def route_qgate(r, dvec, w, gamma=None, beta=None, eps=1e-5, logits=None, stream
 
 
 def route_qgate_topk(r, dvec, w, K, gamma=None, beta=None, eps=1e-5, idx=None, logits=None,
-                     stream=None):
+                     truth=None, hits=None, stream=None):
     """idx [n][K]: the top-K columns of bf16(LN(dvec + r)) . w^T per row (route_topk's
-    order); logits [n][E] written too when given. d in 1024, 2048, 4096; E <= 256."""
+    order); logits [n][E] written too when given. With truth [n][K] and hits (int64 [1],
+    accumulated) the kernel also counts the picks found among the true experts, as
+    hit_count would. d in 1024, 2048, 4096; E <= 256."""
     n, d = r.shape
     E = w.shape[0]
     idx = _empty((n, K), torch.int32, r) if idx is None else idx
+    if (truth is None) != (hits is None):
+        raise ValueError("truth and hits go together")
     _call("route_qgate_topk", _dev(r, _bf16(r), "r"), _dev(dvec, torch.float32, "dvec", d),
           _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
           float(eps), _dev(w, _bf16(w), "w", E * d), E, K,
           _opt(logits, torch.float32, "logits", n * E), _dev(idx, torch.int32, "idx", n * K),
+          _opt(truth, torch.int32, "truth", n * K), _opt(hits, torch.int64, "hits", 1),
           _stream(stream))
     return idx
 

@@ -171,7 +171,8 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
     const uint16_t* __restrict__ w, int E, float* __restrict__ logits, int K,
-    int* __restrict__ idx) {
+    int* __restrict__ idx, const int32_t* __restrict__ truth,
+    unsigned long long* __restrict__ hits) {
   constexpr int CPL = D / 8 / kWave;
   constexpr int NV = D / 8;
   constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
@@ -183,10 +184,18 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   __shared__ __attribute__((aligned(16))) char tile[BM * D * 2];
   __shared__ __attribute__((aligned(16))) char wstage[(kQgThreads / kWave) * 2048];
   const int lane = lane_id(), wv = wave_id();
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  // the top-K epilogue gives row 4 wv + lane / 16 to a 16-lane segment; the
+  // true pick this lane compares against is loaded now, so its latency
+  // overlaps the rest of the kernel
+  int tv = -1;
+  if constexpr (TOPK) {
+    const int rr = 4 * wv + (lane >> 4);
+    if (hits && rr < BM && row0 + rr < n && (lane & 15) < K) tv = truth[(row0 + rr) * K + (lane & 15)];
+  }
   for (int j = threadIdx.x * 4; j < D; j += kQgThreads * 4)
     *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
   __syncthreads();
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   // q rows: wave wv takes tile rows wv, wv + 8, ...; all their loads are
   // issued before the first is normalised. Rows past n repeat row n - 1
   // (their logits are never stored).
@@ -288,6 +297,9 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     }
     __syncthreads();  // every wave is done with the q tile: it now holds the logits
     float* lt = reinterpret_cast<float*>(tile);  // BM x E
+    // this workgroup's hit count, in the W staging area (free from here on)
+    unsigned* hit_lds = reinterpret_cast<unsigned*>(wstage);
+    if (threadIdx.x == 0) *hit_lds = 0u;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int g = wv + NW * gi;
@@ -335,7 +347,25 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
         }
       }
       const int64_t grow = row0 + rr;
-      if (rr < BM && grow < n && sl < K) idx[grow * K + sl] = myc;
+      const bool live = rr < BM && grow < n;
+      if (live && sl < K) idx[grow * K + sl] = myc;
+      if (hits) {
+        // hit count: a pick counts when it is among the row's true experts
+        // (the picks are distinct columns; a repeated true expert counts once)
+        // every lane takes part in each shuffle (a lane left out would hand
+        // the others no value), so no short-circuit here; K is wave-uniform
+        bool in_truth = false;
+        for (int j = 0; j < K; ++j) {
+          const int tj = __shfl(tv, (lane & ~15) + j, kWave);
+          in_truth |= tj == myc;
+        }
+        const unsigned long long ball = __ballot(live && sl < K && in_truth);
+        if (lane == 0) atomicAdd(hit_lds, static_cast<unsigned>(__popcll(ball)));
+      }
+    }
+    if (hits) {
+      __syncthreads();
+      if (threadIdx.x == 0 && *hit_lds) atomicAdd(hits, static_cast<unsigned long long>(*hit_lds));
     }
   }
 }
@@ -379,35 +409,36 @@ ROUTE_API int route_qgate(const uint16_t* r, const float* dvec, const float* gam
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
   if (d == 1024)
     qgate_kernel<32, 1024, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
   else if (d == 2048)
     qgate_kernel<32, 2048, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
   else
     qgate_kernel<16, 4096, false><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr);
+        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
   return launch_status();
 }
 
 ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma,
                                const float* beta, int64_t n, int32_t d, float eps,
                                const uint16_t* w, int32_t E, int32_t K, float* logits,
-                               int32_t* idx, hipStream_t s) {
+                               int32_t* idx, const int32_t* truth, unsigned long long* hits,
+                               hipStream_t s) {
   if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || E < 1 || K < 1 || K > E)
     return ROUTE_ERR_SHAPE;
   if (E > 256 || K > kMaxK || (d != 1024 && d != 2048 && d != 4096)) return ROUTE_ERR_UNSUPPORTED;
   if (n == 0) return ROUTE_OK;
-  if (!r || !dvec || !w || !idx) return ROUTE_ERR_NULL;
+  if (!r || !dvec || !w || !idx || (!truth != !hits)) return ROUTE_ERR_NULL;
   if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
   if (d == 1024)
     qgate_kernel<32, 1024, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
   else if (d == 2048)
     qgate_kernel<32, 2048, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
   else
     qgate_kernel<16, 4096, true><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx);
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
   return launch_status();
 }

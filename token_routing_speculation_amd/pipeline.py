@@ -252,11 +252,14 @@ class PredictorPass:
         in one kernel (route_qgate_topk, q and the logits kept on chip; the
         logits are written only if ``keep_logits``) when ``fused`` and the
         shape allows, else route_qhidden + route_gate + route_topk; on
-        estimator layers q_l, the estimator and top-K. Then the hit count."""
+        estimator layers q_l, the estimator and top-K. Then the hit count (inside
+        the fused kernel on gate layers)."""
         L = self.layer
         if not L["estimator"] and fused and self.d in QGATE_D and self.E <= 256:
             route_qgate_topk(L["r"], L["dvec"], L["w_next"], self.K, eps=L["eps"], idx=self.pred,
-                             logits=self.logits if keep_logits else None)
+                             logits=self.logits if keep_logits else None, truth=self.truth,
+                             hits=self.hits)
+            return
         else:
             route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
             if L["estimator"]:
