@@ -62,6 +62,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_combine_deepseek.json")
 TRAFFIC_SOURCES = ("token_routing_speculation_amd/csrc/combine.hip",
                    "token_routing_speculation_amd/csrc/common.hpp")
+QGATE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qgate_qwen3.json")
+QGATE_TRAFFIC_SOURCES = ("token_routing_speculation_amd/csrc/qhidden.hip",
+                         "token_routing_speculation_amd/csrc/common.hpp",
+                         "token_routing_speculation_amd/csrc/mfma.hpp",
+                         "token_routing_speculation_amd/csrc/topk.hpp")
 
 
 def sources_digest(paths) -> str:
@@ -72,17 +77,17 @@ def sources_digest(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the combine kernel from the committed counter
-    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
-    for a copy of known size), or None when the kernel's sources have changed
-    since they were taken or the workload differs."""
+def measured_traffic(workload: str, path=TRAFFIC_FILE, sources=TRAFFIC_SOURCES):
+    """HBM bytes per launch of a kernel (the combine by default) from the
+    committed counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a copy of known size), or None when the kernel's sources
+    have changed since they were taken or the workload differs."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sha256") != sources_digest(TRAFFIC_SOURCES):
+    if rec.get("workload") != workload or rec.get("sha256") != sources_digest(sources):
         return None
     return (rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
 
@@ -379,6 +384,9 @@ def predictor_cpu_baseline(cfg, n_sample, min_seconds=10.0):
                       f"{t_all:.1f} s (float64 NumPy, BLAS on {threads} threads)"}
 
 
+PREDICTOR_WORKLOAD = "qwen3-30b-a3b-shaped predictor"
+
+
 def predictor_bench(args):
     """The q_l predictor of "Speculating Experts Accelerates Inference for
     Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
@@ -403,6 +411,11 @@ def predictor_bench(args):
 
     stream = torch.cuda.current_stream()
     K = args.steps
+    # a plain copy of known size, untimed: the calibration kernel for the
+    # FETCH_SIZE / WRITE_SIZE counters of a profiled run
+    calib = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    torch.empty_like(calib).copy_(calib)
+    del calib
 
     def timed(fused):
         for _ in range(args.warmup):
@@ -513,7 +526,7 @@ def predictor_bench(args):
         "steps": K, "warmup": args.warmup, "ms_per_step": ms, "launch": "hip graph replay",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3-30b-a3b-shaped predictor", "layers": nl, "N": N, "d": cfg.d,
+        "config": {"workload": PREDICTOR_WORKLOAD, "layers": nl, "N": N, "d": cfg.d,
                    "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
         "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_sweep": total_bytes,
@@ -527,7 +540,9 @@ def predictor_bench(args):
         "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, true> (route_qgate_topk)",
                      "achieved": byt_fused["qgate_topk"] / (qg_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK, "traffic": None},
+                     "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK,
+                     "traffic": measured_traffic(PREDICTOR_WORKLOAD, QGATE_TRAFFIC_FILE,
+                                                 QGATE_TRAFFIC_SOURCES)},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
         "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),
