@@ -58,7 +58,9 @@ def test_predict_flags_out_of_vocabulary():
 # ------------------------------------------------------------------- SRS
 SRS_CASES = [(1, 8, 1, 1), (7, 136, 2, 2), (1000, 512, 2, 8), (3001, 64, 3, 5), (5000, 256, 4, 1),
              (2049, 40, 5, 256), (4096, 4096, 2, 4), (300, 2048, 1, 7),
-             (257, 520, 16, 3), (64, 64, 9, 256)]   # the maximum P (16) and a P past the fast paths
+             (257, 520, 16, 3), (64, 64, 9, 256),   # the maximum P (16) and a P past the fast paths
+             # larger cluster sorts (32 and 33 chunks of 1024 keys)
+             (32768, 16, 2, 8), (32769, 16, 2, 8)]
 
 
 @pytest.mark.parametrize("n,d,P,G", SRS_CASES)
@@ -170,7 +172,9 @@ def test_topk(n, E, K, H, renorm):
 
 # ---------------------------------------------------------- permute / combine
 PERM_CASES = [(1, 4, 2, 1, 8), (500, 4, 2, 1, 136), (1000, 8, 2, 1, 512), (3000, 160, 6, 1, 64),
-              (2000, 64, 8, 4, 128), (1025, 1024, 16, 1, 8), (4096, 16, 4, 2, 40), (77, 3, 3, 1, 16)]
+              (2000, 64, 8, 4, 128), (1025, 1024, 16, 1, 8), (4096, 16, 4, 2, 40), (77, 3, 3, 1, 16),
+              # few experts, many pairs
+              (16384, 8, 2, 1, 16), (20000, 8, 2, 1, 16)]
 
 
 @pytest.mark.parametrize("n,E,K,H,d", PERM_CASES)
