@@ -77,14 +77,26 @@ def test_srs_shuffle(n, d, P, G):
     assert np.array_equal(host(out), want["out"])
 
 
-@pytest.mark.parametrize("n,d,P", [(1, 8, 4), (333, 2048, 4), (64, 128, 2)])
+@pytest.mark.parametrize("n,d,P", [(1, 8, 4), (333, 2048, 4), (64, 128, 2), (300, 136, 3),
+                                   (70, 4096, 4)])
 def test_srs_pure_reduce_without_dest(n, d, P):
+    """One cluster, no sort: the row mover itself writes the offsets {0, n}
+    and the identity maps (buffers start out holding other values)."""
     parts = _bf16((P, n, d), 5 + n)
     want = oracle.srs_shuffle(parts, None, 1)
-    out, offs, ros, sor, rc = tr.srs_shuffle(dev(parts), None, 1)
+    fill = lambda k, dt: torch.full((k,), 7, dtype=dt, device="cuda")
+    out, offs, ros, sor, rc = tr.srs_shuffle(dev(parts), None, 1, offsets=fill(2, torch.int32),
+                                             row_of_src=fill(n, torch.int32),
+                                             src_of_row=fill(n, torch.int32),
+                                             row_cluster=fill(n, torch.uint8))
     assert np.array_equal(host(out), want["out"])
     assert host(offs).tolist() == [0, n]
-    assert np.array_equal(host(sor), np.arange(n)) and np.array_equal(host(rc), np.zeros(n))
+    assert np.array_equal(host(ros), np.arange(n)) and np.array_equal(host(sor), np.arange(n))
+    assert np.array_equal(host(rc), np.zeros(n))
+    # without maps only the offsets are written
+    offs2 = fill(2, torch.int32)
+    tr.srs_shuffle(dev(parts), None, 1, offsets=offs2, maps=False)
+    assert host(offs2).tolist() == [0, n]
 
 
 def test_srs_empty():

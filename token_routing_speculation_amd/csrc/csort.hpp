@@ -280,16 +280,6 @@ __global__ void fill_i32(int* __restrict__ p, int64_t n, int value) {
   if (i < n) p[i] = value;
 }
 
-__global__ void iota_i32(int* __restrict__ p, int64_t n) {
-  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = static_cast<int>(i);
-}
-
-__global__ void fill_u8(uint8_t* __restrict__ p, int64_t n, uint8_t value) {
-  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = value;
-}
-
 inline int bits_for(int B) {
   int nb = 0;
   while ((1 << nb) < B) ++nb;

@@ -14,6 +14,28 @@ namespace route {
 
 constexpr int kMoveThreads = 256;
 
+// Outputs of a shuffle without a sort (one cluster): cluster offsets {0, n}
+// and identity maps, written by the row mover itself instead of by separate
+// fill launches. Each pointer may be null.
+struct SrsIdentity {
+  int* offsets;
+  int* row_of_src;
+  int* src_of_row;
+  uint8_t* row_cluster;
+};
+
+// row i's share of the identity outputs (lane 0 of row i's wave)
+__device__ __forceinline__ void write_identity(const SrsIdentity& id, int64_t i, int64_t n) {
+  if (lane_id() != 0) return;
+  if (id.offsets && i == 0) {
+    id.offsets[0] = 0;
+    id.offsets[1] = static_cast<int>(n);
+  }
+  if (id.row_of_src) id.row_of_src[i] = static_cast<int>(i);
+  if (id.src_of_row) id.src_of_row[i] = static_cast<int>(i);
+  if (id.row_cluster) id.row_cluster[i] = 0;
+}
+
 // One wave per source row: out[dst(i)] = bf16(sum_p partials[p][i]). Every
 // lane first loads all P x CPL of its 16-byte vectors, then sums and stores.
 // Cache policy, measured on MI355X for this pattern: streaming (nontemporal)
@@ -23,9 +45,11 @@ template <int PT, int CPL>
 __global__ __launch_bounds__(kMoveThreads) void srs_move(const uint16_t* __restrict__ partials,
                                                          int64_t n, int d,
                                                          const int* __restrict__ row_of_src,
-                                                         uint16_t* __restrict__ out) {
+                                                         uint16_t* __restrict__ out,
+                                                         SrsIdentity ident) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * (kMoveThreads / kWave) + wave_id();
   if (i >= n) return;
+  write_identity(ident, i, n);
   const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
   if (dst < 0 || dst >= n) return;
   const int lane = lane_id();
@@ -62,9 +86,11 @@ __global__ __launch_bounds__(kMoveThreads) void srs_move(const uint16_t* __restr
 __global__ __launch_bounds__(kMoveThreads) void srs_move_any(const uint16_t* __restrict__ partials,
                                                              int P, int64_t n, int d,
                                                              const int* __restrict__ row_of_src,
-                                                             uint16_t* __restrict__ out) {
+                                                             uint16_t* __restrict__ out,
+                                                             SrsIdentity ident) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * (kMoveThreads / kWave) + wave_id();
   if (i >= n) return;
+  write_identity(ident, i, n);
   const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
   if (dst < 0 || dst >= n) return;
   const int nv = d >> 3;
@@ -92,10 +118,13 @@ static int srs_cpl(int nv) {
 
 template <int PT>
 static bool launch_srs_move(int cpl, unsigned grid, hipStream_t s, const uint16_t* partials,
-                            int64_t n, int d, const int* fwd, uint16_t* out) {
+                            int64_t n, int d, const int* fwd, uint16_t* out,
+                            const SrsIdentity& ident) {
   switch (cpl) {
-#define ROUTE_SRS_CASE(c) \
-  case c: srs_move<PT, c><<<grid, kMoveThreads, 0, s>>>(partials, n, d, fwd, out); return true;
+#define ROUTE_SRS_CASE(c)                                                                   \
+  case c:                                                                                   \
+    srs_move<PT, c><<<grid, kMoveThreads, 0, s>>>(partials, n, d, fwd, out, ident);         \
+    return true;
     ROUTE_SRS_CASE(1) ROUTE_SRS_CASE(2) ROUTE_SRS_CASE(4) ROUTE_SRS_CASE(8) ROUTE_SRS_CASE(10)
 #undef ROUTE_SRS_CASE
     default: return false;
@@ -148,21 +177,16 @@ ROUTE_API int srs_shuffle(const uint16_t* partials, int32_t P, int64_t n, int32_
                                    w, err, ROUTE_EBIT_DEST_RANGE, s);
     if (st != ROUTE_OK) return st;
     fwd = fwd_buf;
-  } else {
-    // single cluster, no shuffle: identity maps
-    int* offs = cluster_offsets;
-    fill_i32<<<1, 64, 0, s>>>(offs, 1, 0);
-    fill_i32<<<1, 64, 0, s>>>(offs + 1, 1, static_cast<int>(n));
-    if (row_of_src) iota_i32<<<ceil_div(n, 256), 256, 0, s>>>(row_of_src, n);
-    if (src_of_row) iota_i32<<<ceil_div(n, 256), 256, 0, s>>>(src_of_row, n);
-    if (row_cluster) fill_u8<<<ceil_div(n, 256), 256, 0, s>>>(row_cluster, n, 0);
   }
+  // single cluster, no shuffle: the mover writes offsets {0, n} and identity maps
+  const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
+                                 : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
   const unsigned grid = ceil_div(n, kMoveThreads / kWave);
   const int cpl = srs_cpl(d / 8);
   bool done = false;
-  if (P == 1) done = launch_srs_move<1>(cpl, grid, s, partials, n, d, fwd, out);
-  if (P == 2) done = launch_srs_move<2>(cpl, grid, s, partials, n, d, fwd, out);
-  if (P == 4 && cpl <= 4) done = launch_srs_move<4>(cpl, grid, s, partials, n, d, fwd, out);
-  if (!done) srs_move_any<<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out);
+  if (P == 1) done = launch_srs_move<1>(cpl, grid, s, partials, n, d, fwd, out, ident);
+  if (P == 2) done = launch_srs_move<2>(cpl, grid, s, partials, n, d, fwd, out, ident);
+  if (P == 4 && cpl <= 4) done = launch_srs_move<4>(cpl, grid, s, partials, n, d, fwd, out, ident);
+  if (!done) srs_move_any<<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out, ident);
   return launch_status();
 }
