@@ -52,6 +52,9 @@ def test_gate_errors(L):
     assert f(A, -1, 64, A, 8, A, None) == SHAPE
     assert f(A, 10, 60, A, 8, A, None) == SHAPE
     assert f(A, 10, 64, A, 1025, A, None) == UNSUP
+    # rows longer than 4194304 with E > 32, on every kernel path (a multiple of 128 or not)
+    assert f(A, 10, (1 << 22) + 128, A, 64, A, None) == UNSUP
+    assert f(A, 10, (1 << 22) + 8, A, 160, A, None) == UNSUP
     assert f(MIS, 10, 64, A, 8, A, None) == ALIGN
     assert f(A, 0, 64, A, 8, A, None) == OK       # n = 0 is a no-op
 

@@ -501,12 +501,14 @@ static void launch_lds(int kg, dim3 grid, hipStream_t s, const uint16_t* A, int6
 static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N,
                        const float* bias, void* C, int epi, hipStream_t s) {
   if (M == 0) return ROUTE_OK;
+  // the staged kernel's tile byte offsets are 32-bit; the same limit holds
+  // for every E > 32, whichever kernel runs
+  if (N > 32 && Kd > (1 << 22)) return ROUTE_ERR_UNSUPPORTED;
   // K a multiple of 128 and 32 < N <= 128 or N > 160: the matrix-core kernel
-  // of mma.hip (on MI355X 1.3-2.1x faster than the kernels below there)
+  // of mma.hip (faster than the staged kernel below on those shapes)
   if (mma_fits(M, Kd, N)) return mma_launch(A, M, Kd, B, N, bias, C, epi, s);
   const int ntiles = (N + 15) / 16;
   if (N > 32) {
-    if (Kd > (1 << 22)) return ROUTE_ERR_UNSUPPORTED;  // tile byte offsets are 32-bit
     // LDS-staged tiles: 64 x 160 for E <= 160 (one pass over A), else 64 x 128
     // blocks of columns; 32-row tiles when 64-row ones would leave CUs idle
     const bool wide = ntiles > 8;
