@@ -1,4 +1,4 @@
-// bf16 matrix-core product shared by the kernels that use it:
+// bf16 matrix-core products shared by the kernels that use them.
 // v_mfma_f32_16x16x32_bf16, D = A . B + C for a 16 x 32 A fragment and a
 // 32 x 16 B fragment. Lane l holds row (A) or column (B) l % 16, elements
 // k = 8 (l / 16) .. 8 (l / 16) + 7 as one 16-byte vector; the result holds
@@ -13,6 +13,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16, D = A . B + C for a 32 x 16 A fragment and a
+// 16 x 32 B fragment: lane l holds row (A) or column (B) l % 32 and eight
+// consecutive k, the halves l / 32 = 0, 1 taking the two 8-wide k halves (any
+// consistent assignment of k to lanes gives the same product); the result
+// holds column l % 32, rows 8 (e / 4) + 4 (l / 32) + e % 4 for e = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 

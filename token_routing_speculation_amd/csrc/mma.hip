@@ -35,18 +35,6 @@ namespace {
 constexpr int kMmaThreads = 256;  // four waves, 2 x 2 over the tile
 constexpr int kMmaStages = 4;     // LDS stages (K steps of 64) in the ring
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// D = A . B + C for a 32 x 16 A fragment and a 16 x 32 B fragment: lane l
-// holds row (A) or column (B) l % 32 and eight consecutive k, the halves
-// l / 32 = 0, 1 taking the two 8-wide k halves (any consistent assignment of
-// k to lanes gives the same product); the result holds column l % 32, rows
-// 8 (e / 4) + 4 (l / 32) + e % 4 for e = 0..15.
-__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
 // One 16-byte piece per lane from global memory into LDS: lane i writes at
 // lds_base + 16 i (lds_base is wave-uniform). Completion is counted by vmcnt.
 __device__ __forceinline__ void lds_load16(const void* g, char* lds_base) {
