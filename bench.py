@@ -797,7 +797,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the routing path has no multi-GPU exchange "
               "(--gpus must be 1)", file=sys.stderr)
         return 2
 
