@@ -131,7 +131,10 @@ GATE_CASES = [(1, 8, 1), (17, 64, 4), (100, 136, 8), (1000, 520, 17), (4133, 204
               (4096, 4096, 8), (257, 72, 160),
               # the matrix-core kernel: its shortest K (two steps), one row, a
               # 33-column tile, and its 128 x 128 tiles with ragged rows and columns
-              (77, 128, 96), (1, 384, 40), (513, 256, 33), (8200, 1024, 520)]
+              (77, 128, 96), (1, 384, 40), (513, 256, 33), (8200, 1024, 520),
+              # its 64 x 160 variant for 129..160 columns: shortest K and one row,
+              # ragged rows and columns, ten steps
+              (1, 128, 129), (4133, 2048, 150), (65, 640, 160)]
 
 
 @pytest.mark.parametrize("n,d,E", GATE_CASES)

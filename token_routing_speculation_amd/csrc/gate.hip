@@ -23,9 +23,8 @@
 // (item 2.A: next gate on q_l; item 2.C: the estimator MLP).
 //
 // gemm_launch picks the kernel per shape: the split-K register kernel for
-// E <= 32, the matrix-core kernel of mma.hip where it applies (K % 128 == 0
-// and 32 < E <= 128 or E > 160), and the staged kernel otherwise (among
-// them E = 160, whose one-pass 64 x 160 tiles read A exactly once).
+// E <= 32, the matrix-core kernels of mma.hip when K % 128 == 0 (faster on
+// every measured shape), and the staged kernel below otherwise.
 #include "common.hpp"
 #include "gemm.hpp"
 #include "mfma.hpp"
@@ -504,8 +503,8 @@ static int gemm_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, 
   // the staged kernel's tile byte offsets are 32-bit; the same limit holds
   // for every E > 32, whichever kernel runs
   if (N > 32 && Kd > (1 << 22)) return ROUTE_ERR_UNSUPPORTED;
-  // K a multiple of 128 and 32 < N <= 128 or N > 160: the matrix-core kernel
-  // of mma.hip (faster than the staged kernel below on those shapes)
+  // K a multiple of 128: the matrix-core kernels of mma.hip (faster than the
+  // staged kernel below on every measured shape)
   if (mma_fits(M, Kd, N)) return mma_launch(A, M, Kd, B, N, bias, C, epi, s);
   const int ntiles = (N + 15) / 16;
   if (N > 32) {

@@ -44,10 +44,10 @@ __device__ __forceinline__ float gelu_erf(float x) {
 int gemm_f32(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, float* C,
              hipStream_t s);
 
-// mma.hip: the LDS-staged 32 x 32 x 16 matrix-core kernel. It takes
-// Kd % 128 == 0 and N > 32 outside 129..160 (where the one-pass 64 x 160
-// tiles of gate.hip read A once); mma_launch returns ROUTE_ERR_UNSUPPORTED
-// for any other shape.
+// mma.hip: the matrix-core kernels with operands staged straight into LDS
+// (32 x 32 x 16 tiles; 64 x 160 tiles of 16 x 16 x 32 for 129..160 columns).
+// They take Kd % 128 == 0 and N > 32; mma_launch returns
+// ROUTE_ERR_UNSUPPORTED for any other shape.
 bool mma_fits(int64_t M, int Kd, int N);
 int mma_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, const float* bias,
                void* C, int epi, hipStream_t s);

@@ -15,7 +15,8 @@
 //    wave's LDS base), four stages deep, one barrier per 64-wide K step.
 //    No register ring, no LDS store instructions.
 //  - A workgroup of four waves owns BM x BN (2 x 2 waves); 128 x 128 when
-//    that still gives a workgroup per CU, 64 x 64 otherwise.
+//    that still gives a workgroup per CU, 64 x 64 otherwise; 129..160
+//    columns get their own 64 x 160 variant (mma_nt160_kernel).
 //  - Slab rows are 128 bytes, 16-byte pieces XOR-swizzled by (row / 2) % 8:
 //    gfx950's LDS serves a 16-byte read for 16 lanes at a time from a
 //    256-byte window of banks, so the 32 rows of a fragment read are
@@ -211,15 +212,182 @@ __global__ __launch_bounds__(kMmaThreads, 1) void mma_nt_kernel(
     }
 }
 
+// The same staging for 129..160 columns (the DeepSeek-V2 router's E = 160),
+// where 32 x 32 tiles do not divide the width: a workgroup owns 64 rows x
+// 160 columns, so A is read exactly once. Eight waves form two K groups of
+// 2 x 2 waves (32 rows x 80 columns each, 2 x 5 tiles of
+// v_mfma_f32_16x16x32_bf16); group g multiplies K chunk g of every 64-wide
+// step, and the two groups' partial tiles are added once, in group order, at
+// the end. A step's 28 loads of 1 KB are shared 4 / 3 over the eight waves.
+// On the DeepSeek-V2 shape (16384 x 5120 x 160) it takes 41.5 us, against
+// 47.2 us for the staged kernel of gate.hip.
+constexpr int kM160Threads = 512;
+
+__global__ __launch_bounds__(kM160Threads, 1) void mma_nt160_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int Kd, const uint16_t* __restrict__ B, int N,
+    const float* __restrict__ bias, void* __restrict__ C, int epi) {
+  constexpr int BM = 64, BN = 160;
+  constexpr int MT = 2, NT = 5;                // 16 x 16 tiles per wave
+  constexpr int STAGE = (BM + BN) * 128;       // 28 KB
+  constexpr int NJ = (BM + BN) / 8;            // 1 KB loads per step (28)
+  constexpr int NW = kM160Threads / kWave;     // 8
+  constexpr int NI_MAX = (NJ + NW - 1) / NW;   // 4 (waves 0-3), 3 for waves 4-7
+  static_assert(NJ == 4 * 4 + 3 * 4, "loads split 4 / 3 over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[kMmaStages * STAGE];
+  const int w = wave_id(), lane = lane_id();
+  const int g = w >> 2, w4 = w & 3;
+  const int wr = w4 & 1, wc = w4 >> 1;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int nsteps = Kd / 64;  // even, >= 2
+  const int ni = w < 4 ? 4 : 3;
+
+  const char* src[NI_MAX];
+  int dst[NI_MAX];
+#pragma unroll
+  for (int i = 0; i < NI_MAX; ++i) {
+    const int j = w + NW * i < NJ ? w + NW * i : w;  // waves 4-7 have no fourth load
+    const int r = 8 * j + lane / 8;
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    if (r < BM) {
+      const int64_t gr = row0 + r < M ? row0 + r : M - 1;
+      src[i] = reinterpret_cast<const char*>(A + gr * Kd) + 16 * p;
+    } else {
+      const int gc = r - BM < N ? r - BM : N - 1;
+      src[i] = reinterpret_cast<const char*>(B + static_cast<int64_t>(gc) * Kd) + 16 * p;
+    }
+    dst[i] = 8 * j * 128;
+  }
+  auto load_one = [&](int i, int st) {
+    st = st < nsteps ? st : nsteps - 1;
+    lds_load16(src[i] + st * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
+  };
+  auto load_step = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NI_MAX; ++i)
+      if (i < ni) load_one(i, st);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's fragments of one step: K chunk g (32 k) is pieces 4g .. 4g + 3
+  u32x4 fa[2][MT], fb[2][NT];
+  auto read_frags = [&](int set, int st) {
+    const char* base = lds + (st % kMmaStages) * STAGE;
+    const int pc = 4 * g + (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      fa[set][m] = *reinterpret_cast<const u32x4*>(
+          base + slab_off(wr * 32 + 16 * m + (lane & 15), pc));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      fb[set][t] = *reinterpret_cast<const u32x4*>(
+          base + BM * 128 + slab_off(wc * 80 + 16 * t + (lane & 15), pc));
+  };
+  auto mfma_step = [&](int set, int st_load) {
+    int q = 0, i = 0;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[m][t] = mfma16x16x32(fa[set][m], fb[set][t], acc[m][t]);
+        if (++q % 2 == 0 && i < NI_MAX) {  // a load after every second MFMA (measured best)
+          __builtin_amdgcn_sched_barrier(0);
+          if (st_load >= 0 && i < ni) load_one(i, st_load);
+          ++i;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+    for (; i < NI_MAX; ++i)
+      if (st_load >= 0 && i < ni) load_one(i, st_load);
+  };
+  auto sync_step = [&]() {
+    wait_lgkm0();
+    if (w < 4)
+      wait_vmcnt<(kMmaStages - 2) * 4>();
+    else
+      wait_vmcnt<(kMmaStages - 2) * 3>();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+#pragma unroll
+  for (int s2 = 0; s2 < kMmaStages - 1; ++s2) load_step(s2);
+  sync_step();
+  load_step(kMmaStages - 1);
+  read_frags(0, 0);
+  for (int st = 0; st < nsteps - 2; st += 2) {
+    sync_step();
+    read_frags(1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0, st + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+    sync_step();
+    read_frags(0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(1, st + 1 + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sync_step();
+  read_frags(1, nsteps - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(0, -1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(1, -1);
+
+  // group 1's partial tiles meet group 0's in LDS (the stages are free once
+  // every wave's loads have landed and every wave is past its last read)
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+  if (g == 1) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) red[((w4 * MT + m) * NT + t) * kWave + lane] = acc[m][t];
+  }
+  __syncthreads();
+  if (g == 1) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[m][t] += red[((w4 * MT + m) * NT + t) * kWave + lane];
+      const int col = wc * 80 + 16 * t + (lane & 15);
+      if (col >= N) continue;
+      const float bcol = epi != kEpiF32 ? bias[col] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t row = row0 + wr * 32 + 16 * m + 4 * (lane >> 4) + j;
+        if (row >= M) continue;
+        const int64_t o = row * N + col;
+        const float v = acc[m][t][j] + bcol;
+        if (epi == kEpiBiasGeluBf16)
+          static_cast<uint16_t*>(C)[o] = static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(v)));
+        else
+          static_cast<float*>(C)[o] = v;
+      }
+    }
+}
+
 }  // namespace
 
 bool mma_fits(int64_t M, int Kd, int N) {
-  return M > 0 && N > 32 && Kd >= 128 && Kd % 128 == 0 && (N <= 128 || N > 160);
+  return M > 0 && N > 32 && Kd >= 128 && Kd % 128 == 0;
 }
 
 int mma_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, const float* bias,
                void* C, int epi, hipStream_t s) {
   if (!mma_fits(M, Kd, N)) return ROUTE_ERR_UNSUPPORTED;
+  if (N > 128 && N <= 160) {
+    mma_nt160_kernel<<<ceil_div(M, 64), kM160Threads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
+    return launch_status();
+  }
   const int64_t big = static_cast<int64_t>(ceil_div(M, 128)) * ceil_div(N, 128);
   if (N >= 128 && big >= 256) {
     dim3 grid(ceil_div(M, 128), ceil_div(N, 128));
