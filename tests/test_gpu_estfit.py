@@ -99,7 +99,8 @@ def test_fit_chain_matches_oracle():
     assert (host(w2) != ww2).mean() < 1e-4
 
 
-@pytest.mark.parametrize("n,d,hd", [(1, 64, 8), (999, 2048, 512), (64, 520, 40)])
+@pytest.mark.parametrize("n,d,hd", [(1, 64, 8), (999, 2048, 512), (64, 520, 40),
+                                    (8200, 1024, 520), (77, 256, 136)])
 def test_est_hidden_is_the_estimators_hidden_layer(n, d, hd):
     rng = np.random.default_rng(n + hd)
     q = _bf16((n, d), 1)

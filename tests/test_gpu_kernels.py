@@ -299,7 +299,8 @@ def test_qhidden(n, d, affine):
     assert_rel(oracle.bf16_to_f64(host(q)), ref, LOGIT_TOL, "q_l")
 
 
-@pytest.mark.parametrize("n,d,hd,E", [(1, 64, 8, 8), (300, 256, 72, 40), (2048, 2048, 512, 128)])
+@pytest.mark.parametrize("n,d,hd,E", [(1, 64, 8, 8), (300, 256, 72, 40), (2048, 2048, 512, 128),
+                                        (300, 256, 136, 40), (8200, 1024, 520, 150)])
 def test_estimator(n, d, hd, E):
     rng = np.random.default_rng(n + hd)
     q = _bf16((n, d), 1)
