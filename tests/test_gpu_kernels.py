@@ -342,6 +342,39 @@ def test_run_twice_bitwise():
         assert np.array_equal(host(getattr(p, k)), v), k
 
 
+def test_run_twice_bitwise_foe_and_predictor():
+    """The FoE pass and the q_l predictor (fused gate with top-K and hit
+    count on a gate layer; q_l, the estimator's two matrix-core products and
+    top-K on an estimator layer), each run twice: bitwise-equal outputs, and
+    the counters add exactly the same amount both times."""
+    from synth import get_config
+    from synth.gen import make_foe_inputs, make_predictor_layer
+    from token_routing_speculation_amd.pipeline import FoEPass, PredictorPass
+    inp = make_foe_inputs(3000, 256, 64, 4, 8, 8, 5000, 13)
+    f = FoEPass(inp)
+    keys = ("r_full", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
+    f.step()
+    first = {k: host(getattr(f, k)).copy() for k in keys}
+    l1 = int(host(f.local)[0])
+    f.step()
+    for k, v in first.items():
+        assert np.array_equal(host(getattr(f, k)), v), k
+    assert int(host(f.local)[0]) == 2 * l1
+    cfg = get_config("qwen3")
+    for layer in (0, 10):                           # an estimator layer, a gate layer
+        lay = make_predictor_layer(cfg, layer, N=1000)
+        p = PredictorPass(1000, cfg.d, cfg.E, cfg.K, cfg.hd).load(lay)
+        p.truth_step()
+        p.hits.zero_()
+        p.step(keep_logits=True)
+        first = {k: host(getattr(p, k)).copy() for k in ("logits", "pred")}
+        h1 = int(host(p.hits)[0])
+        p.step(keep_logits=True)
+        for k, v in first.items():
+            assert np.array_equal(host(getattr(p, k)), v), (layer, k)
+        assert int(host(p.hits)[0]) == 2 * h1, layer
+
+
 # ------------------------------------------------------------ graph replay
 def test_graph_replay_matches_eager():
     """The benchmark replays the pass as a captured graph: every replay, with
