@@ -31,7 +31,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libroute.so")
+# ROUTE_LIBRARY names another build of the same library (the host-sanitizer
+# build the ABI tests can run against); unset, the in-tree libroute.so loads
+_LIB_PATH = os.environ.get("ROUTE_LIBRARY") or os.path.join(_HERE, "libroute.so")
 
 # status codes and device error bits (include/route.h)
 ROUTE_OK = 0
