@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
 // buffer. q is neither written nor read back.
 // ---------------------------------------------------------------------------
 constexpr int kQgThreads = 512;
-constexpr int kQgLead = 7;  // W line loads in flight, in pairs of K steps
+constexpr int kQgLead = 3;  // W line loads in flight, in pairs of K steps (measured: 3 beats 1, 7 and 15)
 
 // LDS offset of 16-byte piece p of tile row rr. Rows are a multiple of 256
 // bytes long, so every row starts at the same bank; gfx950's LDS serves a
