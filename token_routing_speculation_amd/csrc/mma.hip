@@ -63,6 +63,15 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // Byte offset of logical 16-byte piece p (0..7) of 128-byte slab row r.
 __device__ __forceinline__ int slab_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
 
+// The K step that pipeline step st loads when the walk over K starts at step
+// rot (< nsteps); the sums then run in that rotated order. Used where every
+// workgroup streams the same weight rows: when they are not cached, 256
+// workgroups asking for the same lines at once wait on a few HBM channels.
+__device__ __forceinline__ int k_step(int st, int rot, int nsteps) {
+  const int k = st + rot;
+  return k < nsteps ? k : k - nsteps;
+}
+
 template <int BM, int BN>
 __global__ __launch_bounds__(kMmaThreads, 1) void mma_nt_kernel(
     const uint16_t* __restrict__ A, int64_t M, int Kd, const uint16_t* __restrict__ B, int N,
@@ -103,8 +112,8 @@ __global__ __launch_bounds__(kMmaThreads, 1) void mma_nt_kernel(
   // a step past the end re-loads the last step into its own buffer (the same
   // bytes), which keeps every wave's count of pending loads uniform
   auto load_one = [&](int i, int st) {
-    st = st < nsteps ? st : nsteps - 1;
-    lds_load16(src[i] + st * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
+    const int ks = st < nsteps ? st : nsteps - 1;
+    lds_load16(src[i] + ks * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
   };
   auto load_step = [&](int st) {
 #pragma unroll
@@ -239,6 +248,11 @@ __global__ __launch_bounds__(kM160Threads, 1) void mma_nt160_kernel(
   const int wr = w4 & 1, wc = w4 >> 1;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int nsteps = Kd / 64;  // even, >= 2
+  // workgroups are dealt to the eight XCDs in turn; each XCD's share starts
+  // its walk over K an eighth of K further on (the workgroups of one XCD stay
+  // in step, so each W line is fetched into that XCD's L2 once and used by
+  // all of them)
+  const int rot = static_cast<int>((blockIdx.x & 7) * nsteps / 8);
   const int ni = w < 4 ? 4 : 3;
 
   const char* src[NI_MAX];
@@ -258,8 +272,8 @@ __global__ __launch_bounds__(kM160Threads, 1) void mma_nt160_kernel(
     dst[i] = 8 * j * 128;
   }
   auto load_one = [&](int i, int st) {
-    st = st < nsteps ? st : nsteps - 1;
-    lds_load16(src[i] + st * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
+    const int ks = k_step(st < nsteps ? st : nsteps - 1, rot, nsteps);
+    lds_load16(src[i] + ks * 128, lds + (st % kMmaStages) * STAGE + dst[i]);
   };
   auto load_step = [&](int st) {
 #pragma unroll
