@@ -30,9 +30,11 @@ METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofl
 ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
 
 
-def route_bytes(N, d, E, K, P, G, fallback):
+def route_bytes(N, d, E, K, P, G, fallback, fused=False):
     """Algorithmic HBM bytes per pass: every call reads its inputs once and
-    writes its outputs once (bf16 rows = 2 bytes per element)."""
+    writes its outputs once (bf16 rows = 2 bytes per element). With the
+    shuffle and the router fused (srs_shuffle_gate) the reduced rows are
+    written once and not read back."""
     b = 2
     st = {
         "predict": (9 if fallback else 6) * N,
@@ -43,6 +45,9 @@ def route_bytes(N, d, E, K, P, G, fallback):
         "permute": 12 * N * K + 4 * (E + 1) + N * d * b + N * K * d * b,
         "combine": N * K * d * b + 8 * N * K + 4 * N + N * d * b,
     }
+    if fused:
+        st = {"predict": st["predict"], "srs_gate": st.pop("srs") + st.pop("gate") - N * d * b,
+              **{k: v for k, v in st.items() if k != "predict"}}
     return st
 
 
@@ -830,7 +835,7 @@ def main(argv=None):
                 "K": cfg.K, "G": cfg.G}
     else:
         p = RoutePass(inp)
-        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback)
+        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.fused)
         conf = {"workload": ROUTE_WORKLOADS[args.config], "N": cfg.N, "d": cfg.d, "E": cfg.E,
                 "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
                 "fallback": "2-gram" if p.fallback else "none"}
@@ -907,6 +912,7 @@ def main(argv=None):
     N = cfg.N
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
+    gate_stage = "gate" if "gate" in st_us else "srs_gate"  # the stage holding the router product
     # dominant single-kernel stage: the combine (one launch per pass)
     dom = "combine"
     dom_bytes = bytes_st[dom]
@@ -932,7 +938,8 @@ def main(argv=None):
         "pass_ms_p10_p50_p90": pct(per_pass) if per_pass else None,
         "cold_pass_ms_p10_p50_p90": pct(cold) if cold else None,
         "stages_us": {k: round(v, 2) for k, v in st_us.items()},
-        "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us["gate"] * 1e-6) / MFMA_BF16_PEAK,
+        "gate_stage": gate_stage,
+        "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us[gate_stage] * 1e-6) / MFMA_BF16_PEAK,
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
         "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",

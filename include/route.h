@@ -141,6 +141,28 @@ int srs_shuffle(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
 size_t srs_shuffle_workspace_size(int64_t n, int32_t G);
 
 /*
+ * srs_shuffle_gate - srs_shuffle and route_gate on its output in one pass.
+ * [SMOE] section 3.1 (s-TS) for the reduce and the shuffle; [FOE] router
+ * scores g[i] on the reduced rows. Writes every output of srs_shuffle, with
+ * the same bytes, and
+ *   logits[row][e] = out[row] . w[e]^T   (binary32, for every written row),
+ * i.e. route_gate(out, n, d, w, E, logits) up to the order of the binary32
+ * sums. The reduced rows are multiplied while they are still on chip, so
+ * they are written once and not read back.
+ *   Arguments as srs_shuffle, plus w bf16 rows [E][d] (16-byte aligned) and
+ *   logits float[n][E] (row-major). ws: srs_shuffle_workspace_size(n, G).
+ * Errors: as srs_shuffle, plus NULL (w or logits with n > 0), and
+ * UNSUPPORTED unless P is 1, 2 or 4, d % 128 == 0 and 1 <= E <= 160 (use
+ * srs_shuffle + route_gate there). Device bit: DEST_RANGE (rows whose key
+ * is out of range get neither out nor logits).
+ */
+int srs_shuffle_gate(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                     const uint8_t* dest, int32_t G, uint16_t* out, int32_t* cluster_offsets,
+                     int32_t* row_of_src, int32_t* src_of_row, uint8_t* row_cluster,
+                     const uint16_t* w, int32_t E, float* logits, void* ws, size_t ws_bytes,
+                     uint32_t* err, hipStream_t s);
+
+/*
  * route_gate - router logits = x . w^T.
  * [FOE] per-layer comparison (router scores g[i]); [SPEC] item 2.A (the
  * next layer's gate applied to q_l). bf16 operands, binary32 accumulation

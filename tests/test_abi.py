@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 32, names
+    assert len(names) == 33, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -87,6 +87,34 @@ def test_srs_errors(L):
     assert call(args(G=300)) == UNSUP
     assert call(args(partials=MIS)) == ALIGN
 
+
+
+def test_srs_gate_errors(L):
+    f = L.srs_shuffle_gate
+    ws = L.srs_shuffle_workspace_size(1000, 8)
+    args = lambda **k: dict(dict(partials=A, P=2, n=1000, d=256, dest=A, G=8, out=A, offs=A,
+                                 ros=None, sor=None, rc=None, w=A, E=160, logits=A, ws=A, wsb=ws,
+                                 err=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(wsb=ws - 1)) == WS
+    assert call(args(ws=None)) == WS
+    assert call(args(dest=None)) == NULL
+    assert call(args(w=None)) == NULL
+    assert call(args(logits=None)) == NULL
+    assert call(args(out=None)) == NULL
+    assert call(args(offs=None)) == NULL
+    assert call(args(d=12)) == SHAPE
+    assert call(args(E=0)) == SHAPE
+    assert call(args(n=-1)) == SHAPE
+    # the fused kernel's shapes only: P in {1, 2, 4}, d % 128 == 0, E <= 160
+    assert call(args(P=3)) == UNSUP
+    assert call(args(P=8)) == UNSUP
+    assert call(args(d=192)) == UNSUP
+    assert call(args(d=64)) == UNSUP
+    assert call(args(E=161)) == UNSUP
+    assert call(args(G=300)) == UNSUP
+    assert call(args(partials=MIS)) == ALIGN
+    assert call(args(w=MIS)) == ALIGN
 
 def test_permute_and_combine_errors(L):
     ws = L.moe_permute_workspace_size(1000, 6, 160)

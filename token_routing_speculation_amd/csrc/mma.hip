@@ -28,6 +28,7 @@
 #include "common.hpp"
 #include "gemm.hpp"
 #include "mfma.hpp"
+#include "srs.hpp"
 
 namespace route {
 
@@ -389,6 +390,256 @@ __global__ __launch_bounds__(kM160Threads, 1) void mma_nt160_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The shuffled reduce fused with the router product on its output
+// ("Speculative MoE" section 3.1 for the reduce and shuffle; the router
+// scores of the "Federation of Experts (FoE)" article on the reduced rows):
+// X[dst(i)] = bf16(sum_p partials[p][i]) and logits[dst(i)] = X[dst(i)] . W^T.
+// The tile, the W stream and the MFMA schedule are mma_nt160_kernel's (64
+// source rows, 160 columns, 16 x 16 x 32 tiles, two K groups, four LDS
+// stages); the A slab of a step is not loaded from X but built. Thread t
+// owns row t / 8, 16-byte piece t % 8 of each 128-byte step. Its pieces of
+// the P partials go straight into LDS (global_load_lds), kSgLead(P) steps
+// ahead, each lane's 16 bytes landing where that lane reads them back, so
+// only the wave's own load count guards them. The thread then sums them in
+// binary32 (partial order) and rounds once (the row mover's arithmetic, so X
+// is the same bytes), writes the piece into the A slab and stores it to X.
+// X is written once and never read back, and the W stream and matrix work
+// hide under the partials' HBM stream.
+//
+// Wait accounting: every wait counts only this wave's loads issued after the
+// awaited one. Vector-memory operations complete in issue order on gfx9
+// (loads and stores alike), so the X stores, which the count leaves out,
+// can only make a wait stricter.
+// ---------------------------------------------------------------------------
+template <int PT>
+constexpr int sg_lead() { return PT <= 2 ? 3 : 1; }  // partial slots: 112 KB of stages + 48 KB at P = 2
+
+// One 16-byte piece per lane into LDS, as lds_load16, with the nontemporal
+// (streaming) policy: the partials are read once.
+__device__ __forceinline__ void lds_load16_nt(const void* g, char* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   2);
+#endif
+}
+
+template <int PT>
+__global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
+    const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ W, int E, float* __restrict__ logits,
+    SrsIdentity ident) {
+  constexpr int BM = 64, BN = 160;
+  constexpr int MT = 2, NT = 5;             // 16 x 16 tiles per wave
+  constexpr int STAGE = (BM + BN) * 128;    // 28 KB
+  constexpr int NJW = BN / 8;               // 1 KB W loads per step (20)
+  constexpr int NW = kM160Threads / kWave;  // 8
+  constexpr int NIW = (NJW + NW - 1) / NW;  // 3 (waves 0-3), 2 for waves 4-7
+  constexpr int LA = sg_lead<PT>();
+  constexpr int PSLOT = BM * 128;           // one partial's pieces of one step (8 KB)
+  static_assert(NJW == 3 * 4 + 2 * 4, "W loads split 3 / 2 over the waves");
+  static_assert(kMmaStages == 4, "the main loop stages two steps per pass");
+  // loads a wave issues after the awaited ones (see above): nw W loads and PT
+  // partial loads per step
+  constexpr int kWaitA3 = (LA - 1) * (3 + PT) + 3, kWaitA2 = (LA - 1) * (2 + PT) + 2;
+  constexpr int kWaitW3 = PT + 2 * (3 + PT), kWaitW2 = PT + 2 * (2 + PT);
+  // the four stages, then the partial slots
+  __shared__ __attribute__((aligned(1024))) char lds[kMmaStages * STAGE + LA * PT * PSLOT];
+  char* const pst = lds + kMmaStages * STAGE;
+  const int w = wave_id(), lane = lane_id();
+  const int g = w >> 2, w4 = w & 3;
+  const int wr = w4 & 1, wc = w4 >> 1;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int nsteps = d / 64;  // even, >= 2
+  const int ni = w < 4 ? 3 : 2;
+
+  // W: load j = w + 8 i fills slab rows BM + 8 j .. BM + 8 j + 7; lane l
+  // fetches the piece that the swizzle stores at physical piece l % 8.
+  // Columns past E re-read the last valid one (their results are not stored).
+  const char* wsrc[NIW];
+  int wdst[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int j = w + NW * i < NJW ? w + NW * i : w;  // waves 4-7 have no third load
+    const int r = BM + 8 * j + lane / 8;
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    const int gc = r - BM < E ? r - BM : E - 1;
+    wsrc[i] = reinterpret_cast<const char*>(W + static_cast<int64_t>(gc) * d) + 16 * p;
+    wdst[i] = (BM + 8 * j) * 128;
+  }
+  auto load_w = [&](int t) {
+    const int ks = t < nsteps ? t : nsteps - 1;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      if (i < ni) lds_load16(wsrc[i] + ks * 128, lds + (t % kMmaStages) * STAGE + wdst[i]);
+  };
+
+  // A: this thread's row and piece. Rows past n re-read row n - 1 and store
+  // nothing.
+  const int ar = threadIdx.x >> 3, apc = threadIdx.x & 7;
+  const int64_t ai = row0 + ar;
+  const bool alive = ai < n;
+  const int adst = alive ? (row_of_src ? row_of_src[ai] : static_cast<int>(ai)) : -1;
+  const bool astore = alive && adst >= 0 && adst < n;
+  if (alive && apc == 0) write_identity_row(ident, ai, n);
+  const size_t plane = static_cast<size_t>(n) * d;
+  const uint16_t* asrc = partials + static_cast<size_t>(alive ? ai : n - 1) * d + 8 * apc;
+  uint16_t* aout = out + static_cast<size_t>(astore ? adst : 0) * d + 8 * apc;
+  const int alds = slab_off(ar, apc);
+  char* pwave = pst + w * 1024;  // this wave's 1 KB of each partial slot
+  auto load_a = [&](int t) {
+    const int ks = t < nsteps ? t : nsteps - 1;
+    char* slot = pwave + (t % LA) * PT * PSLOT;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) lds_load16_nt(asrc + p * plane + 64 * ks, slot + p * PSLOT);
+  };
+  // step t's slab piece: sum, round, into the A slab and X
+  auto build_a = [&](int t) {
+    const char* slot = pst + (t % LA) * PT * PSLOT + 16 * threadIdx.x;
+    float acc8[8];
+    unpack8(*reinterpret_cast<const u32x4*>(slot), acc8);
+#pragma unroll
+    for (int p = 1; p < PT; ++p) {
+      float f[8];
+      unpack8(*reinterpret_cast<const u32x4*>(slot + p * PSLOT), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc8[e] += f[e];
+    }
+    const u32x4 x = pack8(acc8);
+    *reinterpret_cast<u32x4*>(lds + (t % kMmaStages) * STAGE + alds) = x;
+    if (astore) st16(aout + 64 * t, x);
+  };
+  // after the wave's count shows step t's partials landed: build step t's
+  // piece, then load step t + LA's into the slot just read
+  auto stage_a = [&](int t) {
+    if (w < 4)
+      wait_vmcnt<kWaitA3>();
+    else
+      wait_vmcnt<kWaitA2>();
+    if (t < nsteps) build_a(t);
+    load_a(t + LA);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's fragments of one step: K chunk g (32 k) is pieces 4g .. 4g + 3
+  u32x4 fa[2][MT], fb[2][NT];
+  auto read_frags = [&](int set, int st) {
+    const char* base = lds + (st % kMmaStages) * STAGE;
+    const int pc = 4 * g + (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      fa[set][m] = *reinterpret_cast<const u32x4*>(
+          base + slab_off(wr * 32 + 16 * m + (lane & 15), pc));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      fb[set][t] = *reinterpret_cast<const u32x4*>(
+          base + BM * 128 + slab_off(wc * 80 + 16 * t + (lane & 15), pc));
+  };
+  // the MFMAs of one step with the staging of step tl (tl < 0: none): W's
+  // loads after MFMAs 2, 4 and 6, the A piece after MFMA 8
+  auto mfma_step = [&](int set, int tl) {
+    int q = 0;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[m][t] = mfma16x16x32(fa[set][m], fb[set][t], acc[m][t]);
+        ++q;
+        if (q == 2 || q == 4 || q == 6) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int i = q / 2 - 1;
+          if (tl >= 0 && i < ni) {
+            const int ks = tl < nsteps ? tl : nsteps - 1;
+            lds_load16(wsrc[i] + ks * 128, lds + (tl % kMmaStages) * STAGE + wdst[i]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else if (q == 8) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (tl >= 0) stage_a(tl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  };
+  auto sync_step = [&]() {
+    wait_lgkm0();
+    if (w < 4)
+      wait_vmcnt<kWaitW3>();
+    else
+      wait_vmcnt<kWaitW2>();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+  // prologue: partials of the first LA steps, then steps 0 .. 2 staged (the
+  // first wait drains everything: the counts above hold from step 1 on)
+#pragma unroll
+  for (int t = 0; t < LA; ++t) load_a(t);
+  load_w(0);
+  wait_vmcnt<0>();
+  build_a(0);
+  load_a(LA);
+  load_w(1);
+  stage_a(1);
+  load_w(2);
+  stage_a(2);
+  sync_step();
+  load_w(3);
+  stage_a(3);
+  read_frags(0, 0);
+  for (int st = 0; st < nsteps - 2; st += 2) {
+    sync_step();
+    read_frags(1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0, st + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+    sync_step();
+    read_frags(0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(1, st + 1 + kMmaStages);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sync_step();
+  read_frags(1, nsteps - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(0, -1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(1, -1);
+
+  // group 1's partial tiles meet group 0's in LDS
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+  if (g == 1) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) red[((w4 * MT + m) * NT + t) * kWave + lane] = acc[m][t];
+  }
+  __syncthreads();
+  if (g == 1) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = row0 + wr * 32 + 16 * m + 4 * (lane >> 4) + j;
+      if (row >= n) continue;
+      const int dst = row_of_src ? row_of_src[row] : static_cast<int>(row);
+      if (dst < 0 || dst >= n) continue;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = wc * 80 + 16 * t + (lane & 15);
+        if (col < E)
+          logits[static_cast<int64_t>(dst) * E + col] =
+              acc[m][t][j] + red[((w4 * MT + m) * NT + t) * kWave + lane][j];
+      }
+    }
+}
 }  // namespace
 
 bool mma_fits(int64_t M, int Kd, int N) {
@@ -410,6 +661,27 @@ int mma_launch(const uint16_t* A, int64_t M, int Kd, const uint16_t* B, int N, c
     dim3 grid(ceil_div(M, 64), ceil_div(N, 64));
     mma_nt_kernel<64, 64><<<grid, kMmaThreads, 0, s>>>(A, M, Kd, B, N, bias, C, epi);
   }
+  return launch_status();
+}
+
+bool srs_gate_fits(int P, int d, int E) {
+  return (P == 1 || P == 2 || P == 4) && d >= 128 && d % 128 == 0 && E >= 1 && E <= 160;
+}
+
+int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int* row_of_src,
+                    uint16_t* out, const uint16_t* w, int E, float* logits,
+                    const SrsIdentity& ident, hipStream_t s) {
+  if (!srs_gate_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  const unsigned grid = ceil_div(n, 64);
+  if (P == 1)
+    srs_gate160_kernel<1><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
+                                                        logits, ident);
+  else if (P == 2)
+    srs_gate160_kernel<2><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
+                                                        logits, ident);
+  else
+    srs_gate160_kernel<4><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
+                                                        logits, ident);
   return launch_status();
 }
 

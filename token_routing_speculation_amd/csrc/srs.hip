@@ -9,31 +9,15 @@
 // row with 16-byte vector loads, one wave per row.
 #include "common.hpp"
 #include "csort.hpp"
+#include "srs.hpp"
 
 namespace route {
 
 constexpr int kMoveThreads = 256;
 
-// Outputs of a shuffle without a sort (one cluster): cluster offsets {0, n}
-// and identity maps, written by the row mover itself instead of by separate
-// fill launches. Each pointer may be null.
-struct SrsIdentity {
-  int* offsets;
-  int* row_of_src;
-  int* src_of_row;
-  uint8_t* row_cluster;
-};
-
 // row i's share of the identity outputs (lane 0 of row i's wave)
 __device__ __forceinline__ void write_identity(const SrsIdentity& id, int64_t i, int64_t n) {
-  if (lane_id() != 0) return;
-  if (id.offsets && i == 0) {
-    id.offsets[0] = 0;
-    id.offsets[1] = static_cast<int>(n);
-  }
-  if (id.row_of_src) id.row_of_src[i] = static_cast<int>(i);
-  if (id.src_of_row) id.src_of_row[i] = static_cast<int>(i);
-  if (id.row_cluster) id.row_cluster[i] = 0;
+  if (lane_id() == 0) write_identity_row(id, i, n);
 }
 
 // One wave per source row: out[dst(i)] = bf16(sum_p partials[p][i]). Every
@@ -189,4 +173,43 @@ ROUTE_API int srs_shuffle(const uint16_t* partials, int32_t P, int64_t n, int32_
   if (P == 4 && cpl <= 4) done = launch_srs_move<4>(cpl, grid, s, partials, n, d, fwd, out, ident);
   if (!done) srs_move_any<<<grid, kMoveThreads, 0, s>>>(partials, P, n, d, fwd, out, ident);
   return launch_status();
+}
+
+ROUTE_API int srs_shuffle_gate(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                               const uint8_t* dest, int32_t G, uint16_t* out,
+                               int32_t* cluster_offsets, int32_t* row_of_src,
+                               int32_t* src_of_row, uint8_t* row_cluster, const uint16_t* w,
+                               int32_t E, float* logits, void* ws, size_t ws_bytes,
+                               uint32_t* err, hipStream_t s) {
+  if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || G < 1 || E < 1 || n >= (int64_t(1) << 31))
+    return ROUTE_ERR_SHAPE;
+  if (G > kMaxClusters || !srs_gate_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  if (!cluster_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
+    return launch_status();
+  }
+  if (!partials || !out || !w || !logits) return ROUTE_ERR_NULL;
+  if (!dest && G != 1) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(out) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  const bool sort = dest != nullptr;
+  if (sort) {
+    if (!ws) return ROUTE_ERR_WORKSPACE;
+    if (ws_bytes < srs_ws(n, G)) return ROUTE_ERR_WORKSPACE;
+  }
+  const int* fwd = nullptr;
+  if (sort) {
+    char* wsp = static_cast<char*>(ws);
+    const size_t ct = csort_ws_bytes(n, G);
+    const size_t nt = align_up(static_cast<size_t>(n) * sizeof(int), 256);
+    int* fwd_buf = row_of_src ? row_of_src : reinterpret_cast<int*>(wsp + ct);
+    int* inv_buf = src_of_row ? src_of_row : reinterpret_cast<int*>(wsp + ct + nt);
+    int st = csort_launch<uint8_t>(dest, n, G, cluster_offsets, fwd_buf, inv_buf, row_cluster,
+                                   wsp, err, ROUTE_EBIT_DEST_RANGE, s);
+    if (st != ROUTE_OK) return st;
+    fwd = fwd_buf;
+  }
+  const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
+                                 : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
+  return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, s);
 }

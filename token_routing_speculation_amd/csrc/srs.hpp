@@ -1,0 +1,42 @@
+// Pieces of the shuffled reduce ("Speculative MoE", section 3.1, s-TS)
+// shared by its row mover (srs.hip) and by the mover fused with the router
+// product (mma.hip).
+#pragma once
+
+#include "common.hpp"
+
+namespace route {
+
+// Outputs of a shuffle without a sort (one cluster): cluster offsets {0, n}
+// and identity maps, written by the row mover itself instead of by separate
+// fill launches. Each pointer may be null.
+struct SrsIdentity {
+  int* offsets;
+  int* row_of_src;
+  int* src_of_row;
+  uint8_t* row_cluster;
+};
+
+// Source row i's share of the identity outputs (one thread per row).
+__device__ __forceinline__ void write_identity_row(const SrsIdentity& id, int64_t i, int64_t n) {
+  if (id.offsets && i == 0) {
+    id.offsets[0] = 0;
+    id.offsets[1] = static_cast<int>(n);
+  }
+  if (id.row_of_src) id.row_of_src[i] = static_cast<int>(i);
+  if (id.src_of_row) id.src_of_row[i] = static_cast<int>(i);
+  if (id.row_cluster) id.row_cluster[i] = 0;
+}
+
+// mma.hip: the fused shuffle + router kernel for 1 <= E <= 160 columns,
+// P in {1, 2, 4} partials and d % 128 == 0 (d >= 128). out[dst(i)] =
+// bf16(sum_p partials[p][i]) exactly as the row mover computes it, and
+// logits[dst(i)][e] = out[dst(i)] . w[e] (binary32), dst(i) = row_of_src[i]
+// (the identity when row_of_src is null; rows whose dst is out of range are
+// skipped). Returns ROUTE_ERR_UNSUPPORTED for any other shape.
+bool srs_gate_fits(int P, int d, int E);
+int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int* row_of_src,
+                    uint16_t* out, const uint16_t* w, int E, float* logits,
+                    const SrsIdentity& ident, hipStream_t s);
+
+}  // namespace route

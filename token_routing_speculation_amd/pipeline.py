@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (route_predict, route_lut_build, srs_shuffle, route_gate, route_topk, lar_count,
+from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_gate, route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
@@ -126,6 +126,11 @@ class RoutePass:
         self.ws_perm = e((max(moe_permute_workspace_size(N, K, E), 1),), torch.uint8)
         self.out = e((N, d), out_dtype)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        # the shuffle and the router product in one kernel (srs_shuffle_gate)
+        # for the router shapes of 129..160 columns; two calls otherwise
+        self.fused = P in (1, 2, 4) and d % 128 == 0 and 128 < E <= 160
+        if self.fused:
+            self.STAGES = ("predict", "srs_gate") + RoutePass.STAGES[3:]
 
     def predict(self):
         if self.fallback:
@@ -141,6 +146,12 @@ class RoutePass:
 
     def gate(self):
         route_gate(self.x, self.w, logits=self.logits)
+
+    def srs_gate(self):
+        srs_shuffle_gate(self.partials, self.dest, self.G, self.w, out=self.x, logits=self.logits,
+                         offsets=self.cluster_offsets, row_of_src=self.row_of_src,
+                         src_of_row=self.src_of_row, row_cluster=self.row_cluster, ws=self.ws_srs,
+                         err=self.err)
 
     def topk(self):
         route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
