@@ -376,12 +376,16 @@ def test_run_twice_bitwise_foe_and_predictor():
 
 
 # ------------------------------------------------------------ graph replay
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("E,fused", [(160, True), (64, False)])
+def test_graph_replay_matches_eager(E, fused):
     """The benchmark replays the pass as a captured graph: every replay, with
-    eager work and synchronisations in between, must equal the eager pass."""
+    eager work and synchronisations in between, must equal the eager pass
+    (the shuffle and the router fused into one kernel at 160 columns, two
+    calls at 64)."""
     from token_routing_speculation_amd.pipeline import RoutePass, capture_graph
-    inp = make_route_inputs(2000, 512, 160, 6, 2, 8, 5000, 91, ngram=True)
+    inp = make_route_inputs(2000, 512, E, 6, 2, 8, 5000, 91, ngram=True)
     p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
+    assert p.fused == fused
     keys = ("dest", "x", "row_of_src", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
     p.step()
     sync()
