@@ -3,8 +3,9 @@
 // L2 -> CU operand stream, not HBM, set the pace: the estimator MLP of
 // "Speculating Experts Accelerates Inference for Mixture-of-Experts"
 // (item 2.C: 2048 -> 512 -> 128 for every token) and the router products
-// with E <= 128 columns (the "Federation of Experts (FoE)" article's router
-// scores g[i]; the next gate on q_l, item 2.A).
+// (the "Federation of Experts (FoE)" article's router scores g[i]; the next
+// gate on q_l, item 2.A), plus the router fused with the shuffled reduce that
+// produces its input ("Speculative MoE" section 3.1; srs_gate160_kernel).
 //
 // gfx950 design (measured on MI355X, see the notes at each choice):
 //  - v_mfma_f32_32x32x16_bf16. With one wave per SIMD the 16x16x32 form

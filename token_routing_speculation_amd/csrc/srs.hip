@@ -6,7 +6,9 @@
 //
 // The destination row of every token comes from a stable counting sort of
 // the uint8 cluster ids (csort.hpp); the row mover then streams each source
-// row with 16-byte vector loads, one wave per row.
+// row with 16-byte vector loads, one wave per row. srs_shuffle_gate runs the
+// same sort, then the reduce fused with the router product on its output
+// (mma.hip), so the reduced rows are multiplied before they leave the chip.
 #include "common.hpp"
 #include "csort.hpp"
 #include "srs.hpp"
