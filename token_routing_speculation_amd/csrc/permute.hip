@@ -9,7 +9,10 @@
 
 namespace route {
 
-constexpr int kPermThreads = 256;
+// Two waves per workgroup. Measured on whole passes (graph replay, same box):
+// the FoE-grouped pass 676.7-680.8 us against 687.7-692.8 us with four waves,
+// the DeepSeek-V2-shaped pass unchanged; eight waves were no better.
+constexpr int kPermThreads = 128;
 
 // One wave per (token i, group h): read src[h][i], write it to the slots of
 // the K/H pairs (i, h*kg .. h*kg + kg - 1). The row is loaded whole into
