@@ -17,10 +17,16 @@ constexpr int kPermThreads = 128;
 // One wave per (token i, group h): read src[h][i], write it to the slots of
 // the K/H pairs (i, h*kg .. h*kg + kg - 1). The row is loaded whole into
 // registers (CPL 16-byte vectors per lane) before any store is issued.
-// Cache policy, measured on MI355X for this 1-read : K-write pattern: plain
-// loads with streaming (nontemporal) stores move about 6.0 TB/s, against
-// 4.9 TB/s with both streaming.
-template <int CPL>
+// Cache policy: plain loads. The stores are streaming (nontemporal) when a
+// row goes to many slots (STREAM) and plain otherwise; measured on whole
+// passes (graph replay, same box), streaming stores won at six copies per
+// row (DeepSeek-V2 shape: 573.5 against 587.9 us) and plain ones at two
+// (FoE: 664.4-665.7 against 678.1-678.9 us; Mixtral: 94.6-95.2 against
+// 99.0-99.5 us, where the combine then also finds disp in cache). Both
+// streaming moved 4.9 TB/s against 6.0 TB/s in a probe of the six-copy case.
+constexpr int kPermStreamCopies = 4;  // copies per row from which stores stream
+
+template <int CPL, bool STREAM>
 __global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __restrict__ src,
                                                              int64_t n, int K, int H, int d,
                                                              const int* __restrict__ slot_of_pair,
@@ -58,7 +64,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __r
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int v = lane + c * kWave;
-      if (v < nv) st16_stream(dst + 8 * v, x[c]);
+      if (v < nv) {
+        if constexpr (STREAM)
+          st16_stream(dst + 8 * v, x[c]);
+        else
+          st16(dst + 8 * v, x[c]);
+      }
     }
   }
 }
@@ -103,9 +114,16 @@ ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, i
   if (st != ROUTE_OK || !src || n == 0) return st;
   if (d > 16 * 8 * kWave) return ROUTE_ERR_UNSUPPORTED;
   const unsigned grid = ceil_div(n * H, kPermThreads / kWave);
+  const bool stream = K / H >= kPermStreamCopies;
   switch (cpl_for(d / 8)) {
-#define ROUTE_CPL_CASE(c) \
-  case c: permute_move<c><<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair, disp); break;
+#define ROUTE_CPL_CASE(c)                                                                     \
+  case c:                                                                                     \
+    if (stream)                                                                               \
+      permute_move<c, true><<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair, disp); \
+    else                                                                                      \
+      permute_move<c, false><<<grid, kPermThreads, 0, s>>>(src, n, K, H, d, slot_of_pair,     \
+                                                           disp);                             \
+    break;
     ROUTE_CPL_CASE(1) ROUTE_CPL_CASE(2) ROUTE_CPL_CASE(4) ROUTE_CPL_CASE(8) ROUTE_CPL_CASE(10)
     ROUTE_CPL_CASE(16)
 #undef ROUTE_CPL_CASE
