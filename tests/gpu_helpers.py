@@ -31,9 +31,27 @@ def rel_err_rowfloor(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref) / den)) if got.size else 0.0
 
 
-def assert_rel(got, ref, tol, what):
+def floor_only(got, ref, tol) -> int:
+    """How many elements meet |got - ref| <= tol * rms(row of ref) but not
+    |got - ref| <= tol * |ref|: those the row floor alone lets through
+    (reference values near zero, where a relative error has no meaning)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(got - ref)
+    return int(np.count_nonzero(diff > tol * np.abs(ref)))
+
+
+def assert_rel(got, ref, tol, what, max_floor_frac=None):
+    """Row-floored relative error within ``tol``; prints how many elements
+    pass only through the floor and, when ``max_floor_frac`` is given, bounds
+    that share."""
     e = rel_err_rowfloor(got, ref)
     assert e <= tol, f"{what}: max relative error {e:.3e} > {tol:.1e}"
+    nf = floor_only(got, ref, tol)
+    size = max(np.size(ref), 1)
+    print(f"{what}: max rel err {e:.3e}; {nf} of {np.size(ref)} elements within the row floor only")
+    if max_floor_frac is not None:
+        assert nf <= max_floor_frac * size, f"{what}: {nf} elements pass only through the floor"
     return e
 
 
@@ -48,11 +66,13 @@ def bf16_ulps(got_bits: np.ndarray, ref: np.ndarray) -> int:
     return int(np.max(np.abs(line(got) - line(want)))) if got.size else 0
 
 
-def assert_bf16(got_bits, ref, what, floor=1e-3):
+def assert_bf16(got_bits, ref, what, floor=1e-3, max_floor_frac=1e-3):
     """bf16 outputs against a float64 reference: each element within one bf16
     ulp of the reference's nearest-even rounding, or within floor * rms(row of
     the reference) where the sum cancels (near zero one bf16 ulp is smaller
-    than the binary32 accumulation error)."""
+    than the binary32 accumulation error). The elements that pass only
+    through that floor are counted, printed and bounded: at most
+    ``max_floor_frac`` of all elements. Returns the count."""
     want = round_bf16(ref).astype(np.int64)
     got = np.asarray(got_bits).astype(np.int64)
     line = lambda b: np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
@@ -62,6 +82,10 @@ def assert_bf16(got_bits, ref, what, floor=1e-3):
     near = np.abs(bf16_to_f64(got_bits) - ref) <= floor * rms
     bad = (ulps > 1) & ~near
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp / {floor} rms; max ulps {int(ulps.max())}"
+    nf = int(np.count_nonzero((ulps > 1) & near))
+    print(f"{what}: {nf} of {ulps.size} elements beyond 1 ulp, within {floor} x row rms")
+    assert nf <= max_floor_frac * max(ulps.size, 1), f"{what}: {nf} elements pass only through the floor"
+    return nf
 
 
 def sync():

@@ -83,29 +83,45 @@ def test_qgate_topk_is_route_topk_of_its_logits(n, d, E, K, affine):
     opt = lambda a: None if a is None else dev(a)
     lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
     idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, opt(g), opt(b), 1e-5, logits=lg)
+    # the oracle's top-K on the kernel's own logits, bit for bit
+    assert np.array_equal(host(idx), oracle.route_topk(host(lg), K, 1, 1)[0])
     want, _ = tr.route_topk(lg, K, 1, 1)
-    assert np.array_equal(host(idx), host(want))              # the same picks, bit for bit
+    assert np.array_equal(host(idx), host(want))              # and route_topk's picks
     same = host(tr.route_qgate(dev(r), dev(dv), dev(w), opt(g), opt(b), 1e-5))
     assert np.array_equal(host(lg), same)                     # the same logits as route_qgate
     idx2 = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, opt(g), opt(b), 1e-5)   # no logits
     assert np.array_equal(host(idx2), host(idx))
 
 
-def test_qgate_topk_ties_and_signed_zeros():
+@pytest.mark.parametrize("zero_rows", [False, True])
+def test_qgate_topk_ties_and_signed_zeros(zero_rows):
     """W rows repeated and zeroed give equal logits and signed zeros; the
-    picks follow route_topk (lower column on equal logits, -0.0 == +0.0)."""
+    picks are the oracle's on the kernel's logits (lower column on equal
+    logits, -0.0 == +0.0) and route_topk's. With ``zero_rows`` only six W
+    rows are nonzero (0-4 and 7), so every row's top 8 reaches into the zero logits and
+    the tie rule decides most of its picks."""
     n, d, E, K = 64, 1024, 64, 8
     r, dv, _, _, w = _case(n, d, E, False, 9)
-    w[10] = w[3]
-    w[40] = w[3]
     w[20] = 0
     w[21] = 0
-    w[22] = 0x8000                         # a row of -0.0: its logits are signed zeros
+    w[22] = 0x8000                         # a row of -0.0
+    tied = (10, 40)
+    if zero_rows:
+        w[5:] = 0
+        w[5::2] = 0x8000
+        tied = (7,)
+    for c in tied:
+        w[c] = w[3]
     lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
     idx = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, logits=lg)
+    lgh = host(lg)
+    assert all((lgh[:, c] == lgh[:, 3]).all() for c in tied) and (lgh[:, 22] == 0).all()  # ties exist
+    picks = host(idx)
+    if zero_rows:
+        assert (np.take_along_axis(lgh, picks, 1) == 0).sum() >= n   # zero logits are picked
+    assert np.array_equal(picks, oracle.route_topk(lgh, K, 1, 1)[0])
     want, _ = tr.route_topk(lg, K, 1, 1)
-    assert np.array_equal(host(idx), host(want))
-
+    assert np.array_equal(picks, host(want))
 
 
 @pytest.mark.parametrize("n,d,E,K", [(1, 2048, 128, 8), (8192, 2048, 128, 8), (37, 1024, 8, 2),
