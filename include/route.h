@@ -227,6 +227,27 @@ int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
 size_t moe_permute_workspace_size(int64_t n, int32_t K, int32_t E);
 
 /*
+ * moe_permute_noalloc - moe_permute without a workspace argument and without
+ * any allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, outputs, status codes and device bits as moe_permute, minus ws.
+ * The sort's histogram table lives in a static device array of 512 KiB
+ * (128 chunks x 1024 experts of int32) that each GPU holds until the process
+ * ends; it is found on the first call for the GPU of stream s (a
+ * hipGetSymbolAddress with that GPU current) and is fully rewritten by every
+ * call, so nothing needs clearing. All calls on one GPU share that array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.
+ * Errors: those of moe_permute; WORKSPACE if the table would exceed the
+ * array (not reachable within the supported E and n*K); HIP if the array's
+ * address cannot be found; UNSUPPORTED for a device ordinal above 63.
+ */
+int moe_permute_noalloc(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                        const uint16_t* src, int32_t d, int32_t* expert_offsets,
+                        int32_t* slot_of_pair, int32_t* pair_of_slot, uint16_t* disp,
+                        uint32_t* err, hipStream_t s);
+
+/*
  * moe_combine - weighted combine of the expert outputs, with the SAG unshuffle.
  * [SMOE] section 1 (combine returns expert outputs to the token and sums
  * them) and section 3.1 (SAG, the inverse shuffle: out_row); [FOE] (the K

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -131,6 +131,22 @@ def test_permute_and_combine_errors(L):
     assert g(A, A, None, 100, 6, 64, None, A, 0, None, None) == NULL
     assert g(A, A, A, 100, 17, 64, None, A, 0, None, None) == UNSUP
     assert g(A, A, A, 0, 6, 64, None, A, 0, None, None) == OK
+
+
+def test_permute_noalloc_errors(L):
+    """The host checks of moe_permute, all made before the static scratch is
+    looked up (so none of these reaches the GPU)."""
+    f = L.moe_permute_noalloc
+    assert f(A, 1000, 6, 160, 1, A, 64, A, A, A, None, None, None) == NULL   # src w/o disp
+    assert f(A, 1000, 6, 160, 1, A, 64, None, A, A, A, None, None) == NULL   # no offsets
+    assert f(A, 1000, 6, 160, 4, A, 64, A, A, A, A, None, None) == SHAPE    # K % H
+    assert f(A, 1000, 6, 160, 1, A, 60, A, A, A, A, None, None) == SHAPE    # d % 8
+    assert f(A, 1000, 17, 160, 1, None, 0, A, A, A, None, None, None) == UNSUP
+    assert f(A, 1000, 6, 2000, 1, None, 0, A, A, A, None, None, None) == UNSUP
+    assert f(A, 1000, 6, 160, 1, A, 64, A, A, A, MIS, None, None) == ALIGN
+    # the 512 KiB table covers the largest supported sort (n*K < 2^31, E <= 1024)
+    assert L.moe_permute_workspace_size((1 << 31) // 16 - 1, 16, 1024) <= 512 * 1024
+    assert L.moe_permute_workspace_size((1 << 31) // 16 - 1, 16, 1024) == 512 * 1024
 
 
 def test_predict_lut_errors(L):

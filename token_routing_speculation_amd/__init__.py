@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "RouteError", "lib", "library_path",
     "route_predict", "route_lut_build", "srs_shuffle", "srs_shuffle_gate", "route_gate", "route_topk",
-    "lar_count", "moe_permute", "moe_combine", "route_qhidden", "route_estimator",
+    "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "route_qhidden",
+    "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
     "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
@@ -57,6 +58,8 @@ EXPORTS = {
     "lar_count": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
     "moe_permute": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_permute_noalloc": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p,
+                                           _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
     "route_qhidden": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p]),
     "route_qgate": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _p, _p]),
@@ -293,6 +296,32 @@ def moe_permute(idx, E, src=None, H=1, expert_offsets=None, slot_of_pair=None, p
           _dev(pair_of_slot, torch.int32, "pair_of_slot", n * K),
           _opt(disp, bt, "disp", n * K * d if src is not None else None),
           _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return expert_offsets, slot_of_pair, pair_of_slot, disp
+
+
+def moe_permute_noalloc(idx, E, src=None, H=1, expert_offsets=None, slot_of_pair=None,
+                        pair_of_slot=None, disp=None, err=None, stream=None):
+    """moe_permute on the library's static per-GPU scratch (no workspace). With
+    every output passed in, nothing is allocated on either side of the call."""
+    n, K = idx.shape
+    expert_offsets = _empty((E + 1,), torch.int32, idx) if expert_offsets is None else expert_offsets
+    slot_of_pair = _empty((n * K,), torch.int32, idx) if slot_of_pair is None else slot_of_pair
+    pair_of_slot = _empty((n * K,), torch.int32, idx) if pair_of_slot is None else pair_of_slot
+    d = 0
+    if src is not None:
+        if src.dim() == 2:
+            src = src.unsqueeze(0)
+        if src.shape[0] != H or src.shape[1] != n:
+            raise ValueError("src must be [H][n][d]")
+        d = src.shape[2]
+        disp = _empty((n * K, d), _bf16(src), idx) if disp is None else disp
+    bt = _bf16(src) if src is not None else torch.bfloat16
+    _call("moe_permute_noalloc", _dev(idx, torch.int32, "idx"), n, K, E, H, _opt(src, bt, "src"), d,
+          _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+          _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K),
+          _dev(pair_of_slot, torch.int32, "pair_of_slot", n * K),
+          _opt(disp, bt, "disp", n * K * d if src is not None else None),
+          _opt(err, torch.int32, "err", 1), _stream(stream))
     return expert_offsets, slot_of_pair, pair_of_slot, disp
 
 

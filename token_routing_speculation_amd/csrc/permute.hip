@@ -4,6 +4,8 @@
 // by expert (csort.hpp) followed by a row scatter. With H groups ("Federation
 // of Experts (FoE)" article) pair (i, k) reads the group-(k / (K/H)) row of
 // token i, so each source row is read once and written K/H times.
+#include <mutex>
+
 #include "common.hpp"
 #include "csort.hpp"
 
@@ -80,6 +82,39 @@ inline int cpl_for(int nv) {
   return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 10 ? 10 : 16;
 }
 
+// Scratch of moe_permute_noalloc: the sort's chunk-major histogram table at
+// its largest, kMaxChunks chunks x kMaxExperts bins of int32 (512 KiB). Every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code this name stands for the host-side shadow, not a device address: host
+// code only ever uses the per-device address from hipGetSymbolAddress.
+constexpr size_t kPermScratchBytes = static_cast<size_t>(kMaxChunks) * kMaxExperts * sizeof(int);
+static __device__ __align__(256) unsigned char scratch[kPermScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the GPU that stream s runs on, looked up
+// with that GPU current on the first call for it and kept afterwards.
+int scratch_address(hipStream_t s, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ROUTE_ERR_HIP;
+  int dev = cur;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return ROUTE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ROUTE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ROUTE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return ROUTE_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return ROUTE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ROUTE_OK;
+}
+
 }  // namespace route
 
 using namespace route;
@@ -89,24 +124,36 @@ ROUTE_API size_t moe_permute_workspace_size(int64_t n, int32_t K, int32_t E) {
   return csort_ws_bytes(n * K, E);
 }
 
-ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
-                          const uint16_t* src, int32_t d, int32_t* expert_offsets,
-                          int32_t* slot_of_pair, int32_t* pair_of_slot, uint16_t* disp,
-                          void* ws, size_t ws_bytes, uint32_t* err, hipStream_t s) {
+// Host checks shared by both entry points (everything but the workspace).
+static int permute_check(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                         const uint16_t* src, int32_t d, const int32_t* expert_offsets,
+                         const int32_t* slot_of_pair, const int32_t* pair_of_slot,
+                         const uint16_t* disp) {
   if (n < 0 || K < 1 || E < 1 || H < 1 || K % H != 0) return ROUTE_ERR_SHAPE;
   if (n * static_cast<int64_t>(K) >= (int64_t(1) << 31)) return ROUTE_ERR_SHAPE;
   if (E > kMaxExperts || K > kMaxK) return ROUTE_ERR_UNSUPPORTED;
   if (!expert_offsets) return ROUTE_ERR_NULL;
-  if (n == 0) {
-    fill_i32<<<ceil_div(E + 1, 256), 256, 0, s>>>(expert_offsets, E + 1, 0);
-    return launch_status();
-  }
+  if (n == 0) return ROUTE_OK;
   if (!idx || !slot_of_pair || !pair_of_slot) return ROUTE_ERR_NULL;
   if ((src == nullptr) != (disp == nullptr)) return ROUTE_ERR_NULL;
   if (src) {
     if (d < 8 || d % 8 != 0) return ROUTE_ERR_SHAPE;
     if (d > 16 * 8 * kWave) return ROUTE_ERR_UNSUPPORTED;
     if (!aligned16(src) || !aligned16(disp)) return ROUTE_ERR_ALIGN;
+  }
+  return ROUTE_OK;
+}
+
+ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                          const uint16_t* src, int32_t d, int32_t* expert_offsets,
+                          int32_t* slot_of_pair, int32_t* pair_of_slot, uint16_t* disp,
+                          void* ws, size_t ws_bytes, uint32_t* err, hipStream_t s) {
+  const int chk = permute_check(idx, n, K, E, H, src, d, expert_offsets, slot_of_pair,
+                                pair_of_slot, disp);
+  if (chk != ROUTE_OK) return chk;
+  if (n == 0) {
+    fill_i32<<<ceil_div(E + 1, 256), 256, 0, s>>>(expert_offsets, E + 1, 0);
+    return launch_status();
   }
   if (!ws || ws_bytes < moe_permute_workspace_size(n, K, E)) return ROUTE_ERR_WORKSPACE;
   int st = csort_launch<int32_t>(idx, n * K, E, expert_offsets, slot_of_pair, pair_of_slot,
@@ -130,4 +177,23 @@ ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, i
     default: return ROUTE_ERR_UNSUPPORTED;
   }
   return launch_status();
+}
+
+ROUTE_API int moe_permute_noalloc(const int32_t* idx, int64_t n, int32_t K, int32_t E, int32_t H,
+                                  const uint16_t* src, int32_t d, int32_t* expert_offsets,
+                                  int32_t* slot_of_pair, int32_t* pair_of_slot, uint16_t* disp,
+                                  uint32_t* err, hipStream_t s) {
+  // every host check before the scratch is looked up; n = 0 needs no scratch
+  const int chk = permute_check(idx, n, K, E, H, src, d, expert_offsets, slot_of_pair,
+                                pair_of_slot, disp);
+  if (chk != ROUTE_OK) return chk;
+  if (n == 0)
+    return moe_permute(idx, n, K, E, H, src, d, expert_offsets, slot_of_pair, pair_of_slot, disp,
+                       nullptr, 0, err, s);
+  if (moe_permute_workspace_size(n, K, E) > kPermScratchBytes) return ROUTE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_address(s, &ws);
+  if (st != ROUTE_OK) return st;
+  return moe_permute(idx, n, K, E, H, src, d, expert_offsets, slot_of_pair, pair_of_slot, disp,
+                     ws, kPermScratchBytes, err, s);
 }
