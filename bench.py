@@ -97,7 +97,7 @@ def measured_traffic(workload: str, path=TRAFFIC_FILE, sources=TRAFFIC_SOURCES):
     return (rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
 
 
-def _oracle_passes(name, inp, tables, n_sample, min_seconds):
+def _oracle_passes(name, inp, tables, min_seconds):
     import oracle.pipeline as op
     passes, dt = 0, 0.0
     while dt < min_seconds:
@@ -111,28 +111,39 @@ def _oracle_passes(name, inp, tables, n_sample, min_seconds):
     return passes, dt
 
 
-def cpu_baseline(name: str, n_sample: int, min_seconds: float = 10.0):
-    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
-    same workload: n_sample tokens drawn with the workload's recipe, full
-    passes repeated until min_seconds of host time have been spent. Run with
-    the BLAS pool at its default size (the reported value) and again with
-    one thread (threadpoolctl limits the pool in-process)."""
-    from threadpoolctl import threadpool_info, threadpool_limits
-    from synth import make_config_inputs
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+
+
+def cpu_baseline(name: str, inp: dict, n_sample: int, min_seconds: float = 10.0):
+    """The oracle (float64 NumPy, as it stands) on the first n_sample tokens
+    of the benchmarked batch itself, full passes repeated until min_seconds of
+    host time have been spent. Run with the BLAS pool at its default size (the
+    reported value) and again with one thread (threadpoolctl limits the pool
+    in-process)."""
+    from threadpoolctl import threadpool_limits
+    from synth import first_tokens
     import oracle.pipeline as op
 
-    inp = make_config_inputs(name, N=n_sample)
-    tables = None if name == "foe" else op.build_tables(inp)
-    passes, dt = _oracle_passes(name, inp, tables, n_sample, min_seconds)
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    sub = first_tokens(inp, n_sample)
+    n = sub["N"]
+    tables = None if name == "foe" else op.build_tables(sub)
+    passes, dt = _oracle_passes(name, sub, tables, min_seconds)
+    threads = blas_threads()
     with threadpool_limits(limits=1):
-        passes1, dt1 = _oracle_passes(name, inp, tables, n_sample, min_seconds / 2)
-    return {"value": passes * n_sample / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{passes} full passes over {n_sample} tokens of the {name} workload "
-                      f"(float64 NumPy; BLAS on {threads} threads, elementwise steps "
-                      f"single-threaded); {dt:.1f} s",
-            "value_1_thread": passes1 * n_sample / dt1,
+        passes1, dt1 = _oracle_passes(name, sub, tables, min_seconds / 2)
+    return {"value": passes * n / dt, "unit": "tokens/s", "cores": host_cores(),
+            "blas_threads": threads, "kind": "oracle",
+            "sample": f"{passes} full passes over the first {n} of the {inp['N']} benchmarked "
+                      f"tokens of the {name} workload (float64 NumPy; matrix products on "
+                      f"{threads} BLAS threads, elementwise steps on one); {dt:.1f} s",
+            "value_1_thread": passes1 * n / dt1,
             "sample_1_thread": f"{passes1} passes with the BLAS pool limited to 1 thread; "
                                f"{dt1:.1f} s"}
 
@@ -304,15 +315,14 @@ def fit_estimator(cfg, l, lay, n_train, ridge, time_oracle=False):
             "solve_ms": t[2], "weights_ms": t[3]}
     if time_oracle:
         # the oracle's float64 fit (Gram, LAPACK solve, rounding) on the same features
-        from threadpoolctl import threadpool_info
         from oracle import estfit as oest
         h_np = h.view(torch.int16).cpu().numpy().view(np.uint16)
         y_np = y.cpu().numpy()
         t0 = time.perf_counter()
         ow2, _, _ = oest.est_fit(h_np, y_np, ridge)
-        threads = max([p_.get("num_threads", 1) for p_ in threadpool_info()] or [1])
         info["cpu_baseline"] = {"value": (time.perf_counter() - t0) * 1e3, "unit": "ms per fit",
-                                "cores": int(threads), "kind": "oracle",
+                                "cores": host_cores(), "blas_threads": blas_threads(),
+                                "kind": "oracle",
                                 "sample": "the same layer's fit, once (float64 NumPy and LAPACK)",
                                 "bf16_codes_equal": float((ow2 == lay["w2"]).mean())}
     return info
@@ -347,9 +357,10 @@ def predictor_setup(cfg, args):
 
 def predictor_cpu_baseline(cfg, n_sample, min_seconds=10.0):
     """The oracle's prediction step (q_l, the next gate or the estimator,
-    top-K, hits against the precomputed truth) on n_sample tokens of one gate
-    layer and one estimator layer, weighted to the sweep's mix of layers."""
-    from threadpoolctl import threadpool_info
+    top-K, hits against the precomputed truth) on the first n_sample tokens of
+    one benchmarked gate layer and one estimator layer, weighted to the
+    sweep's mix of layers."""
+    from synth import first_tokens
     from synth.gen import make_predictor_layer
     import oracle
 
@@ -364,7 +375,7 @@ def predictor_cpu_baseline(cfg, n_sample, min_seconds=10.0):
         return oracle.hit_count(pred, truth)
 
     est_l, gate_l = cfg.est_layers[0], cfg.L - 2
-    lays = {l: make_predictor_layer(cfg, l, N=n_sample) for l in (est_l, gate_l)}
+    lays = {l: first_tokens(make_predictor_layer(cfg, l), n_sample) for l in (est_l, gate_l)}
     truths = {l: oracle.route_topk(oracle.route_gate(lay["s_next"], lay["w_next"]), cfg.K, 1, 1)[0]
               for l, lay in lays.items()}
     spent = {est_l: [0.0, 0], gate_l: [0.0, 0]}
@@ -381,18 +392,30 @@ def predictor_cpu_baseline(cfg, n_sample, min_seconds=10.0):
     ne = len(cfg.est_layers)
     per_layer = {l: spent[l][0] / spent[l][1] for l in spent}
     per_token = (ne * per_layer[est_l] + (nl - ne) * per_layer[gate_l]) / nl / n_sample
-    threads = max([p_.get("num_threads", 1) for p_ in threadpool_info()] or [1])
-    return {"value": 1.0 / per_token, "unit": "token-predictions/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n_sample} tokens of layer {gate_l} (gate) and layer {est_l} (estimator), "
-                      f"{spent[gate_l][1]} + {spent[est_l][1]} passes, weighted {nl - ne}:{ne}; "
-                      f"{t_all:.1f} s (float64 NumPy, BLAS on {threads} threads)"}
+    threads = blas_threads()
+    return {"value": 1.0 / per_token, "unit": "token-predictions/s", "cores": host_cores(),
+            "blas_threads": threads, "kind": "oracle",
+            "sample": f"the first {n_sample} benchmarked tokens of layer {gate_l} (gate) and layer "
+                      f"{est_l} (estimator), {spent[gate_l][1]} + {spent[est_l][1]} passes, "
+                      f"weighted {nl - ne}:{ne}; {t_all:.1f} s (float64 NumPy, matrix products on "
+                      f"{threads} BLAS threads)"}
 
 
 PREDICTOR_WORKLOAD = "qwen3-30b-a3b-shaped predictor"
 
 
 def predictor_bench(args):
+    """The q_l predictor sweep as its own bench line, with the oracle timed on
+    the first tokens of the same layers."""
+    from synth import get_config
+    out = predictor_measure(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = predictor_cpu_baseline(get_config("qwen3"), min(args.cpu_sample, 1024))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def predictor_measure(args):
     """The q_l predictor of "Speculating Experts Accelerates Inference for
     Mixture-of-Experts" (technical summary items 2.A, 2.C and 4) over all
     source layers of the Qwen3-30B-A3B-shaped workload: per layer q_l = LN(d_l
@@ -437,10 +460,14 @@ def predictor_bench(args):
             graph.replay()
             ev[k + 1].record(stream)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[K]) / K, time.perf_counter() - wall0
+        wall = time.perf_counter() - wall0
+        per = [ev[k].elapsed_time(ev[k + 1]) for k in range(K)]
+        cold = cold_times(graph.replay, K) if fused else None
+        del graph
+        return ev[0].elapsed_time(ev[K]) / K, wall, per, cold
 
-    ms_unfused, _ = timed(False)
-    ms, wall = timed(True)
+    ms_unfused, _, _, _ = timed(False)
+    ms, wall, per_sweep, cold_sweep = timed(True)
     # per-stage times of one eager sweep, on an estimator layer and a gate layer
     def stage_times(i):
         p.layer, p.truth = layers[i], truths[i]
@@ -535,6 +562,8 @@ def predictor_bench(args):
                    "E": cfg.E, "K": cfg.K, "estimator_layers": list(cfg.est_layers), "hd": cfg.hd},
         "hbm_frac_sweep": total_bytes / (ms * 1e-3) / HBM_PEAK,
         "alg_bytes_sweep": total_bytes,
+        "sweep_ms_p10_p50_p90": pct(per_sweep),
+        "cold_sweep_ms_p10_p50_p90": pct(cold_sweep),
         "gate_layers": "route_qgate_topk with the hit count (q_l and the logits kept on chip)",
         "unfused": {"ms_per_step": ms_unfused, "value": N * nl / (ms_unfused * 1e-3),
                     "alg_bytes_sweep": total_unfused,
@@ -559,10 +588,7 @@ def predictor_bench(args):
         "hit_rate_per_estimator_layer": [round(r, 4) for r, e_ in zip(rates, est) if e_],
         "wall_s_timed": wall,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = predictor_cpu_baseline(cfg, min(args.cpu_sample, 1024))
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
 PCIE_PEAK = 64.0e9           # PCIe 5.0 x16 host link, bytes/s per direction (32 GT/s x 16 lanes)
@@ -784,6 +810,8 @@ def main(argv=None):
                     choices=["tiny", "mixtral", "deepseek", "foe", "qwen3"])
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="deepseek: leave the other four workloads out of the line")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the pass replayed as a HIP graph)")
     ap.add_argument("--eg", action="store_true",
@@ -826,9 +854,62 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
     torch.cuda.set_device(0)
-    cfg = get_config(args.config)
-    inp = make_config_inputs(args.config)
-    if args.config == "foe":
+    out, inp = route_measure(args, args.config)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, inp, min(args.cpu_sample, out["config"]["N"]))
+    del inp
+    if args.config == "deepseek" and not args.no_workloads:
+        # the other four workloads, each timed the same way (no CPU baseline)
+        wl = {}
+        for name in ("tiny", "mixtral", "foe"):
+            o, _ = route_measure(args, name)
+            wl[name] = workload_summary(o)
+            torch.cuda.empty_cache()
+        o = predictor_measure(args)
+        wl["qwen3"] = predictor_summary(o)
+        out["workloads"] = wl
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def workload_summary(o: dict) -> dict:
+    """The figures of one routing or FoE workload kept in the default line."""
+    return {"config": o["config"], "tokens_per_s": o["value"], "ms_per_pass": o["ms_per_step"],
+            "warm_pass_ms_p50": o["pass_ms_p10_p50_p90"][1] if o["pass_ms_p10_p50_p90"] else None,
+            "cold_pass_ms_p50": (o["cold_pass_ms_p10_p50_p90"][1]
+                                 if o["cold_pass_ms_p10_p50_p90"] else None),
+            "alg_bytes_pass": o["alg_bytes_pass"], "hbm_frac_pass": o["hbm_frac_pass"],
+            "stages_us": o["stages_us"], "stage_hbm_frac": o["stage_hbm_frac"],
+            "dominant_kernel": {k: o["roofline"][k] for k in ("kernel", "achieved", "unit", "frac")},
+            "lar": o["lar"]}
+
+
+def predictor_summary(o: dict) -> dict:
+    """The figures of the q_l predictor sweep kept in the default line."""
+    return {"config": o["config"], "token_predictions_per_s": o["value"],
+            "ms_per_sweep": o["ms_per_step"],
+            "sweep_ms_p10_p50_p90": o["sweep_ms_p10_p50_p90"],
+            "cold_sweep_ms_p10_p50_p90": o["cold_sweep_ms_p10_p50_p90"],
+            "alg_bytes_sweep": o["alg_bytes_sweep"], "hbm_frac_sweep": o["hbm_frac_sweep"],
+            "dominant_kernel": {k: o["roofline"][k] for k in ("kernel", "achieved", "unit", "frac")},
+            "estimator_mfma_frac": o["estimator_mfma_frac"],
+            "hit_rate_gate_layers": o["hit_rate_gate_layers"],
+            "hit_rate_estimator_layers": o["hit_rate_estimator_layers"]}
+
+
+def route_measure(args, name):
+    """One routing (tiny, mixtral, deepseek) or FoE workload: per-stage event
+    times over eager passes, then the pass captured as a HIP graph and timed
+    warm (replayed back to back) and cold (a 512 MiB read before each pass).
+    Returns the bench line's fields (without the CPU baseline) and the
+    inputs."""
+    import torch
+    from synth import make_config_inputs, get_config
+    from token_routing_speculation_amd.pipeline import RoutePass, FoEPass, capture_graph
+
+    cfg = get_config(name)
+    inp = make_config_inputs(name)
+    if name == "foe":
         p = FoEPass(inp)
         bytes_st = foe_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.H)
         conf = {"workload": "foe-grouped", "N": cfg.N, "d": cfg.d, "E": cfg.E, "H": cfg.H,
@@ -836,7 +917,7 @@ def main(argv=None):
     else:
         p = RoutePass(inp)
         bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.fused)
-        conf = {"workload": ROUTE_WORKLOADS[args.config], "N": cfg.N, "d": cfg.d, "E": cfg.E,
+        conf = {"workload": ROUTE_WORKLOADS[name], "N": cfg.N, "d": cfg.d, "E": cfg.E,
                 "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
                 "fallback": "2-gram" if p.fallback else "none"}
     stages = p.STAGES
@@ -847,6 +928,7 @@ def main(argv=None):
     calib = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     calib_dst = torch.empty_like(calib)
     calib_dst.copy_(calib)
+    del calib, calib_dst
 
     for _ in range(args.warmup):
         p.step()
@@ -861,16 +943,16 @@ def main(argv=None):
     wall0 = time.perf_counter()
     t_start.record(stream)
     for k in range(K):
-        for s, name in enumerate(stages):
+        for s, st in enumerate(stages):
             ev[k][s].record(stream)
-            getattr(p, name)()
+            getattr(p, st)()
         ev[k][len(stages)].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_eager = t_start.elapsed_time(t_end) / K
-    st_us = {name: 1e3 * sum(ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)) / K
-             for s, name in enumerate(stages)}
+    st_us = {st: 1e3 * sum(ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)) / K
+             for s, st in enumerate(stages)}
     ms = ms_eager
     per_pass = cold = None
     if not args.no_graph:
@@ -890,24 +972,8 @@ def main(argv=None):
         wall = time.perf_counter() - wall0
         ms = ge[0].elapsed_time(ge[K]) / K
         per_pass = [ge[k].elapsed_time(ge[k + 1]) for k in range(K)]
-        # cold protocol: a 512 MiB read before every timed pass, so nothing a
-        # previous pass left in the 256 MB memory-side cache helps. The scrub
-        # only reads (the cache then holds clean lines): a writing scrub would
-        # charge the write-back of its own dirty lines to the pass.
-        scrub = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
-        sink = torch.zeros((), dtype=torch.float32, device="cuda")
-        for _ in range(3):
-            torch.sum(scrub, dim=0, out=sink)
-        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)]
-        for k in range(K):
-            torch.sum(scrub, dim=0, out=sink)
-            ce[k][0].record(stream)
-            graph.replay()
-            ce[k][1].record(stream)
-        torch.cuda.synchronize()
-        cold = [a.elapsed_time(b) for a, b in ce]
-        del scrub, sink
+        cold = cold_times(graph.replay, K)
+        del graph
 
     N = cfg.N
     tokens_per_s = N / (ms * 1e-3)
@@ -948,12 +1014,30 @@ def main(argv=None):
         "lar": lar_rate(p, N * cfg.K),
         "wall_s_timed": wall,
     }
-    if not args.no_cpu_baseline and args.config != "tiny":
-        out["cpu_baseline"] = cpu_baseline(args.config, min(args.cpu_sample, N))
-    elif not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.config, N)
-    print(json.dumps(out), flush=True)
-    return 0
+    del p
+    return out, inp
+
+
+def cold_times(replay, K):
+    """Per-pass times (ms) of K replays, each after a 512 MiB read, so nothing
+    a previous pass left in the 256 MB memory-side cache helps. The scrub only
+    reads (the cache then holds clean lines): a writing scrub would charge the
+    write-back of its own dirty lines to the pass."""
+    import torch
+    stream = torch.cuda.current_stream()
+    scrub = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        torch.sum(scrub, dim=0, out=sink)
+    ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for k in range(K):
+        torch.sum(scrub, dim=0, out=sink)
+        ce[k][0].record(stream)
+        replay()
+        ce[k][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ce]
 
 
 if __name__ == "__main__":

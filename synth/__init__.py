@@ -20,6 +20,7 @@ from .gen import (
     make_foe_inputs,
     make_predictor_layer,
     make_config_inputs,
+    first_tokens,
     default_expert_cluster,
     foe_row_cluster,
 )
@@ -37,6 +38,7 @@ __all__ = [
     "make_foe_inputs",
     "make_predictor_layer",
     "make_config_inputs",
+    "first_tokens",
     "default_expert_cluster",
     "foe_row_cluster",
 ]

@@ -187,6 +187,25 @@ def make_predictor_layer(cfg: PredictorConfig, l: int, N=None, sample=0):
     return out
 
 
+def first_tokens(inp: dict, n: int) -> dict:
+    """The first n tokens of a drawn batch (route, FoE or predictor layer):
+    every per-token array cut to its first n tokens, every table and weight
+    kept as it is. A batch drawn with N=n is not this one (the P-way split
+    draws all N tokens of a part before the next part)."""
+    N = inp["N"]
+    n = min(n, N)
+    out = dict(inp, N=n)
+    for k in ("tok", "prev2", "prev1", "r", "s_next"):
+        if k in inp:
+            out[k] = inp[k][:n]
+    for k in ("partials", "x"):
+        if k in inp:
+            out[k] = np.ascontiguousarray(inp[k][:, :n])
+    if "row_cluster" in inp:
+        out["row_cluster"] = inp["row_cluster"][: n * inp["H"]]
+    return out
+
+
 def make_config_inputs(name: str, N=None, sample=0):
     """Inputs of a named workload (route or FoE); N overrides the token count;
     ``sample`` > 0 draws another batch of a routing workload's model."""

@@ -54,3 +54,19 @@ def test_foe_and_predictor_shapes():
     assert lay["estimator"] and lay["w1"].shape == (512, 2048) and lay["w2"].shape == (128, 512)
     lay = make_predictor_layer(cfg, 10, N=16)
     assert not lay["estimator"] and lay["s_next"].shape == (16, 2048)
+
+
+def test_first_tokens_cuts_every_per_token_array():
+    """first_tokens keeps the first n tokens of a drawn batch: the same ids,
+    partial rows, previous clusters and FoE rows, and every table unchanged."""
+    from synth import first_tokens, make_config_inputs
+    a = make_config_inputs("tiny", N=64)
+    b = first_tokens(a, 10)
+    assert b["N"] == 10 and np.array_equal(b["tok"], a["tok"][:10])
+    assert np.array_equal(b["partials"], a["partials"][:, :10]) and b["partials"].flags.c_contiguous
+    assert b["lut"] is a["lut"] and b["w"] is a["w"]
+    f = make_config_inputs("foe", N=32)
+    g = first_tokens(f, 5)
+    assert np.array_equal(g["x"], f["x"][:, :5]) and len(g["row_cluster"]) == 5 * f["H"]
+    assert np.array_equal(g["row_cluster"], f["row_cluster"][:20])
+    assert first_tokens(a, 1000)["N"] == 64
