@@ -17,6 +17,7 @@ from gpu_helpers import dev, host
 pytestmark = pytest.mark.gpu
 
 LOGIT_TOL = 1e-2
+TWO_CALL_TOL = 1e-5
 
 
 def assert_rel(got, ref, tol, what):
@@ -27,6 +28,7 @@ def assert_rel(got, ref, tol, what):
     ref = np.asarray(ref, np.float64)
     den = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref)))
     e = float(np.max(np.abs(got - ref) / den))
+    print(f"{what}: max relative error {e:.3e}")
     assert e <= tol, f"{what}: max relative error {e:.3e} > {tol:.1e}"
 
 
@@ -56,7 +58,7 @@ def test_qgate(n, d, E, affine):
     q = tr.route_qhidden(dev(r), dev(dv), opt(g), opt(b), 1e-5)
     two = host(tr.route_gate(q, dev(w)))
     ref = oracle.bf16_to_f64(host(q)) @ oracle.bf16_to_f64(w).T   # exact products of the bf16 q
-    assert_rel(got, ref, 1e-5, "qgate vs bf16 q")
+    assert_rel(got, ref, TWO_CALL_TOL, "qgate vs the two-call path's bf16 q")
     assert_rel(two, ref, 1e-5, "two-call vs bf16 q")
 
 

@@ -38,23 +38,6 @@ namespace {
 constexpr int kMmaThreads = 256;  // four waves, 2 x 2 over the tile
 constexpr int kMmaStages = 4;     // LDS stages (K steps of 64) in the ring
 
-// One 16-byte piece per lane from global memory into LDS: lane i writes at
-// lds_base + 16 i (lds_base is wave-uniform). Completion is counted by vmcnt.
-__device__ __forceinline__ void lds_load16(const void* g, char* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
-                                   0);
-#endif
-}
-
-// Waits until at most N of this wave's vector-memory operations are pending
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt untouched).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Waits until this wave's LDS reads have completed.
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));

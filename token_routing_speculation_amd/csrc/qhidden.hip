@@ -163,10 +163,11 @@ __device__ __forceinline__ int qg_off(int rr, int p) {
 // window, so the piece is XOR-ed with (row / 2) % 8.
 __device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ ((rr >> 1) & 7)) << 4); }
 
-// TOPK: also pick each row's top K columns (E <= 256, K <= 16), in
+// TOPK > 0: also pick each row's top K columns (E <= 128 TOPK, K <= 16), in
 // route_topk's order (largest logit first, equal logits to the lower column,
 // -0.0 == +0.0), from the logits gathered in LDS; logits may then be NULL.
-template <int BM, int D, bool TOPK>
+// TOPK = 0: the product alone.
+template <int BM, int D, int TOPK>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   // true pick this lane compares against is loaded now, so its latency
   // overlaps the rest of the kernel
   int tv = -1;
-  if constexpr (TOPK) {
+  if constexpr (TOPK > 0) {
     const int rr = 4 * wv + (lane >> 4);
     if (hits && rr < BM && row0 + rr < n && (lane & 15) < K) tv = truth[(row0 + rr) * K + (lane & 15)];
   }
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
         }
     }
   };
-  if constexpr (!TOPK) {
+  if constexpr (TOPK == 0) {
     for (int g = wv; g < ngroups; g += kQgThreads / kWave) {
       f32x4 acc[MT];
       gemm_group(g, acc);
@@ -313,15 +314,17 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     }
     __syncthreads();
     // a 16-lane segment per row, four rows per wave (rows 4 wv + seg): lane
-    // s of a segment holds columns s, s + 16, ...; K rounds of a segment max
-    // of the keys, equal keys resolved to the lowest column
+    // s of a segment holds columns s, s + 16, ... (8 of them for E <= 128);
+    // K rounds of a segment max of the keys, equal keys resolved to the
+    // lowest column
+    constexpr int KPL = 8 * TOPK;  // keys per lane
     const int seg = lane >> 4, sl = lane & 15;
     const int rr = 4 * wv + seg;
     if (4 * wv < BM) {
       const int rrc = rr < BM ? rr : BM - 1;
-      uint32_t key[16];
+      uint32_t key[KPL];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < KPL; ++v) {
         const int c = sl + 16 * v;
         key[v] = c < E ? order_key(lt[rrc * E + c]) : 0u;
       }
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
           uint32_t best = 0u;
           int bv = 0;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
+          for (int v = 0; v < KPL; ++v)
             if (key[v] > best) {  // strict: the lowest v on equal keys
               best = key[v];
               bv = v;
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
               seg_min<16>(best == mx ? static_cast<uint32_t>(sl + 16 * bv) : 0xffffffffu));
           const bool mine = sl == (col & 15);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) key[v] = (mine && bv == v) ? 0u : key[v];
+          for (int v = 0; v < KPL; ++v) key[v] = (mine && bv == v) ? 0u : key[v];
           if (sl == pick) myc = col;
         }
       }
@@ -350,15 +353,24 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
       const bool live = rr < BM && grow < n;
       if (live && sl < K) idx[grow * K + sl] = myc;
       if (hits) {
-        // hit count: a pick counts when it is among the row's true experts
-        // (the picks are distinct columns; a repeated true expert counts once)
-        // every lane takes part in each shuffle (a lane left out would hand
-        // the others no value), so no short-circuit here; K is wave-uniform
-        bool in_truth = false;
-        for (int j = 0; j < K; ++j) {
-          const int tj = __shfl(tv, (lane & ~15) + j, kWave);
-          in_truth |= tj == myc;
+        // hit count: a pick counts when it is among the row's true experts.
+        // The segment ORs its true picks into a bitmask over the columns (a
+        // repeated or foreign true pick sets no extra bit) and each lane
+        // tests its own pick's bit
+        uint32_t mask[KPL / 2];
+#pragma unroll
+        for (int q = 0; q < KPL / 2; ++q) {
+          uint32_t m = (tv >= 32 * q && tv < 32 * q + 32) ? 1u << (tv - 32 * q) : 0u;
+          m |= dpp<kDppXor1>(m);
+          m |= dpp<kDppXor2>(m);
+          m |= dpp<kDppHalfMirror>(m);
+          m |= dpp<kDppMirror>(m);
+          mask[q] = m;
         }
+        uint32_t word = mask[0];
+#pragma unroll
+        for (int q = 1; q < KPL / 2; ++q) word = (myc >> 5) == q ? mask[q] : word;
+        const bool in_truth = (word >> (myc & 31)) & 1u;
         const unsigned long long ball = __ballot(live && sl < K && in_truth);
         if (lane == 0) atomicAdd(hit_lds, static_cast<unsigned>(__popcll(ball)));
       }
@@ -368,6 +380,22 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
       if (threadIdx.x == 0 && *hit_lds) atomicAdd(hits, static_cast<unsigned long long>(*hit_lds));
     }
   }
+}
+
+// 32 rows per workgroup (16 at d = 4096, where the q tile's rows are twice as long)
+template <int TOPK>
+void qgate_launch(int d, int64_t n, hipStream_t s, const uint16_t* r, const float* dvec,
+                  const float* gamma, const float* beta, float eps, const uint16_t* w, int E,
+                  float* logits, int K, int* idx, const int32_t* truth, unsigned long long* hits) {
+  if (d == 1024)
+    qgate_kernel<32, 1024, TOPK><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
+  else if (d == 2048)
+    qgate_kernel<32, 2048, TOPK><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
+  else
+    qgate_kernel<16, 4096, TOPK><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
 }
 
 }  // namespace route
@@ -407,15 +435,7 @@ ROUTE_API int route_qgate(const uint16_t* r, const float* dvec, const float* gam
   if (!r || !dvec || !w || !logits) return ROUTE_ERR_NULL;
   if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
-  if (d == 1024)
-    qgate_kernel<32, 1024, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
-  else if (d == 2048)
-    qgate_kernel<32, 2048, false><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
-  else
-    qgate_kernel<16, 4096, false><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
+  qgate_launch<0>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, 0, nullptr, nullptr, nullptr);
   return launch_status();
 }
 
@@ -431,14 +451,9 @@ ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float
   if (!r || !dvec || !w || !idx || (!truth != !hits)) return ROUTE_ERR_NULL;
   if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
-  if (d == 1024)
-    qgate_kernel<32, 1024, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
-  else if (d == 2048)
-    qgate_kernel<32, 2048, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
+  if (E <= 128)
+    qgate_launch<1>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
   else
-    qgate_kernel<16, 4096, true><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
-        r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
+    qgate_launch<2>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
   return launch_status();
 }
