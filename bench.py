@@ -600,15 +600,20 @@ def prefetch_bench(args):
     Qwen3-30B-A3B-shaped model whose expert weights sit in pinned host memory.
     For each decoded token and source layer l, layer l+1's experts are
     predicted from q_l (the predictor pass) and planned into C = K * batch
-    staging slots. Three schedules of the transfers are timed per token:
+    staging slots. Four schedules of the transfers are timed per token:
       on_demand:   after layer l+1's routing, its true experts are copied
                    (prefetch_copy: the list stays on the GPU, which waits);
-      speculative: the predicted list comes back to pinned host memory and
-                   prefetch_issue copies those experts on a second stream
-                   (DMA engines); layer l+1 waits only for that copy
-                   (speculative execution runs the prefetched experts);
-      prefetch_then_misses: the same, then the true experts that were not
-                   prefetched are copied after routing (no speculative execution).
+      speculative: the predicted experts are copied on a second stream by the
+                   copy kernel, each layer's transfer planned while the one
+                   before it still runs, so the transfers run back to back;
+                   layer l+1 waits only for its copy (speculative execution
+                   runs the prefetched experts);
+      speculative_dma: the same through the DMA engines (prefetch_issue),
+                   the list taken back to pinned host memory while the
+                   previous transfer runs;
+      prefetch_then_misses: the speculative schedule, then the true experts
+                   that were not prefetched are copied after routing (no
+                   speculative execution).
     The layers' own compute (attention, expert FFNs) is not built, so the
     schedules differ only by what they transfer and when. The overlap leg
     runs the N-row predictor sweep (compute) beside the transfers, through
@@ -647,7 +652,11 @@ def prefetch_bench(args):
     misses = torch.empty((T, nl, E), dtype=torch.int32, device="cuda")
     nmisses = torch.zeros((T, nl), dtype=torch.int32, device="cuda")
     covered = torch.zeros((nl,), dtype=torch.int64, device="cuda")
-    comp = torch.cuda.current_stream()
+    # the compute stream is a created one (default priority), made current, so
+    # the schedules can also be captured as graphs on it
+    torch.cuda.synchronize()
+    comp = torch.cuda.Stream()
+    torch.cuda.set_stream(comp)
     copy = torch.cuda.Stream()                     # default priority
     rows = lambda t: slice(t * B, (t + 1) * B)
     ev_plan = [torch.cuda.Event() for _ in range(nl)]
@@ -658,16 +667,35 @@ def prefetch_bench(args):
             tr.prefetch_plan(truths[l][rows(t)], E, C, lst=tlists[t, l], nlist=ntlists[t, l:l + 1])
             tr.prefetch_copy(bank, tlists[t, l], slots[l % 2])
 
-    def token_speculative(t, with_misses):
-        for l in range(nl):
-            # during layer l: plan layer l+1 from q_l's prediction, list back to the host
+    def token_speculative(t, with_misses, dma=False):
+        """Transfer l brings the experts predicted for layer l + 1 (from q_l).
+        Transfer l + 1 is planned before the compute stream waits for
+        transfer l: q_{l+1} exists once layer l has run, which needed only
+        transfer l - 1. So the transfers queue back to back on the copy
+        stream. The copy kernel keeps the list on the GPU; the DMA form
+        (dma=True) takes it back to pinned host memory and issues
+        prefetch_issue, while transfer l is still running."""
+        def issue(l):
             tr.prefetch_plan(preds[l][rows(t)], E, C, lst=lists[t, l], nlist=nlists[t, l:l + 1])
-            lists_h[t, l].copy_(lists[t, l], non_blocking=True)
+            if dma:
+                lists_h[t, l].copy_(lists[t, l], non_blocking=True)
+            # one wait covers the plan and the slots: ev_plan[l] follows, on the
+            # compute stream, the work of the layer that used slots[l % 2] last
             ev_plan[l].record(comp)
-            ev_plan[l].synchronize()
-            tr.prefetch_issue(bank, lists_h[t, l], slots[l % 2], stream=copy)
+            copy.wait_event(ev_plan[l])
+            if dma:
+                ev_plan[l].synchronize()
+                tr.prefetch_issue(bank, lists_h[t, l], slots[l % 2], stream=copy)
+            else:
+                with torch.cuda.stream(copy):
+                    tr.prefetch_copy(bank, lists[t, l], slots[l % 2])
             ev_copy[l].record(copy)
-            # layer l+1 starts once its experts are in (speculative execution)
+
+        issue(0)
+        for l in range(nl):
+            if l + 1 < nl:
+                issue(l + 1)
+            # the layer these experts belong to starts once they are in
             comp.wait_event(ev_copy[l])
             tr.prefetch_coverage(truths[l][rows(t)], lists[t, l], E, covered[l:l + 1],
                                  miss=misses[t, l], nmiss=nmisses[t, l:l + 1])
@@ -686,10 +714,37 @@ def prefetch_bench(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / T
 
+    def timed_graph(fn):
+        """Per-token time with each token's schedule captured once as a HIP
+        graph (both streams; the cross-stream waits become graph edges)."""
+        graphs = []
+        for t in range(T):
+            copy.wait_stream(comp)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=comp):
+                copy.wait_stream(comp)
+                fn(t)
+                comp.wait_stream(copy)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs[:W]:
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        for g in graphs:
+            g.replay()
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / T
+
     ms_od = timed(token_on_demand)
+    ms_sp_dma = timed(lambda t: token_speculative(t, False, dma=True))
     ms_sp = timed(lambda t: token_speculative(t, False))
     covered.zero_()
     ms_pm = timed(lambda t: token_speculative(t, True))
+    ms_od_graph = timed_graph(token_on_demand)
+    ms_sp_graph = timed_graph(lambda t: token_speculative(t, False))
     cov_by_layer = covered.cpu().numpy() / ((T + W) * B * K)
     byt_od = int(ntlists.sum()) * EB / T
     byt_sp = int(nlists.sum()) * EB / T
@@ -775,7 +830,9 @@ def prefetch_bench(args):
                            "experts": n_copied},
         "dma_us": {"mean": float(np.mean(dma_us)), "p50": float(np.median(dma_us))},
         "dma_frac_of_pcie": dma_gbs * 1e9 / PCIE_PEAK,
-        "ms_per_token": {"on_demand": ms_od, "speculative": ms_sp, "prefetch_then_misses": ms_pm},
+        "ms_per_token": {"on_demand": ms_od, "speculative": ms_sp, "speculative_dma": ms_sp_dma,
+                         "prefetch_then_misses": ms_pm},
+        "ms_per_token_graph": {"on_demand": ms_od_graph, "speculative": ms_sp_graph},
         "bytes_per_token": {"on_demand": byt_od, "speculative": byt_sp,
                             "prefetch_then_misses": byt_pm},
         "coverage": {"gate_layers": float(np.mean([c for c, e_ in zip(cov_by_layer, est) if not e_])),
