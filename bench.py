@@ -571,7 +571,7 @@ def predictor_measure(args):
                     "stages_us_gate_layer": st_gate},
         "stages_us_gate_layer": st_fused, "stages_us_estimator_layer": st_est,
         "qgate_topk_us_per_launch": qg_launch_us,
-        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, true> (route_qgate_topk)",
+        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, 1> (route_qgate_topk)",
                      "achieved": byt_fused["qgate_topk"] / (qg_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK,
@@ -858,6 +858,42 @@ def prefetch_bench(args):
     return 0
 
 
+def ceilings_bench(args):
+    """Reference HBM rates of plain access patterns on this GPU, measured with
+    torch's own kernels on 1 GiB buffers (no routing arithmetic): a pure read
+    (a float32 sum), a pure write (a fill) and a copy. They bound the row
+    movers from above (the combine is mostly reads, the dispatch mostly
+    writes); the line reports each rate and its fraction of the 8 TB/s peak."""
+    import torch
+    torch.cuda.set_device(0)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    pats = {"read": (lambda: torch.sum(src, dim=0, out=sink), nbytes),
+            "write": (lambda: dst.fill_(7), nbytes),
+            "copy": (lambda: dst.copy_(src), 2 * nbytes)}
+    reps = max(args.steps, 5)
+    out = {}
+    for name, (fn, moved) in pats.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) * 1e-3 / reps
+        out[name] = {"gbs": moved / sec / 1e9, "frac": moved / sec / HBM_PEAK, "bytes": moved}
+    line = {"metric": "HBM ceilings of plain access patterns (torch kernels, 1 GiB)",
+            "value": out["read"]["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": reps,
+            "higher_is_better": True, "data": "synthetic", "patterns": out}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -880,6 +916,8 @@ def main(argv=None):
                     help="qwen3: fit the estimator layers' output weights before timing")
     ap.add_argument("--fit-tokens", type=int, default=32768)
     ap.add_argument("--fit-ridge", type=float, default=1e-3)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure plain read / write / copy HBM rates with torch kernels")
     ap.add_argument("--prefetch", action="store_true",
                     help="qwen3: measure speculative expert prefetch from pinned host memory")
     ap.add_argument("--prefetch-tokens", type=int, default=16)
@@ -898,6 +936,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if args.ceilings:
+        return ceilings_bench(args)
     if args.prefetch:
         return prefetch_bench(args)
     if args.config == "qwen3":
