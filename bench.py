@@ -30,11 +30,12 @@ METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofl
 ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
 
 
-def route_bytes(N, d, E, K, P, G, fallback, fused=False):
+def route_bytes(N, d, E, K, P, G, fallback, fused=False, routed=False):
     """Algorithmic HBM bytes per pass: every call reads its inputs once and
     writes its outputs once (bf16 rows = 2 bytes per element). With the
     shuffle and the router fused (srs_shuffle_gate) the reduced rows are
-    written once and not read back."""
+    written once and not read back; with the shuffle, router, top-K and count
+    in one kernel (srs_shuffle_route) neither are the logits nor the picks."""
     b = 2
     st = {
         "predict": (9 if fallback else 6) * N,
@@ -45,6 +46,11 @@ def route_bytes(N, d, E, K, P, G, fallback, fused=False):
         "permute": 12 * N * K + 4 * (E + 1) + N * d * b + N * K * d * b,
         "combine": N * K * d * b + 8 * N * K + 4 * N + N * d * b,
     }
+    if routed:
+        return {"predict": st["predict"],
+                "srs_route": (st["srs"] + st["gate"] - N * d * b + st["topk"] - 4 * N * E
+                              + st["lar"] - 4 * N * K),
+                "permute": st["permute"], "combine": st["combine"]}
     if fused:
         st = {"predict": st["predict"], "srs_gate": st.pop("srs") + st.pop("gate") - N * d * b,
               **{k: v for k, v in st.items() if k != "predict"}}
@@ -1013,7 +1019,8 @@ def route_measure(args, name):
                 "K": cfg.K, "G": cfg.G}
     else:
         p = RoutePass(inp)
-        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.fused)
+        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.fused,
+                               p.routed)
         conf = {"workload": ROUTE_WORKLOADS[name], "N": cfg.N, "d": cfg.d, "E": cfg.E,
                 "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
                 "fallback": "2-gram" if p.fallback else "none"}
@@ -1075,7 +1082,8 @@ def route_measure(args, name):
     N = cfg.N
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
-    gate_stage = "gate" if "gate" in st_us else "srs_gate"  # the stage holding the router product
+    # the stage holding the router product
+    gate_stage = next(g for g in ("gate", "srs_gate", "srs_route") if g in st_us)
     # dominant single-kernel stage: the combine (one launch per pass)
     dom = "combine"
     dom_bytes = bytes_st[dom]

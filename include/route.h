@@ -163,6 +163,42 @@ int srs_shuffle_gate(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
                      uint32_t* err, hipStream_t s);
 
 /*
+ * srs_shuffle_route - srs_shuffle, then the router, top-K and local
+ * activation count of each reduced row, in one pass over the rows.
+ * [SMOE] section 3.1 (s-TS) for the reduce and the shuffle, glossary (top-K
+ * experts per token; local activation rate); [FOE] router scores g[i]. For a
+ * small expert set the router's work per row is a few dot products, done
+ * while the reduced row is still on chip. Writes every output of
+ * srs_shuffle with the same bytes, and for every written row `row`:
+ *   logits[row][e] = out[row] . w[e]^T   (binary32; nullable), as route_gate
+ *     up to the order of the binary32 sums;
+ *   idx[row][:], weights[row][:] = route_topk of those logits with H = 1
+ *     and the given renorm (weights nullable): the same ranking rules, so
+ *     idx equals route_topk(logits) bit for bit;
+ *   *local += #{k : expert_cluster[idx[row][k]] == cluster of the row}, the
+ *     cluster of the row being its predicted cluster dest[i] (0 without
+ *     dest), i.e. lar_count(idx, K, 1, row_cluster, expert_cluster).
+ *   Arguments as srs_shuffle_gate, plus K, renorm, idx int32[n][K], weights
+ *   float[n][K], expert_cluster uint8[E] and local (device uint64,
+ *   accumulated); expert_cluster and local are both given or both NULL (no
+ *   count). ws: srs_shuffle_workspace_size(n, G).
+ * Errors: as srs_shuffle, plus SHAPE (K < 1, K > E), NULL (w or idx with
+ * n > 0; only one of expert_cluster and local), and UNSUPPORTED unless
+ * 1 <= E <= 64, d <= 4096, E * C * 1024 <= 65536 with C the smallest of
+ * 1, 2, 4, 8 such that C * 512 >= d (the router rows, padded to C * 512
+ * elements, are staged in on-chip memory), P in {1, 2, 4} (P = 4:
+ * d <= 2048) and K <= 16; use the separate calls there. Device bit: DEST_RANGE (rows whose key is out
+ * of range get none of the row outputs and add nothing to *local).
+ */
+int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                      const uint8_t* dest, int32_t G, uint16_t* out, int32_t* cluster_offsets,
+                      int32_t* row_of_src, int32_t* src_of_row, uint8_t* row_cluster,
+                      const uint16_t* w, int32_t E, float* logits, int32_t K, int32_t renorm,
+                      int32_t* idx, float* weights, const uint8_t* expert_cluster,
+                      unsigned long long* local, void* ws, size_t ws_bytes, uint32_t* err,
+                      hipStream_t s);
+
+/*
  * route_gate - router logits = x . w^T.
  * [FOE] per-layer comparison (router scores g[i]); [SPEC] item 2.A (the
  * next layer's gate applied to q_l). bf16 operands, binary32 accumulation

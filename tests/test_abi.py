@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 34, names
+    assert len(names) == 35, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -115,6 +115,44 @@ def test_srs_gate_errors(L):
     assert call(args(G=300)) == UNSUP
     assert call(args(partials=MIS)) == ALIGN
     assert call(args(w=MIS)) == ALIGN
+
+def test_srs_route_errors(L):
+    f = L.srs_shuffle_route
+    ws = L.srs_shuffle_workspace_size(1000, 8)
+    args = lambda **k: dict(dict(partials=A, P=2, n=1000, d=512, dest=A, G=8, out=A, offs=A,
+                                 ros=None, sor=None, rc=None, w=A, E=8, logits=A, K=2, renorm=1,
+                                 idx=A, weights=A, ec=A, local=A, ws=A, wsb=ws, err=None,
+                                 s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(wsb=ws - 1)) == WS
+    assert call(args(ws=None)) == WS
+    assert call(args(dest=None)) == NULL
+    assert call(args(w=None)) == NULL
+    assert call(args(idx=None)) == NULL
+    assert call(args(out=None)) == NULL
+    assert call(args(offs=None)) == NULL
+    assert call(args(local=None)) == NULL      # the count needs both
+    assert call(args(ec=None)) == NULL
+    assert call(args(d=12)) == SHAPE
+    assert call(args(E=0)) == SHAPE
+    assert call(args(K=0)) == SHAPE
+    assert call(args(K=9)) == SHAPE            # K > E
+    assert call(args(n=-1)) == SHAPE
+    # one lane per expert, the padded router rows within 64 KiB of LDS,
+    # d <= 4096, P in {1, 2, 4} (four partials up to d = 2048), K <= 16
+    assert call(args(E=65, K=2, d=256)) == UNSUP
+    assert call(args(E=9, d=4096)) == UNSUP
+    assert call(args(E=40, d=520)) == UNSUP    # 41600 bytes, 81920 padded
+    assert call(args(E=32, d=520, ws=None)) == WS   # 65536 padded: supported
+    assert call(args(E=1, K=1, d=4104)) == UNSUP
+    assert call(args(P=3)) == UNSUP
+    assert call(args(P=4, d=2056, E=4)) == UNSUP
+    assert call(args(E=32, K=17, d=512)) == UNSUP
+    assert call(args(G=300)) == UNSUP
+    assert call(args(partials=MIS)) == ALIGN
+    assert call(args(w=MIS)) == ALIGN
+    assert call(args(out=MIS)) == ALIGN
+
 
 def test_permute_and_combine_errors(L):
     ws = L.moe_permute_workspace_size(1000, 6, 160)

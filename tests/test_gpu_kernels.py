@@ -331,15 +331,18 @@ def test_lut_build(n, E, K, G):
 
 
 # ------------------------------------------------------------ determinism
-def test_run_twice_bitwise():
-    inp = make_route_inputs(3000, 256, 160, 6, 2, 8, 5000, 77, ngram=True)
+@pytest.mark.parametrize("E", [160, 8])
+def test_run_twice_bitwise(E):
+    inp = make_route_inputs(3000, 256, E, 6 if E > 8 else 2, 2, 8, 5000, 77, ngram=True)
     from token_routing_speculation_amd.pipeline import RoutePass
     p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
     p.step()
     first = {k: host(getattr(p, k)).copy() for k in ("x", "logits", "idx", "weights", "slot_of_pair", "disp", "out")}
+    l1 = int(host(p.local)[0])
     p.step()
     for k, v in first.items():
         assert np.array_equal(host(getattr(p, k)), v), k
+    assert int(host(p.local)[0]) == 2 * l1
 
 
 def test_run_twice_bitwise_foe_and_predictor():
@@ -376,16 +379,16 @@ def test_run_twice_bitwise_foe_and_predictor():
 
 
 # ------------------------------------------------------------ graph replay
-@pytest.mark.parametrize("E,fused", [(160, True), (64, False)])
-def test_graph_replay_matches_eager(E, fused):
+@pytest.mark.parametrize("E,mode", [(160, "fused"), (64, "routed"), (96, "separate")])
+def test_graph_replay_matches_eager(E, mode):
     """The benchmark replays the pass as a captured graph: every replay, with
     eager work and synchronisations in between, must equal the eager pass
-    (the shuffle and the router fused into one kernel at 160 columns, two
-    calls at 64)."""
+    (the shuffle and the router product in one kernel at 160 columns; the
+    shuffle, router, top-K and count in one at 64; separate calls at 96)."""
     from token_routing_speculation_amd.pipeline import RoutePass, capture_graph
     inp = make_route_inputs(2000, 512, E, 6, 2, 8, 5000, 91, ngram=True)
     p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
-    assert p.fused == fused
+    assert (p.fused, p.routed) == (mode == "fused", mode == "routed")
     keys = ("dest", "x", "row_of_src", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
     p.step()
     sync()

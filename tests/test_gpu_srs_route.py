@@ -1,0 +1,208 @@
+"""GPU parity of srs_shuffle_route (the shuffled reduce, then the router,
+top-K and local activation count of every reduced row, one kernel after the
+sort): every shuffle output bit-exact against the oracle's shuffle; the
+logits against the oracle's gate on the oracle's reduced rows; the top-K
+indices bit-exact against the oracle's top-K of the logits the kernel wrote
+(the ranking is decided in binary32 on both sides), the weights within 1e-5
+of the oracle's softmax of them; the count exactly the oracle's LAR of those
+picks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_routing_speculation_amd as tr
+from synth import to_bf16_bits
+from tests.gpu_helpers import dev, host, assert_rel, sync
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 1e-2      # the gate's stated bar (max relative error, row-rms floored)
+F32_TOL = 1e-4        # binary32 accumulation of exact bf16 products
+
+
+def _bf16(shape, seed, scale=1.0):
+    return to_bf16_bits((np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32))
+
+
+def _inputs(n, d, P, G, E):
+    rng = np.random.default_rng(n * 3 + d + E)
+    parts = _bf16((P, n, d), n * 7 + d + P)
+    dest = rng.integers(0, G, n, dtype=np.int64).astype(np.uint8)
+    w = _bf16((E, d), E + d, 1 / np.sqrt(d))
+    ec = rng.integers(0, G, E, dtype=np.int64).astype(np.uint8)
+    return parts, dest, w, ec
+
+
+def _run(parts, dest, G, w, K, ec, renorm=1, **kw):
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    r = tr.srs_shuffle_route(dev(parts), None if dest is None else dev(dest), G, dev(w), K,
+                             renorm=renorm, expert_cluster=None if ec is None else dev(ec),
+                             local=None if ec is None else local, **kw)
+    sync()
+    return r, local
+
+
+def _check(parts, dest, G, w, K, ec, renorm, got, local):
+    out, offs, ros, sor, rc, lg, idx, wt = got
+    want = oracle.srs_shuffle(parts, None if dest is None else dest.astype(np.int64), G)
+    assert np.array_equal(host(offs), want["offsets"])
+    assert np.array_equal(host(ros), want["row_of_src"])
+    assert np.array_equal(host(sor), want["src_of_row"])
+    assert np.array_equal(host(rc), want["row_cluster"])
+    assert np.array_equal(host(out), want["out"])
+    ref = oracle.route_gate(want["out"], w)
+    lgh = host(lg)
+    assert_rel(lgh, ref, LOGIT_TOL, "fused logits")
+    assert_rel(lgh, ref, F32_TOL, "fused logits (binary32 level)")
+    widx, ww = oracle.route_topk(lgh, K, 1, renorm)
+    assert np.array_equal(host(idx), widx)
+    np.testing.assert_allclose(host(wt), ww, rtol=1e-5, atol=1e-7)
+    if ec is not None:
+        assert int(local.item()) == oracle.lar_count(widx, K, 1, want["row_cluster"], ec)
+
+
+# (n, d, P, G, E, K): one row; less than a workgroup; the tiny workload's
+# shape; a ragged 16-byte-vector tail; every supported P; E from 1 to 64;
+# K from 1 to 16; the router rows at the 64 KiB limit; the Mixtral-8x7B
+# shape (4096 rows of 4096, E = 8, K = 2) and more rows than one pass of the
+# grid covers (each wave loops)
+CASES = [(1, 128, 2, 2, 4, 2), (7, 64, 1, 3, 3, 1), (64, 128, 2, 2, 4, 2),
+         (1000, 520, 2, 8, 8, 2), (777, 384, 4, 5, 16, 4), (333, 1024, 1, 8, 32, 8),
+         (129, 2048, 4, 3, 16, 16), (500, 512, 2, 4, 64, 6), (300, 256, 2, 256, 1, 1),
+         (4096, 4096, 2, 4, 8, 2), (9000, 256, 2, 8, 8, 2)]
+
+
+@pytest.mark.parametrize("n,d,P,G,E,K", CASES)
+def test_srs_route_against_oracle(n, d, P, G, E, K):
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    got, local = _run(parts, dest, G, w, K, ec)
+    _check(parts, dest, G, w, K, ec, 1, got, local)
+
+
+def test_srs_route_full_softmax_and_no_count():
+    """renorm = 0 (softmax over all E, read at the picks); no count."""
+    n, d, P, G, E, K = 700, 640, 2, 4, 12, 3
+    parts, dest, w, _ = _inputs(n, d, P, G, E)
+    got, local = _run(parts, dest, G, w, K, None, renorm=0)
+    _check(parts, dest, G, w, K, None, 0, got, local)
+
+
+def test_srs_route_without_logits():
+    """Leaving the logits out changes nothing else: the same picks, weights
+    and count as the call that writes them (itself checked against the
+    oracle)."""
+    n, d, P, G, E, K = 640, 1024, 2, 4, 8, 2
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    got, local = _run(parts, dest, G, w, K, ec)
+    _check(parts, dest, G, w, K, ec, 1, got, local)
+    got2, local2 = _run(parts, dest, G, w, K, ec, with_logits=False)
+    assert got2[5] is None
+    assert torch.equal(got[0], got2[0]) and torch.equal(got[6], got2[6])
+    assert torch.equal(got[7], got2[7]) and int(local.item()) == int(local2.item())
+
+
+def test_srs_route_pure_reduce_without_dest():
+    """One cluster, no sort: offsets {0, n} and identity maps written by the
+    kernel (the buffers start out holding other values); every row's cluster
+    is 0 for the count."""
+    n, d, P, E, K = 333, 256, 2, 8, 2
+    parts = _bf16((P, n, d), 3 + n)
+    w = _bf16((E, d), d, 1 / np.sqrt(d))
+    ec = np.array([0, 1, 0, 2, 0, 1, 1, 0], dtype=np.uint8)
+    fill = lambda k, dt: torch.full((k,), 7, dtype=dt, device="cuda")
+    got, local = _run(parts, None, 1, w, K, ec, offsets=fill(2, torch.int32),
+                      row_of_src=fill(n, torch.int32), src_of_row=fill(n, torch.int32),
+                      row_cluster=fill(n, torch.uint8))
+    _check(parts, None, 1, w, K, ec, 1, got, local)
+
+
+def test_srs_route_ties_go_to_the_lower_expert():
+    """Equal router rows give bit-equal logits: the lower index ranks first.
+    All-zero rows give +0 logits for every expert (from -0.0 partials too),
+    so the picks are experts 0..K-1 with equal weights."""
+    n, d, P, G, E, K = 256, 512, 2, 4, 16, 4
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    w[9] = w[2]
+    w[14] = w[2]
+    w[5] = w[11]
+    parts[:, :40] = 0
+    parts[0, 40:60] = 0x8000
+    parts[1, 40:60] = 0x8000
+    got, local = _run(parts, dest, G, w, K, ec)
+    _check(parts, dest, G, w, K, ec, 1, got, local)
+    rows = host(got[2])[:60]
+    idx, wt = host(got[6])[rows], host(got[7])[rows]
+    assert np.all(host(got[5])[rows] == 0)
+    assert np.array_equal(idx, np.tile(np.arange(K), (60, 1)))
+    np.testing.assert_allclose(wt, 1.0 / K, rtol=1e-6)
+
+
+def test_srs_route_empty():
+    parts = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    dest = torch.empty((0,), dtype=torch.uint8, device="cuda")
+    w = dev(_bf16((8, 128), 0))
+    r = tr.srs_shuffle_route(parts, dest, 4, w, 2)
+    assert host(r[1]).tolist() == [0] * 5 and r[6].shape == (0, 2)
+
+
+def test_srs_route_flags_bad_cluster_and_skips_its_row():
+    """A key past G is flagged; its row gets no outputs and adds nothing to
+    the count; every other row is exact."""
+    n, d, G, E, K = 200, 256, 4, 8, 2
+    parts, dest, w, ec = _inputs(n, d, 2, G, E)
+    dest[7] = 9
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx = torch.full((n, K), -5, dtype=torch.int32, device="cuda")
+    (out, offs, ros, sor, rc, lg, idx, wt), local = _run(parts, dest, G, w, K, ec, err=err, idx=idx)
+    assert int(err.item()) & tr.EBIT_DEST_RANGE
+    r = host(ros)
+    assert r[7] == -1 and host(offs)[-1] == n - 1
+    keep = np.array([i for i in range(n) if i != 7])
+    red = oracle.srs_shuffle(parts, np.zeros(n, dtype=np.int64), 1)["out"]
+    assert np.array_equal(host(out)[r[keep]], red[keep])
+    lgh = host(lg)[r[keep]]
+    assert_rel(lgh, oracle.route_gate(red[keep], w), F32_TOL, "logits of the valid rows")
+    widx, _ = oracle.route_topk(lgh, K, 1, 1)
+    assert np.array_equal(host(idx)[r[keep]], widx)
+    free = sorted(set(range(n)) - set(r[keep].tolist()))
+    assert len(free) == 1 and np.all(host(idx)[free[0]] == -5)
+    assert int(local.item()) == oracle.lar_count(widx, K, 1, dest[keep].astype(np.int64), ec)
+
+
+def test_srs_route_count_accumulates():
+    """The count adds to what the counter holds."""
+    n, d, P, G, E, K = 500, 256, 2, 4, 8, 2
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    local = torch.full((1,), 1000, dtype=torch.int64, device="cuda")
+    r = tr.srs_shuffle_route(dev(parts), dev(dest), G, dev(w), K, expert_cluster=dev(ec), local=local)
+    sync()
+    want = oracle.srs_shuffle(parts, dest.astype(np.int64), G)
+    widx, _ = oracle.route_topk(host(r[5]), K, 1, 1)
+    assert int(local.item()) == 1000 + oracle.lar_count(widx, K, 1, want["row_cluster"], ec)
+
+
+@pytest.mark.filterwarnings("ignore:overflow encountered")   # the oracle's binary32 sums
+@pytest.mark.parametrize("kind", ["any_bits", "subnormal_sums"])
+def test_srs_route_rows_bit_exact_on_special_values(kind):
+    """The reduced rows keep the oracle's bytes on every bf16 pattern: NaN
+    (to the canonical 0x7FC0), infinities, overflow to infinity, and sums
+    that land among the subnormals (rounded to nearest even there). The
+    router results of such rows are outside the contract (NaN logits); only
+    the shuffle outputs are compared."""
+    n, d, P, G, E, K = 300, 264, 2, 4, 8, 2
+    rng = np.random.default_rng(17)
+    if kind == "any_bits":
+        parts = rng.integers(0, 1 << 16, (P, n, d), dtype=np.int64).astype(np.uint16)
+    else:
+        sign = rng.integers(0, 2, (P, n, d), dtype=np.int64) << 15
+        expo = rng.integers(0, 2, (P, n, d), dtype=np.int64) << 7
+        mant = rng.integers(0, 128, (P, n, d), dtype=np.int64)
+        parts = (sign | expo | mant).astype(np.uint16)
+    dest = rng.integers(0, G, n, dtype=np.int64).astype(np.uint8)
+    w = _bf16((E, d), 5, 1 / np.sqrt(d))
+    (out, offs, ros, sor, rc, *_), _ = _run(parts, dest, G, w, K, None)
+    want = oracle.srs_shuffle(parts, dest.astype(np.int64), G)
+    assert np.array_equal(host(offs), want["offsets"])
+    assert np.array_equal(host(ros), want["row_of_src"])
+    assert np.array_equal(host(out), want["out"])

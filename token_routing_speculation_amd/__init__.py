@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "RouteError", "lib", "library_path",
-    "route_predict", "route_lut_build", "srs_shuffle", "srs_shuffle_gate", "route_gate", "route_topk",
+    "route_predict", "route_lut_build", "srs_shuffle", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "route_qhidden",
     "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
@@ -52,6 +52,9 @@ EXPORTS = {
     "srs_shuffle": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "srs_shuffle_gate": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p,
                                         _p, _i32, _p, _p, _sz, _p, _p]),
+    "srs_shuffle_route": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p,
+                                         _p, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p,
+                                         _p]),
     "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
     "route_gate": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _p]),
     "route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p]),
@@ -238,6 +241,41 @@ def srs_shuffle_gate(partials, dest, G, w, out=None, logits=None, offsets=None, 
           _dev(w, _bf16(w), "w", E * d), E, _dev(logits, torch.float32, "logits", n * E),
           _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
     return out, offsets, row_of_src, src_of_row, row_cluster, logits
+
+def srs_shuffle_route(partials, dest, G, w, K, renorm=1, expert_cluster=None, local=None,
+                      out=None, logits=None, idx=None, weights=None, offsets=None, row_of_src=None,
+                      src_of_row=None, row_cluster=None, maps=True, with_logits=True, ws=None,
+                      err=None, stream=None):
+    """srs_shuffle, then the router, top-K and the local activation count of
+    every reduced row in one pass: returns (out, offsets, row_of_src,
+    src_of_row, row_cluster, logits, idx, weights). ``local`` (uint64 as
+    int64, accumulated) goes with ``expert_cluster``; ``with_logits=False``
+    leaves the logits unwritten (None returned)."""
+    P, n, d = partials.shape
+    E = w.shape[0]
+    bt = _bf16(partials)
+    out = _empty((n, d), bt, partials) if out is None else out
+    if with_logits and logits is None:
+        logits = _empty((n, E), torch.float32, partials)
+    idx = _empty((n, K), torch.int32, partials) if idx is None else idx
+    weights = _empty((n, K), torch.float32, partials) if weights is None else weights
+    offsets = _empty((G + 1,), torch.int32, partials) if offsets is None else offsets
+    if maps:
+        row_of_src = _empty((n,), torch.int32, partials) if row_of_src is None else row_of_src
+        src_of_row = _empty((n,), torch.int32, partials) if src_of_row is None else src_of_row
+        row_cluster = _empty((n,), torch.uint8, partials) if row_cluster is None else row_cluster
+    need = srs_shuffle_workspace_size(n, G)
+    ws = _empty((max(need, 1),), torch.uint8, partials) if ws is None else ws
+    _call("srs_shuffle_route", _dev(partials, bt, "partials"), P, n, d,
+          _opt(dest, torch.uint8, "dest", n), G, _dev(out, bt, "out", n * d),
+          _dev(offsets, torch.int32, "offsets", G + 1), _opt(row_of_src, torch.int32, "row_of_src", n),
+          _opt(src_of_row, torch.int32, "src_of_row", n), _opt(row_cluster, torch.uint8, "row_cluster", n),
+          _dev(w, _bf16(w), "w", E * d), E, _opt(logits, torch.float32, "logits", n * E), K, renorm,
+          _dev(idx, torch.int32, "idx", n * K), _opt(weights, torch.float32, "weights", n * K),
+          _opt(expert_cluster, torch.uint8, "expert_cluster", E), _opt(local, torch.int64, "local", 1),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return out, offsets, row_of_src, src_of_row, row_cluster, logits, idx, weights
+
 
 def route_gate(x, w, logits=None, stream=None):
     n, d = x.shape

@@ -50,6 +50,26 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return v;
 }
 
+// pack8 through the hardware conversion (v_cvt_pk_bf16_f32, round to nearest
+// even): the same bits as pack8 for every non-NaN value, denormals included;
+// a vector holding a NaN takes pack8 itself, so NaN still becomes 0x7FC0.
+__device__ __forceinline__ u32x4 pack8_cvt(const float* f) {
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nan |= f[i] != f[i];
+  if (__builtin_expect(nan, 0)) return pack8(f);
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_v h = {static_cast<__bf16>(f[2 * i]), static_cast<__bf16>(f[2 * i + 1])};
+    uint32_t w;
+    __builtin_memcpy(&w, &h, 4);
+    v[i] = w;
+  }
+  return v;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

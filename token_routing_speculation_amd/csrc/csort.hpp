@@ -8,6 +8,8 @@
 //                   then ranks a contiguous share of the chunk (ballot-
 //                   matched equal keys, wave-private running counts), giving
 //                   each key its stable position.
+// Up to kSortOneMax keys the two become one launch (csort_one): a single
+// workgroup counts, scans and ranks the whole array.
 // Keys >= B (or negative) are skipped: flagged in err, position -1.
 #pragma once
 
@@ -94,6 +96,120 @@ __device__ __forceinline__ uint64_t match_key(uint32_t k, bool valid, int nbits)
   return m;
 }
 
+// Exclusive scan of the B bin totals in tot[] by one wave (each lane a
+// contiguous run of bins); *total receives the sum.
+__device__ __forceinline__ void scan_bins(int* tot, int B, int* total) {
+  const int lane = lane_id();
+  const int per = (B + kWave - 1) / kWave;
+  const int lo = lane * per;
+  const int hi = lo + per < B ? lo + per : B;
+  int local = 0;
+  for (int b = lo; b < hi; ++b) local += tot[b];
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - local;
+  for (int b = lo; b < hi; ++b) {
+    const int v = tot[b];
+    tot[b] = run;
+    run += v;
+  }
+  if (lane == kWave - 1) *total = incl;
+}
+
+constexpr int64_t kSpan = static_cast<int64_t>(kBatch) * kWave;  // keys per batch of tiles
+
+// keys [base, base + kSpan) of a share ending at qhi, one per lane and tile
+template <typename KeyT>
+__device__ __forceinline__ void load_batch(const KeyT* __restrict__ keys, uint32_t (&kb)[kBatch],
+                                           int64_t base, int64_t qhi) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    const int64_t j = base + q * kWave + lane;
+    kb[q] = j < qhi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
+  }
+}
+
+// Pass 1 of the ranking: per-bin counts of the keys [qlo, qhi) into this
+// wave's LDS row (per 64-key tile, the lowest lane of each key's match adds
+// the match size). first[] holds the share's first batch, already loaded.
+// Returns whether a key of the share was out of range.
+template <typename KeyT>
+__device__ __forceinline__ bool count_share(const KeyT* __restrict__ keys, int64_t qlo,
+                                            int64_t qhi, int B, int nbits,
+                                            const uint32_t (&first)[kBatch], int* myrow) {
+  const int lane = lane_id();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  bool bad = false;
+  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
+    uint32_t kb[kBatch];
+    if (jb == qlo) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+    } else {
+      load_batch(keys, kb, jb, qhi);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (jb + q * kWave >= qhi) break;
+      const uint32_t k = kb[q];
+      const bool valid = k < static_cast<uint32_t>(B);
+      if (!valid && jb + q * kWave + lane < qhi) bad = true;
+      const uint64_t m = match_key(k, valid, nbits);
+      if (valid && __popcll(m & below) == 0) myrow[k] += __popcll(m);
+    }
+  }
+  return bad;
+}
+
+// Pass 2: each key of [qlo, qhi) in order takes its wave's running start for
+// its bin plus its rank among equal keys of its tile; the lowest lane of the
+// match then advances the start. fwd[j] = position, inv[pos] = j,
+// inv_key[pos] = key (nullable); out-of-range keys get position -1.
+template <typename KeyT>
+__device__ __forceinline__ void place_share(const KeyT* __restrict__ keys, int64_t qlo,
+                                            int64_t qhi, int B, int nbits,
+                                            const uint32_t (&first)[kBatch], int* myrow,
+                                            int* __restrict__ fwd, int* __restrict__ inv,
+                                            uint8_t* __restrict__ inv_key) {
+  const int lane = lane_id();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
+    uint32_t kb[kBatch];
+    if (jb == qlo) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+    } else {
+      load_batch(keys, kb, jb, qhi);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t j0 = jb + q * kWave;
+      if (j0 >= qhi) break;
+      const int64_t j = j0 + lane;
+      const uint32_t k = kb[q];
+      const bool valid = k < static_cast<uint32_t>(B);
+      const uint64_t m = match_key(k, valid, nbits);
+      const int rank = __popcll(m & below);
+      int start = 0;
+      if (valid) start = myrow[k];
+      if (valid) {
+        const int pos = start + rank;
+        fwd[j] = pos;
+        inv[pos] = static_cast<int>(j);
+        if (inv_key) inv_key[pos] = static_cast<uint8_t>(k);
+      } else if (j < qhi) {
+        fwd[j] = -1;
+      }
+      if (valid && rank == 0) myrow[k] = start + __popcll(m);
+    }
+  }
+}
+
 // Ranks the keys of chunk blockIdx.x. fwd[j] = position of key j,
 // inv[pos] = j, inv_key[pos] = key (inv_key nullable). THREADS / 64 waves.
 //
@@ -102,16 +218,13 @@ __device__ __forceinline__ uint64_t match_key(uint32_t k, bool valid, int nbits)
 // r, r + R, ... so the loads spread over all threads, and the R partial sums
 // meet in LDS.
 //
-// The chunk is split into NW contiguous shares, one per wave. Pass 1: each
-// wave counts its share per bin into its own LDS row (per 64-key tile, the
-// lowest lane of each key's match adds the match size). After one barrier the
-// rows become per-wave starting positions (the chunk's base for the bin plus
-// the counts of the earlier shares). Pass 2: each wave walks its share again
-// in order; a key's position is its wave's running start for the bin plus its
-// rank among equal keys in the tile, then the lowest lane advances the start.
-// Waves touch only their own LDS row, in program order, so pass 2 needs no
-// barriers. More waves make each wave's serial walk shorter: the kernel is
-// bound by that walk's latency, not by throughput.
+// The chunk is split into NW contiguous shares, one per wave. Pass 1
+// (count_share) counts each share per bin into its wave's LDS row. After one
+// barrier the rows become per-wave starting positions (the chunk's base for
+// the bin plus the counts of the earlier shares). Pass 2 (place_share) walks
+// each share again in order. Waves touch only their own LDS row, in program
+// order, so pass 2 needs no barriers. More waves make each wave's serial walk
+// shorter: the kernel is bound by that walk's latency, not by throughput.
 template <typename KeyT, int THREADS>
 __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ keys, int64_t n,
                                                       int B, int nbits, int64_t chunk,
@@ -134,7 +247,6 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
   __shared__ int stotal;
   const int t = threadIdx.x;
   const int w = wave_id();
-  const int lane = t & (kWave - 1);
   const int c = blockIdx.x;
   for (int i = t; i < NW * B; i += THREADS) wrow[i] = 0;
 
@@ -162,27 +274,7 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
     stot[b] = tot;
   }
   __syncthreads();
-  // exclusive scan of the bin totals by wave 0 (each lane a contiguous run)
-  if (w == 0) {
-    const int per = (B + kWave - 1) / kWave;
-    const int lo = lane * per;
-    const int hi = lo + per < B ? lo + per : B;
-    int local = 0;
-    for (int b = lo; b < hi; ++b) local += stot[b];
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - local;
-    for (int b = lo; b < hi; ++b) {
-      const int v = stot[b];
-      stot[b] = run;
-      run += v;
-    }
-    if (lane == kWave - 1) stotal = incl;
-  }
+  if (w == 0) scan_bins(stot, B, &stotal);
   __syncthreads();
   for (int b = t; b < B; b += THREADS) {
     if (c == 0) offsets[b] = stot[b];
@@ -196,40 +288,13 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
   const int64_t share = chunk / NW;
   const int64_t qlo = clo + w * share;
   const int64_t qhi = qlo + share < chi ? qlo + share : chi;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int* myrow = wrow + w * B;
 
   // keys are read kBatch tiles (of 64) at a time, all loads issued before
   // any tile is processed; the first batch stays in registers for pass 2
-  auto load_batch = [&](uint32_t (&kb)[kBatch], int64_t base) {
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int64_t j = base + q * kWave + lane;
-      kb[q] = j < qhi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
-    }
-  };
-  constexpr int64_t kSpan = static_cast<int64_t>(kBatch) * kWave;
   uint32_t first[kBatch];
-  load_batch(first, qlo);
-
-  // pass 1: per-bin counts of the share
-  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
-    uint32_t kb[kBatch];
-    if (jb == qlo) {
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
-    } else {
-      load_batch(kb, jb);
-    }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      if (jb + q * kWave >= qhi) break;
-      const uint32_t k = kb[q];
-      const bool valid = k < static_cast<uint32_t>(B);
-      const uint64_t m = match_key(k, valid, nbits);
-      if (valid && __popcll(m & below) == 0) myrow[k] += __popcll(m);
-    }
-  }
+  load_batch(keys, first, qlo, qhi);
+  count_share(keys, qlo, qhi, B, nbits, first, myrow);  // csort_hist flagged bad keys
   __syncthreads();
   // counts -> per-wave starting positions
   for (int b = t; b < B; b += THREADS) {
@@ -242,37 +307,67 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
     }
   }
   __syncthreads();
-  // pass 2: positions
-  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
-    uint32_t kb[kBatch];
-    if (jb == qlo) {
+  place_share(keys, qlo, qhi, B, nbits, first, myrow, fwd, inv, inv_key);
+}
+
+// The whole sort in one workgroup of sixteen waves, for n <= kSortOneMax keys
+// and B <= kMaxExperts / 4 bins: the shares of csort_rank span the array, and
+// the bin totals come from pass 1's own counts instead of a histogram table.
+// One launch instead of two, but one CU's vector units walk every tile, so it
+// only pays for small arrays. Measured per sort (graph replay, MI355X), one
+// launch against two: 4096 keys of 8 bins 6.5 against 7.1 us, 2048 keys of 4
+// bins (with a minimal row move) 7.1 against 8.8; 8192 keys 9.8 against 7.3,
+// 16384 keys 17.5 against 7.5 (8 bins) and 28.3 against 9.2 (160 bins).
+constexpr int64_t kSortOneMax = 4096;
+constexpr int kSortOneThreads = 1024;
+
+template <typename KeyT>
+__global__ __launch_bounds__(kSortOneThreads) void csort_one(
+    const KeyT* __restrict__ keys, int64_t n, int B, int nbits, int* __restrict__ offsets,
+    int* __restrict__ fwd, int* __restrict__ inv, uint8_t* __restrict__ inv_key, uint32_t* err,
+    uint32_t ebit) {
+  constexpr int NW = kSortOneThreads / kWave;
+  constexpr int kMaxB = kMaxExperts / 4;
+  __shared__ int stot[kMaxB];
+  __shared__ int wrow[NW * kMaxB];
+  __shared__ int stotal;
+  const int t = threadIdx.x;
+  const int w = wave_id();
+  for (int i = t; i < NW * B; i += kSortOneThreads) wrow[i] = 0;
+  // shares of whole tiles, one per wave
+  const int64_t share = ((n + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int64_t qlo = w * share < n ? w * share : n;
+  const int64_t qhi = qlo + share < n ? qlo + share : n;
+  int* myrow = wrow + w * B;
+  uint32_t first[kBatch];
+  load_batch(keys, first, qlo, qhi);
+  __syncthreads();
+  const bool bad = count_share(keys, qlo, qhi, B, nbits, first, myrow);
+  if (bad) set_err(err, ebit);
+  __syncthreads();
+  for (int b = t; b < B; b += kSortOneThreads) {
+    int tot = 0;
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
-    } else {
-      load_batch(kb, jb);
-    }
+    for (int v = 0; v < NW; ++v) tot += wrow[v * B + b];
+    stot[b] = tot;
+  }
+  __syncthreads();
+  if (w == 0) scan_bins(stot, B, &stotal);
+  __syncthreads();
+  // bin starts -> per-wave starting positions
+  for (int b = t; b < B; b += kSortOneThreads) {
+    offsets[b] = stot[b];
+    int run = stot[b];
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int64_t j0 = jb + q * kWave;
-      if (j0 >= qhi) break;
-      const int64_t j = j0 + lane;
-      const uint32_t k = kb[q];
-      const bool valid = k < static_cast<uint32_t>(B);
-      const uint64_t m = match_key(k, valid, nbits);
-      const int rank = __popcll(m & below);
-      int start = 0;
-      if (valid) start = myrow[k];
-      if (valid) {
-        const int pos = start + rank;
-        fwd[j] = pos;
-        inv[pos] = static_cast<int>(j);
-        if (inv_key) inv_key[pos] = static_cast<uint8_t>(k);
-      } else if (j < qhi) {
-        fwd[j] = -1;
-      }
-      if (valid && rank == 0) myrow[k] = start + __popcll(m);
+    for (int v = 0; v < NW; ++v) {
+      const int cnt = wrow[v * B + b];
+      wrow[v * B + b] = run;
+      run += cnt;
     }
   }
+  if (t == 0) offsets[B] = stotal;
+  __syncthreads();
+  place_share(keys, qlo, qhi, B, nbits, first, myrow, fwd, inv, inv_key);
 }
 
 __global__ void fill_i32(int* __restrict__ p, int64_t n, int value) {
@@ -286,12 +381,18 @@ inline int bits_for(int B) {
   return nb;
 }
 
-// Enqueues the two sort launches. ws holds the histogram table.
+// Enqueues the sort: one launch up to kSortOneMax keys, else two. ws holds
+// the histogram table (unused by the one-launch form).
 template <typename KeyT>
 int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int* inv,
                  uint8_t* inv_key, void* ws, uint32_t* err, uint32_t ebit, hipStream_t s) {
   if (n == 0) {
     fill_i32<<<ceil_div(B + 1, 256), 256, 0, s>>>(offsets, B + 1, 0);
+    return launch_status();
+  }
+  if (n <= kSortOneMax && B <= kMaxExperts / 4) {
+    csort_one<KeyT><<<1, kSortOneThreads, 0, s>>>(keys, n, B, bits_for(B), offsets, fwd, inv,
+                                                  inv_key, err, ebit);
     return launch_status();
   }
   const int64_t chunk = csort_chunk(n, B);

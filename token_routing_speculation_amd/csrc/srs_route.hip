@@ -1,0 +1,379 @@
+// srs_shuffle_route: the shuffled reduce of "Speculative MoE" (section 3.1,
+// s-TS) carried on through the router of a small expert set while each
+// reduced row is still in registers: router logits ("Federation of Experts
+// (FoE)" article, router scores g[i]), top-K with its softmax weights, and
+// the local activation count ("Speculative MoE" glossary) against the row's
+// predicted cluster. For E <= 32 the router is a handful of dot products per
+// row; run as separate launches it costs a re-read of the rows and three
+// launches that each do almost nothing, so here it rides along with the move.
+//
+// Layout of the work. The router rows w [E][d] are staged once per workgroup
+// into LDS, each padded with zeros to a whole number of 64-lane vector sets
+// (at most 64 KiB in all). Each wave owns one source row at a time:
+// lane l holds the 16-byte vectors l, l + 64, ... of every partial, sums them
+// in binary32 (partial order 0..P-1), rounds to bf16 and stores the row at its
+// sorted position (the same bytes as srs_shuffle). The bf16 row is multiplied
+// by each staged router row with v_dot2_f32_bf16 (binary32 accumulation of
+// exact bf16 products) and summed over the wave; lane e keeps expert e's
+// logit, so the top-K ranks one expert per lane on wave-uniform values.
+#include "common.hpp"
+#include "csort.hpp"
+#include "mfma.hpp"
+#include "srs.hpp"
+#include "topk.hpp"
+
+namespace route {
+namespace {
+
+// Sixteen waves per workgroup and at most one workgroup per CU: the router
+// rows are staged once per CU, and every wave loops over rows.
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kRouteWBytes = 64 * 1024;  // largest E * d * 2 staged in LDS
+constexpr int kRouteMaxE = kWave;  // one lane per expert
+constexpr int kRouteMaxGrid = 256;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// (the pairs go through memcpy: a bit cast taken straight from a vector
+// element has been seen to read element 0)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  bf16x2_t av, bv;
+  __builtin_memcpy(&av, &a, 4);
+  __builtin_memcpy(&bv, &b, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(av, bv, c, false);
+}
+
+// c + the dot product of eight bf16 pairs (binary32 accumulation)
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
+  const uint32_t a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+  const uint32_t b0 = b[0], b1 = b[1], b2 = b[2], b3 = b[3];
+  c = dot2(a0, b0, c);
+  c = dot2(a1, b1, c);
+  c = dot2(a2, b2, c);
+  return dot2(a3, b3, c);
+}
+
+// Sum over the wave, returned to every lane: DPP sums inside each row of
+// 16 lanes, then the four row sums read through scalar registers.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += __uint_as_float(dpp<kDppXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppMirror>(__float_as_uint(v)));
+  const uint32_t u = __float_as_uint(v);
+  return (__uint_as_float(__builtin_amdgcn_readlane(u, 0)) +
+          __uint_as_float(__builtin_amdgcn_readlane(u, 16))) +
+         (__uint_as_float(__builtin_amdgcn_readlane(u, 32)) +
+          __uint_as_float(__builtin_amdgcn_readlane(u, 48)));
+}
+
+struct RouteOut {
+  float* logits;                  // [n][E], nullable
+  int* idx;                       // [n][K]
+  float* weights;                 // [n][K], nullable
+  const uint8_t* expert_cluster;  // [E], nullable (then no count)
+  unsigned long long* local;
+};
+
+template <int PT, int CPL, int EB>
+__global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
+    const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
+    const uint8_t* __restrict__ dest, uint16_t* __restrict__ out, const uint16_t* __restrict__ w,
+    int E, int K, int renorm, RouteOut ro, SrsIdentity ident) {
+  static_assert(EB * CPL <= 64, "staged router rows fit in 64 KiB");
+  extern __shared__ __align__(16) char wl[];
+  const int wv = wave_id();
+  const int lane = lane_id();
+  const int nv = d >> 3;  // 16-byte vectors per row
+  const size_t plane = static_cast<size_t>(n) * d;
+
+  // The router rows into LDS as EB rows of CPL * 64 vectors, zeros past the
+  // row end and in the rows past E, so every lane's vectors meet a router
+  // value without a guard: 16 bytes per lane, lane i of a wave writing at the
+  // wave's base + 16 i.
+  constexpr int kRowV = CPL * kWave;  // vectors per staged router row
+  constexpr int kPieces = EB * kRowV;
+  for (int q0 = wv * kWave; q0 < kPieces; q0 += kRouteThreads) {
+    const int q = q0 + lane;
+    const int e = q / kRowV, v = q - e * kRowV;
+    if (e < E && v < nv)
+      lds_load16(w + 8 * (static_cast<size_t>(e) * nv + v), wl + 16 * q0);
+    else
+      *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = u32x4{0, 0, 0, 0};
+  }
+  // Row loads: streaming (nt) buffer loads through a descriptor spanning the
+  // one row, so vectors past the row end read as zeros without a per-vector
+  // address. Issued vector by vector (every partial of vector c, then c + 1),
+  // so the work on vector c waits only for its own loads.
+  u32x4 x[PT][CPL];
+  auto load_row = [&](int64_t r) {
+    __amdgpu_buffer_rsrc_t rs[PT];
+#pragma unroll
+    for (int p = 0; p < PT; ++p)
+      rs[p] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(partials + p * plane + static_cast<size_t>(r) * d),
+          static_cast<short>(0), d * 2, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int p = 0; p < PT; ++p)
+        x[p][c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[p], lane * 16, c * kWave * 16, 2));
+  };
+  // the first row's loads go out with the staging, then both are waited for
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kRouteWaves;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteWaves + wv;
+  if (i < n) load_row(i);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // lane e < E stands for expert e in the top-K and the count
+  const int my_ec = (ro.expert_cluster && lane < E) ? static_cast<int>(ro.expert_cluster[lane]) : -1;
+  unsigned lar = 0;
+
+  for (; i < n; i += stride) {
+    if (lane == 0) write_identity_row(ident, i, n);
+    const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
+    const bool keep = dst >= 0 && dst < n;  // key out of range (flagged by the sort): no outputs
+    const int cl = dest ? static_cast<int>(dest[i]) : 0;
+    // The row's store through a descriptor spanning the destination row
+    // (vectors past its end are dropped; for a row without a destination the
+    // descriptor is empty and drops them all).
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        out + (keep ? static_cast<size_t>(dst) * d : 0), static_cast<short>(0), keep ? d * 2 : 0,
+        0x00020000);
+    // Vector by vector, as its loads land: reduce, round, store, and add its
+    // products with every staged router row (binary32 dot products of exact
+    // bf16 pairs) into one accumulator per expert. The work runs in steps of
+    // (vector c, four router rows); each step's router reads are issued one
+    // step ahead, into a ring of two. An empty asm statement after each step
+    // takes the step's accumulators and the lane's LDS offset, and the next
+    // reads address through that offset: the reads cannot run ahead of the
+    // ring, and the products cannot sink past their step (left free, the
+    // compiler hoists every router read and holds them all in registers).
+    float acc[EB];
+#pragma unroll
+    for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+    constexpr int kGroups = EB / 4;
+    constexpr int kSteps = CPL * kGroups;
+    uint32_t off = 16u * lane;
+    u32x4 wr[2][4];
+    auto read_step = [&](int st, u32x4 (&dst)[4]) {
+      const int c = st / kGroups, g = st - c * kGroups;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        dst[k] = *reinterpret_cast<const u32x4*>(
+            wl + off + 16 * (static_cast<size_t>(g * 4 + k) * kRowV + c * kWave));
+    };
+    read_step(0, wr[0]);
+    u32x4 xb = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int c = st / kGroups, g = st - c * kGroups;
+      if (g == 0) {
+        // this vector's partials (waited for here, not before)
+#pragma unroll
+        for (int p = 0; p < PT; ++p) asm volatile("" : "+v"(x[p][c]));
+        float f[8];
+        unpack8(x[0][c], f);
+#pragma unroll
+        for (int p = 1; p < PT; ++p) {
+          float h[8];
+          unpack8(x[p][c], h);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) f[k] += h[k];
+        }
+        xb = pack8_cvt(f);
+        __builtin_amdgcn_raw_buffer_store_b128(xb, ors, lane * 16, c * kWave * 16, 0);
+      }
+      if (st + 1 < kSteps) read_step(st + 1, wr[(st + 1) & 1]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[g * 4 + k] = dot8(xb, wr[st & 1][k], acc[g * 4 + k]);
+      asm volatile(""
+                   : "+v"(off), "+v"(acc[g * 4]), "+v"(acc[g * 4 + 1]), "+v"(acc[g * 4 + 2]),
+                     "+v"(acc[g * 4 + 3]));
+    }
+    // Expert e's logit, a wave-uniform sum, kept by lane e. The sums are
+    // taken for every staged row (those past E hold zeros) and with no branch
+    // around them: a guard would let the compiler sink each expert's products
+    // to its sum, and every router read would stay live until then.
+    float logit = 0.f;
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+      const float sum = wave_sum_uniform(acc[e]);
+      logit = lane == e ? sum : logit;
+    }
+    // top-K on the order keys (lanes past E: key 0, below every logit)
+    const uint32_t mykey = lane < E ? order_key(logit) : 0u;
+    int rank = 0;  // experts ahead of this lane's: larger key, or equal key and lower index
+    uint32_t kmax = 0;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = __builtin_amdgcn_readlane(mykey, e);
+      rank += (k > mykey || (k == mykey && e < lane)) ? 1 : 0;
+      kmax = k > kmax ? k : kmax;
+    }
+    const bool pick = keep && lane < E && rank < K;
+    const float ex = (renorm ? pick : lane < E) ? __expf(logit - key_float(kmax)) : 0.f;
+    const float z = wave_sum_uniform(ex);
+    if (keep) {
+      if (ro.logits && lane < E) ro.logits[static_cast<size_t>(dst) * E + lane] = logit;
+      const size_t base = static_cast<size_t>(dst) * K;
+      if (pick) {
+        ro.idx[base + rank] = lane;
+        if (ro.weights) ro.weights[base + rank] = __fdividef(ex, z);
+      }
+      if (ro.expert_cluster) lar += __popcll(__ballot(pick && my_ec == cl));
+    }
+    if (i + stride < n) load_row(i + stride);
+  }
+
+  if (ro.expert_cluster) {
+    // every wave is done with the router rows: their LDS takes the counts
+    __syncthreads();
+    unsigned* cnt = reinterpret_cast<unsigned*>(wl);
+    if (lane == 0) cnt[wv] = lar;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long tot = 0;
+#pragma unroll
+      for (int v = 0; v < kRouteWaves; ++v) tot += cnt[v];
+      if (tot) atomicAdd(ro.local, tot);
+    }
+  }
+}
+
+int route_cpl(int nv) {
+  const int need = (nv + kWave - 1) / kWave;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+}
+
+// the smallest expert bound (8, 16, 32, 64) holding E
+int route_eb(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
+
+template <int PT, int CPL, int EB>
+bool launch_one(unsigned grid, size_t lds, hipStream_t s, const uint16_t* partials, int64_t n,
+                int d, const int* fwd, const uint8_t* dest, uint16_t* out, const uint16_t* w,
+                int E, int K, int renorm, const RouteOut& ro, const SrsIdentity& ident) {
+  if constexpr (EB * CPL > 64 || (PT == 4 && CPL == 8)) {
+    return false;  // beyond the staged rows' 64 KiB, or the registers
+  } else {
+    srs_route_kernel<PT, CPL, EB><<<grid, kRouteThreads, lds, s>>>(partials, n, d, fwd, dest, out,
+                                                                   w, E, K, renorm, ro, ident);
+    return true;
+  }
+}
+
+template <int PT, int CPL>
+bool launch_cpl(int eb, unsigned grid, size_t lds, hipStream_t s, const uint16_t* partials,
+                int64_t n, int d, const int* fwd, const uint8_t* dest, uint16_t* out,
+                const uint16_t* w, int E, int K, int renorm, const RouteOut& ro,
+                const SrsIdentity& ident) {
+  switch (eb) {
+#define ROUTE_EB(b)                                                                            \
+  case b:                                                                                      \
+    return launch_one<PT, CPL, b>(grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,       \
+                                  renorm, ro, ident);
+    ROUTE_EB(8) ROUTE_EB(16) ROUTE_EB(32) ROUTE_EB(64)
+#undef ROUTE_EB
+    default: return false;
+  }
+}
+
+template <int PT>
+bool launch_route(int cpl, int eb, unsigned grid, size_t lds, hipStream_t s,
+                  const uint16_t* partials, int64_t n, int d, const int* fwd, const uint8_t* dest,
+                  uint16_t* out, const uint16_t* w, int E, int K, int renorm, const RouteOut& ro,
+                  const SrsIdentity& ident) {
+  switch (cpl) {
+#define ROUTE_CPL(c)                                                                           \
+  case c:                                                                                      \
+    return launch_cpl<PT, c>(eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K, renorm, \
+                             ro, ident);
+    ROUTE_CPL(1) ROUTE_CPL(2) ROUTE_CPL(4) ROUTE_CPL(8)
+#undef ROUTE_CPL
+    default: return false;
+  }
+}
+
+// bytes of the staged router rows: route_eb(E) rows of CPL * 64 vectors of
+// 16 bytes (the expert bound times CPL is at most 64 exactly when E * CPL is)
+int64_t route_lds(int d, int E) {
+  return static_cast<int64_t>(route_eb(E)) * route_cpl(d / 8) * kWave * 16;
+}
+
+bool route_fits(int P, int d, int E) {
+  if (E < 1 || E > kRouteMaxE) return false;
+  const int cpl = route_cpl(d / 8);
+  if (cpl == 0 || route_lds(d, E) > kRouteWBytes) return false;
+  return P == 1 || P == 2 || (P == 4 && cpl <= 4);
+}
+
+size_t route_ws(int64_t n, int G) {
+  return csort_ws_bytes(n, G) + align_up(static_cast<size_t>(n) * sizeof(int), 256) +
+         align_up(static_cast<size_t>(n) * sizeof(int), 256);
+}
+
+}  // namespace
+}  // namespace route
+
+using namespace route;
+
+ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                                const uint8_t* dest, int32_t G, uint16_t* out,
+                                int32_t* cluster_offsets, int32_t* row_of_src,
+                                int32_t* src_of_row, uint8_t* row_cluster, const uint16_t* w,
+                                int32_t E, float* logits, int32_t K, int32_t renorm,
+                                int32_t* idx, float* weights, const uint8_t* expert_cluster,
+                                unsigned long long* local, void* ws, size_t ws_bytes,
+                                uint32_t* err, hipStream_t s) {
+  if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || G < 1 || E < 1 || K < 1 || K > E ||
+      n >= (int64_t(1) << 31))
+    return ROUTE_ERR_SHAPE;
+  if (G > kMaxClusters || K > kMaxK || !route_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  if (!cluster_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
+    return launch_status();
+  }
+  if (!partials || !out || !w || !idx) return ROUTE_ERR_NULL;
+  if ((expert_cluster == nullptr) != (local == nullptr)) return ROUTE_ERR_NULL;
+  if (!dest && G != 1) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(out) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  const bool sort = dest != nullptr;
+  if (sort && (!ws || ws_bytes < route_ws(n, G))) return ROUTE_ERR_WORKSPACE;
+  const int* fwd = nullptr;
+  if (sort) {
+    char* wsp = static_cast<char*>(ws);
+    const size_t ct = csort_ws_bytes(n, G);
+    const size_t nt = align_up(static_cast<size_t>(n) * sizeof(int), 256);
+    int* fwd_buf = row_of_src ? row_of_src : reinterpret_cast<int*>(wsp + ct);
+    int* inv_buf = src_of_row ? src_of_row : reinterpret_cast<int*>(wsp + ct + nt);
+    const int st = csort_launch<uint8_t>(dest, n, G, cluster_offsets, fwd_buf, inv_buf,
+                                         row_cluster, wsp, err, ROUTE_EBIT_DEST_RANGE, s);
+    if (st != ROUTE_OK) return st;
+    fwd = fwd_buf;
+  }
+  const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
+                                 : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
+  const RouteOut ro{logits, idx, weights, expert_cluster, local};
+  const int64_t need = (n + kRouteWaves - 1) / kRouteWaves;
+  const unsigned grid = static_cast<unsigned>(need < kRouteMaxGrid ? need : kRouteMaxGrid);
+  // the padded router rows (room for the per-wave counts at the end too)
+  size_t lds = static_cast<size_t>(route_lds(d, E));
+  if (lds < kRouteWaves * sizeof(unsigned)) lds = kRouteWaves * sizeof(unsigned);
+  const int cpl = route_cpl(d / 8);
+  const int eb = route_eb(E);
+  bool done = false;
+  if (P == 1)
+    done = launch_route<1>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (P == 2)
+    done = launch_route<2>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (P == 4)
+    done = launch_route<4>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (!done) return ROUTE_ERR_UNSUPPORTED;
+  return launch_status();
+}

@@ -3,7 +3,8 @@
 ``RoutePass``: predict -> SRS -> gate -> top-K -> LAR -> permute -> combine
 (identity experts: the combine reads the dispatched rows themselves), the
 s-MoE layer of the "Speculative MoE" notes (section 3.1 and Figure 3's online
-path) on one GPU.
+path) on one GPU. For small expert sets the SRS, gate, top-K and LAR stages
+are one kernel after the sort (``srs_route``).
 
 ``FoEPass``: cross-group reduce of the H group activations -> gate ->
 grouped top-k/H -> LAR -> permute from the group activations -> combine
@@ -31,13 +32,27 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_gate, route_gate, route_topk, lar_count,
+from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_gate, srs_shuffle_route,
+               route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
                eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
+
+
+def srs_route_fits(P: int, d: int, E: int, K: int) -> bool:
+    """The shapes srs_shuffle_route takes (its UNSUPPORTED rule): one lane per
+    expert; the router rows, padded to C * 512 elements (C the smallest of 1,
+    2, 4, 8 covering d), within 64 KiB; rows of at most 4096 (2048 with four
+    partials); K <= 16."""
+    if not (1 <= E <= 64 and 1 <= K <= min(E, 16) and d % 8 == 0 and 8 <= d <= 4096):
+        return False
+    C = next(c for c in (1, 2, 4, 8) if c * 512 >= d)
+    if E * C * 1024 > 65536:
+        return False
+    return P in (1, 2) or (P == 4 and d <= 2048)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -126,10 +141,15 @@ class RoutePass:
         self.ws_perm = e((max(moe_permute_workspace_size(N, K, E), 1),), torch.uint8)
         self.out = e((N, d), out_dtype)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
-        # the shuffle and the router product in one kernel (srs_shuffle_gate)
-        # for the router shapes of 129..160 columns; two calls otherwise
-        self.fused = P in (1, 2, 4) and d % 128 == 0 and 128 < E <= 160
-        if self.fused:
+        # small expert sets: the shuffle, router, top-K and count in one
+        # kernel after the sort (srs_shuffle_route); 129..160 router columns:
+        # the shuffle and the router product in one (srs_shuffle_gate);
+        # separate calls otherwise
+        self.routed = srs_route_fits(P, d, E, K)
+        self.fused = not self.routed and P in (1, 2, 4) and d % 128 == 0 and 128 < E <= 160
+        if self.routed:
+            self.STAGES = ("predict", "srs_route", "permute", "combine")
+        elif self.fused:
             self.STAGES = ("predict", "srs_gate") + RoutePass.STAGES[3:]
 
     def predict(self):
@@ -152,6 +172,14 @@ class RoutePass:
                          offsets=self.cluster_offsets, row_of_src=self.row_of_src,
                          src_of_row=self.src_of_row, row_cluster=self.row_cluster, ws=self.ws_srs,
                          err=self.err)
+
+    def srs_route(self):
+        srs_shuffle_route(self.partials, self.dest, self.G, self.w, self.K, 1,
+                          expert_cluster=self.expert_cluster, local=self.local, out=self.x,
+                          logits=self.logits, idx=self.idx, weights=self.weights,
+                          offsets=self.cluster_offsets, row_of_src=self.row_of_src,
+                          src_of_row=self.src_of_row, row_cluster=self.row_cluster,
+                          ws=self.ws_srs, err=self.err)
 
     def topk(self):
         route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
