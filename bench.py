@@ -30,12 +30,12 @@ METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofl
 ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
 
 
-def route_bytes(N, d, E, K, P, G, fallback, fused=False, routed=False):
+def route_bytes(N, d, E, K, P, G, fallback, routed=False):
     """Algorithmic HBM bytes per pass: every call reads its inputs once and
     writes its outputs once (bf16 rows = 2 bytes per element). With the
-    shuffle and the router fused (srs_shuffle_gate) the reduced rows are
-    written once and not read back; with the shuffle, router, top-K and count
-    in one kernel (srs_shuffle_route) neither are the logits nor the picks."""
+    shuffle, router, top-K and count in one kernel (srs_shuffle_route) the
+    reduced rows are written once and not read back, and neither are the
+    logits nor the picks."""
     b = 2
     st = {
         "predict": (9 if fallback else 6) * N,
@@ -51,9 +51,6 @@ def route_bytes(N, d, E, K, P, G, fallback, fused=False, routed=False):
                 "srs_route": (st["srs"] + st["gate"] - N * d * b + st["topk"] - 4 * N * E
                               + st["lar"] - 4 * N * K),
                 "permute": st["permute"], "combine": st["combine"]}
-    if fused:
-        st = {"predict": st["predict"], "srs_gate": st.pop("srs") + st.pop("gate") - N * d * b,
-              **{k: v for k, v in st.items() if k != "predict"}}
     return st
 
 
@@ -1019,8 +1016,7 @@ def route_measure(args, name):
                 "K": cfg.K, "G": cfg.G}
     else:
         p = RoutePass(inp)
-        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.fused,
-                               p.routed)
+        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.routed)
         conf = {"workload": ROUTE_WORKLOADS[name], "N": cfg.N, "d": cfg.d, "E": cfg.E,
                 "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
                 "fallback": "2-gram" if p.fallback else "none"}
@@ -1083,7 +1079,7 @@ def route_measure(args, name):
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
     # the stage holding the router product
-    gate_stage = next(g for g in ("gate", "srs_gate", "srs_route") if g in st_us)
+    gate_stage = next(g for g in ("gate", "srs_route") if g in st_us)
     # dominant single-kernel stage: the combine (one launch per pass)
     dom = "combine"
     dom_bytes = bytes_st[dom]
@@ -1112,7 +1108,7 @@ def route_measure(args, name):
         "gate_stage": gate_stage,
         "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us[gate_stage] * 1e-6) / MFMA_BF16_PEAK,
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
-        "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine)",
+        "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine_gather)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK,
                      "traffic": measured_traffic(conf["workload"])},

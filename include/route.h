@@ -182,12 +182,17 @@ int srs_shuffle_gate(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
  *   float[n][K], expert_cluster uint8[E] and local (device uint64,
  *   accumulated); expert_cluster and local are both given or both NULL (no
  *   count). ws: srs_shuffle_workspace_size(n, G).
+ * Two kernels serve it: one lane per expert for small expert sets, the
+ * matrix-core shuffle + router kernel of srs_shuffle_gate (top-K and count
+ * in its epilogue, the same bits as route_topk) up to 160 experts.
  * Errors: as srs_shuffle, plus SHAPE (K < 1, K > E), NULL (w or idx with
- * n > 0; only one of expert_cluster and local), and UNSUPPORTED unless
+ * n > 0; only one of expert_cluster and local), and UNSUPPORTED (K > 16,
+ * or neither kernel takes the shape). The small-set kernel takes
  * 1 <= E <= 64, d <= 4096, E * C * 1024 <= 65536 with C the smallest of
  * 1, 2, 4, 8 such that C * 512 >= d (the router rows, padded to C * 512
  * elements, are staged in on-chip memory), P in {1, 2, 4} (P = 4:
- * d <= 2048) and K <= 16; use the separate calls there. Device bit: DEST_RANGE (rows whose key is out
+ * d <= 2048); the matrix-core kernel P in {1, 2, 4}, d % 128 == 0 and
+ * 1 <= E <= 160. Use the separate calls for other shapes. Device bit: DEST_RANGE (rows whose key is out
  * of range get none of the row outputs and add nothing to *local).
  */
 int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
@@ -299,6 +304,25 @@ int moe_permute_noalloc(const int32_t* idx, int64_t n, int32_t K, int32_t E, int
 int moe_combine(const uint16_t* y, const float* weights, const int32_t* slot_of_pair,
                 int64_t n, int32_t K, int32_t d, const int32_t* out_row, void* out,
                 int32_t out_dtype, uint32_t* err, hipStream_t s);
+
+/*
+ * moe_combine_gather - moe_combine with the unshuffle taken from the other
+ * side: output row t combines token in_row[t].
+ * [SMOE] section 1 and section 3.1 (SAG), as moe_combine. With
+ * in_row[out_row[j]] == j for every j (in_row the inverse permutation, e.g.
+ * srs_shuffle's row_of_src where moe_combine takes its src_of_row) the
+ * output equals moe_combine's bit for bit; here the rows are written in
+ * order and the token's slots and weights are read through in_row.
+ *   out[t] = sum_{k=0..K-1} weights[j][k] * y[slot_of_pair[j*K + k]],
+ *   j = in_row[t]  (binary32, k order); in_row int32[n], a permutation of
+ *   0..n-1; the other arguments as moe_combine.
+ * Errors: as moe_combine, plus NULL (in_row with n > 0).
+ * Device bit: INDEX_RANGE (slot >= n*K, or in_row[t] out of range: row t
+ * is not written).
+ */
+int moe_combine_gather(const uint16_t* y, const float* weights, const int32_t* slot_of_pair,
+                       int64_t n, int32_t K, int32_t d, const int32_t* in_row, void* out,
+                       int32_t out_dtype, uint32_t* err, hipStream_t s);
 
 /*
  * route_qhidden - quasi-hidden state q_l = LN_{l+1}(d_l + r_l).

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 35, names
+    assert len(names) == 36, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -138,12 +138,15 @@ def test_srs_route_errors(L):
     assert call(args(K=0)) == SHAPE
     assert call(args(K=9)) == SHAPE            # K > E
     assert call(args(n=-1)) == SHAPE
-    # one lane per expert, the padded router rows within 64 KiB of LDS,
-    # d <= 4096, P in {1, 2, 4} (four partials up to d = 2048), K <= 16
-    assert call(args(E=65, K=2, d=256)) == UNSUP
-    assert call(args(E=9, d=4096)) == UNSUP
+    # neither kernel: the lane-per-expert one needs E <= 64, the padded
+    # router rows within 64 KiB of LDS, d <= 4096, P in {1, 2, 4} (four
+    # partials up to d = 2048); the matrix-core one d % 128 == 0, E <= 160;
+    # both K <= 16
+    assert call(args(E=65, K=2, d=264)) == UNSUP
+    assert call(args(E=161, d=4096)) == UNSUP
     assert call(args(E=40, d=520)) == UNSUP    # 41600 bytes, 81920 padded
     assert call(args(E=32, d=520, ws=None)) == WS   # 65536 padded: supported
+    assert call(args(E=160, K=6, d=5120, ws=None)) == WS   # the matrix-core kernel
     assert call(args(E=1, K=1, d=4104)) == UNSUP
     assert call(args(P=3)) == UNSUP
     assert call(args(P=4, d=2056, E=4)) == UNSUP
@@ -169,6 +172,12 @@ def test_permute_and_combine_errors(L):
     assert g(A, A, None, 100, 6, 64, None, A, 0, None, None) == NULL
     assert g(A, A, A, 100, 17, 64, None, A, 0, None, None) == UNSUP
     assert g(A, A, A, 0, 6, 64, None, A, 0, None, None) == OK
+    h = L.moe_combine_gather
+    assert h(A, A, A, 100, 6, 64, None, A, 0, None, None) == NULL      # in_row
+    assert h(A, A, A, 100, 6, 64, A, A, 2, None, None) == SHAPE
+    assert h(A, A, A, 100, 17, 64, A, A, 0, None, None) == UNSUP
+    assert h(A, A, A, 100, 6, 64, A, MIS, 0, None, None) == ALIGN
+    assert h(A, A, A, 0, 6, 64, None, A, 0, None, None) == OK
 
 
 def test_permute_noalloc_errors(L):

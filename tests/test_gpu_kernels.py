@@ -215,6 +215,56 @@ def test_permute_and_combine(n, E, K, H, d):
     o16n = host(tr.moe_combine(disp, w, sop))
     if H == 1:
         assert np.array_equal(o16n, src[0])
+    # the gather form of the unshuffle (row t combines token in_row[t]): the
+    # scatter form's bytes, both output types
+    in_row = np.empty(n, dtype=np.int32)
+    in_row[out_row] = np.arange(n, dtype=np.int32)
+    g16 = tr.moe_combine(disp, w, sop, in_row=dev(in_row))
+    assert np.array_equal(host(g16), host(o16))
+    g32 = tr.moe_combine(disp, w, sop, in_row=dev(in_row), out_dtype=torch.float32)
+    assert np.array_equal(host(g32), host(o32))
+
+
+@pytest.mark.parametrize("K,d", [(2, 4096), (6, 5120), (8, 128), (3, 136), (1, 8)])
+def test_combine_gather_form(K, d):
+    """moe_combine_gather against the oracle's combine (rows placed by the
+    inverse map) and against the scatter form's bytes, for the instantiated
+    K (2, 6, 8) and the plain loop (3, 1), full and ragged rows."""
+    n = 777
+    rng = np.random.default_rng(K * 1000 + d)
+    y = _bf16((n * K, d), K + d)
+    w = rng.random((n, K)).astype(np.float32)
+    sop = rng.permutation(n * K).astype(np.int32)
+    out_row = rng.permutation(n).astype(np.int32)
+    in_row = np.empty(n, dtype=np.int32)
+    in_row[out_row] = np.arange(n, dtype=np.int32)
+    ref = oracle.moe_combine(y, w.astype(np.float64), sop, out_row)
+    g = tr.moe_combine(dev(y), dev(w), dev(sop), in_row=dev(in_row))
+    assert_bf16(host(g), ref, "combine gather bf16")
+    s = tr.moe_combine(dev(y), dev(w), dev(sop), out_row=dev(out_row))
+    assert np.array_equal(host(g), host(s))
+
+
+def test_combine_gather_flags_bad_row():
+    """An in_row entry out of range is flagged and its output row left as it
+    was; every other row is combined."""
+    n, K, d = 100, 2, 64
+    rng = np.random.default_rng(3)
+    y = _bf16((n * K, d), 5)
+    w = rng.random((n, K)).astype(np.float32)
+    sop = rng.permutation(n * K).astype(np.int32)
+    in_row = rng.permutation(n).astype(np.int32)
+    in_row[17] = n + 4
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((n, d), 2.0, dtype=torch.bfloat16, device="cuda")
+    tr.moe_combine(dev(y), dev(w), dev(sop), in_row=dev(in_row), out=out, err=err)
+    sync()
+    assert int(err.item()) & tr.EBIT_INDEX_RANGE
+    o = host(out)
+    assert np.all(o[17] == 0x4000)                      # bf16 2.0, untouched
+    keep = np.array([t for t in range(n) if t != 17])
+    full = oracle.moe_combine(y, w.astype(np.float64), sop, None)
+    assert_bf16(o[keep], full[in_row[keep]], "combine gather, valid rows")
 
 
 def test_permute_indices_only_and_empty():
@@ -379,16 +429,17 @@ def test_run_twice_bitwise_foe_and_predictor():
 
 
 # ------------------------------------------------------------ graph replay
-@pytest.mark.parametrize("E,mode", [(160, "fused"), (64, "routed"), (96, "separate")])
-def test_graph_replay_matches_eager(E, mode):
+@pytest.mark.parametrize("E,d,routed", [(160, 512, True), (64, 512, True), (96, 520, False)])
+def test_graph_replay_matches_eager(E, d, routed):
     """The benchmark replays the pass as a captured graph: every replay, with
     eager work and synchronisations in between, must equal the eager pass
-    (the shuffle and the router product in one kernel at 160 columns; the
-    shuffle, router, top-K and count in one at 64; separate calls at 96)."""
+    (the shuffle, router, top-K and count in one kernel: the matrix-core one
+    at 160 columns, the lane-per-expert one at 64; separate calls where
+    neither takes the shape)."""
     from token_routing_speculation_amd.pipeline import RoutePass, capture_graph
-    inp = make_route_inputs(2000, 512, E, 6, 2, 8, 5000, 91, ngram=True)
+    inp = make_route_inputs(2000, d, E, 6, 2, 8, 5000, 91, ngram=True)
     p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
-    assert (p.fused, p.routed) == (mode == "fused", mode == "routed")
+    assert p.routed == routed
     keys = ("dest", "x", "row_of_src", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
     p.step()
     sync()

@@ -70,7 +70,12 @@ def _check(parts, dest, G, w, K, ec, renorm, got, local):
 CASES = [(1, 128, 2, 2, 4, 2), (7, 64, 1, 3, 3, 1), (64, 128, 2, 2, 4, 2),
          (1000, 520, 2, 8, 8, 2), (777, 384, 4, 5, 16, 4), (333, 1024, 1, 8, 32, 8),
          (129, 2048, 4, 3, 16, 16), (500, 512, 2, 4, 64, 6), (300, 256, 2, 256, 1, 1),
-         (4096, 4096, 2, 4, 8, 2), (9000, 256, 2, 8, 8, 2)]
+         (4096, 4096, 2, 4, 8, 2), (9000, 256, 2, 8, 8, 2),
+         # the matrix-core kernel (65..160 experts, d % 128 == 0), with the
+         # top-K in its epilogue: the DeepSeek-V2 width, K up to 16, every P,
+         # a ragged last tile, one row
+         (1000, 512, 2, 8, 160, 6), (777, 384, 4, 5, 150, 8), (513, 1024, 1, 8, 100, 16),
+         (2049, 5120, 2, 8, 160, 6), (64, 128, 2, 2, 65, 1), (1, 256, 2, 3, 160, 6)]
 
 
 @pytest.mark.parametrize("n,d,P,G,E,K", CASES)
@@ -80,19 +85,43 @@ def test_srs_route_against_oracle(n, d, P, G, E, K):
     _check(parts, dest, G, w, K, ec, 1, got, local)
 
 
-def test_srs_route_full_softmax_and_no_count():
+@pytest.mark.parametrize("E,K", [(12, 3), (160, 6)])
+def test_srs_route_full_softmax_and_no_count(E, K):
     """renorm = 0 (softmax over all E, read at the picks); no count."""
-    n, d, P, G, E, K = 700, 640, 2, 4, 12, 3
+    n, d, P, G = 700, 640, 2, 4
     parts, dest, w, _ = _inputs(n, d, P, G, E)
     got, local = _run(parts, dest, G, w, K, None, renorm=0)
     _check(parts, dest, G, w, K, None, 0, got, local)
 
 
-def test_srs_route_without_logits():
+@pytest.mark.parametrize("E,K", [(160, 6), (150, 8)])
+def test_srs_route_matrix_core_equals_separate_calls(E, K):
+    """The matrix-core path against srs_shuffle_gate + route_topk + lar_count
+    on the GPU: the logits are the same kernel's, so the picks match bit for
+    bit; the weights too where route_topk has a fixed-shape kernel of the
+    same arithmetic (160 experts, K = 6), else within a few ulp."""
+    n, d, P, G = 3000, 1024, 2, 8
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    (out, offs, ros, sor, rc, lg, idx, wt), local = _run(parts, dest, G, w, K, ec)
+    o2, f2, r2, s2, c2, l2 = tr.srs_shuffle_gate(dev(parts), dev(dest), G, dev(w))
+    i2, w2 = tr.route_topk(l2, K, 1, 1)
+    loc2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tr.lar_count(i2, 1, c2, dev(ec), loc2)
+    sync()
+    assert torch.equal(out, o2) and torch.equal(lg, l2) and torch.equal(idx, i2)
+    if (E, K) == (160, 6):
+        assert torch.equal(wt, w2)
+    else:
+        np.testing.assert_allclose(host(wt), host(w2), rtol=1e-6, atol=1e-8)
+    assert int(local.item()) == int(loc2.item())
+
+
+@pytest.mark.parametrize("E", [8, 160])
+def test_srs_route_without_logits(E):
     """Leaving the logits out changes nothing else: the same picks, weights
     and count as the call that writes them (itself checked against the
     oracle)."""
-    n, d, P, G, E, K = 640, 1024, 2, 4, 8, 2
+    n, d, P, G, K = 640, 1024, 2, 4, 2
     parts, dest, w, ec = _inputs(n, d, P, G, E)
     got, local = _run(parts, dest, G, w, K, ec)
     _check(parts, dest, G, w, K, ec, 1, got, local)
@@ -117,11 +146,12 @@ def test_srs_route_pure_reduce_without_dest():
     _check(parts, None, 1, w, K, ec, 1, got, local)
 
 
-def test_srs_route_ties_go_to_the_lower_expert():
+@pytest.mark.parametrize("E", [16, 160])
+def test_srs_route_ties_go_to_the_lower_expert(E):
     """Equal router rows give bit-equal logits: the lower index ranks first.
     All-zero rows give +0 logits for every expert (from -0.0 partials too),
     so the picks are experts 0..K-1 with equal weights."""
-    n, d, P, G, E, K = 256, 512, 2, 4, 16, 4
+    n, d, P, G, K = 256, 512, 2, 4, 4
     parts, dest, w, ec = _inputs(n, d, P, G, E)
     w[9] = w[2]
     w[14] = w[2]
@@ -146,10 +176,11 @@ def test_srs_route_empty():
     assert host(r[1]).tolist() == [0] * 5 and r[6].shape == (0, 2)
 
 
-def test_srs_route_flags_bad_cluster_and_skips_its_row():
+@pytest.mark.parametrize("E,K", [(8, 2), (160, 6)])
+def test_srs_route_flags_bad_cluster_and_skips_its_row(E, K):
     """A key past G is flagged; its row gets no outputs and adds nothing to
     the count; every other row is exact."""
-    n, d, G, E, K = 200, 256, 4, 8, 2
+    n, d, G = 200, 256, 4
     parts, dest, w, ec = _inputs(n, d, 2, G, E)
     dest[7] = 9
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -170,9 +201,10 @@ def test_srs_route_flags_bad_cluster_and_skips_its_row():
     assert int(local.item()) == oracle.lar_count(widx, K, 1, dest[keep].astype(np.int64), ec)
 
 
-def test_srs_route_count_accumulates():
+@pytest.mark.parametrize("E,K", [(8, 2), (160, 6)])
+def test_srs_route_count_accumulates(E, K):
     """The count adds to what the counter holds."""
-    n, d, P, G, E, K = 500, 256, 2, 4, 8, 2
+    n, d, P, G = 500, 256, 2, 4
     parts, dest, w, ec = _inputs(n, d, P, G, E)
     local = torch.full((1,), 1000, dtype=torch.int64, device="cuda")
     r = tr.srs_shuffle_route(dev(parts), dev(dest), G, dev(w), K, expert_cluster=dev(ec), local=local)

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "RouteError", "lib", "library_path",
     "route_predict", "route_lut_build", "srs_shuffle", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
-    "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "route_qhidden",
+    "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "moe_combine_gather", "route_qhidden",
     "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
     "route_estimator_workspace_size", "eg_profile", "eg_init", "eg_sample",
@@ -64,6 +64,7 @@ EXPORTS = {
     "moe_permute_noalloc": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p,
                                            _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
+    "moe_combine_gather": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p, _p, _i32, _p, _p]),
     "route_qhidden": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p]),
     "route_qgate": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _p, _p]),
     "route_qgate_topk": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _i32, _p, _p,
@@ -364,16 +365,24 @@ def moe_permute_noalloc(idx, E, src=None, H=1, expert_offsets=None, slot_of_pair
 
 
 def moe_combine(y, weights, slot_of_pair, out_row=None, out=None, out_dtype=torch.bfloat16,
-                err=None, stream=None):
+                err=None, stream=None, in_row=None):
+    """Weighted combine with the unshuffle: out[out_row[j]] = o[j] (moe_combine),
+    or, given ``in_row`` instead, out[t] = o[in_row[t]] (moe_combine_gather)."""
     n, K = weights.shape
     d = y.shape[1]
     code = {torch.bfloat16: 0, torch.int16: 0, torch.float32: 1}[out.dtype if out is not None else out_dtype]
     if out is None:
         out = _empty((n, d), out_dtype, y)
-    _call("moe_combine", _dev(y, _bf16(y), "y", n * K * d), _dev(weights, torch.float32, "weights"),
-          _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K), n, K, d,
-          _opt(out_row, torch.int32, "out_row", n), _dev(out, out.dtype, "out", n * d), code,
-          _opt(err, torch.int32, "err", 1), _stream(stream))
+    if in_row is not None and out_row is not None:
+        raise ValueError("give out_row or in_row, not both")
+    common = (_dev(y, _bf16(y), "y", n * K * d), _dev(weights, torch.float32, "weights"),
+              _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K), n, K, d)
+    tail = (_dev(out, out.dtype, "out", n * d), code, _opt(err, torch.int32, "err", 1),
+            _stream(stream))
+    if in_row is not None:
+        _call("moe_combine_gather", *common, _dev(in_row, torch.int32, "in_row", n), *tail)
+    else:
+        _call("moe_combine", *common, _opt(out_row, torch.int32, "out_row", n), *tail)
     return out
 
 

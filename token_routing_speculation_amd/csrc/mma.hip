@@ -30,6 +30,7 @@
 #include "gemm.hpp"
 #include "mfma.hpp"
 #include "srs.hpp"
+#include "topk.hpp"
 
 namespace route {
 
@@ -412,7 +413,7 @@ template <int PT>
 __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
     const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ W, int E, float* __restrict__ logits,
-    SrsIdentity ident) {
+    SrsIdentity ident, GateTopk tk) {
   constexpr int BM = 64, BN = 160;
   constexpr int MT = 2, NT = 5;             // 16 x 16 tiles per wave
   constexpr int STAGE = (BM + BN) * 128;    // 28 KB
@@ -606,23 +607,73 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
       for (int t = 0; t < NT; ++t) red[((w4 * MT + m) * NT + t) * kWave + lane] = acc[m][t];
   }
   __syncthreads();
-  if (g == 1) return;
+  // with the top-K, the finished tile also goes to LDS, after the partial
+  // tiles: [BM][BN] binary32, the columns past E as -inf
+  float* tile = reinterpret_cast<float*>(lds + MT * NT * 4 * kWave * sizeof(f32x4));
+  if (g == 0) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = row0 + wr * 32 + 16 * m + 4 * (lane >> 4) + j;
-      if (row >= n) continue;
-      const int dst = row_of_src ? row_of_src[row] : static_cast<int>(row);
-      if (dst < 0 || dst >= n) continue;
+      for (int j = 0; j < 4; ++j) {
+        const int r = wr * 32 + 16 * m + 4 * (lane >> 4) + j;
+        const int64_t row = row0 + r;
+        int dst = -1;
+        if (row < n) dst = row_of_src ? row_of_src[row] : static_cast<int>(row);
+        const bool ok = dst >= 0 && dst < n;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int col = wc * 80 + 16 * t + (lane & 15);
-        if (col < E)
-          logits[static_cast<int64_t>(dst) * E + col] =
-              acc[m][t][j] + red[((w4 * MT + m) * NT + t) * kWave + lane][j];
+        for (int t = 0; t < NT; ++t) {
+          const int col = wc * 80 + 16 * t + (lane & 15);
+          const float v = acc[m][t][j] + red[((w4 * MT + m) * NT + t) * kWave + lane][j];
+          if (logits && ok && col < E) logits[static_cast<int64_t>(dst) * E + col] = v;
+          if (tk.idx) tile[r * BN + col] = col < E ? v : -__builtin_inff();
+        }
       }
+  }
+  if (!tk.idx) return;
+  __syncthreads();
+  // Top-K of each row from the tile: one row per 16-lane segment (ten values
+  // a lane), the eight waves taking 32 rows at a time.
+  unsigned hits = 0;
+  const int s16 = lane & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = half * 32 + w * 4 + (lane >> 4);
+    const int64_t row = row0 + r;
+    float val[BN / 16];
+    uint32_t key[BN / 16];
+#pragma unroll
+    for (int v = 0; v < BN / 16; ++v) {
+      val[v] = tile[r * BN + s16 + 16 * v];
+      key[v] = s16 + 16 * v < E ? order_key(val[v]) : 0u;
     }
+    int col;
+    float wgt;
+    seg_topk<16, BN / 16>(val, key, tk.K, tk.renorm, &col, &wgt);
+    int dst = -1;
+    if (row < n) dst = row_of_src ? row_of_src[row] : static_cast<int>(row);
+    const bool pick = dst >= 0 && dst < n && s16 < tk.K;
+    if (pick) {
+      tk.idx[static_cast<int64_t>(dst) * tk.K + s16] = col;
+      if (tk.weights) tk.weights[static_cast<int64_t>(dst) * tk.K + s16] = wgt;
+    }
+    if (tk.expert_cluster) {
+      const int cl = tk.dest && row < n ? static_cast<int>(tk.dest[row]) : 0;
+      hits += __popcll(__ballot(pick && static_cast<int>(tk.expert_cluster[col]) == cl));
+    }
+  }
+  if (tk.expert_cluster) {
+    // the workgroup's count, one atomic: the partial tiles' LDS takes it
+    __syncthreads();
+    unsigned* cnt = reinterpret_cast<unsigned*>(lds);
+    if (lane == 0) cnt[w] = hits;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long tot = 0;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) tot += cnt[v];
+      if (tot) atomicAdd(tk.local, tot);
+    }
+  }
 }
 }  // namespace
 
@@ -654,18 +705,19 @@ bool srs_gate_fits(int P, int d, int E) {
 
 int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int* row_of_src,
                     uint16_t* out, const uint16_t* w, int E, float* logits,
-                    const SrsIdentity& ident, hipStream_t s) {
+                    const SrsIdentity& ident, const GateTopk* topk, hipStream_t s) {
   if (!srs_gate_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  const GateTopk tk = topk ? *topk : GateTopk{0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
   const unsigned grid = ceil_div(n, 64);
   if (P == 1)
     srs_gate160_kernel<1><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident);
+                                                        logits, ident, tk);
   else if (P == 2)
     srs_gate160_kernel<2><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident);
+                                                        logits, ident, tk);
   else
     srs_gate160_kernel<4><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident);
+                                                        logits, ident, tk);
   return launch_status();
 }
 

@@ -213,5 +213,5 @@ ROUTE_API int srs_shuffle_gate(const uint16_t* partials, int32_t P, int64_t n, i
   }
   const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
                                  : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
-  return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, s);
+  return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, nullptr, s);
 }

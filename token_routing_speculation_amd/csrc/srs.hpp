@@ -28,15 +28,31 @@ __device__ __forceinline__ void write_identity_row(const SrsIdentity& id, int64_
   if (id.row_cluster) id.row_cluster[i] = 0;
 }
 
+// The router's top-K and local count taken in the fused kernel's epilogue
+// (srs_shuffle_route): idx [n][K] and weights [n][K] (nullable) at the sorted
+// row, *local += the picks whose expert_cluster equals the row's predicted
+// cluster dest[i] (0 without dest); no count when expert_cluster is null.
+struct GateTopk {
+  int K;
+  int renorm;
+  int* idx;
+  float* weights;
+  const uint8_t* dest;
+  const uint8_t* expert_cluster;
+  unsigned long long* local;
+};
+
 // mma.hip: the fused shuffle + router kernel for 1 <= E <= 160 columns,
 // P in {1, 2, 4} partials and d % 128 == 0 (d >= 128). out[dst(i)] =
 // bf16(sum_p partials[p][i]) exactly as the row mover computes it, and
 // logits[dst(i)][e] = out[dst(i)] . w[e] (binary32), dst(i) = row_of_src[i]
 // (the identity when row_of_src is null; rows whose dst is out of range are
-// skipped). Returns ROUTE_ERR_UNSUPPORTED for any other shape.
+// skipped; logits may be null when topk is given). With topk (nullable) the
+// epilogue also takes each row's top-K and count. Returns
+// ROUTE_ERR_UNSUPPORTED for any other shape.
 bool srs_gate_fits(int P, int d, int E);
 int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int* row_of_src,
                     uint16_t* out, const uint16_t* w, int E, float* logits,
-                    const SrsIdentity& ident, hipStream_t s);
+                    const SrsIdentity& ident, const GateTopk* topk, hipStream_t s);
 
 }  // namespace route

@@ -1,11 +1,13 @@
 // srs_shuffle_route: the shuffled reduce of "Speculative MoE" (section 3.1,
-// s-TS) carried on through the router of a small expert set while each
-// reduced row is still in registers: router logits ("Federation of Experts
+// s-TS) carried on through the router while each reduced row is still on
+// chip: router logits ("Federation of Experts
 // (FoE)" article, router scores g[i]), top-K with its softmax weights, and
 // the local activation count ("Speculative MoE" glossary) against the row's
-// predicted cluster. For E <= 32 the router is a handful of dot products per
-// row; run as separate launches it costs a re-read of the rows and three
-// launches that each do almost nothing, so here it rides along with the move.
+// predicted cluster. For a small expert set (this file's kernel) the router
+// is a handful of dot products per row; run as separate launches it costs a
+// re-read of the rows and three launches that each do almost nothing, so it
+// rides along with the move. For 65..160 experts the matrix-core shuffle +
+// router kernel (mma.hip) takes the top-K and the count in its epilogue.
 //
 // Layout of the work. The router rows w [E][d] are staged once per workgroup
 // into LDS, each padded with zeros to a whole number of 64-lane vector sets
@@ -330,7 +332,11 @@ ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, 
   if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || G < 1 || E < 1 || K < 1 || K > E ||
       n >= (int64_t(1) << 31))
     return ROUTE_ERR_SHAPE;
-  if (G > kMaxClusters || K > kMaxK || !route_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  // the lane-per-expert kernel for small expert sets, else the matrix-core
+  // shuffle + router kernel with the top-K in its epilogue
+  const bool small = route_fits(P, d, E);
+  if (G > kMaxClusters || K > kMaxK || (!small && !srs_gate_fits(P, d, E)))
+    return ROUTE_ERR_UNSUPPORTED;
   if (!cluster_offsets) return ROUTE_ERR_NULL;
   if (n == 0) {
     fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
@@ -356,6 +362,10 @@ ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, 
   }
   const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
                                  : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
+  if (!small) {
+    const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local};
+    return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
+  }
   const RouteOut ro{logits, idx, weights, expert_cluster, local};
   const int64_t need = (n + kRouteWaves - 1) / kRouteWaves;
   const unsigned grid = static_cast<unsigned>(need < kRouteMaxGrid ? need : kRouteMaxGrid);

@@ -63,4 +63,63 @@ __device__ __forceinline__ uint32_t seg_min(uint32_t v) {
   return v;
 }
 
+// Top-K of one row held by an aligned segment of S lanes (S >= 16), V values
+// per lane: lane s holds columns s + S v, their order keys in key[] (0 for an
+// absent column, whose value must then be -inf). Picks go in the library's
+// order, larger key first and the lower column on equal keys; each round
+// takes the segment's best key, the lowest column holding it, and clears it.
+// K (<= kMaxK) may vary at run time. On return lane s < K of the segment
+// holds pick s: its column and its softmax weight, over the K picks
+// (renorm) or over every present column (renorm = 0). The arithmetic is the
+// fixed-shape top-K kernel's with one group, so the results are the same
+// bits.
+template <int S, int V>
+__device__ __forceinline__ void seg_topk(const float (&val)[V], uint32_t (&key)[V], int K,
+                                         int renorm, int* col, float* weight) {
+  const int s = lane_id() & (S - 1);
+  float mysel = 0.f, top = 0.f;
+  int mycol = 0;
+#pragma unroll
+  for (int r = 0; r < kMaxK; ++r) {
+    if (r >= K) break;
+    uint32_t best = 0u;
+    int bv = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if (key[v] > best) {  // strict: lowest v on equal keys
+        best = key[v];
+        bv = v;
+      }
+    }
+    const uint32_t m = seg_max<S>(best);
+    const int c =
+        static_cast<int>(seg_min<S>(best == m ? static_cast<uint32_t>(s + S * bv) : 0xffffffffu));
+    const bool mine = s == (c & (S - 1));
+#pragma unroll
+    for (int v = 0; v < V; ++v) key[v] = (mine && bv == v) ? 0u : key[v];
+    if (r == 0) top = key_float(m);
+    if (s == r) {
+      mysel = key_float(m);
+      mycol = c;
+    }
+  }
+  float w;
+  if (renorm) {
+    const float e = s < K ? __expf(mysel - top) : 0.f;
+    float z = e;
+#pragma unroll
+    for (int o = S / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+    w = __fdividef(e, z);
+  } else {
+    float zl = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) zl += __expf(val[v] - top);
+#pragma unroll
+    for (int o = S / 2; o > 0; o >>= 1) zl += __shfl_xor(zl, o, kWave);
+    w = __fdividef(__expf(mysel - top), zl);
+  }
+  *col = mycol;
+  *weight = w;
+}
+
 }  // namespace route

@@ -32,7 +32,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_gate, srs_shuffle_route,
+from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_route,
                route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
@@ -53,6 +53,16 @@ def srs_route_fits(P: int, d: int, E: int, K: int) -> bool:
     if E * C * 1024 > 65536:
         return False
     return P in (1, 2) or (P == 4 and d <= 2048)
+
+
+def srs_route_takes(P: int, d: int, E: int, K: int) -> bool:
+    """Whether srs_shuffle_route takes the shape at all: the small-set kernel
+    (srs_route_fits) or the matrix-core shuffle + router kernel (P in 1, 2,
+    4; d % 128 == 0; E <= 160)."""
+    if not 1 <= K <= min(E, 16):
+        return False
+    return srs_route_fits(P, d, E, K) or (P in (1, 2, 4) and d >= 128 and d % 128 == 0
+                                          and 1 <= E <= 160)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -141,16 +151,12 @@ class RoutePass:
         self.ws_perm = e((max(moe_permute_workspace_size(N, K, E), 1),), torch.uint8)
         self.out = e((N, d), out_dtype)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
-        # small expert sets: the shuffle, router, top-K and count in one
-        # kernel after the sort (srs_shuffle_route); 129..160 router columns:
-        # the shuffle and the router product in one (srs_shuffle_gate);
-        # separate calls otherwise
-        self.routed = srs_route_fits(P, d, E, K)
-        self.fused = not self.routed and P in (1, 2, 4) and d % 128 == 0 and 128 < E <= 160
+        # the shuffle, router, top-K and count in one kernel after the sort
+        # (srs_shuffle_route) where it takes the shape; separate calls
+        # otherwise
+        self.routed = srs_route_takes(P, d, E, K)
         if self.routed:
             self.STAGES = ("predict", "srs_route", "permute", "combine")
-        elif self.fused:
-            self.STAGES = ("predict", "srs_gate") + RoutePass.STAGES[3:]
 
     def predict(self):
         if self.fallback:
@@ -166,12 +172,6 @@ class RoutePass:
 
     def gate(self):
         route_gate(self.x, self.w, logits=self.logits)
-
-    def srs_gate(self):
-        srs_shuffle_gate(self.partials, self.dest, self.G, self.w, out=self.x, logits=self.logits,
-                         offsets=self.cluster_offsets, row_of_src=self.row_of_src,
-                         src_of_row=self.src_of_row, row_cluster=self.row_cluster, ws=self.ws_srs,
-                         err=self.err)
 
     def srs_route(self):
         srs_shuffle_route(self.partials, self.dest, self.G, self.w, self.K, 1,
@@ -193,7 +193,9 @@ class RoutePass:
                     disp=self.disp, ws=self.ws_perm, err=self.err)
 
     def combine(self):
-        moe_combine(self.disp, self.weights, self.slot_of_pair, out_row=self.src_of_row,
+        # the unshuffle in gather form: output row t combines shuffled row
+        # row_of_src[t], so the rows are written in order
+        moe_combine(self.disp, self.weights, self.slot_of_pair, in_row=self.row_of_src,
                     out=self.out, err=self.err)
 
     STAGES = ("predict", "srs", "gate", "topk", "lar", "permute", "combine")
