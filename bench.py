@@ -1108,7 +1108,9 @@ def route_measure(args, name):
         "gate_stage": gate_stage,
         "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us[gate_stage] * 1e-6) / MFMA_BF16_PEAK,
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
-        "roofline": {"bound": "hbm", "kernel": "combine_kernel (moe_combine_gather)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("combine_kernel (moe_combine)" if name == "foe"
+                                else "combine_kernel (moe_combine_gather)"),
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK,
                      "traffic": measured_traffic(conf["workload"])},
