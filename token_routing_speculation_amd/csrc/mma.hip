@@ -657,8 +657,11 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
       if (tk.weights) tk.weights[static_cast<int64_t>(dst) * tk.K + s16] = wgt;
     }
     if (tk.expert_cluster) {
+      // (a NaN logit with every bit set has key 0 like the columns past E and
+      // may tie with them: outside the contract, but no read past E)
       const int cl = tk.dest && row < n ? static_cast<int>(tk.dest[row]) : 0;
-      hits += __popcll(__ballot(pick && static_cast<int>(tk.expert_cluster[col]) == cl));
+      const int ec = pick && col < E ? static_cast<int>(tk.expert_cluster[col]) : -1;
+      hits += __popcll(__ballot(ec == cl));
     }
   }
   if (tk.expert_cluster) {
