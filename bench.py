@@ -497,15 +497,15 @@ def predictor_measure(args):
         return {k_: round(float(np.median(v)), 2) for k_, v in tt.items()}
 
     def fused_stage_times(i):
-        from token_routing_speculation_amd import route_qgate_topk
+        from token_routing_speculation_amd import route_qgate_topk_packed
         p.layer, p.truth = layers[i], truths[i]
         L_ = p.layer
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         tt = {"qgate_topk_hits": []}
         for _ in range(10):
             e[0].record(stream)
-            route_qgate_topk(L_["r"], L_["dvec"], L_["w_next"], p.K, eps=L_["eps"], idx=p.pred,
-                             truth=p.truth, hits=p.hits)
+            route_qgate_topk_packed(L_["r"], L_["dvec"], L_["w_next_packed"], p.E, p.K,
+                                    eps=L_["eps"], idx=p.pred, truth=p.truth, hits=p.hits)
             e[1].record(stream)
             torch.cuda.synchronize()
             for j, k_ in enumerate(tt):
@@ -525,9 +525,13 @@ def predictor_measure(args):
         b.record(stream)
         torch.cuda.synchronize()
         return 1e3 * a.elapsed_time(b) / reps
-    from token_routing_speculation_amd import route_qgate_topk
+    from token_routing_speculation_amd import route_qgate_topk, route_qgate_topk_packed
     Lg = layers[cfg.L - 2]
     qg_launch_us = back_to_back_us(
+        lambda: route_qgate_topk_packed(Lg["r"], Lg["dvec"], Lg["w_next_packed"], p.E, p.K,
+                                        eps=Lg["eps"], idx=p.pred, truth=p.truth, hits=p.hits))
+    # the same call on the router's plain rows, for comparison
+    qg_unpacked_us = back_to_back_us(
         lambda: route_qgate_topk(Lg["r"], Lg["dvec"], Lg["w_next"], p.K, eps=Lg["eps"], idx=p.pred,
                                  truth=p.truth, hits=p.hits))
     # hit rates per layer (one sweep from zeroed counters)
@@ -574,7 +578,8 @@ def predictor_measure(args):
                     "stages_us_gate_layer": st_gate},
         "stages_us_gate_layer": st_fused, "stages_us_estimator_layer": st_est,
         "qgate_topk_us_per_launch": qg_launch_us,
-        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, 1> (route_qgate_topk)",
+        "qgate_topk_unpacked_us_per_launch": qg_unpacked_us,
+        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, 1, true> (route_qgate_topk_packed)",
                      "achieved": byt_fused["qgate_topk"] / (qg_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK,

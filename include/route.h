@@ -373,6 +373,39 @@ int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma, c
                      hipStream_t s);
 
 /*
+ * route_gate_packed_size - bytes of route_gate_pack's output for E router
+ * rows of d elements: ceil(E / 16) * 16 * d * 2, or 0 for a shape it does
+ * not take (E < 1, d % 32 != 0).
+ */
+size_t route_gate_packed_size(int32_t E, int32_t d);
+
+/*
+ * route_gate_pack - a router's rows in the fragment order route_qgate_topk_packed
+ * reads. [SPEC] item 2.A (the next layer's router, a fixed weight of the
+ * model, applied to q_l on every step): packed once, read on every call.
+ *   w bf16 rows [E][d]; wp bf16, route_gate_packed_size(E, d) bytes:
+ *   wp[((g * (d/32) + t) * 64 + l) * 8 + e] = w[16 g + l % 16][32 t + 8 (l / 16) + e]
+ *   for groups g of 16 rows, K steps t of 32 and lanes l < 64 (rows past E
+ *   are zeros). Both pointers 16-byte aligned.
+ * Errors: SHAPE (E < 1, d % 32 != 0), UNSUPPORTED (E > 1024), NULL, ALIGN.
+ */
+int route_gate_pack(const uint16_t* w, int32_t E, int32_t d, uint16_t* wp, hipStream_t s);
+
+/*
+ * route_qgate_topk_packed - route_qgate_topk with the router given packed
+ * (wp from route_gate_pack for the same E and d). [SPEC] items 2.A and 4.
+ * The same results, bit for bit: the matrix products see the same operands
+ * in the same order, read straight into registers instead of through a
+ * per-wave transpose in on-chip memory.
+ * Errors: as route_qgate_topk.
+ */
+int route_qgate_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                            const float* beta, int64_t n, int32_t d, float eps,
+                            const uint16_t* wp, int32_t E, int32_t K, float* logits,
+                            int32_t* idx, const int32_t* truth, unsigned long long* hits,
+                            hipStream_t s);
+
+/*
  * route_estimator - lightweight neural estimator of next-layer logits.
  * [SPEC] item 2.C: logits = GELU(q . w1^T + b1) . w2^T + b2 (GELU with erf).
  * The hidden activation is kept in bf16 (nearest even) in the workspace

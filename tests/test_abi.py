@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 36, names
+    assert len(names) == 39, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -355,4 +355,24 @@ def test_qgate_topk_errors(L):
     assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, A, A, None, None) == NULL  # truth without hits
     assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 8, None, A, None, A, None) == NULL  # hits without truth
     assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, 8, None, A, None, None, None) == OK
+
+
+def test_qgate_packed_errors(L):
+    """The packed form's checks are the unpacked one's; packing takes d % 32 == 0."""
+    f = L.route_qgate_topk_packed
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 128, 0, None, A, None, None, None) == SHAPE
+    assert f(A, A, None, None, 10, 2048, 1e-5, A, 257, 8, None, A, None, None, None) == UNSUP
+    assert f(A, A, None, None, 10, 512, 1e-5, A, 128, 8, None, A, None, None, None) == UNSUP
+    assert f(A, A, None, None, 10, 2048, 1e-5, None, 128, 8, None, A, None, None, None) == NULL
+    assert f(A, A, None, None, 10, 2048, 1e-5, MIS, 128, 8, None, A, None, None, None) == ALIGN
+    assert f(A, A, None, None, 0, 2048, 1e-5, A, 128, 8, None, A, None, None, None) == OK
+    g = L.route_gate_pack
+    assert g(A, 128, 2040, A, None) == SHAPE
+    assert g(A, 0, 2048, A, None) == SHAPE
+    assert g(A, 1025, 2048, A, None) == UNSUP
+    assert g(None, 128, 2048, A, None) == NULL
+    assert g(A, 128, 2048, MIS, None) == ALIGN
+    assert L.route_gate_packed_size(128, 2048) == 128 * 2048 * 2
+    assert L.route_gate_packed_size(100, 1024) == 112 * 1024 * 2   # rows padded to 16
+    assert L.route_gate_packed_size(8, 100) == 0
 

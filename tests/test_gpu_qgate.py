@@ -157,3 +157,53 @@ def test_qgate_topk_hits_when_truth_is_the_prediction():
     hits = torch.zeros(1, dtype=torch.int64, device="cuda")
     tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, truth=idx.clone(), hits=hits)
     assert int(host(hits)[0]) == n * K
+
+
+def _pack_ref(w, d):
+    """route_gate_pack's layout written out from its definition: group g of
+    16 rows, K step t of 32, lane l holds w[16 g + l % 16][32 t + 8 (l // 16) + e],
+    e < 8; rows past E are zeros."""
+    E = w.shape[0]
+    G = (E + 15) // 16
+    wpad = np.zeros((16 * G, d), dtype=np.uint16)
+    wpad[:E] = w
+    out = np.empty((G, d // 32, 64, 8), dtype=np.uint16)
+    for l in range(64):
+        rows = 16 * np.arange(G) + (l % 16)
+        for t in range(d // 32):
+            out[:, t, l, :] = wpad[rows, 32 * t + 8 * (l // 16): 32 * t + 8 * (l // 16) + 8]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,d", [(128, 2048), (100, 1024), (1, 32), (256, 4096)])
+def test_gate_pack_layout(E, d):
+    w = round_bf16(np.random.default_rng(E + d).standard_normal((E, d)))
+    wp = tr.route_gate_pack(dev(w))
+    assert wp.numel() * 2 == tr.route_gate_packed_size(E, d)
+    assert np.array_equal(host(wp), _pack_ref(w, d))
+
+
+@pytest.mark.parametrize("n,d,E,K,affine", [(1, 2048, 128, 8, False), (8192, 2048, 128, 8, False),
+                                            (37, 1024, 8, 2, True), (1000, 4096, 160, 6, True),
+                                            (77, 2048, 256, 16, False), (100, 2048, 1, 1, False),
+                                            (33, 1024, 200, 5, True), (16, 4096, 64, 8, False)])
+def test_qgate_topk_packed_equals_unpacked(n, d, E, K, affine):
+    """The packed router gives the unpacked call's logits, picks and hit count
+    bit for bit (the same operands in the same order), and its picks are the
+    oracle's top-K of those logits."""
+    r, dv, g, b, w = _case(n, d, E, affine, 2 * n + d + E + K)
+    opt = lambda a: None if a is None else dev(a)
+    truth = np.random.default_rng(n + E).integers(0, E, (n, K)).astype(np.int32)
+    lg1 = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    h1 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    i1 = tr.route_qgate_topk(dev(r), dev(dv), dev(w), K, opt(g), opt(b), 1e-5, logits=lg1,
+                             truth=dev(truth), hits=h1)
+    wp = tr.route_gate_pack(dev(w))
+    lg2 = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    h2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    i2 = tr.route_qgate_topk_packed(dev(r), dev(dv), wp, E, K, opt(g), opt(b), 1e-5, logits=lg2,
+                                    truth=dev(truth), hits=h2)
+    assert torch.equal(lg1, lg2) and torch.equal(i1, i2)
+    assert int(host(h1)[0]) == int(host(h2)[0])
+    assert np.array_equal(host(i2), oracle.route_topk(host(lg2), K, 1, 1)[0])
+    assert int(host(h2)[0]) == oracle.hit_count(host(i2), truth)

@@ -28,7 +28,8 @@ __all__ = [
     "eg_score_workspace_size", "eg_score", "eg_update", "route_est_hidden",
     "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
     "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "route_qgate",
-    "route_qgate_topk", "EXPORTS",
+    "route_qgate_topk", "route_gate_packed_size", "route_gate_pack", "route_qgate_topk_packed",
+    "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +70,10 @@ EXPORTS = {
     "route_qgate": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _p, _p]),
     "route_qgate_topk": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _i32, _p, _p,
                                         _p, _p, _p]),
+    "route_gate_packed_size": (_sz, [_i32, _i32]),
+    "route_gate_pack": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
+    "route_qgate_topk_packed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _i32, _p,
+                                               _p, _p, _p, _p]),
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
@@ -421,6 +426,40 @@ def route_qgate_topk(r, dvec, w, K, gamma=None, beta=None, eps=1e-5, idx=None, l
     _call("route_qgate_topk", _dev(r, _bf16(r), "r"), _dev(dvec, torch.float32, "dvec", d),
           _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
           float(eps), _dev(w, _bf16(w), "w", E * d), E, K,
+          _opt(logits, torch.float32, "logits", n * E), _dev(idx, torch.int32, "idx", n * K),
+          _opt(truth, torch.int32, "truth", n * K), _opt(hits, torch.int64, "hits", 1),
+          _stream(stream))
+    return idx
+
+
+def route_gate_packed_size(E: int, d: int) -> int:
+    return int(lib().route_gate_packed_size(E, d))
+
+
+def route_gate_pack(w, wp=None, stream=None):
+    """w [E][d] bf16 -> its rows in route_qgate_topk_packed's fragment order
+    (a flat bf16 tensor of route_gate_packed_size(E, d) bytes)."""
+    E, d = w.shape
+    nbytes = route_gate_packed_size(E, d)
+    if nbytes == 0:
+        raise ValueError(f"route_gate_pack: E={E}, d={d} not taken (d % 32 != 0)")
+    wp = _empty((nbytes // 2,), _bf16(w), w) if wp is None else wp
+    _call("route_gate_pack", _dev(w, _bf16(w), "w", E * d), E, d,
+          _dev(wp, _bf16(w), "wp", nbytes // 2), _stream(stream))
+    return wp
+
+
+def route_qgate_topk_packed(r, dvec, wp, E, K, gamma=None, beta=None, eps=1e-5, idx=None,
+                            logits=None, truth=None, hits=None, stream=None):
+    """route_qgate_topk with the router packed by route_gate_pack (the same
+    results, bit for bit)."""
+    n, d = r.shape
+    idx = _empty((n, K), torch.int32, r) if idx is None else idx
+    if (truth is None) != (hits is None):
+        raise ValueError("truth and hits go together")
+    _call("route_qgate_topk_packed", _dev(r, _bf16(r), "r"), _dev(dvec, torch.float32, "dvec", d),
+          _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d,
+          float(eps), _dev(wp, _bf16(wp), "wp", route_gate_packed_size(E, d) // 2), E, K,
           _opt(logits, torch.float32, "logits", n * E), _dev(idx, torch.int32, "idx", n * K),
           _opt(truth, torch.int32, "truth", n * K), _opt(hits, torch.int64, "hits", 1),
           _stream(stream))

@@ -10,6 +10,7 @@ namespace route {
 
 constexpr int kCntThreads = 256;
 constexpr unsigned kCntMaxBlocks = 128;  // few blocks: few atomics on one address
+constexpr int kLarBatch = 8;
 
 // Block-wide sum of one count per thread; thread 0 adds it to *dst.
 __device__ __forceinline__ void block_add(unsigned v, unsigned long long* dst) {
@@ -30,13 +31,32 @@ __global__ __launch_bounds__(kCntThreads) void lar_kernel(
     const uint8_t* __restrict__ row_cluster, const uint8_t* __restrict__ expert_cluster, int E,
     unsigned long long* __restrict__ local) {
   const int kg = K / H;
+  const int64_t np = n * K;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kCntThreads;
   unsigned hit = 0;
-  for (int64_t p = static_cast<int64_t>(blockIdx.x) * kCntThreads + threadIdx.x; p < n * K;
-       p += static_cast<int64_t>(gridDim.x) * kCntThreads) {
-    const int64_t i = p / K;
-    const int k = static_cast<int>(p - i * K);
-    const int e = idx[p];
-    if (e >= 0 && e < E) hit += expert_cluster[e] == row_cluster[i * H + k / kg] ? 1u : 0u;
+  // kLarBatch pairs a thread at a time, every load of a batch issued before
+  // any is used: the grid is capped, so each thread walks many pairs, and one
+  // at a time each would wait out two dependent loads
+  for (int64_t p0 = static_cast<int64_t>(blockIdx.x) * kCntThreads + threadIdx.x; p0 < np;
+       p0 += stride * kLarBatch) {
+    int e[kLarBatch];
+#pragma unroll
+    for (int b = 0; b < kLarBatch; ++b) {
+      const int64_t p = p0 + b * stride;
+      e[b] = p < np ? idx[p] : -1;
+    }
+    int ec[kLarBatch], rc[kLarBatch];
+#pragma unroll
+    for (int b = 0; b < kLarBatch; ++b) {
+      const int64_t p = p0 + b * stride;
+      const bool ok = e[b] >= 0 && e[b] < E;
+      const int64_t i = p / K;
+      const int k = static_cast<int>(p - i * K);
+      ec[b] = ok ? static_cast<int>(expert_cluster[e[b]]) : -1;
+      rc[b] = ok ? static_cast<int>(row_cluster[i * H + k / kg]) : -2;
+    }
+#pragma unroll
+    for (int b = 0; b < kLarBatch; ++b) hit += ec[b] == rc[b] ? 1u : 0u;
   }
   block_add(hit, local);
 }

@@ -147,6 +147,11 @@ __global__ __launch_bounds__(kLnThreads) void qhidden_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kQgThreads = 512;
 constexpr int kQgLead = 3;  // W line loads in flight, in pairs of K steps (measured: 3 beats 1, 7 and 15)
+// With W packed in fragment order (route_gate_pack), each wave streams its
+// column group's fragments straight into registers, this many K steps ahead
+// (measured at the Qwen3 shape: 4, 8 and 16 steps 22.4, 22.0 and 22.7 us per
+// launch, against 24.9 us for the line loads through LDS; the same bits).
+constexpr int kQgPackLead = 8;
 
 // LDS offset of 16-byte piece p of tile row rr. Rows are a multiple of 256
 // bytes long, so every row starts at the same bank; gfx950's LDS serves a
@@ -166,8 +171,9 @@ __device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ 
 // TOPK > 0: also pick each row's top K columns (E <= 128 TOPK, K <= 16), in
 // route_topk's order (largest logit first, equal logits to the lower column,
 // -0.0 == +0.0), from the logits gathered in LDS; logits may then be NULL.
-// TOPK = 0: the product alone.
-template <int BM, int D, int TOPK>
+// TOPK = 0: the product alone. PW: w is in the packed fragment order of
+// route_gate_pack instead of rows.
+template <int BM, int D, int TOPK, bool PW>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
@@ -183,7 +189,9 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   static_assert(NPAIRS % (kQgLead + 1) == 0, "the ring cycles whole");
   __shared__ __attribute__((aligned(16))) float sd[D];
   __shared__ __attribute__((aligned(16))) char tile[BM * D * 2];
-  __shared__ __attribute__((aligned(16))) char wstage[(kQgThreads / kWave) * 2048];
+  // the line loads' per-wave staging (16 bytes when W comes packed: the hit
+  // count's word only)
+  __shared__ __attribute__((aligned(16))) char wstage[PW ? 16 : (kQgThreads / kWave) * 2048];
   const int lane = lane_id(), wv = wave_id();
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   // the top-K epilogue gives row 4 wv + lane / 16 to a 16-lane segment; the
@@ -222,9 +230,38 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   // complete in order, so no barrier is needed).
   const int r16 = lane & 15, kq = lane >> 4;
   const int ngroups = (E + 15) / 16;
-  char* wst = wstage + wv * 2048;
+  // packed W: group g, K step st (32 k), lane l's fragment at
+  // (g * NSTEPS + st) * 64 + l in 16-byte units
+  constexpr int NSTEPS = D / 32;
+  auto gemm_group_packed = [&](int g, f32x4 (&acc)[MT]) {
+    const u32x4* wp = reinterpret_cast<const u32x4*>(w) + static_cast<size_t>(g) * NSTEPS * kWave + lane;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_assert(NSTEPS % kQgPackLead == 0, "the ring cycles whole");
+    u32x4 ring[kQgPackLead];
+#pragma unroll
+    for (int j = 0; j < kQgPackLead; ++j) ring[j] = wp[j * kWave];
+#pragma unroll 1
+    for (int st0 = 0; st0 < NSTEPS; st0 += kQgPackLead) {
+#pragma unroll
+      for (int j = 0; j < kQgPackLead; ++j) {
+        const int st = st0 + j;
+        const u32x4 bf = ring[j];
+        // past the last step: reload the last one (in bounds, never used)
+        const int nx = st + kQgPackLead < NSTEPS ? st + kQgPackLead : NSTEPS - 1;
+        ring[j] = wp[nx * kWave];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 af =
+              *reinterpret_cast<const u32x4*>(tile + qg_off<D>(16 * m + r16, 4 * st + kq));
+          acc[m] = mfma16x16x32(af, bf, acc[m]);
+        }
+      }
+    }
+  };
+  char* wst = wstage + (PW ? 0 : wv * 2048);
   const int lrow = lane >> 3, lchunk = lane & 7;  // line-load mapping: row, 16-byte chunk
-  auto gemm_group = [&](int g, f32x4 (&acc)[MT]) {
+  auto gemm_group_lines = [&](int g, f32x4 (&acc)[MT]) {
     const uint16_t* wq[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -265,6 +302,12 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
         }
       }
     }
+  };
+  auto gemm_group = [&](int g, f32x4 (&acc)[MT]) {
+    if constexpr (PW)
+      gemm_group_packed(g, acc);
+    else
+      gemm_group_lines(g, acc);
   };
   auto store_logits = [&](int g, const f32x4 (&acc)[MT]) {
     const int colr = 16 * g + r16;
@@ -383,24 +426,59 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
 }
 
 // 32 rows per workgroup (16 at d = 4096, where the q tile's rows are twice as long)
-template <int TOPK>
+template <int TOPK, bool PW = false>
 void qgate_launch(int d, int64_t n, hipStream_t s, const uint16_t* r, const float* dvec,
                   const float* gamma, const float* beta, float eps, const uint16_t* w, int E,
                   float* logits, int K, int* idx, const int32_t* truth, unsigned long long* hits) {
   if (d == 1024)
-    qgate_kernel<32, 1024, TOPK><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+    qgate_kernel<32, 1024, TOPK, PW><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
         r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
   else if (d == 2048)
-    qgate_kernel<32, 2048, TOPK><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+    qgate_kernel<32, 2048, TOPK, PW><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
         r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
   else
-    qgate_kernel<16, 4096, TOPK><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
+    qgate_kernel<16, 4096, TOPK, PW><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
         r, dvec, gamma, beta, n, eps, w, E, logits, K, idx, truth, hits);
+}
+
+// route_gate_pack: one thread per 16-byte fragment piece of the packed
+// layout (group g of 16 router rows, K step st of 32, lane l); rows past E
+// are zeros.
+__global__ void gate_pack_kernel(const uint16_t* __restrict__ w, int E, int d,
+                                 uint16_t* __restrict__ wp) {
+  const int nsteps = d / 32;
+  const int64_t total = static_cast<int64_t>((E + 15) / 16) * nsteps * kWave;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= total) return;
+  const int l = static_cast<int>(q & (kWave - 1));
+  const int64_t gs = q / kWave;
+  const int st = static_cast<int>(gs % nsteps);
+  const int g = static_cast<int>(gs / nsteps);
+  const int row = 16 * g + (l & 15);
+  u32x4 v = u32x4{0, 0, 0, 0};
+  if (row < E) v = ld16(w + static_cast<size_t>(row) * d + 32 * st + 8 * (l >> 4));
+  st16(wp + q * 8, v);
 }
 
 }  // namespace route
 
 using namespace route;
+
+ROUTE_API size_t route_gate_packed_size(int32_t E, int32_t d) {
+  if (E < 1 || d < 32 || d % 32 != 0) return 0;
+  return static_cast<size_t>((E + 15) / 16) * 16 * static_cast<size_t>(d) * sizeof(uint16_t);
+}
+
+ROUTE_API int route_gate_pack(const uint16_t* w, int32_t E, int32_t d, uint16_t* wp,
+                              hipStream_t s) {
+  if (E < 1 || d < 32 || d % 32 != 0) return ROUTE_ERR_SHAPE;
+  if (E > kMaxExperts) return ROUTE_ERR_UNSUPPORTED;
+  if (!w || !wp) return ROUTE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wp)) return ROUTE_ERR_ALIGN;
+  const int64_t total = static_cast<int64_t>((E + 15) / 16) * (d / 32) * kWave;
+  gate_pack_kernel<<<ceil_div(total, 256), 256, 0, s>>>(w, E, d, wp);
+  return launch_status();
+}
 
 ROUTE_API int route_qhidden(const uint16_t* r, const float* dvec, const float* gamma,
                             const float* beta, int64_t n, int32_t d, float eps, uint16_t* q,
@@ -439,11 +517,11 @@ ROUTE_API int route_qgate(const uint16_t* r, const float* dvec, const float* gam
   return launch_status();
 }
 
-ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma,
-                               const float* beta, int64_t n, int32_t d, float eps,
-                               const uint16_t* w, int32_t E, int32_t K, float* logits,
-                               int32_t* idx, const int32_t* truth, unsigned long long* hits,
-                               hipStream_t s) {
+// Host checks shared by the two top-K forms.
+static int qgate_topk_check(const uint16_t* r, const float* dvec, const float* gamma,
+                            const float* beta, int64_t n, int32_t d, float eps, const uint16_t* w,
+                            int32_t E, int32_t K, const int32_t* idx, const int32_t* truth,
+                            const unsigned long long* hits) {
   if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || E < 1 || K < 1 || K > E)
     return ROUTE_ERR_SHAPE;
   if (E > 256 || K > kMaxK || (d != 1024 && d != 2048 && d != 4096)) return ROUTE_ERR_UNSUPPORTED;
@@ -451,9 +529,33 @@ ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float
   if (!r || !dvec || !w || !idx || (!truth != !hits)) return ROUTE_ERR_NULL;
   if (!aligned16(r) || !aligned16(dvec) || !aligned16(w)) return ROUTE_ERR_ALIGN;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
+  return ROUTE_OK;
+}
+
+ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float* gamma,
+                               const float* beta, int64_t n, int32_t d, float eps,
+                               const uint16_t* w, int32_t E, int32_t K, float* logits,
+                               int32_t* idx, const int32_t* truth, unsigned long long* hits,
+                               hipStream_t s) {
+  const int st = qgate_topk_check(r, dvec, gamma, beta, n, d, eps, w, E, K, idx, truth, hits);
+  if (st != ROUTE_OK || n == 0) return st;
   if (E <= 128)
     qgate_launch<1>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
   else
     qgate_launch<2>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
+  return launch_status();
+}
+
+ROUTE_API int route_qgate_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                                      const float* beta, int64_t n, int32_t d, float eps,
+                                      const uint16_t* wp, int32_t E, int32_t K, float* logits,
+                                      int32_t* idx, const int32_t* truth,
+                                      unsigned long long* hits, hipStream_t s) {
+  const int st = qgate_topk_check(r, dvec, gamma, beta, n, d, eps, wp, E, K, idx, truth, hits);
+  if (st != ROUTE_OK || n == 0) return st;
+  if (E <= 128)
+    qgate_launch<1, true>(d, n, s, r, dvec, gamma, beta, eps, wp, E, logits, K, idx, truth, hits);
+  else
+    qgate_launch<2, true>(d, n, s, r, dvec, gamma, beta, eps, wp, E, logits, K, idx, truth, hits);
   return launch_status();
 }

@@ -37,7 +37,8 @@ from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_route,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
-               eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk)
+               eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk,
+               route_gate_pack, route_qgate_topk_packed)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
@@ -277,9 +278,14 @@ class PredictorPass:
         self.layer = None
 
     def load(self, layer: dict):
+        """Moves the layer's inputs to the device; on gate layers the next
+        router is also packed once (route_gate_pack) for the fused kernel,
+        like any fixed weight prepared at load time."""
         dev = self.device
         self.layer = {k: (to_device(v, dev) if isinstance(v, np.ndarray) else v)
                       for k, v in layer.items()}
+        if not self.layer["estimator"] and self.d in QGATE_D and self.E <= 256:
+            self.layer["w_next_packed"] = route_gate_pack(self.layer["w_next"])
         return self
 
     def truth_step(self):
@@ -290,16 +296,17 @@ class PredictorPass:
 
     def step(self, fused=True, keep_logits=False):
         """One source layer: on gate layers the next gate on q_l and its top-K
-        in one kernel (route_qgate_topk, q and the logits kept on chip; the
+        in one kernel (route_qgate_topk_packed, q and the logits kept on chip; the
         logits are written only if ``keep_logits``) when ``fused`` and the
         shape allows, else route_qhidden + route_gate + route_topk; on
         estimator layers q_l, the estimator and top-K. Then the hit count (inside
         the fused kernel on gate layers)."""
         L = self.layer
-        if not L["estimator"] and fused and self.d in QGATE_D and self.E <= 256:
-            route_qgate_topk(L["r"], L["dvec"], L["w_next"], self.K, eps=L["eps"], idx=self.pred,
-                             logits=self.logits if keep_logits else None, truth=self.truth,
-                             hits=self.hits)
+        if not L["estimator"] and fused and "w_next_packed" in L:
+            route_qgate_topk_packed(L["r"], L["dvec"], L["w_next_packed"], self.E, self.K,
+                                    eps=L["eps"], idx=self.pred,
+                                    logits=self.logits if keep_logits else None,
+                                    truth=self.truth, hits=self.hits)
             return
         else:
             route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
