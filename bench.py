@@ -47,9 +47,11 @@ def route_bytes(N, d, E, K, P, G, fallback, routed=False):
         "combine": N * K * d * b + 8 * N * K + 4 * N + N * d * b,
     }
     if routed:
-        return {"predict": st["predict"],
-                "srs_route": (st["srs"] + st["gate"] - N * d * b + st["topk"] - 4 * N * E
-                              + st["lar"] - 4 * N * K),
+        # prediction folded into the cluster sort (its maps: 9 bytes a token
+        # and the offsets), then the rows with their router, top-K and count
+        return {"predict_sort": st["predict"] + 9 * N + 4 * (G + 1),
+                "srs_route": (P * N * d * b + N * d * b + E * d * b + 4 * N * E + 8 * N * K
+                              + 5 * N + E),
                 "permute": st["permute"], "combine": st["combine"]}
     return st
 

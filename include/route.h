@@ -98,6 +98,29 @@ int route_predict(const int32_t* tok, int64_t n, const uint8_t* lut, const uint8
                   uint32_t* err, hipStream_t s);
 
 /*
+ * route_predict_sort - route_predict, then the stable sort of the predicted
+ * clusters that srs_shuffle makes (the s-TS destination order), in the
+ * launches of the sort alone: each key is predicted where the sort reads it.
+ * [SMOE] section 4.1 (prediction) and section 3.1 (tokens grouped by their
+ * predicted cluster, in order inside a cluster).
+ *   Arguments up to dest as route_predict (dest uint8[n] written, the same
+ *   bytes); cluster_offsets int32[G+1], row_of_src int32[n], src_of_row
+ *   int32[n] and row_cluster uint8[n] (nullable) as srs_shuffle writes them
+ *   for these clusters. ws: route_predict_sort_workspace_size(n, G) bytes.
+ * Errors: as route_predict, plus NULL (cluster_offsets; row_of_src or
+ * src_of_row with n > 0), WORKSPACE. Device bits: TOKEN_RANGE (that token
+ * goes to cluster 0), DEST_RANGE (a cluster >= G: flagged, row_of_src -1,
+ * the token gets no sorted row).
+ */
+int route_predict_sort(const int32_t* tok, int64_t n, const uint8_t* lut, const uint8_t* conf,
+                       int32_t vocab, const uint8_t* prev2, const uint8_t* prev1,
+                       const uint8_t* ngram, int32_t G, int32_t conf_thr, uint8_t* dest,
+                       int32_t* cluster_offsets, int32_t* row_of_src, int32_t* src_of_row,
+                       uint8_t* row_cluster, void* ws, size_t ws_bytes, uint32_t* err,
+                       hipStream_t s);
+size_t route_predict_sort_workspace_size(int64_t n, int32_t G);
+
+/*
  * route_lut_build - offline table builder for route_predict.
  * [SMOE] section 4.1: the token-expert confidence table is reduced to a
  * token -> cluster table. For row i (id ids[i], routing idx[i][K] with
@@ -202,6 +225,24 @@ int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
                       int32_t* idx, float* weights, const uint8_t* expert_cluster,
                       unsigned long long* local, void* ws, size_t ws_bytes, uint32_t* err,
                       hipStream_t s);
+
+/*
+ * srs_route_sorted - srs_shuffle_route's row work for a destination order
+ * already made (row_of_src from route_predict_sort or srs_shuffle): each
+ * source row i is reduced and written to row row_of_src[i] with its logits,
+ * top-K and count, exactly as srs_shuffle_route does after its sort (the
+ * same bytes). [SMOE] section 3.1, glossary; [FOE] router scores g[i].
+ *   row_of_src int32[n] (a row < 0 or >= n gets no outputs); dest uint8[n]
+ *   (nullable: every row's cluster is 0) gives the predicted cluster for
+ *   the count; the other arguments as srs_shuffle_route.
+ * Errors: as srs_shuffle_route (without G and the workspace), plus NULL
+ * (row_of_src with n > 0).
+ */
+int srs_route_sorted(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                     const int32_t* row_of_src, const uint8_t* dest, uint16_t* out,
+                     const uint16_t* w, int32_t E, float* logits, int32_t K, int32_t renorm,
+                     int32_t* idx, float* weights, const uint8_t* expert_cluster,
+                     unsigned long long* local, hipStream_t s);
 
 /*
  * route_gate - router logits = x . w^T.

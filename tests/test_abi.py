@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 39, names
+    assert len(names) == 42, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -155,6 +155,41 @@ def test_srs_route_errors(L):
     assert call(args(partials=MIS)) == ALIGN
     assert call(args(w=MIS)) == ALIGN
     assert call(args(out=MIS)) == ALIGN
+
+
+def test_predict_sort_and_route_sorted_errors(L):
+    f = L.route_predict_sort
+    ws = L.route_predict_sort_workspace_size(1000, 8)
+    args = lambda **k: dict(dict(tok=A, n=1000, lut=A, conf=None, vocab=5000, p2=None, p1=None,
+                                 ng=None, G=8, thr=128, dest=A, offs=A, ros=A, sor=A, rc=None,
+                                 ws=A, wsb=ws, err=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(n=-1)) == SHAPE
+    assert call(args(G=0)) == SHAPE
+    assert call(args(vocab=0)) == SHAPE
+    assert call(args(G=257)) == UNSUP
+    assert call(args(offs=None)) == NULL
+    assert call(args(ros=None)) == NULL
+    assert call(args(sor=None)) == NULL
+    assert call(args(dest=None)) == NULL
+    assert call(args(conf=A)) == NULL          # the fallback needs prev2, prev1, ngram
+    assert call(args(ws=None)) == WS
+    assert call(args(wsb=ws - 1)) == WS
+    assert L.route_predict_sort_workspace_size(1000, 300) == 0
+    g = L.srs_route_sorted
+    args = lambda **k: dict(dict(partials=A, P=2, n=1000, d=512, ros=A, dest=None, out=A, w=A,
+                                 E=8, logits=None, K=2, renorm=1, idx=A, weights=None, ec=None,
+                                 local=None, s=None), **k)
+    call = lambda a: g(*a.values())
+    assert call(args(K=9)) == SHAPE
+    assert call(args(d=12)) == SHAPE
+    assert call(args(E=161, d=4096)) == UNSUP
+    assert call(args(K=17, E=32)) == UNSUP
+    assert call(args(ros=None)) == NULL
+    assert call(args(idx=None)) == NULL
+    assert call(args(ec=A)) == NULL            # the count needs both
+    assert call(args(out=MIS)) == ALIGN
+    assert call(args(n=0, ros=None)) == OK
 
 
 def test_permute_and_combine_errors(L):

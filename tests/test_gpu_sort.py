@@ -72,3 +72,68 @@ def test_sort_flags_out_of_range_keys(n):
     assert np.array_equal(host(offs), ref["expert_offsets"])
     assert np.array_equal(s[good], ref["slot_of_pair"])
     assert np.array_equal(host(pos)[: n - 7], good[ref["pair_of_slot"]])
+
+
+def _predict_inputs(n, G, V, seed, fallback):
+    rng = np.random.default_rng(seed)
+    tok = rng.zipf(1.2, n).astype(np.int64) % V
+    lut = rng.integers(0, G, V).astype(np.uint8)
+    out = dict(tok=tok.astype(np.int32), lut=lut)
+    if fallback:
+        out.update(conf=rng.integers(0, 256, V).astype(np.uint8),
+                   prev2=rng.integers(0, G, n).astype(np.uint8),
+                   prev1=rng.integers(0, G, n).astype(np.uint8),
+                   ngram=rng.integers(0, G, (G, G)).astype(np.uint8))
+    return out
+
+
+@pytest.mark.parametrize("n,G,fallback", [(64, 2, False), (4096, 4, False), (4096, 8, True),
+                                          (4097, 4, True), (16384, 8, True), (1, 1, False),
+                                          (3000, 256, True), (20000, 3, False)])
+def test_predict_sort_against_oracle(n, G, fallback):
+    """route_predict_sort on both sides of the one-workgroup limit: dest is
+    the oracle's prediction and the maps are the oracle's stable shuffle of
+    it, bit for bit."""
+    a = _predict_inputs(n, G, 5000, n + G, fallback)
+    fb = dict(conf=dev(a["conf"]), prev2=dev(a["prev2"]), prev1=dev(a["prev1"]),
+              ngram=dev(a["ngram"])) if fallback else {}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dest, offs, ros, sor, rc = tr.route_predict_sort(dev(a["tok"]), dev(a["lut"]), G, err=err, **fb)
+    sync()
+    assert int(err.item()) == 0
+    want = oracle.route_predict(a["tok"], a["lut"], a.get("conf"), a.get("prev2"), a.get("prev1"),
+                                a.get("ngram"), 128, G=G)
+    assert np.array_equal(host(dest), want)
+    srs = oracle.srs_shuffle(np.zeros((1, n, 8), dtype=np.uint16), want, G)
+    assert np.array_equal(host(offs), srs["offsets"])
+    assert np.array_equal(host(ros), srs["row_of_src"])
+    assert np.array_equal(host(sor), srs["src_of_row"])
+    assert np.array_equal(host(rc), srs["row_cluster"])
+
+
+@pytest.mark.parametrize("n", [3000, 9000])
+def test_predict_sort_flags_like_predict_then_sort(n):
+    """Tokens outside the vocabulary (cluster 0, TOKEN_RANGE), table entries
+    past G and previous clusters past G (DEST_RANGE) come out as
+    route_predict followed by srs_shuffle's sort: the same bytes and bits."""
+    G, V = 4, 5000
+    a = _predict_inputs(n, G, V, n, True)
+    a["tok"][::97] = V + 5
+    a["tok"][::131] = -3
+    a["lut"][a["tok"][5]] = G + 2 if a["tok"][5] >= 0 else 0
+    a["prev2"][7::211] = G
+    a["conf"][:] = np.where(np.arange(V) % 3 == 0, 0, 255).astype(np.uint8)
+    fb = dict(conf=dev(a["conf"]), prev2=dev(a["prev2"]), prev1=dev(a["prev1"]),
+              ngram=dev(a["ngram"]))
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dest, offs, ros, sor, rc = tr.route_predict_sort(dev(a["tok"]), dev(a["lut"]), G, err=e1, **fb)
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d2 = tr.route_predict(dev(a["tok"]), dev(a["lut"]), G, err=e2, **fb)
+    parts = torch.zeros((1, n, 8), dtype=torch.bfloat16, device="cuda")
+    _, o2, r2, s2, c2 = tr.srs_shuffle(parts, d2, G, err=e2)
+    sync()
+    assert int(e1.item()) == int(e2.item())
+    assert int(e1.item()) & tr.EBIT_TOKEN_RANGE and int(e1.item()) & tr.EBIT_DEST_RANGE
+    assert torch.equal(dest, d2) and torch.equal(offs, o2) and torch.equal(ros, r2)
+    valid = int(host(o2)[-1])
+    assert torch.equal(sor[:valid], s2[:valid]) and torch.equal(rc[:valid], c2[:valid])

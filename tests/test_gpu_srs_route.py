@@ -238,3 +238,20 @@ def test_srs_route_rows_bit_exact_on_special_values(kind):
     assert np.array_equal(host(offs), want["offsets"])
     assert np.array_equal(host(ros), want["row_of_src"])
     assert np.array_equal(host(out), want["out"])
+
+
+@pytest.mark.parametrize("n,d,P,G,E,K", [(1000, 520, 2, 8, 8, 2), (777, 384, 4, 5, 16, 4),
+                                         (2049, 5120, 2, 8, 160, 6), (300, 256, 2, 3, 150, 8)])
+def test_srs_route_sorted_equals_srs_shuffle_route(n, d, P, G, E, K):
+    """Given srs_shuffle_route's own order, srs_route_sorted writes the same
+    bytes (rows, logits, picks, weights) and the same count, through both
+    kernels."""
+    parts, dest, w, ec = _inputs(n, d, P, G, E)
+    (out, offs, ros, sor, rc, lg, idx, wt), local = _run(parts, dest, G, w, K, ec)
+    loc2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    o2, l2, i2, w2 = tr.srs_route_sorted(dev(parts), ros, dev(w), K, 1, dest=dev(dest),
+                                         expert_cluster=dev(ec), local=loc2)
+    sync()
+    for a, b in ((out, o2), (lg, l2), (idx, i2), (wt, w2)):
+        assert torch.equal(a, b)
+    assert int(local.item()) == int(loc2.item())

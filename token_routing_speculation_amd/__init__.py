@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "RouteError", "lib", "library_path",
-    "route_predict", "route_lut_build", "srs_shuffle", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
+    "route_predict", "route_predict_sort", "route_predict_sort_workspace_size", "route_lut_build",
+    "srs_shuffle", "srs_route_sorted", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "moe_combine_gather", "route_qhidden",
     "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
@@ -49,6 +50,9 @@ _u64, _f64 = ctypes.c_uint64, ctypes.c_double
 EXPORTS = {
     "route_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "route_predict": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _p]),
+    "route_predict_sort": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _p,
+                                          _p, _p, _p, _p, _sz, _p, _p]),
+    "route_predict_sort_workspace_size": (_sz, [_i64, _i32]),
     "route_lut_build": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _p]),
     "srs_shuffle": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "srs_shuffle_gate": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p,
@@ -56,6 +60,8 @@ EXPORTS = {
     "srs_shuffle_route": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _i32, _p, _p, _p, _p, _p,
                                          _p, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p,
                                          _p]),
+    "srs_route_sorted": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _p, _p, _i32, _p, _i32, _i32,
+                                        _p, _p, _p, _p, _p]),
     "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
     "route_gate": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _p]),
     "route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p]),
@@ -188,6 +194,38 @@ def route_predict(tok, lut, G, conf=None, prev2=None, prev1=None, ngram=None, co
     return dest
 
 
+def route_predict_sort_workspace_size(n: int, G: int) -> int:
+    return int(lib().route_predict_sort_workspace_size(n, G))
+
+
+def route_predict_sort(tok, lut, G, conf=None, prev2=None, prev1=None, ngram=None, conf_thr=128,
+                       dest=None, offsets=None, row_of_src=None, src_of_row=None,
+                       row_cluster=None, ws=None, err=None, stream=None):
+    """route_predict and the stable sort of its clusters in one go: returns
+    (dest, offsets, row_of_src, src_of_row, row_cluster)."""
+    n = tok.numel()
+    e = lambda shape, dt: _empty(shape, dt, tok)
+    dest = e((n,), torch.uint8) if dest is None else dest
+    offsets = e((G + 1,), torch.int32) if offsets is None else offsets
+    row_of_src = e((n,), torch.int32) if row_of_src is None else row_of_src
+    src_of_row = e((n,), torch.int32) if src_of_row is None else src_of_row
+    row_cluster = e((n,), torch.uint8) if row_cluster is None else row_cluster
+    need = route_predict_sort_workspace_size(n, G)
+    ws = e((max(need, 1),), torch.uint8) if ws is None else ws
+    fb = conf is not None
+    _call("route_predict_sort", _dev(tok, torch.int32, "tok"), n, _dev(lut, torch.uint8, "lut"),
+          _opt(conf, torch.uint8, "conf"), lut.numel(),
+          _opt(prev2, torch.uint8, "prev2", n if fb else None),
+          _opt(prev1, torch.uint8, "prev1", n if fb else None),
+          _opt(ngram, torch.uint8, "ngram", G * G if fb else None), G, conf_thr,
+          _dev(dest, torch.uint8, "dest", n), _dev(offsets, torch.int32, "offsets", G + 1),
+          _dev(row_of_src, torch.int32, "row_of_src", n),
+          _dev(src_of_row, torch.int32, "src_of_row", n),
+          _opt(row_cluster, torch.uint8, "row_cluster", n), _dev(ws, torch.uint8, "ws"),
+          ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return dest, offsets, row_of_src, src_of_row, row_cluster
+
+
 def route_lut_build(ids, idx, w, expert_cluster, G, lut, conf=None, err=None, stream=None):
     n, K = idx.shape
     _call("route_lut_build", _dev(ids, torch.int32, "ids", n), n, _dev(idx, torch.int32, "idx"),
@@ -281,6 +319,29 @@ def srs_shuffle_route(partials, dest, G, w, K, renorm=1, expert_cluster=None, lo
           _opt(expert_cluster, torch.uint8, "expert_cluster", E), _opt(local, torch.int64, "local", 1),
           _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1), _stream(stream))
     return out, offsets, row_of_src, src_of_row, row_cluster, logits, idx, weights
+
+
+def srs_route_sorted(partials, row_of_src, w, K, renorm=1, dest=None, expert_cluster=None,
+                     local=None, out=None, logits=None, idx=None, weights=None,
+                     with_logits=True, stream=None):
+    """srs_shuffle_route's row work for an order already made (row_of_src):
+    returns (out, logits, idx, weights)."""
+    P, n, d = partials.shape
+    E = w.shape[0]
+    bt = _bf16(partials)
+    out = _empty((n, d), bt, partials) if out is None else out
+    if with_logits and logits is None:
+        logits = _empty((n, E), torch.float32, partials)
+    idx = _empty((n, K), torch.int32, partials) if idx is None else idx
+    weights = _empty((n, K), torch.float32, partials) if weights is None else weights
+    _call("srs_route_sorted", _dev(partials, bt, "partials"), P, n, d,
+          _dev(row_of_src, torch.int32, "row_of_src", n), _opt(dest, torch.uint8, "dest", n),
+          _dev(out, bt, "out", n * d), _dev(w, _bf16(w), "w", E * d), E,
+          _opt(logits, torch.float32, "logits", n * E), K, renorm,
+          _dev(idx, torch.int32, "idx", n * K), _opt(weights, torch.float32, "weights", n * K),
+          _opt(expert_cluster, torch.uint8, "expert_cluster", E), _opt(local, torch.int64, "local", 1),
+          _stream(stream))
+    return out, logits, idx, weights
 
 
 def route_gate(x, w, logits=None, stream=None):

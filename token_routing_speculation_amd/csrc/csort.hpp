@@ -50,11 +50,19 @@ __device__ __forceinline__ uint32_t key_u32<int32_t>(int32_t k) {
   return k < 0 ? 0xffffffffu : static_cast<uint32_t>(k);
 }
 
+// Key sources: key j of the array (ArrayKeys), or any functor with the same
+// call (route_predict_sort's computes each key from the token as it goes).
 template <typename KeyT>
-__global__ __launch_bounds__(kSortThreads) void csort_hist(const KeyT* __restrict__ keys,
-                                                           int64_t n, int B, int64_t chunk,
-                                                           int nchunks, int* __restrict__ hist,
-                                                           uint32_t* err, uint32_t ebit) {
+struct ArrayKeys {
+  const KeyT* __restrict__ p;
+  __device__ __forceinline__ uint32_t operator()(int64_t j) const { return key_u32<KeyT>(p[j]); }
+};
+
+template <typename Src>
+__global__ __launch_bounds__(kSortThreads) void csort_hist(Src keys, int64_t n, int B,
+                                                           int64_t chunk, int nchunks,
+                                                           int* __restrict__ hist, uint32_t* err,
+                                                           uint32_t ebit) {
   __shared__ int h[kMaxExperts];
   for (int b = threadIdx.x; b < B; b += kSortThreads) h[b] = 0;
   __syncthreads();
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(kSortThreads) void csort_hist(const KeyT* __restric
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int64_t j = j0 + q * kSortThreads;
-      k[q] = j < hi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
+      k[q] = j < hi ? keys(j) : 0xffffffffu;
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
@@ -123,14 +131,14 @@ __device__ __forceinline__ void scan_bins(int* tot, int B, int* total) {
 constexpr int64_t kSpan = static_cast<int64_t>(kBatch) * kWave;  // keys per batch of tiles
 
 // keys [base, base + kSpan) of a share ending at qhi, one per lane and tile
-template <typename KeyT>
-__device__ __forceinline__ void load_batch(const KeyT* __restrict__ keys, uint32_t (&kb)[kBatch],
-                                           int64_t base, int64_t qhi) {
+template <typename Src>
+__device__ __forceinline__ void load_batch(const Src& keys, uint32_t (&kb)[kBatch], int64_t base,
+                                           int64_t qhi) {
   const int lane = lane_id();
 #pragma unroll
   for (int q = 0; q < kBatch; ++q) {
     const int64_t j = base + q * kWave + lane;
-    kb[q] = j < qhi ? key_u32<KeyT>(keys[j]) : 0xffffffffu;
+    kb[q] = j < qhi ? keys(j) : 0xffffffffu;
   }
 }
 
@@ -138,10 +146,10 @@ __device__ __forceinline__ void load_batch(const KeyT* __restrict__ keys, uint32
 // wave's LDS row (per 64-key tile, the lowest lane of each key's match adds
 // the match size). first[] holds the share's first batch, already loaded.
 // Returns whether a key of the share was out of range.
-template <typename KeyT>
-__device__ __forceinline__ bool count_share(const KeyT* __restrict__ keys, int64_t qlo,
-                                            int64_t qhi, int B, int nbits,
-                                            const uint32_t (&first)[kBatch], int* myrow) {
+template <typename Src>
+__device__ __forceinline__ bool count_share(const Src& keys, int64_t qlo, int64_t qhi, int B,
+                                            int nbits, const uint32_t (&first)[kBatch],
+                                            int* myrow) {
   const int lane = lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   bool bad = false;
@@ -170,12 +178,11 @@ __device__ __forceinline__ bool count_share(const KeyT* __restrict__ keys, int64
 // its bin plus its rank among equal keys of its tile; the lowest lane of the
 // match then advances the start. fwd[j] = position, inv[pos] = j,
 // inv_key[pos] = key (nullable); out-of-range keys get position -1.
-template <typename KeyT>
-__device__ __forceinline__ void place_share(const KeyT* __restrict__ keys, int64_t qlo,
-                                            int64_t qhi, int B, int nbits,
-                                            const uint32_t (&first)[kBatch], int* myrow,
-                                            int* __restrict__ fwd, int* __restrict__ inv,
-                                            uint8_t* __restrict__ inv_key) {
+template <typename Src>
+__device__ __forceinline__ void place_share(const Src& keys, int64_t qlo, int64_t qhi, int B,
+                                            int nbits, const uint32_t (&first)[kBatch],
+                                            int* myrow, int* __restrict__ fwd,
+                                            int* __restrict__ inv, uint8_t* __restrict__ inv_key) {
   const int lane = lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
@@ -292,9 +299,10 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
 
   // keys are read kBatch tiles (of 64) at a time, all loads issued before
   // any tile is processed; the first batch stays in registers for pass 2
+  const ArrayKeys<KeyT> src{keys};
   uint32_t first[kBatch];
-  load_batch(keys, first, qlo, qhi);
-  count_share(keys, qlo, qhi, B, nbits, first, myrow);  // csort_hist flagged bad keys
+  load_batch(src, first, qlo, qhi);
+  count_share(src, qlo, qhi, B, nbits, first, myrow);  // csort_hist flagged bad keys
   __syncthreads();
   // counts -> per-wave starting positions
   for (int b = t; b < B; b += THREADS) {
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
     }
   }
   __syncthreads();
-  place_share(keys, qlo, qhi, B, nbits, first, myrow, fwd, inv, inv_key);
+  place_share(src, qlo, qhi, B, nbits, first, myrow, fwd, inv, inv_key);
 }
 
 // The whole sort in one workgroup of sixteen waves, for n <= kSortOneMax keys
@@ -321,11 +329,10 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
 constexpr int64_t kSortOneMax = 4096;
 constexpr int kSortOneThreads = 1024;
 
-template <typename KeyT>
+template <typename Src>
 __global__ __launch_bounds__(kSortOneThreads) void csort_one(
-    const KeyT* __restrict__ keys, int64_t n, int B, int nbits, int* __restrict__ offsets,
-    int* __restrict__ fwd, int* __restrict__ inv, uint8_t* __restrict__ inv_key, uint32_t* err,
-    uint32_t ebit) {
+    Src keys, int64_t n, int B, int nbits, int* __restrict__ offsets, int* __restrict__ fwd,
+    int* __restrict__ inv, uint8_t* __restrict__ inv_key, uint32_t* err, uint32_t ebit) {
   constexpr int NW = kSortOneThreads / kWave;
   constexpr int kMaxB = kMaxExperts / 4;
   __shared__ int stot[kMaxB];
@@ -382,23 +389,26 @@ inline int bits_for(int B) {
 }
 
 // Enqueues the sort: one launch up to kSortOneMax keys, else two. ws holds
-// the histogram table (unused by the one-launch form).
-template <typename KeyT>
-int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int* inv,
-                 uint8_t* inv_key, void* ws, uint32_t* err, uint32_t ebit, hipStream_t s) {
+// the histogram table (unused by the one-launch form). The keys come from
+// src; `keys` holds them once src has been read (the rank launch reads them
+// there): the same array for a plain sort, the array src writes otherwise.
+template <typename KeyT, typename Src>
+int csort_launch_src(const Src& src, const KeyT* keys, int64_t n, int B, int* offsets, int* fwd,
+                     int* inv, uint8_t* inv_key, void* ws, uint32_t* err, uint32_t ebit,
+                     hipStream_t s) {
   if (n == 0) {
     fill_i32<<<ceil_div(B + 1, 256), 256, 0, s>>>(offsets, B + 1, 0);
     return launch_status();
   }
   if (n <= kSortOneMax && B <= kMaxExperts / 4) {
-    csort_one<KeyT><<<1, kSortOneThreads, 0, s>>>(keys, n, B, bits_for(B), offsets, fwd, inv,
-                                                  inv_key, err, ebit);
+    csort_one<Src><<<1, kSortOneThreads, 0, s>>>(src, n, B, bits_for(B), offsets, fwd, inv,
+                                                 inv_key, err, ebit);
     return launch_status();
   }
   const int64_t chunk = csort_chunk(n, B);
   const int nch = static_cast<int>(csort_nchunks(n, B));
   int* hist = static_cast<int*>(ws);
-  csort_hist<KeyT><<<nch, kSortThreads, 0, s>>>(keys, n, B, chunk, nch, hist, err, ebit);
+  csort_hist<Src><<<nch, kSortThreads, 0, s>>>(src, n, B, chunk, nch, hist, err, ebit);
   // sixteen waves per chunk where their LDS rows fit (B <= 256), else four
   if (B <= kMaxExperts / 4)
     csort_rank<KeyT, 1024><<<nch, 1024, 0, s>>>(keys, n, B, bits_for(B), chunk, nch, hist,
@@ -408,6 +418,13 @@ int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int
                                                                 nch, hist, offsets, fwd, inv,
                                                                 inv_key);
   return launch_status();
+}
+
+template <typename KeyT>
+int csort_launch(const KeyT* keys, int64_t n, int B, int* offsets, int* fwd, int* inv,
+                 uint8_t* inv_key, void* ws, uint32_t* err, uint32_t ebit, hipStream_t s) {
+  return csort_launch_src(ArrayKeys<KeyT>{keys}, keys, n, B, offsets, fwd, inv, inv_key, ws, err,
+                          ebit, s);
 }
 
 }  // namespace

@@ -45,4 +45,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waits for this wave's LDS (and scalar memory) operations.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// Keeps the compiler from moving memory accesses across this point (the
+// bare barrier below does not order them by itself).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier after this wave's LDS writes have completed, without the
+// full fence of __syncthreads (which also waits for every pending global
+// load): the caller waits for whatever else the other waves must see.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
 }  // namespace route

@@ -40,12 +40,6 @@ constexpr int kMmaThreads = 256;  // four waves, 2 x 2 over the tile
 constexpr int kMmaStages = 4;     // LDS stages (K steps of 64) in the ring
 
 // Waits until this wave's LDS reads have completed.
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
 // Byte offset of logical 16-byte piece p (0..7) of 128-byte slab row r.
 __device__ __forceinline__ int slab_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
 

@@ -4,38 +4,33 @@
 // the token table's confidence is low); the builder reduces each token id's
 // routing to its most-weighted cluster and a confidence byte.
 #include "common.hpp"
+#include "csort.hpp"
+#include "predict.hpp"
 
 namespace route {
 
 constexpr int kPredThreads = 256;
 
-__global__ __launch_bounds__(kPredThreads) void predict_kernel(
-    const int32_t* __restrict__ tok, int64_t n, const uint8_t* __restrict__ lut,
-    const uint8_t* __restrict__ conf, int vocab, const uint8_t* __restrict__ prev2,
-    const uint8_t* __restrict__ prev1, const uint8_t* __restrict__ ngram, int G, int conf_thr,
-    uint8_t* __restrict__ dest, uint32_t* err) {
+__global__ __launch_bounds__(kPredThreads) void predict_kernel(PredictArgs a, int64_t n,
+                                                              uint8_t* __restrict__ dest) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kPredThreads + threadIdx.x;
   if (i >= n) return;
-  const int t = tok[i];
-  if (t < 0 || t >= vocab) {
-    dest[i] = 0;
-    set_err(err, ROUTE_EBIT_TOKEN_RANGE);
-    return;
-  }
-  int c = lut[t];
-  if (conf && static_cast<int>(conf[t]) < conf_thr) {
-    const int a = prev2[i];
-    const int b = prev1[i];
-    if (a < G && b < G) {
-      c = ngram[a * G + b];
-    } else {
-      c = 0;
-      set_err(err, ROUTE_EBIT_DEST_RANGE);
-    }
-  }
-  if (c >= G) set_err(err, ROUTE_EBIT_DEST_RANGE);
+  const int c = predict_cluster(a, i);
+  if (c >= a.G) set_err(a.err, ROUTE_EBIT_DEST_RANGE);
   dest[i] = static_cast<uint8_t>(c);
 }
+
+// The sort's key source for route_predict_sort: token j's prediction, also
+// written to dest[j] (a key read again writes the same byte).
+struct PredictKeys {
+  PredictArgs a;
+  uint8_t* dest;
+  __device__ __forceinline__ uint32_t operator()(int64_t j) const {
+    const int c = predict_cluster(a, j);
+    dest[j] = static_cast<uint8_t>(c);
+    return static_cast<uint32_t>(c);
+  }
+};
 
 // One thread per row. The share of the cluster of slot k is recomputed as a
 // binary32 sum over the slots in k order, so every cluster's share has one
@@ -112,9 +107,36 @@ ROUTE_API int route_predict(const int32_t* tok, int64_t n, const uint8_t* lut,
   if (n == 0) return ROUTE_OK;
   if (!tok || !lut || !dest) return ROUTE_ERR_NULL;
   if (conf && (!prev2 || !prev1 || !ngram)) return ROUTE_ERR_NULL;
-  predict_kernel<<<ceil_div(n, kPredThreads), kPredThreads, 0, s>>>(
-      tok, n, lut, conf, vocab, prev2, prev1, ngram, G, conf_thr, dest, err);
+  const PredictArgs a{tok, lut, conf, vocab, prev2, prev1, ngram, G, conf_thr, err};
+  predict_kernel<<<ceil_div(n, kPredThreads), kPredThreads, 0, s>>>(a, n, dest);
   return launch_status();
+}
+
+ROUTE_API int route_predict_sort(const int32_t* tok, int64_t n, const uint8_t* lut,
+                                 const uint8_t* conf, int32_t vocab, const uint8_t* prev2,
+                                 const uint8_t* prev1, const uint8_t* ngram, int32_t G,
+                                 int32_t conf_thr, uint8_t* dest, int32_t* cluster_offsets,
+                                 int32_t* row_of_src, int32_t* src_of_row, uint8_t* row_cluster,
+                                 void* ws, size_t ws_bytes, uint32_t* err, hipStream_t s) {
+  if (n < 0 || vocab < 1 || G < 1 || n >= (int64_t(1) << 31)) return ROUTE_ERR_SHAPE;
+  if (G > kMaxClusters) return ROUTE_ERR_UNSUPPORTED;
+  if (!cluster_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
+    return launch_status();
+  }
+  if (!tok || !lut || !dest || !row_of_src || !src_of_row) return ROUTE_ERR_NULL;
+  if (conf && (!prev2 || !prev1 || !ngram)) return ROUTE_ERR_NULL;
+  if (!ws || ws_bytes < csort_ws_bytes(n, G)) return ROUTE_ERR_WORKSPACE;
+  const PredictKeys src{PredictArgs{tok, lut, conf, vocab, prev2, prev1, ngram, G, conf_thr, err},
+                        dest};
+  return csort_launch_src(src, static_cast<const uint8_t*>(dest), n, G, cluster_offsets,
+                          row_of_src, src_of_row, row_cluster, ws, err, ROUTE_EBIT_DEST_RANGE, s);
+}
+
+ROUTE_API size_t route_predict_sort_workspace_size(int64_t n, int32_t G) {
+  if (n < 0 || G < 1 || G > kMaxClusters) return 0;
+  return csort_ws_bytes(n, G);
 }
 
 ROUTE_API int route_lut_build(const int32_t* ids, int64_t n, const int32_t* idx, const float* w,

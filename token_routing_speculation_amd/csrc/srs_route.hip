@@ -92,30 +92,34 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
 
   // The router rows into LDS as EB rows of CPL * 64 vectors, zeros past the
   // row end and in the rows past E, so every lane's vectors meet a router
-  // value without a guard: 16 bytes per lane, lane i of a wave writing at the
-  // wave's base + 16 i.
+  // value without a guard: piece q (16 bytes) at byte 16 q. The pieces are
+  // loaded into registers here and written to LDS once the first row's loads
+  // are out too; only these older loads are waited for before the barrier.
   constexpr int kRowV = CPL * kWave;  // vectors per staged router row
   constexpr int kPieces = EB * kRowV;
-  for (int q0 = wv * kWave; q0 < kPieces; q0 += kRouteThreads) {
-    const int q = q0 + lane;
+  constexpr int kStage = (kPieces + kRouteThreads - 1) / kRouteThreads;
+  u32x4 wst[kStage];
+#pragma unroll
+  for (int r = 0; r < kStage; ++r) {
+    const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
     const int e = q / kRowV, v = q - e * kRowV;
-    if (e < E && v < nv)
-      lds_load16(w + 8 * (static_cast<size_t>(e) * nv + v), wl + 16 * q0);
-    else
-      *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = u32x4{0, 0, 0, 0};
+    wst[r] = u32x4{0, 0, 0, 0};
+    if (q < kPieces && e < E && v < nv) wst[r] = ld16(w + 8 * (static_cast<size_t>(e) * nv + v));
   }
   // Row loads: streaming (nt) buffer loads through a descriptor spanning the
   // one row, so vectors past the row end read as zeros without a per-vector
   // address. Issued vector by vector (every partial of vector c, then c + 1),
   // so the work on vector c waits only for its own loads.
   u32x4 x[PT][CPL];
-  auto load_row = [&](int64_t r) {
+  // (valid false: an empty descriptor, every vector reads as zeros and no
+  // memory is touched)
+  auto load_row = [&](int64_t r, bool valid) {
     __amdgpu_buffer_rsrc_t rs[PT];
 #pragma unroll
     for (int p = 0; p < PT; ++p)
       rs[p] = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(partials + p * plane + static_cast<size_t>(r) * d),
-          static_cast<short>(0), d * 2, 0x00020000);
+          const_cast<uint16_t*>(partials + (valid ? p * plane + static_cast<size_t>(r) * d : 0)),
+          static_cast<short>(0), valid ? d * 2 : 0, 0x00020000);
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -123,22 +127,31 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
         x[p][c] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[p], lane * 16, c * kWave * 16, 2));
   };
-  // the first row's loads go out with the staging, then both are waited for
+  // The first row's loads go out behind the staging loads, which retire
+  // first (loads count down in issue order): the row's first vectors can be
+  // reduced and stored while its later ones are in flight.
+  // A row's predicted cluster is loaded just before the row itself, so no
+  // later load stands between the row and its first use. Both loads are
+  // issued by every wave (a wave without a row reads zeros and a valid
+  // byte), so the waits for the staging loads count the same on every path.
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kRouteWaves;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteWaves + wv;
-  if (i < n) load_row(i);
-  wait_vmcnt<0>();
-  __syncthreads();
+  int cl = dest ? static_cast<int>(dest[i < n ? i : n - 1]) : 0;
+  load_row(i, i < n);
+#pragma unroll
+  for (int r = 0; r < kStage; ++r) {
+    const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+    if (q < kPieces) *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = wst[r];
+  }
+  lds_barrier();
 
   // lane e < E stands for expert e in the top-K and the count
   const int my_ec = (ro.expert_cluster && lane < E) ? static_cast<int>(ro.expert_cluster[lane]) : -1;
   unsigned lar = 0;
 
   for (; i < n; i += stride) {
-    if (lane == 0) write_identity_row(ident, i, n);
     const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
     const bool keep = dst >= 0 && dst < n;  // key out of range (flagged by the sort): no outputs
-    const int cl = dest ? static_cast<int>(dest[i]) : 0;
     // The row's store through a descriptor spanning the destination row
     // (vectors past its end are dropped; for a row without a destination the
     // descriptor is empty and drops them all).
@@ -227,7 +240,11 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
       }
       if (ro.expert_cluster) lar += __popcll(__ballot(pick && my_ec == cl));
     }
-    if (i + stride < n) load_row(i + stride);
+    if (lane == 0) write_identity_row(ident, i, n);
+    if (i + stride < n) {
+      cl = dest ? static_cast<int>(dest[i + stride]) : 0;
+      load_row(i + stride, true);
+    }
   }
 
   if (ro.expert_cluster) {
@@ -321,6 +338,50 @@ size_t route_ws(int64_t n, int G) {
 
 using namespace route;
 
+// The row work of both entry points: the lane-per-expert kernel for small
+// expert sets, else the matrix-core shuffle + router kernel with the top-K in
+// its epilogue. fwd: each source row's sorted row (null: the identity).
+static int route_rows(const uint16_t* partials, int P, int64_t n, int d, const int* fwd,
+                      const uint8_t* dest, uint16_t* out, const uint16_t* w, int E,
+                      float* logits, int K, int renorm, int* idx, float* weights,
+                      const uint8_t* expert_cluster, unsigned long long* local,
+                      const SrsIdentity& ident, hipStream_t s) {
+  if (!route_fits(P, d, E)) {
+    const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local};
+    return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
+  }
+  const RouteOut ro{logits, idx, weights, expert_cluster, local};
+  const int64_t need = (n + kRouteWaves - 1) / kRouteWaves;
+  const unsigned grid = static_cast<unsigned>(need < kRouteMaxGrid ? need : kRouteMaxGrid);
+  // the padded router rows (room for the per-wave counts at the end too)
+  size_t lds = static_cast<size_t>(route_lds(d, E));
+  if (lds < kRouteWaves * sizeof(unsigned)) lds = kRouteWaves * sizeof(unsigned);
+  const int cpl = route_cpl(d / 8);
+  const int eb = route_eb(E);
+  bool done = false;
+  if (P == 1)
+    done = launch_route<1>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (P == 2)
+    done = launch_route<2>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (P == 4)
+    done = launch_route<4>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
+                           renorm != 0, ro, ident);
+  if (!done) return ROUTE_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+// Shape checks shared by both entry points (SHAPE, then UNSUPPORTED).
+static int route_shape(int P, int64_t n, int d, int E, int K) {
+  if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || E < 1 || K < 1 || K > E ||
+      n >= (int64_t(1) << 31))
+    return ROUTE_ERR_SHAPE;
+  if (K > kMaxK || (!route_fits(P, d, E) && !srs_gate_fits(P, d, E)))
+    return ROUTE_ERR_UNSUPPORTED;
+  return ROUTE_OK;
+}
+
 ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
                                 const uint8_t* dest, int32_t G, uint16_t* out,
                                 int32_t* cluster_offsets, int32_t* row_of_src,
@@ -329,14 +390,10 @@ ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, 
                                 int32_t* idx, float* weights, const uint8_t* expert_cluster,
                                 unsigned long long* local, void* ws, size_t ws_bytes,
                                 uint32_t* err, hipStream_t s) {
-  if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || G < 1 || E < 1 || K < 1 || K > E ||
-      n >= (int64_t(1) << 31))
-    return ROUTE_ERR_SHAPE;
-  // the lane-per-expert kernel for small expert sets, else the matrix-core
-  // shuffle + router kernel with the top-K in its epilogue
-  const bool small = route_fits(P, d, E);
-  if (G > kMaxClusters || K > kMaxK || (!small && !srs_gate_fits(P, d, E)))
-    return ROUTE_ERR_UNSUPPORTED;
+  if (G < 1) return ROUTE_ERR_SHAPE;
+  const int chk = route_shape(P, n, d, E, K);
+  if (chk != ROUTE_OK) return chk;
+  if (G > kMaxClusters) return ROUTE_ERR_UNSUPPORTED;
   if (!cluster_offsets) return ROUTE_ERR_NULL;
   if (n == 0) {
     fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
@@ -362,28 +419,23 @@ ROUTE_API int srs_shuffle_route(const uint16_t* partials, int32_t P, int64_t n, 
   }
   const SrsIdentity ident = sort ? SrsIdentity{nullptr, nullptr, nullptr, nullptr}
                                  : SrsIdentity{cluster_offsets, row_of_src, src_of_row, row_cluster};
-  if (!small) {
-    const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local};
-    return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
-  }
-  const RouteOut ro{logits, idx, weights, expert_cluster, local};
-  const int64_t need = (n + kRouteWaves - 1) / kRouteWaves;
-  const unsigned grid = static_cast<unsigned>(need < kRouteMaxGrid ? need : kRouteMaxGrid);
-  // the padded router rows (room for the per-wave counts at the end too)
-  size_t lds = static_cast<size_t>(route_lds(d, E));
-  if (lds < kRouteWaves * sizeof(unsigned)) lds = kRouteWaves * sizeof(unsigned);
-  const int cpl = route_cpl(d / 8);
-  const int eb = route_eb(E);
-  bool done = false;
-  if (P == 1)
-    done = launch_route<1>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
-  if (P == 2)
-    done = launch_route<2>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
-  if (P == 4)
-    done = launch_route<4>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
-  if (!done) return ROUTE_ERR_UNSUPPORTED;
-  return launch_status();
+  return route_rows(partials, P, n, d, fwd, dest, out, w, E, logits, K, renorm, idx, weights,
+                    expert_cluster, local, ident, s);
+}
+
+ROUTE_API int srs_route_sorted(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                               const int32_t* row_of_src, const uint8_t* dest, uint16_t* out,
+                               const uint16_t* w, int32_t E, float* logits, int32_t K,
+                               int32_t renorm, int32_t* idx, float* weights,
+                               const uint8_t* expert_cluster, unsigned long long* local,
+                               hipStream_t s) {
+  const int chk = route_shape(P, n, d, E, K);
+  if (chk != ROUTE_OK) return chk;
+  if (n == 0) return ROUTE_OK;
+  if (!partials || !out || !w || !idx || !row_of_src) return ROUTE_ERR_NULL;
+  if ((expert_cluster == nullptr) != (local == nullptr)) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(out) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
+  return route_rows(partials, P, n, d, row_of_src, dest, out, w, E, logits, K, renorm, idx,
+                    weights, expert_cluster, local, none, s);
 }

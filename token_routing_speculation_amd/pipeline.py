@@ -3,8 +3,9 @@
 ``RoutePass``: predict -> SRS -> gate -> top-K -> LAR -> permute -> combine
 (identity experts: the combine reads the dispatched rows themselves), the
 s-MoE layer of the "Speculative MoE" notes (section 3.1 and Figure 3's online
-path) on one GPU. For small expert sets the SRS, gate, top-K and LAR stages
-are one kernel after the sort (``srs_route``).
+path) on one GPU. Where the shapes allow, prediction is folded into the
+cluster sort (``predict_sort``) and the SRS, gate, top-K and LAR stages are
+one kernel after it (``srs_route``).
 
 ``FoEPass``: cross-group reduce of the H group activations -> gate ->
 grouped top-k/H -> LAR -> permute from the group activations -> combine
@@ -32,7 +33,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (route_predict, route_lut_build, srs_shuffle, srs_shuffle_route,
+from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
+               srs_shuffle_route, srs_route_sorted,
                route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
@@ -157,7 +159,7 @@ class RoutePass:
         # otherwise
         self.routed = srs_route_takes(P, d, E, K)
         if self.routed:
-            self.STAGES = ("predict", "srs_route", "permute", "combine")
+            self.STAGES = ("predict_sort", "srs_route", "permute", "combine")
 
     def predict(self):
         if self.fallback:
@@ -174,13 +176,18 @@ class RoutePass:
     def gate(self):
         route_gate(self.x, self.w, logits=self.logits)
 
+    def predict_sort(self):
+        # the prediction made where the cluster sort reads each key
+        fb = dict(conf=self.conf, prev2=self.prev2, prev1=self.prev1, ngram=self.ngram,
+                  conf_thr=self.conf_thr) if self.fallback else {}
+        route_predict_sort(self.tok, self.lut, self.G, dest=self.dest, offsets=self.cluster_offsets,
+                           row_of_src=self.row_of_src, src_of_row=self.src_of_row,
+                           row_cluster=self.row_cluster, ws=self.ws_srs, err=self.err, **fb)
+
     def srs_route(self):
-        srs_shuffle_route(self.partials, self.dest, self.G, self.w, self.K, 1,
-                          expert_cluster=self.expert_cluster, local=self.local, out=self.x,
-                          logits=self.logits, idx=self.idx, weights=self.weights,
-                          offsets=self.cluster_offsets, row_of_src=self.row_of_src,
-                          src_of_row=self.src_of_row, row_cluster=self.row_cluster,
-                          ws=self.ws_srs, err=self.err)
+        srs_route_sorted(self.partials, self.row_of_src, self.w, self.K, 1, dest=self.dest,
+                         expert_cluster=self.expert_cluster, local=self.local, out=self.x,
+                         logits=self.logits, idx=self.idx, weights=self.weights)
 
     def topk(self):
         route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
