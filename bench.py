@@ -536,6 +536,18 @@ def predictor_measure(args):
     qg_unpacked_us = back_to_back_us(
         lambda: route_qgate_topk(Lg["r"], Lg["dvec"], Lg["w_next"], p.K, eps=Lg["eps"], idx=p.pred,
                                  truth=p.truth, hits=p.hits))
+    # the estimator's first product (with its bias, GELU and bf16 rounding)
+    # beside the vendor GEMM on the same operands (torch.matmul, bf16 out, no
+    # bias or GELU), both back to back on a resident q: context for
+    # estimator_mfma_frac, not a part of the path
+    from token_routing_speculation_amd import route_est_hidden
+    Le = layers[0]
+    h_est = torch.empty((N, cfg.hd), dtype=torch.bfloat16, device="cuda")
+    w1_t = Le["w1"].view(torch.bfloat16).t().contiguous()
+    q_bf = p.q.view(torch.bfloat16)
+    est_first_us = back_to_back_us(lambda: route_est_hidden(p.q, Le["w1"], Le["b1"], h=h_est))
+    vendor_first_us = back_to_back_us(lambda: torch.matmul(q_bf, w1_t, out=h_est))
+    del h_est, w1_t
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
     rates = []
@@ -589,6 +601,10 @@ def predictor_measure(args):
                                                  QGATE_TRAFFIC_SOURCES)},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
+        "estimator_first_product_us": {"route_est_hidden": est_first_us,
+                                       "vendor_gemm_no_epilogue": vendor_first_us,
+                                       "mfma_frac": 2.0 * N * cfg.d * cfg.hd
+                                       / (est_first_us * 1e-6) / MFMA_BF16_PEAK},
         "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),
         "estimator_weights": ("fitted (ridge on a held-out batch of %d tokens)" % args.fit_tokens)
         if args.fit else "random (as drawn)",

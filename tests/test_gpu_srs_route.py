@@ -242,16 +242,53 @@ def test_srs_route_rows_bit_exact_on_special_values(kind):
 
 @pytest.mark.parametrize("n,d,P,G,E,K", [(1000, 520, 2, 8, 8, 2), (777, 384, 4, 5, 16, 4),
                                          (2049, 5120, 2, 8, 160, 6), (300, 256, 2, 3, 150, 8)])
-def test_srs_route_sorted_equals_srs_shuffle_route(n, d, P, G, E, K):
-    """Given srs_shuffle_route's own order, srs_route_sorted writes the same
-    bytes (rows, logits, picks, weights) and the same count, through both
-    kernels."""
+def test_srs_route_sorted_against_oracle(n, d, P, G, E, K):
+    """srs_route_sorted on the oracle's own shuffle order: rows, logits,
+    picks, weights and count against the oracle (as srs_shuffle_route's
+    are), and the same bytes as srs_shuffle_route, through both kernels."""
     parts, dest, w, ec = _inputs(n, d, P, G, E)
-    (out, offs, ros, sor, rc, lg, idx, wt), local = _run(parts, dest, G, w, K, ec)
+    want = oracle.srs_shuffle(parts, dest.astype(np.int64), G)
+    ros_o = torch.from_numpy(want["row_of_src"].astype(np.int32)).cuda()
     loc2 = torch.zeros(1, dtype=torch.int64, device="cuda")
-    o2, l2, i2, w2 = tr.srs_route_sorted(dev(parts), ros, dev(w), K, 1, dest=dev(dest),
+    o2, l2, i2, w2 = tr.srs_route_sorted(dev(parts), ros_o, dev(w), K, 1, dest=dev(dest),
                                          expert_cluster=dev(ec), local=loc2)
     sync()
+    maps = tuple(torch.from_numpy(np.asarray(want[k]).astype(dt)).cuda() for k, dt in
+                 (("offsets", np.int32), ("row_of_src", np.int32), ("src_of_row", np.int32),
+                  ("row_cluster", np.uint8)))
+    _check(parts, dest, G, w, K, ec, 1, (o2,) + maps + (l2, i2, w2), loc2)
+    (out, _, _, _, _, lg, idx, wt), local = _run(parts, dest, G, w, K, ec)
     for a, b in ((out, o2), (lg, l2), (idx, i2), (wt, w2)):
         assert torch.equal(a, b)
     assert int(local.item()) == int(loc2.item())
+
+
+@pytest.mark.parametrize("n,d,G,E,K,fallback", [(4096, 1024, 4, 8, 2, False),
+                                                (5000, 512, 8, 160, 6, True)])
+def test_predict_sort_then_route_against_oracle(n, d, G, E, K, fallback):
+    """The routed pass's first two calls, route_predict_sort then
+    srs_route_sorted, against the oracle's prediction, shuffle, gate, top-K
+    and count of the same inputs (one-workgroup and two-launch sorts, the
+    lane-per-expert and the matrix-core route kernels)."""
+    P, V = 2, 3000
+    rng = np.random.default_rng(n + E)
+    parts, _, w, ec = _inputs(n, d, P, G, E)
+    tok = rng.integers(0, V, n).astype(np.int32)
+    lut = rng.integers(0, G, V).astype(np.uint8)
+    fb = {}
+    conf = prev2 = prev1 = ngram = None
+    if fallback:
+        conf = rng.integers(0, 256, V).astype(np.uint8)
+        prev2 = rng.integers(0, G, n).astype(np.uint8)
+        prev1 = rng.integers(0, G, n).astype(np.uint8)
+        ngram = rng.integers(0, G, (G, G)).astype(np.uint8)
+        fb = dict(conf=dev(conf), prev2=dev(prev2), prev1=dev(prev1), ngram=dev(ngram))
+    dest, offs, ros, sor, rc = tr.route_predict_sort(dev(tok), dev(lut), G, **fb)
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lg, idx, wt = tr.srs_route_sorted(dev(parts), ros, dev(w), K, 1, dest=dest,
+                                           expert_cluster=dev(ec), local=local)
+    sync()
+    want_dest = oracle.route_predict(tok, lut, conf, prev2, prev1, ngram, 128, G=G)
+    assert np.array_equal(host(dest), want_dest)
+    _check(parts, want_dest.astype(np.uint8), G, w, K, ec, 1,
+           (out, offs, ros, sor, rc, lg, idx, wt), local)
