@@ -189,7 +189,13 @@ def test_topk(n, E, K, H, renorm):
 PERM_CASES = [(1, 4, 2, 1, 8), (500, 4, 2, 1, 136), (1000, 8, 2, 1, 512), (3000, 160, 6, 1, 64),
               (2000, 64, 8, 4, 128), (1025, 1024, 16, 1, 8), (4096, 16, 4, 2, 40), (77, 3, 3, 1, 16),
               # few experts, many pairs
-              (16384, 8, 2, 1, 16), (20000, 8, 2, 1, 16)]
+              (16384, 8, 2, 1, 16), (20000, 8, 2, 1, 16),
+              # the one-launch dispatch (at most 16 experts and 16384 pairs) on
+              # both sides of its pair limit, with 9..16 experts (two lane
+              # counter registers), one expert, groups, ragged rows, and K = 16
+              # (a chunk ranked by several waves)
+              (8192, 8, 2, 1, 64), (8193, 8, 2, 1, 64), (1024, 16, 16, 1, 24), (3000, 9, 3, 3, 32),
+              (33, 1, 1, 1, 8), (2500, 12, 4, 2, 4096), (700, 8, 2, 1, 5120)]
 
 
 @pytest.mark.parametrize("n,E,K,H,d", PERM_CASES)
@@ -286,6 +292,32 @@ def test_permute_flags_bad_expert():
     sync()
     assert int(err.item()) & tr.EBIT_EXPERT_RANGE
     assert host(sop)[2] == -1 and host(offs)[-1] == 3
+
+
+@pytest.mark.parametrize("n", [3000, 20000])
+def test_permute_rows_flag_bad_experts(n):
+    """Out-of-range expert ids with rows, in the one-launch dispatch (3000
+    pairs) and the sort + move (20000): flagged, slot -1, nothing moved for
+    them; the rest dispatched as if they were absent."""
+    E, d = 8, 64
+    rng = np.random.default_rng(n)
+    idx = rng.integers(0, E, (n, 1)).astype(np.int32)
+    bad = rng.choice(n, 9, replace=False)
+    idx[bad[:5], 0] = E + 3
+    idx[bad[5:], 0] = -2
+    src = _bf16((1, n, d), n)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs, sop, pos, disp = tr.moe_permute(dev(idx), E, dev(src), err=err)
+    sync()
+    assert int(err.item()) & tr.EBIT_EXPERT_RANGE
+    good = np.setdiff1d(np.arange(n), bad)
+    ref = oracle.moe_permute(idx[good], E, 1, src[:, good])
+    s = host(sop)
+    assert np.all(s[bad] == -1)
+    assert np.array_equal(host(offs), ref["expert_offsets"])
+    assert np.array_equal(s[good], ref["slot_of_pair"])
+    assert np.array_equal(host(pos)[: len(good)], good[ref["pair_of_slot"]])
+    assert np.array_equal(host(disp)[: len(good)], ref["disp"])
 
 
 # ------------------------------------------------------------ counters

@@ -50,12 +50,23 @@ __device__ __forceinline__ uint32_t key_u32<int32_t>(int32_t k) {
   return k < 0 ? 0xffffffffu : static_cast<uint32_t>(k);
 }
 
-// Key sources: key j of the array (ArrayKeys), or any functor with the same
-// call (route_predict_sort's computes each key from the token as it goes).
+// Key sources. A source fills a batch of keys at once: k[q] = key j[q] where
+// in[q], else 0xffffffff. Every load is issued unmasked (at key 0 in place of
+// a masked one) and masked afterwards: a load under a branch is waited for
+// inside it, so a batch would arrive one key at a time. ArrayKeys reads an
+// array; route_predict_sort's source computes each key from its token.
 template <typename KeyT>
 struct ArrayKeys {
   const KeyT* __restrict__ p;
-  __device__ __forceinline__ uint32_t operator()(int64_t j) const { return key_u32<KeyT>(p[j]); }
+  template <int NB>
+  __device__ __forceinline__ void batch(const int64_t (&j)[NB], const bool (&in)[NB],
+                                        uint32_t (&k)[NB]) const {
+    KeyT v[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v[q] = p[in[q] ? j[q] : 0];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) k[q] = in[q] ? key_u32<KeyT>(v[q]) : 0xffffffffu;
+  }
 };
 
 template <typename Src>
@@ -74,11 +85,14 @@ __global__ __launch_bounds__(kSortThreads) void csort_hist(Src keys, int64_t n, 
   // overlap instead of each waiting behind the previous count
   for (int64_t j0 = lo + threadIdx.x; j0 < hi; j0 += kBatch * kSortThreads) {
     uint32_t k[kBatch];
+    int64_t jq[kBatch];
+    bool in[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int64_t j = j0 + q * kSortThreads;
-      k[q] = j < hi ? keys(j) : 0xffffffffu;
+      jq[q] = j0 + q * kSortThreads;
+      in[q] = jq[q] < hi;
     }
+    keys.batch(jq, in, k);
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (k[q] < static_cast<uint32_t>(B))
@@ -128,41 +142,43 @@ __device__ __forceinline__ void scan_bins(int* tot, int B, int* total) {
   if (lane == kWave - 1) *total = incl;
 }
 
-constexpr int64_t kSpan = static_cast<int64_t>(kBatch) * kWave;  // keys per batch of tiles
-
-// keys [base, base + kSpan) of a share ending at qhi, one per lane and tile
-template <typename Src>
-__device__ __forceinline__ void load_batch(const Src& keys, uint32_t (&kb)[kBatch], int64_t base,
+// keys [base, base + NB * 64) of a share ending at qhi, one per lane and tile
+// (NB tiles)
+template <typename Src, int NB>
+__device__ __forceinline__ void load_batch(const Src& keys, uint32_t (&kb)[NB], int64_t base,
                                            int64_t qhi) {
   const int lane = lane_id();
+  int64_t jq[NB];
+  bool in[NB];
 #pragma unroll
-  for (int q = 0; q < kBatch; ++q) {
-    const int64_t j = base + q * kWave + lane;
-    kb[q] = j < qhi ? keys(j) : 0xffffffffu;
+  for (int q = 0; q < NB; ++q) {
+    jq[q] = base + q * kWave + lane;
+    in[q] = jq[q] < qhi;
   }
+  keys.batch(jq, in, kb);
 }
 
 // Pass 1 of the ranking: per-bin counts of the keys [qlo, qhi) into this
 // wave's LDS row (per 64-key tile, the lowest lane of each key's match adds
 // the match size). first[] holds the share's first batch, already loaded.
 // Returns whether a key of the share was out of range.
-template <typename Src>
+template <typename Src, int NB>
 __device__ __forceinline__ bool count_share(const Src& keys, int64_t qlo, int64_t qhi, int B,
-                                            int nbits, const uint32_t (&first)[kBatch],
+                                            int nbits, const uint32_t (&first)[NB],
                                             int* myrow) {
   const int lane = lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   bool bad = false;
-  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
-    uint32_t kb[kBatch];
+  for (int64_t jb = qlo; jb < qhi; jb += NB * kWave) {
+    uint32_t kb[NB];
     if (jb == qlo) {
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+      for (int q = 0; q < NB; ++q) kb[q] = first[q];
     } else {
       load_batch(keys, kb, jb, qhi);
     }
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
+    for (int q = 0; q < NB; ++q) {
       if (jb + q * kWave >= qhi) break;
       const uint32_t k = kb[q];
       const bool valid = k < static_cast<uint32_t>(B);
@@ -178,23 +194,25 @@ __device__ __forceinline__ bool count_share(const Src& keys, int64_t qlo, int64_
 // its bin plus its rank among equal keys of its tile; the lowest lane of the
 // match then advances the start. fwd[j] = position, inv[pos] = j,
 // inv_key[pos] = key (nullable); out-of-range keys get position -1.
-template <typename Src>
+// With lpos given, each key's position (or -1) also goes to lpos[j - lbase].
+template <typename Src, int NB>
 __device__ __forceinline__ void place_share(const Src& keys, int64_t qlo, int64_t qhi, int B,
-                                            int nbits, const uint32_t (&first)[kBatch],
+                                            int nbits, const uint32_t (&first)[NB],
                                             int* myrow, int* __restrict__ fwd,
-                                            int* __restrict__ inv, uint8_t* __restrict__ inv_key) {
+                                            int* __restrict__ inv, uint8_t* __restrict__ inv_key,
+                                            int* lpos = nullptr, int64_t lbase = 0) {
   const int lane = lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t jb = qlo; jb < qhi; jb += kSpan) {
-    uint32_t kb[kBatch];
+  for (int64_t jb = qlo; jb < qhi; jb += NB * kWave) {
+    uint32_t kb[NB];
     if (jb == qlo) {
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) kb[q] = first[q];
+      for (int q = 0; q < NB; ++q) kb[q] = first[q];
     } else {
       load_batch(keys, kb, jb, qhi);
     }
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
+    for (int q = 0; q < NB; ++q) {
       const int64_t j0 = jb + q * kWave;
       if (j0 >= qhi) break;
       const int64_t j = j0 + lane;
@@ -209,8 +227,10 @@ __device__ __forceinline__ void place_share(const Src& keys, int64_t qlo, int64_
         fwd[j] = pos;
         inv[pos] = static_cast<int>(j);
         if (inv_key) inv_key[pos] = static_cast<uint8_t>(k);
+        if (lpos) lpos[j - lbase] = pos;
       } else if (j < qhi) {
         fwd[j] = -1;
+        if (lpos) lpos[j - lbase] = -1;
       }
       if (valid && rank == 0) myrow[k] = start + __popcll(m);
     }
@@ -375,6 +395,97 @@ __global__ __launch_bounds__(kSortOneThreads) void csort_one(
   if (t == 0) offsets[B] = stotal;
   __syncthreads();
   place_share(keys, qlo, qhi, B, nbits, first, myrow, fwd, inv, inv_key);
+}
+
+// Counting every key outside chunk [clo, chi) of [0, n), for kernels that
+// rank one chunk each without a histogram table (every workgroup counts the
+// whole array for itself, so this pays for small arrays only). Per bin, for
+// this wave's share of those keys: the keys before the chunk go to pre[b],
+// those after it to post[b], for B <= 8 * NR bins. The keys outside the
+// chunk are taken as one range (index j' < clo is key j', else key j' +
+// chunk length), split into NW shares of whole tiles, counted a batch of NBO
+// keys per lane at a time. Each lane keeps 8-bit counters, eight to a 64-bit
+// register (a lane meets at most kCountMaxPerLane keys); the wave's totals
+// are summed in 16-bit fields. Out-of-range keys are not counted (their
+// owner flags them).
+constexpr int kCountMaxPerLane = 255;
+
+// This wave's share of the keys outside the chunk (indices of the joined
+// range; NW shares of whole tiles).
+template <int NW>
+__device__ __forceinline__ void others_share(int64_t n, int64_t clo, int64_t chi, int w,
+                                             int64_t* qlo, int64_t* qhi) {
+  const int64_t len = n - (chi - clo);
+  const int64_t share = ((len + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  *qlo = w * share < len ? w * share : len;
+  *qhi = *qlo + share < len ? *qlo + share : len;
+}
+
+// The first batch of the share [qlo, qhi), NBO keys per lane
+// (0xffffffff past the share), so the caller can issue it early. Index
+// arithmetic in 32 bits (n < 2^31).
+template <typename Src, int NBO>
+__device__ __forceinline__ void others_load(const Src& keys, int64_t qlo, int64_t qhi,
+                                            int64_t clo, int64_t chi,
+                                            uint32_t (&k)[NBO]) {
+  const int lane = lane_id();
+  const int lo = static_cast<int>(qlo), hi = static_cast<int>(qhi);
+  const int c0 = static_cast<int>(clo), gap = static_cast<int>(chi - clo);
+  int64_t jq[NBO];
+  bool in[NBO];
+#pragma unroll
+  for (int q = 0; q < NBO; ++q) {
+    const int jp = lo + q * kWave + lane;
+    in[q] = jp < hi;
+    jq[q] = jp < c0 ? jp : jp + gap;
+  }
+  keys.batch(jq, in, k);
+}
+
+// Counts the share, its first batch already in k[] (loaded by others_load).
+template <int NR, typename Src, int NBO>
+__device__ __forceinline__ void others_count(const Src& keys, int64_t qlo, int64_t qhi,
+                                             int64_t clo, int64_t chi, int B,
+                                             uint32_t (&k)[NBO], int* pre, int* post) {
+  const int lane = lane_id();
+  uint64_t cp[NR], cq[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) cp[r] = cq[r] = 0;
+  for (int64_t jb = qlo; jb < qhi; jb += NBO * kWave) {
+    if (jb != qlo) others_load(keys, jb, qhi, clo, chi, k);
+    const int rel = static_cast<int>(jb - clo) + lane;  // < 0: before the chunk
+#pragma unroll
+    for (int q = 0; q < NBO; ++q) {
+      const uint64_t one = k[q] < static_cast<uint32_t>(B) ? 1ull << (8 * (k[q] & 7u)) : 0ull;
+      const bool before = rel + q * kWave < 0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint64_t add = (k[q] >> 3) == static_cast<uint32_t>(r) ? one : 0ull;
+        cp[r] += before ? add : 0ull;
+        cq[r] += before ? 0ull : add;
+      }
+    }
+  }
+  auto flush = [&](uint64_t c, int r, int* row) {
+    // bins 8r + {0, 2, 4, 6} and 8r + {1, 3, 5, 7} as 16-bit fields
+    const uint64_t even = c & 0x00ff00ff00ff00ffull;
+    const uint64_t odd = (c >> 8) & 0x00ff00ff00ff00ffull;
+    const uint32_t s0 = static_cast<uint32_t>(wave_sum_dpp(static_cast<int>(even)));
+    const uint32_t s1 = static_cast<uint32_t>(wave_sum_dpp(static_cast<int>(even >> 32)));
+    const uint32_t s2 = static_cast<uint32_t>(wave_sum_dpp(static_cast<int>(odd)));
+    const uint32_t s3 = static_cast<uint32_t>(wave_sum_dpp(static_cast<int>(odd >> 32)));
+    // lane l < 8 takes bin 8r + l: word (l & 1 ? odd : even), half (l & 2)
+    const int l = lane & 7;
+    const uint32_t word = (l & 1) ? ((l & 4) ? s3 : s2) : ((l & 4) ? s1 : s0);
+    const int v = static_cast<int>((l & 2) ? word >> 16 : word & 0xffffu);
+    const int b = 8 * r + l;
+    if (lane < 8 && b < B) row[b] = v;
+  };
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    flush(cp[r], r, pre);
+    flush(cq[r], r, post);
+  }
 }
 
 __global__ void fill_i32(int* __restrict__ p, int64_t n, int value) {

@@ -8,6 +8,7 @@
 
 #include "common.hpp"
 #include "csort.hpp"
+#include "mfma.hpp"
 
 namespace route {
 
@@ -71,6 +72,138 @@ __global__ __launch_bounds__(kPermThreads) void permute_move(const uint16_t* __r
           st16_stream(dst + 8 * v, x[c]);
         else
           st16(dst + 8 * v, x[c]);
+      }
+    }
+  }
+}
+
+// The dispatch in one launch, for small batches over few experts: workgroup
+// b owns tokens [16 b, 16 b + 16), one wave each, and so the contiguous
+// chunk of their pairs. Each wave issues, in this order, the loads of its
+// share of the chunk's expert ids, of its share of all the other ids, and of
+// its token's row; counts the others by expert (those before the chunk, and
+// all of them), ranks the chunk as csort_rank does, keeps the chunk's slots
+// in LDS and stores its row to them: the sort's two launches and the move's
+// in one. The sort's ids are waited for alone (loads retire in issue order)
+// and its barriers wait only for LDS, so the rows stay in flight throughout.
+// Workgroup 0 writes the expert offsets. Every workgroup reads all n K
+// expert ids (from L2 after the first), which bounds the form to small n K;
+// rows of up to eight 16-byte vectors per lane (d <= 4096) keep it within
+// the registers of sixteen waves.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedTokens = kFusedThreads / kWave;
+constexpr int64_t kFusedMaxPairs = 16384;
+constexpr int kFusedMaxE = 16;
+constexpr int kFusedMaxK = kMaxK;
+// Other ids per lane loaded ahead of counting (a wave's share of them is one
+// batch up to 8192 pairs, two up to 16384); a lane meets at most
+// kFusedMaxPairs / 1024 of them, within its 8-bit counters.
+constexpr int kFusedOthers = 8;
+static_assert(kFusedMaxPairs / kFusedThreads + 1 <= kCountMaxPerLane, "lane counters");
+// the chunk (16 K pairs) is one tile per wave: ceil(16 K / 16) <= 64
+
+template <int CPL, bool STREAM>
+__global__ __launch_bounds__(kFusedThreads) void permute_fused(
+    const int32_t* __restrict__ idx, int64_t n, int K, int E, int H, int nbits,
+    const uint16_t* __restrict__ src, int d, int* __restrict__ offsets,
+    int* __restrict__ slot_of_pair, int* __restrict__ pair_of_slot,
+    uint16_t* __restrict__ disp, uint32_t* err) {
+  constexpr int NW = kFusedTokens;
+  __shared__ int stot[kFusedMaxE];
+  __shared__ int sbase[kFusedMaxE];
+  __shared__ int wrow[NW * kFusedMaxE];  // this chunk's counts per wave, then starts
+  __shared__ int orow[NW * kFusedMaxE];  // the other pairs' counts: before the chunk
+  __shared__ int prow[NW * kFusedMaxE];  // and after it
+  __shared__ int spos[NW * kFusedMaxK];  // the chunk's slots
+  __shared__ int stotal;
+  const int t = threadIdx.x;
+  const int w = wave_id();
+  const int lane = lane_id();
+  const int64_t b = blockIdx.x;
+  const int64_t i = b * NW + w;  // this wave's token
+  const int kg = K / H;
+  const int nv = d >> 3;
+  const int64_t nK = n * K;
+  const ArrayKeys<int32_t> keys{idx};
+
+  // this wave's share of the chunk's pairs (ranked as in csort_rank), then
+  // its share of the other pairs, then its token's first group row
+  const int64_t clo = b * NW * K;
+  const int64_t chi = clo + NW * K < nK ? clo + NW * K : nK;
+  const int64_t share = ((chi - clo + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int64_t qlo = clo + (w * share < chi - clo ? w * share : chi - clo);
+  const int64_t qhi = qlo + share < chi ? qlo + share : chi;
+  uint32_t first[1];
+  load_batch(keys, first, qlo, qhi);
+  int64_t olo, ohi;
+  others_share<NW>(nK, clo, chi, w, &olo, &ohi);
+  uint32_t ok[kFusedOthers];
+  others_load(keys, olo, ohi, clo, chi, ok);
+  u32x4 x[CPL];
+  auto load_row = [&](int h) {
+    const uint16_t* row = src + (static_cast<size_t>(h) * n + i) * d;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int v = lane + c * kWave;
+      x[c] = ld16(row + 8 * (v < nv ? v : 0));  // past the row end: vector 0, never stored
+    }
+  };
+  if (i < n) load_row(0);
+
+  if (E <= 8)
+    others_count<1>(keys, olo, ohi, clo, chi, E, ok, orow + w * E, prow + w * E);
+  else
+    others_count<2>(keys, olo, ohi, clo, chi, E, ok, orow + w * E, prow + w * E);
+  int* myrow = wrow + w * E;
+  if (lane < E) myrow[lane] = 0;  // each wave touches only its own rows, in order
+  const bool bad = qlo < qhi && count_share(keys, qlo, qhi, E, nbits, first, myrow);
+  if (bad) set_err(err, ROUTE_EBIT_EXPERT_RANGE);
+  lds_barrier();
+  for (int e = t; e < E; e += kFusedThreads) {
+    int pre = 0, rest = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      pre += orow[v * E + e];
+      rest += wrow[v * E + e] + prow[v * E + e];
+    }
+    sbase[e] = pre;
+    stot[e] = pre + rest;
+  }
+  lds_barrier();
+  if (w == 0) scan_bins(stot, E, &stotal);
+  lds_barrier();
+  for (int e = t; e < E; e += kFusedThreads) {
+    if (b == 0) offsets[e] = stot[e];
+    int run = stot[e] + sbase[e];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int cnt = wrow[v * E + e];
+      wrow[v * E + e] = run;
+      run += cnt;
+    }
+  }
+  if (b == 0 && t == 0) offsets[E] = stotal;
+  lds_barrier();
+  if (qlo < qhi)
+    place_share(keys, qlo, qhi, E, nbits, first, myrow, slot_of_pair, pair_of_slot,
+                static_cast<uint8_t*>(nullptr), spos, clo);
+  lds_barrier();
+  if (i >= n) return;
+  for (int h = 0; h < H; ++h) {
+    if (h > 0) load_row(h);
+    for (int q = 0; q < kg; ++q) {
+      const int sl = spos[w * K + h * kg + q];
+      if (sl < 0 || sl >= nK) continue;  // out-of-range expert: no slot
+      uint16_t* dst = disp + static_cast<size_t>(sl) * d;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int v = lane + c * kWave;
+        if (v < nv) {
+          if constexpr (STREAM)
+            st16_stream(dst + 8 * v, x[c]);
+          else
+            st16(dst + 8 * v, x[c]);
+        }
       }
     }
   }
@@ -155,13 +288,35 @@ ROUTE_API int moe_permute(const int32_t* idx, int64_t n, int32_t K, int32_t E, i
     fill_i32<<<ceil_div(E + 1, 256), 256, 0, s>>>(expert_offsets, E + 1, 0);
     return launch_status();
   }
+  const bool stream = K / H >= kPermStreamCopies;
+  if (src && E <= kFusedMaxE && n * K <= kFusedMaxPairs && cpl_for(d / 8) <= 8) {
+    // the sort and the move in one launch (no workspace used)
+    const unsigned grid = ceil_div(n, kFusedTokens);
+    switch (cpl_for(d / 8)) {
+#define ROUTE_FUSED_CASE(c)                                                                   \
+  case c:                                                                                     \
+    if (stream)                                                                               \
+      permute_fused<c, true><<<grid, kFusedThreads, 0, s>>>(idx, n, K, E, H, bits_for(E), src, \
+                                                            d, expert_offsets, slot_of_pair,  \
+                                                            pair_of_slot, disp, err);         \
+    else                                                                                      \
+      permute_fused<c, false><<<grid, kFusedThreads, 0, s>>>(idx, n, K, E, H, bits_for(E),    \
+                                                             src, d, expert_offsets,          \
+                                                             slot_of_pair, pair_of_slot, disp, \
+                                                             err);                            \
+    break;
+      ROUTE_FUSED_CASE(1) ROUTE_FUSED_CASE(2) ROUTE_FUSED_CASE(4) ROUTE_FUSED_CASE(8)
+#undef ROUTE_FUSED_CASE
+      default: return ROUTE_ERR_UNSUPPORTED;
+    }
+    return launch_status();
+  }
   if (!ws || ws_bytes < moe_permute_workspace_size(n, K, E)) return ROUTE_ERR_WORKSPACE;
   int st = csort_launch<int32_t>(idx, n * K, E, expert_offsets, slot_of_pair, pair_of_slot,
                                  nullptr, ws, err, ROUTE_EBIT_EXPERT_RANGE, s);
   if (st != ROUTE_OK || !src || n == 0) return st;
   if (d > 16 * 8 * kWave) return ROUTE_ERR_UNSUPPORTED;
   const unsigned grid = ceil_div(n * H, kPermThreads / kWave);
-  const bool stream = K / H >= kPermStreamCopies;
   switch (cpl_for(d / 8)) {
 #define ROUTE_CPL_CASE(c)                                                                     \
   case c:                                                                                     \

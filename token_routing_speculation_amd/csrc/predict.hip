@@ -21,14 +21,32 @@ __global__ __launch_bounds__(kPredThreads) void predict_kernel(PredictArgs a, in
 }
 
 // The sort's key source for route_predict_sort: token j's prediction, also
-// written to dest[j] (a key read again writes the same byte).
+// written to dest[j] (a key read again writes the same byte). A batch is
+// predicted in stages (predict_stage1/2/3), each stage's loads issued for
+// every key before any is used, and its error bits are flagged once.
 struct PredictKeys {
   PredictArgs a;
   uint8_t* dest;
-  __device__ __forceinline__ uint32_t operator()(int64_t j) const {
-    const int c = predict_cluster(a, j);
-    dest[j] = static_cast<uint8_t>(c);
-    return static_cast<uint32_t>(c);
+  template <int NB>
+  __device__ __forceinline__ void batch(const int64_t (&j)[NB], const bool (&in)[NB],
+                                        uint32_t (&k)[NB]) const {
+    PredictLoads s[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) s[q] = predict_stage1(a, in[q] ? j[q] : 0);
+#pragma unroll
+    for (int q = 0; q < NB; ++q) predict_stage2(a, s[q]);
+    uint32_t e = 0;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      uint32_t eq = 0;
+      const int c = predict_stage3(a, s[q], &eq);
+      if (in[q]) {
+        dest[j[q]] = static_cast<uint8_t>(c);
+        e |= eq;
+      }
+      k[q] = in[q] ? static_cast<uint32_t>(c) : 0xffffffffu;
+    }
+    if (e) set_err(a.err, e);
   }
 };
 

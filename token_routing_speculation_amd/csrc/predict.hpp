@@ -45,4 +45,47 @@ __device__ __forceinline__ int predict_cluster(const PredictArgs& a, int64_t i) 
   return c;
 }
 
+// The same prediction in three stages with no branch around a load, for
+// callers that predict a batch at once (every stage's loads issued for the
+// whole batch before any is used). Stage 1 loads the token and the previous
+// clusters, stage 2 the table entries (at token 0 and 2-gram entry 0 in place
+// of out-of-range ones), stage 3 chooses and returns the cluster, with the
+// error bits that predict_cluster would flag put in *e.
+struct PredictLoads {
+  int t, p2, p1, c, cf, g;
+};
+
+__device__ __forceinline__ PredictLoads predict_stage1(const PredictArgs& a, int64_t i) {
+  PredictLoads s{};
+  s.t = a.tok[i];
+  if (a.conf) {
+    s.p2 = a.prev2[i];
+    s.p1 = a.prev1[i];
+  }
+  return s;
+}
+
+__device__ __forceinline__ void predict_stage2(const PredictArgs& a, PredictLoads& s) {
+  const int tc = (s.t >= 0 && s.t < a.vocab) ? s.t : 0;
+  s.c = a.lut[tc];
+  if (a.conf) {
+    s.cf = a.conf[tc];
+    s.g = a.ngram[(s.p2 < a.G && s.p1 < a.G) ? s.p2 * a.G + s.p1 : 0];
+  }
+}
+
+__device__ __forceinline__ int predict_stage3(const PredictArgs& a, const PredictLoads& s,
+                                              uint32_t* e) {
+  if (s.t < 0 || s.t >= a.vocab) {
+    *e |= ROUTE_EBIT_TOKEN_RANGE;
+    return 0;
+  }
+  if (a.conf && s.cf < a.conf_thr) {
+    if (s.p2 < a.G && s.p1 < a.G) return s.g;
+    *e |= ROUTE_EBIT_DEST_RANGE;
+    return 0;
+  }
+  return s.c;
+}
+
 }  // namespace route
