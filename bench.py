@@ -30,12 +30,13 @@ METRIC = "routed tokens/s (gate->top-K->SRS shuffle->combine) and % of HBM roofl
 ROUTE_WORKLOADS = {"tiny": "tiny", "mixtral": "mixtral-8x7b-shaped", "deepseek": "deepseek-v2-shaped"}
 
 
-def route_bytes(N, d, E, K, P, G, fallback, routed=False):
+def route_bytes(N, d, E, K, P, G, fallback, routed=False, stages=None):
     """Algorithmic HBM bytes per pass: every call reads its inputs once and
     writes its outputs once (bf16 rows = 2 bytes per element). With the
     shuffle, router, top-K and count in one kernel (srs_shuffle_route) the
     reduced rows are written once and not read back, and neither are the
-    logits nor the picks."""
+    logits nor the picks; with the prediction in that kernel too
+    (srs_predict_route) the predicted clusters are not read back either."""
     b = 2
     st = {
         "predict": (9 if fallback else 6) * N,
@@ -49,10 +50,15 @@ def route_bytes(N, d, E, K, P, G, fallback, routed=False):
     if routed:
         # prediction folded into the cluster sort (its maps: 9 bytes a token
         # and the offsets), then the rows with their router, top-K and count
-        return {"predict_sort": st["predict"] + 9 * N + 4 * (G + 1),
-                "srs_route": (P * N * d * b + N * d * b + E * d * b + 4 * N * E + 8 * N * K
-                              + 5 * N + E),
-                "permute": st["permute"], "combine": st["combine"]}
+        rt = {"predict_sort": st["predict"] + 9 * N + 4 * (G + 1),
+              "srs_route": (P * N * d * b + N * d * b + E * d * b + 4 * N * E + 8 * N * K
+                            + 5 * N + E),
+              "permute": st["permute"], "combine": st["combine"]}
+        if stages is not None and "predict_route" in stages:
+            # both in one kernel: the clusters are not read back (N bytes)
+            rt = {"predict_route": rt["predict_sort"] + rt["srs_route"] - N,
+                  "permute": rt["permute"], "combine": rt["combine"]}
+        return rt
     return st
 
 
@@ -1039,7 +1045,8 @@ def route_measure(args, name):
                 "K": cfg.K, "G": cfg.G}
     else:
         p = RoutePass(inp)
-        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.routed)
+        bytes_st = route_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.P, cfg.G, p.fallback, p.routed,
+                               p.STAGES)
         conf = {"workload": ROUTE_WORKLOADS[name], "N": cfg.N, "d": cfg.d, "E": cfg.E,
                 "K": cfg.K, "P": cfg.P, "G": cfg.G, "vocab": cfg.V,
                 "fallback": "2-gram" if p.fallback else "none"}
@@ -1102,7 +1109,7 @@ def route_measure(args, name):
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
     # the stage holding the router product
-    gate_stage = next(g for g in ("gate", "srs_route") if g in st_us)
+    gate_stage = next(g for g in ("gate", "srs_route", "predict_route") if g in st_us)
     # dominant single-kernel stage: the combine (one launch per pass)
     dom = "combine"
     dom_bytes = bytes_st[dom]

@@ -245,6 +245,33 @@ int srs_route_sorted(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
                      unsigned long long* local, hipStream_t s);
 
 /*
+ * srs_predict_route - route_predict_sort followed by srs_route_sorted, in
+ * one launch for small batches: [SMOE] section 4.1 (the prediction), section
+ * 3.1 and glossary (the shuffled reduce, router, top-K and count); [FOE]
+ * router scores g[i]. Each workgroup predicts every token's cluster and
+ * counts them itself, so it knows where its own rows go without a separate
+ * sort. Every output is the bytes the two calls write: dest,
+ * cluster_offsets, row_of_src, src_of_row and row_cluster as
+ * route_predict_sort, out, logits, idx, weights and *local as
+ * srs_route_sorted on that order.
+ *   tok .. conf_thr: as route_predict_sort; partials .. local: as
+ *   srs_route_sorted (row_cluster nullable).
+ * Errors: as the two calls, plus UNSUPPORTED beyond n = 4096 tokens, G = 16
+ * clusters or the lane-per-expert route kernel's shapes (E <= 64, the
+ * padded router rows <= 64 KiB, P in {1, 2, 4}); use the two calls there.
+ * Device bits: TOKEN_RANGE, DEST_RANGE as route_predict_sort.
+ */
+int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut, const uint8_t* conf,
+                      int32_t vocab, const uint8_t* prev2, const uint8_t* prev1,
+                      const uint8_t* ngram, int32_t G, int32_t conf_thr,
+                      const uint16_t* partials, int32_t P, int32_t d, const uint16_t* w,
+                      int32_t E, int32_t K, int32_t renorm, uint8_t* dest,
+                      int32_t* cluster_offsets, int32_t* row_of_src, int32_t* src_of_row,
+                      uint8_t* row_cluster, uint16_t* out, float* logits, int32_t* idx,
+                      float* weights, const uint8_t* expert_cluster, unsigned long long* local,
+                      uint32_t* err, hipStream_t s);
+
+/*
  * route_gate - router logits = x . w^T.
  * [FOE] per-layer comparison (router scores g[i]); [SPEC] item 2.A (the
  * next layer's gate applied to q_l). bf16 operands, binary32 accumulation

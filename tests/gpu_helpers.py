@@ -90,3 +90,17 @@ def assert_bf16(got_bits, ref, what, floor=1e-3, max_floor_frac=1e-3):
 
 def sync():
     torch.cuda.synchronize()
+
+
+def assert_dot_bound(got, ref, absref, d, what):
+    """Binary32 dot products of d exact bf16 products against the float64
+    ones: |got - ref| <= d * 2^-24 * sum_k |x_k w_k| (absref), the forward
+    error bound of binary32 summation in any order (gamma_d with the d u
+    first-order term; d u << 1 here). Unlike a relative error, this holds
+    where the products cancel."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = d * 2.0 ** -24 * np.asarray(absref, dtype=np.float64) * 1.001
+    over = np.abs(got - ref) > bound
+    assert not np.any(over), (f"{what}: {int(np.count_nonzero(over))} elements beyond the binary32 "
+                              f"summation bound")

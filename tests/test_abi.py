@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 42, names
+    assert len(names) == 43, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -190,6 +190,33 @@ def test_predict_sort_and_route_sorted_errors(L):
     assert call(args(ec=A)) == NULL            # the count needs both
     assert call(args(out=MIS)) == ALIGN
     assert call(args(n=0, ros=None)) == OK
+
+
+def test_predict_route_errors(L):
+    f = L.srs_predict_route
+    args = lambda **k: dict(dict(tok=A, n=1000, lut=A, conf=None, vocab=5000, p2=None, p1=None,
+                                 ng=None, G=4, thr=128, partials=A, P=2, d=512, w=A, E=8, K=2,
+                                 renorm=1, dest=A, offs=A, ros=A, sor=A, rc=None, out=A,
+                                 logits=None, idx=A, weights=None, ec=None, local=None, err=None,
+                                 s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(vocab=0)) == SHAPE
+    assert call(args(G=0)) == SHAPE
+    assert call(args(K=9)) == SHAPE
+    assert call(args(d=12)) == SHAPE
+    assert call(args(n=4097)) == UNSUP         # one row per wave of at most 256 workgroups
+    assert call(args(G=17)) == UNSUP
+    assert call(args(E=65)) == UNSUP            # the lane-per-expert kernel only
+    assert call(args(P=3)) == UNSUP
+    assert call(args(offs=None)) == NULL
+    assert call(args(tok=None)) == NULL
+    assert call(args(dest=None)) == NULL
+    assert call(args(ros=None)) == NULL
+    assert call(args(sor=None)) == NULL
+    assert call(args(conf=A)) == NULL           # the fallback needs prev2, prev1, ngram
+    assert call(args(idx=None)) == NULL
+    assert call(args(ec=A)) == NULL             # the count needs both
+    assert call(args(partials=MIS)) == ALIGN
 
 
 def test_permute_and_combine_errors(L):

@@ -13,7 +13,7 @@ import torch
 import oracle
 import token_routing_speculation_amd as tr
 from synth import to_bf16_bits
-from tests.gpu_helpers import dev, host, assert_rel, sync
+from tests.gpu_helpers import dev, host, assert_rel, assert_dot_bound, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,9 @@ def _check(parts, dest, G, w, K, ec, renorm, got, local):
     ref = oracle.route_gate(want["out"], w)
     lgh = host(lg)
     assert_rel(lgh, ref, LOGIT_TOL, "fused logits")
-    assert_rel(lgh, ref, F32_TOL, "fused logits (binary32 level)")
+    # the binary32 level: the summation bound over |x| |w| (sign bits cleared)
+    absref = oracle.route_gate(want["out"] & 0x7FFF, w & 0x7FFF)
+    assert_dot_bound(lgh, ref, absref, w.shape[1], "fused logits (binary32 level)")
     widx, ww = oracle.route_topk(lgh, K, 1, renorm)
     assert np.array_equal(host(idx), widx)
     np.testing.assert_allclose(host(wt), ww, rtol=1e-5, atol=1e-7)
@@ -292,3 +294,97 @@ def test_predict_sort_then_route_against_oracle(n, d, G, E, K, fallback):
     assert np.array_equal(host(dest), want_dest)
     _check(parts, want_dest.astype(np.uint8), G, w, K, ec, 1,
            (out, offs, ros, sor, rc, lg, idx, wt), local)
+
+
+def _predict_route_inputs(n, G, V, seed, fallback):
+    rng = np.random.default_rng(seed)
+    a = dict(tok=rng.integers(0, V, n).astype(np.int32), lut=rng.integers(0, G, V).astype(np.uint8))
+    if fallback:
+        a.update(conf=rng.integers(0, 256, V).astype(np.uint8),
+                 prev2=rng.integers(0, G, n).astype(np.uint8),
+                 prev1=rng.integers(0, G, n).astype(np.uint8),
+                 ngram=rng.integers(0, G, (G, G)).astype(np.uint8))
+    return a
+
+
+def _two_calls(a, G, parts, w, K, ec, renorm=1):
+    fb = {k: dev(a[k]) for k in ("conf", "prev2", "prev1", "ngram") if k in a}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dest, offs, ros, sor, rc = tr.route_predict_sort(dev(a["tok"]), dev(a["lut"]), G, err=err, **fb)
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lg, idx, wt = tr.srs_route_sorted(dev(parts), ros, dev(w), K, renorm, dest=dest,
+                                           expert_cluster=None if ec is None else dev(ec),
+                                           local=None if ec is None else local)
+    return (dest, offs, ros, sor, rc, out, lg, idx, wt), local, err
+
+
+def _one_call(a, G, parts, w, K, ec, renorm=1):
+    fb = {k: dev(a[k]) for k in ("conf", "prev2", "prev1", "ngram") if k in a}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    r = tr.srs_predict_route(dev(a["tok"]), dev(a["lut"]), G, dev(parts), dev(w), K, renorm,
+                             expert_cluster=None if ec is None else dev(ec),
+                             local=None if ec is None else local, err=err, **fb)
+    return r, local, err
+
+
+# (n, d, P, G, E, K, fallback): one row; a partial workgroup; exactly one and
+# one-and-a-bit workgroups; the Mixtral-8x7B shape (4096 rows, the limit);
+# 9..16 clusters (two registers of lane counters); one cluster; every P; E
+# from 1 to 64; the 2-gram fallback
+PRED_CASES = [(1, 128, 2, 2, 4, 2, False), (15, 256, 1, 3, 3, 1, True), (16, 512, 2, 4, 8, 2, False),
+              (17, 520, 4, 4, 16, 4, True), (1000, 1024, 2, 9, 32, 8, True),
+              (4096, 4096, 2, 4, 8, 2, False), (3000, 256, 2, 16, 64, 6, True),
+              (777, 384, 4, 1, 12, 3, False), (2049, 128, 1, 8, 1, 1, True)]
+
+
+@pytest.mark.parametrize("n,d,P,G,E,K,fallback", PRED_CASES)
+def test_predict_route_against_oracle_and_two_calls(n, d, P, G, E, K, fallback):
+    """srs_predict_route writes the bytes of route_predict_sort followed by
+    srs_route_sorted (every output, the count and the error word), and those
+    are the oracle's prediction, shuffle, gate, top-K and count."""
+    a = _predict_route_inputs(n, G, 3000, n + G + E, fallback)
+    parts, _, w, ec = _inputs(n, d, P, G, E)
+    got, local, err = _one_call(a, G, parts, w, K, ec)
+    want, local2, err2 = _two_calls(a, G, parts, w, K, ec)
+    sync()
+    for x, y in zip(got, want):
+        assert torch.equal(x, y)
+    assert int(local.item()) == int(local2.item())
+    assert int(err.item()) == int(err2.item()) == 0
+    want_dest = oracle.route_predict(a["tok"], a["lut"], a.get("conf"), a.get("prev2"),
+                                     a.get("prev1"), a.get("ngram"), 128, G=G)
+    assert np.array_equal(host(got[0]), want_dest)
+    dest, offs, ros, sor, rc, out, lg, idx, wt = got
+    _check(parts, want_dest.astype(np.uint8), G, w, K, ec, 1,
+           (out, offs, ros, sor, rc, lg, idx, wt), local)
+
+
+@pytest.mark.parametrize("fallback", [False, True])
+def test_predict_route_flags_like_two_calls(fallback):
+    """Tokens outside the vocabulary, table entries past G and (with the
+    fallback) previous clusters past G: the same error bits, maps, rows,
+    picks and count as the two calls; renorm = 0 and no count."""
+    n, d, P, G, E, K, V = 2500, 512, 2, 4, 16, 4, 3000
+    a = _predict_route_inputs(n, G, V, 7, fallback)
+    a["tok"][::97] = V + 5
+    a["tok"][::131] = -3
+    a["lut"][a["tok"][5]] = G + 2
+    if fallback:
+        a["prev2"][7::211] = G
+        a["conf"][:] = np.where(np.arange(V) % 3 == 0, 0, 255).astype(np.uint8)
+    parts, _, w, _ = _inputs(n, d, P, G, E)
+    got, _, err = _one_call(a, G, parts, w, K, None, renorm=0)
+    want, _, err2 = _two_calls(a, G, parts, w, K, None, renorm=0)
+    sync()
+    e = int(err.item())
+    assert e == int(err2.item())
+    assert e & tr.EBIT_TOKEN_RANGE and e & tr.EBIT_DEST_RANGE
+    dest, offs, ros, sor, rc, out, lg, idx, wt = got
+    dest2, offs2, ros2, sor2, rc2, out2, lg2, idx2, wt2 = want
+    assert torch.equal(dest, dest2) and torch.equal(offs, offs2) and torch.equal(ros, ros2)
+    valid = int(host(offs2)[-1])
+    assert valid < n
+    assert torch.equal(sor[:valid], sor2[:valid]) and torch.equal(rc[:valid], rc2[:valid])
+    for x, y in ((out, out2), (lg, lg2), (idx, idx2), (wt, wt2)):
+        assert torch.equal(x[:valid], y[:valid])

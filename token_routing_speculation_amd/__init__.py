@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "RouteError", "lib", "library_path",
     "route_predict", "route_predict_sort", "route_predict_sort_workspace_size", "route_lut_build",
-    "srs_shuffle", "srs_route_sorted", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
+    "srs_shuffle", "srs_route_sorted", "srs_predict_route", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "moe_combine_gather", "route_qhidden",
     "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
@@ -62,6 +62,9 @@ EXPORTS = {
                                          _p]),
     "srs_route_sorted": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _p, _p, _i32, _p, _i32, _i32,
                                         _p, _p, _p, _p, _p]),
+    "srs_predict_route": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _i32,
+                                         _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                         _p, _p, _p, _p, _p, _p]),
     "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
     "route_gate": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _p]),
     "route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p]),
@@ -342,6 +345,46 @@ def srs_route_sorted(partials, row_of_src, w, K, renorm=1, dest=None, expert_clu
           _opt(expert_cluster, torch.uint8, "expert_cluster", E), _opt(local, torch.int64, "local", 1),
           _stream(stream))
     return out, logits, idx, weights
+
+
+def srs_predict_route(tok, lut, G, partials, w, K, renorm=1, conf=None, prev2=None, prev1=None,
+                      ngram=None, conf_thr=128, expert_cluster=None, local=None, dest=None,
+                      offsets=None, row_of_src=None, src_of_row=None, row_cluster=None, out=None,
+                      logits=None, idx=None, weights=None, with_logits=True, err=None,
+                      stream=None):
+    """route_predict_sort + srs_route_sorted in one launch (small batches):
+    returns (dest, offsets, row_of_src, src_of_row, row_cluster, out, logits,
+    idx, weights)."""
+    P, n, d = partials.shape
+    E = w.shape[0]
+    bt = _bf16(partials)
+    e = lambda shape, dt: _empty(shape, dt, partials)
+    dest = e((n,), torch.uint8) if dest is None else dest
+    offsets = e((G + 1,), torch.int32) if offsets is None else offsets
+    row_of_src = e((n,), torch.int32) if row_of_src is None else row_of_src
+    src_of_row = e((n,), torch.int32) if src_of_row is None else src_of_row
+    row_cluster = e((n,), torch.uint8) if row_cluster is None else row_cluster
+    out = e((n, d), bt) if out is None else out
+    if with_logits and logits is None:
+        logits = e((n, E), torch.float32)
+    idx = e((n, K), torch.int32) if idx is None else idx
+    weights = e((n, K), torch.float32) if weights is None else weights
+    fb = conf is not None
+    _call("srs_predict_route", _dev(tok, torch.int32, "tok", n), n, _dev(lut, torch.uint8, "lut"),
+          _opt(conf, torch.uint8, "conf"), lut.numel(),
+          _opt(prev2, torch.uint8, "prev2", n if fb else None),
+          _opt(prev1, torch.uint8, "prev1", n if fb else None),
+          _opt(ngram, torch.uint8, "ngram", G * G if fb else None), G, conf_thr,
+          _dev(partials, bt, "partials"), P, d, _dev(w, _bf16(w), "w", E * d), E, K, renorm,
+          _dev(dest, torch.uint8, "dest", n), _dev(offsets, torch.int32, "offsets", G + 1),
+          _dev(row_of_src, torch.int32, "row_of_src", n),
+          _dev(src_of_row, torch.int32, "src_of_row", n),
+          _opt(row_cluster, torch.uint8, "row_cluster", n), _dev(out, bt, "out", n * d),
+          _opt(logits, torch.float32, "logits", n * E), _dev(idx, torch.int32, "idx", n * K),
+          _opt(weights, torch.float32, "weights", n * K),
+          _opt(expert_cluster, torch.uint8, "expert_cluster", E),
+          _opt(local, torch.int64, "local", 1), _opt(err, torch.int32, "err", 1), _stream(stream))
+    return dest, offsets, row_of_src, src_of_row, row_cluster, out, logits, idx, weights
 
 
 def route_gate(x, w, logits=None, stream=None):

@@ -55,23 +55,24 @@ struct PredictLoads {
   int t, p2, p1, c, cf, g;
 };
 
+// (Without the fallback the previous clusters, the confidence byte and the
+// 2-gram entry are read from the token table's first byte instead, so that
+// no load sits under a branch; stage 3 does not use them then.)
 __device__ __forceinline__ PredictLoads predict_stage1(const PredictArgs& a, int64_t i) {
+  const bool fb = a.conf != nullptr;
   PredictLoads s{};
   s.t = a.tok[i];
-  if (a.conf) {
-    s.p2 = a.prev2[i];
-    s.p1 = a.prev1[i];
-  }
+  s.p2 = (fb ? a.prev2 : a.lut)[fb ? i : 0];
+  s.p1 = (fb ? a.prev1 : a.lut)[fb ? i : 0];
   return s;
 }
 
 __device__ __forceinline__ void predict_stage2(const PredictArgs& a, PredictLoads& s) {
+  const bool fb = a.conf != nullptr;
   const int tc = (s.t >= 0 && s.t < a.vocab) ? s.t : 0;
   s.c = a.lut[tc];
-  if (a.conf) {
-    s.cf = a.conf[tc];
-    s.g = a.ngram[(s.p2 < a.G && s.p1 < a.G) ? s.p2 * a.G + s.p1 : 0];
-  }
+  s.cf = (fb ? a.conf : a.lut)[fb ? tc : 0];
+  s.g = (fb ? a.ngram : a.lut)[fb && s.p2 < a.G && s.p1 < a.G ? s.p2 * a.G + s.p1 : 0];
 }
 
 __device__ __forceinline__ int predict_stage3(const PredictArgs& a, const PredictLoads& s,

@@ -21,6 +21,7 @@
 #include "common.hpp"
 #include "csort.hpp"
 #include "mfma.hpp"
+#include "predict.hpp"
 #include "srs.hpp"
 #include "topk.hpp"
 
@@ -78,11 +79,45 @@ struct RouteOut {
   unsigned long long* local;
 };
 
-template <int PT, int CPL, int EB>
+// srs_predict_route: the route prediction ("Speculative MoE" notes, section
+// 4.1) and the stable shuffle's order made inside the route kernel. Every
+// workgroup predicts the cluster of every token outside its own sixteen and
+// counts them by cluster (those before its rows, and all), predicts its own
+// rows' clusters and ranks them, and so knows each of its rows' sorted
+// position without a separate sort: the sort's results are written as
+// route_predict_sort writes them. At most kPredRouteMax tokens (one row per
+// wave, a wave's share of the others one batch of lane counters) and
+// kPredRouteMaxG clusters (two registers of packed counters).
+constexpr int64_t kPredRouteMax = kRouteMaxGrid * kRouteWaves;
+constexpr int kPredRouteMaxG = 16;
+constexpr int kPredOthers = 4;  // other tokens per lane: (4096 - 16) / 16 waves / 64 lanes
+static_assert((kPredRouteMax - kRouteWaves + kRouteWaves - 1) / kRouteWaves <= kPredOthers * kWave,
+              "one batch of others per wave");
+
+struct PredSort {
+  PredictArgs a;          // the prediction's inputs and the error word
+  uint8_t* dest;          // [n] predicted clusters (out)
+  int* offsets;           // [G + 1]
+  int* row_of_src;        // [n]
+  int* src_of_row;        // [n]
+  uint8_t* row_cluster;   // [n]
+};
+
+// A key source that never runs (the others' one batch is filled by hand).
+struct NoKeys {
+  template <int NB>
+  __device__ __forceinline__ void batch(const int64_t (&)[NB], const bool (&)[NB],
+                                        uint32_t (&k)[NB]) const {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) k[q] = 0xffffffffu;
+  }
+};
+
+template <int PT, int CPL, int EB, bool PRED>
 __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
     const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
     const uint8_t* __restrict__ dest, uint16_t* __restrict__ out, const uint16_t* __restrict__ w,
-    int E, int K, int renorm, RouteOut ro, SrsIdentity ident) {
+    int E, int K, int renorm, RouteOut ro, SrsIdentity ident, PredSort ps) {
   static_assert(EB * CPL <= 64, "staged router rows fit in 64 KiB");
   extern __shared__ __align__(16) char wl[];
   const int wv = wave_id();
@@ -98,6 +133,29 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   constexpr int kRowV = CPL * kWave;  // vectors per staged router row
   constexpr int kPieces = EB * kRowV;
   constexpr int kStage = (kPieces + kRouteThreads - 1) / kRouteThreads;
+
+  // With the prediction: the first loads of every token this wave predicts
+  // (its own row's, and its share of the tokens outside the workgroup's
+  // sixteen), then the router staging, then the tables' entries; the rows
+  // go out after those, so waiting for the predictions never waits for them.
+  const int64_t clo = static_cast<int64_t>(blockIdx.x) * kRouteWaves;
+  const int64_t chi = clo + kRouteWaves < n ? clo + kRouteWaves : n;
+  const int64_t i_own = clo + wv;
+  int64_t olo = 0, ohi = 0;
+  PredictLoads so[kPredOthers], sm{};
+  bool oin[kPredOthers];
+  PredictArgs quiet = ps.a;
+  quiet.err = nullptr;
+  if constexpr (PRED) {
+    others_share<kRouteWaves>(n, clo, chi, wv, &olo, &ohi);
+#pragma unroll
+    for (int q = 0; q < kPredOthers; ++q) {
+      const int64_t jp = olo + q * kWave + lane;
+      oin[q] = jp < ohi;
+      so[q] = predict_stage1(quiet, oin[q] ? (jp < clo ? jp : jp + (chi - clo)) : 0);
+    }
+    sm = predict_stage1(ps.a, i_own < n ? i_own : 0);
+  }
   u32x4 wst[kStage];
 #pragma unroll
   for (int r = 0; r < kStage; ++r) {
@@ -136,12 +194,80 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   // byte), so the waits for the staging loads count the same on every path.
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kRouteWaves;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteWaves + wv;
-  int cl = dest ? static_cast<int>(dest[i < n ? i : n - 1]) : 0;
+  int cl = 0;
+  if constexpr (PRED) {
+#pragma unroll
+    for (int q = 0; q < kPredOthers; ++q) predict_stage2(quiet, so[q]);
+    predict_stage2(ps.a, sm);
+  } else {
+    cl = dest ? static_cast<int>(dest[i < n ? i : n - 1]) : 0;
+  }
   load_row(i, i < n);
 #pragma unroll
   for (int r = 0; r < kStage; ++r) {
     const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
     if (q < kPieces) *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = wst[r];
+  }
+  int pdst = -1;  // with the prediction: this wave's row's sorted position
+  if constexpr (PRED) {
+    __shared__ int orow[kRouteWaves * kPredRouteMaxG];  // others before the rows, per wave
+    __shared__ int prow[kRouteWaves * kPredRouteMaxG];  // and after them
+    __shared__ int ckey[kRouteWaves];                   // the rows' clusters
+    __shared__ int stot[kPredRouteMaxG];
+    __shared__ int sbase[kPredRouteMaxG];
+    __shared__ int stotal;
+    const int G = ps.a.G;
+    uint32_t ok[kPredOthers];
+#pragma unroll
+    for (int q = 0; q < kPredOthers; ++q) {
+      uint32_t e = 0;
+      const int c = predict_stage3(quiet, so[q], &e);
+      ok[q] = oin[q] ? static_cast<uint32_t>(c) : 0xffffffffu;
+    }
+    const NoKeys none;
+    if (G <= 8)
+      others_count<1>(none, olo, ohi, clo, chi, G, ok, orow + wv * G, prow + wv * G);
+    else
+      others_count<2>(none, olo, ohi, clo, chi, G, ok, orow + wv * G, prow + wv * G);
+    uint32_t e_own = 0;
+    const int c_own = __builtin_amdgcn_readfirstlane(predict_stage3(ps.a, sm, &e_own));
+    if (lane == 0) ckey[wv] = i_own < n ? c_own : -1;
+    lds_barrier();
+    for (int b = threadIdx.x; b < G; b += kRouteThreads) {
+      int pre = 0, rest = 0;
+#pragma unroll
+      for (int v = 0; v < kRouteWaves; ++v) {
+        pre += orow[v * G + b];
+        rest += prow[v * G + b] + (ckey[v] == b ? 1 : 0);
+      }
+      sbase[b] = pre;
+      stot[b] = pre + rest;
+    }
+    lds_barrier();
+    if (wv == 0) scan_bins(stot, G, &stotal);
+    lds_barrier();
+    if (blockIdx.x == 0) {
+      for (int b = threadIdx.x; b < G; b += kRouteThreads) ps.offsets[b] = stot[b];
+      if (threadIdx.x == 0) ps.offsets[G] = stotal;
+    }
+    if (i_own < n) {
+      // rank among the workgroup's rows of the same cluster before this one
+      int rank = 0;
+      for (int v = 0; v < wv; ++v) rank += ckey[v] == c_own ? 1 : 0;
+      const bool valid = c_own < G;  // a table entry past G: no position, flagged
+      pdst = valid ? stot[c_own] + sbase[c_own] + rank : -1;
+      if (lane == 0) {
+        const uint32_t e = e_own | (valid ? 0u : static_cast<uint32_t>(ROUTE_EBIT_DEST_RANGE));
+        if (e) set_err(ps.a.err, e);
+        ps.dest[i_own] = static_cast<uint8_t>(c_own);
+        ps.row_of_src[i_own] = pdst;
+        if (valid) {
+          ps.src_of_row[pdst] = static_cast<int>(i_own);
+          if (ps.row_cluster) ps.row_cluster[pdst] = static_cast<uint8_t>(c_own);
+        }
+      }
+    }
+    cl = c_own;
   }
   lds_barrier();
 
@@ -150,7 +276,11 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   unsigned lar = 0;
 
   for (; i < n; i += stride) {
-    const int dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
+    int dst;
+    if constexpr (PRED)
+      dst = pdst;  // one row per wave
+    else
+      dst = row_of_src ? row_of_src[i] : static_cast<int>(i);
     const bool keep = dst >= 0 && dst < n;  // key out of range (flagged by the sort): no outputs
     // The row's store through a descriptor spanning the destination row
     // (vectors past its end are dropped; for a row without a destination the
@@ -241,7 +371,7 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
       if (ro.expert_cluster) lar += __popcll(__ballot(pick && my_ec == cl));
     }
     if (lane == 0) write_identity_row(ident, i, n);
-    if (i + stride < n) {
+    if (!PRED && i + stride < n) {
       cl = dest ? static_cast<int>(dest[i + stride]) : 0;
       load_row(i + stride, true);
     }
@@ -273,12 +403,17 @@ int route_eb(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
 template <int PT, int CPL, int EB>
 bool launch_one(unsigned grid, size_t lds, hipStream_t s, const uint16_t* partials, int64_t n,
                 int d, const int* fwd, const uint8_t* dest, uint16_t* out, const uint16_t* w,
-                int E, int K, int renorm, const RouteOut& ro, const SrsIdentity& ident) {
+                int E, int K, int renorm, const RouteOut& ro, const SrsIdentity& ident,
+                const PredSort* ps) {
   if constexpr (EB * CPL > 64 || (PT == 4 && CPL == 8)) {
     return false;  // beyond the staged rows' 64 KiB, or the registers
   } else {
-    srs_route_kernel<PT, CPL, EB><<<grid, kRouteThreads, lds, s>>>(partials, n, d, fwd, dest, out,
-                                                                   w, E, K, renorm, ro, ident);
+    if (ps)
+      srs_route_kernel<PT, CPL, EB, true><<<grid, kRouteThreads, lds, s>>>(
+          partials, n, d, fwd, dest, out, w, E, K, renorm, ro, ident, *ps);
+    else
+      srs_route_kernel<PT, CPL, EB, false><<<grid, kRouteThreads, lds, s>>>(
+          partials, n, d, fwd, dest, out, w, E, K, renorm, ro, ident, PredSort{});
     return true;
   }
 }
@@ -287,12 +422,12 @@ template <int PT, int CPL>
 bool launch_cpl(int eb, unsigned grid, size_t lds, hipStream_t s, const uint16_t* partials,
                 int64_t n, int d, const int* fwd, const uint8_t* dest, uint16_t* out,
                 const uint16_t* w, int E, int K, int renorm, const RouteOut& ro,
-                const SrsIdentity& ident) {
+                const SrsIdentity& ident, const PredSort* ps) {
   switch (eb) {
 #define ROUTE_EB(b)                                                                            \
   case b:                                                                                      \
     return launch_one<PT, CPL, b>(grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,       \
-                                  renorm, ro, ident);
+                                  renorm, ro, ident, ps);
     ROUTE_EB(8) ROUTE_EB(16) ROUTE_EB(32) ROUTE_EB(64)
 #undef ROUTE_EB
     default: return false;
@@ -303,12 +438,12 @@ template <int PT>
 bool launch_route(int cpl, int eb, unsigned grid, size_t lds, hipStream_t s,
                   const uint16_t* partials, int64_t n, int d, const int* fwd, const uint8_t* dest,
                   uint16_t* out, const uint16_t* w, int E, int K, int renorm, const RouteOut& ro,
-                  const SrsIdentity& ident) {
+                  const SrsIdentity& ident, const PredSort* ps) {
   switch (cpl) {
 #define ROUTE_CPL(c)                                                                           \
   case c:                                                                                      \
     return launch_cpl<PT, c>(eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K, renorm, \
-                             ro, ident);
+                             ro, ident, ps);
     ROUTE_CPL(1) ROUTE_CPL(2) ROUTE_CPL(4) ROUTE_CPL(8)
 #undef ROUTE_CPL
     default: return false;
@@ -345,8 +480,10 @@ static int route_rows(const uint16_t* partials, int P, int64_t n, int d, const i
                       const uint8_t* dest, uint16_t* out, const uint16_t* w, int E,
                       float* logits, int K, int renorm, int* idx, float* weights,
                       const uint8_t* expert_cluster, unsigned long long* local,
-                      const SrsIdentity& ident, hipStream_t s) {
+                      const SrsIdentity& ident, hipStream_t s,
+                      const PredSort* ps = nullptr) {
   if (!route_fits(P, d, E)) {
+    if (ps) return ROUTE_ERR_UNSUPPORTED;
     const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local};
     return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
   }
@@ -361,13 +498,13 @@ static int route_rows(const uint16_t* partials, int P, int64_t n, int d, const i
   bool done = false;
   if (P == 1)
     done = launch_route<1>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
+                           renorm != 0, ro, ident, ps);
   if (P == 2)
     done = launch_route<2>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
+                           renorm != 0, ro, ident, ps);
   if (P == 4)
     done = launch_route<4>(cpl, eb, grid, lds, s, partials, n, d, fwd, dest, out, w, E, K,
-                           renorm != 0, ro, ident);
+                           renorm != 0, ro, ident, ps);
   if (!done) return ROUTE_ERR_UNSUPPORTED;
   return launch_status();
 }
@@ -438,4 +575,36 @@ ROUTE_API int srs_route_sorted(const uint16_t* partials, int32_t P, int64_t n, i
   const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
   return route_rows(partials, P, n, d, row_of_src, dest, out, w, E, logits, K, renorm, idx,
                     weights, expert_cluster, local, none, s);
+}
+
+ROUTE_API int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut,
+                                const uint8_t* conf, int32_t vocab, const uint8_t* prev2,
+                                const uint8_t* prev1, const uint8_t* ngram, int32_t G,
+                                int32_t conf_thr, const uint16_t* partials, int32_t P, int32_t d,
+                                const uint16_t* w, int32_t E, int32_t K, int32_t renorm,
+                                uint8_t* dest, int32_t* cluster_offsets, int32_t* row_of_src,
+                                int32_t* src_of_row, uint8_t* row_cluster, uint16_t* out,
+                                float* logits, int32_t* idx, float* weights,
+                                const uint8_t* expert_cluster, unsigned long long* local,
+                                uint32_t* err, hipStream_t s) {
+  if (vocab < 1 || G < 1) return ROUTE_ERR_SHAPE;
+  const int chk = route_shape(P, n, d, E, K);
+  if (chk != ROUTE_OK) return chk;
+  if (n > kPredRouteMax || G > kPredRouteMaxG || !route_fits(P, d, E))
+    return ROUTE_ERR_UNSUPPORTED;
+  if (!cluster_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
+    return launch_status();
+  }
+  if (!tok || !lut || !dest || !row_of_src || !src_of_row) return ROUTE_ERR_NULL;
+  if (conf && (!prev2 || !prev1 || !ngram)) return ROUTE_ERR_NULL;
+  if (!partials || !out || !w || !idx) return ROUTE_ERR_NULL;
+  if ((expert_cluster == nullptr) != (local == nullptr)) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(out) || !aligned16(w)) return ROUTE_ERR_ALIGN;
+  const PredSort ps{PredictArgs{tok, lut, conf, vocab, prev2, prev1, ngram, G, conf_thr, err},
+                    dest, cluster_offsets, row_of_src, src_of_row, row_cluster};
+  const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
+  return route_rows(partials, P, n, d, nullptr, dest, out, w, E, logits, K, renorm, idx, weights,
+                    expert_cluster, local, none, s, &ps);
 }

@@ -5,7 +5,8 @@
 s-MoE layer of the "Speculative MoE" notes (section 3.1 and Figure 3's online
 path) on one GPU. Where the shapes allow, prediction is folded into the
 cluster sort (``predict_sort``) and the SRS, gate, top-K and LAR stages are
-one kernel after it (``srs_route``).
+one kernel after it (``srs_route``); for small batches all of these are one
+kernel (``predict_route``).
 
 ``FoEPass``: cross-group reduce of the H group activations -> gate ->
 grouped top-k/H -> LAR -> permute from the group activations -> combine
@@ -34,7 +35,7 @@ import numpy as np
 import torch
 
 from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
-               srs_shuffle_route, srs_route_sorted,
+               srs_shuffle_route, srs_route_sorted, srs_predict_route,
                route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
@@ -66,6 +67,12 @@ def srs_route_takes(P: int, d: int, E: int, K: int) -> bool:
         return False
     return srs_route_fits(P, d, E, K) or (P in (1, 2, 4) and d >= 128 and d % 128 == 0
                                           and 1 <= E <= 160)
+
+
+def predict_route_takes(n: int, P: int, d: int, E: int, K: int, G: int) -> bool:
+    """The shapes srs_predict_route takes: at most 4096 tokens and 16
+    clusters, on the small-set route kernel (srs_route_fits)."""
+    return 0 < n <= 4096 and 1 <= G <= 16 and srs_route_fits(P, d, E, K)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -160,6 +167,10 @@ class RoutePass:
         self.routed = srs_route_takes(P, d, E, K)
         if self.routed:
             self.STAGES = ("predict_sort", "srs_route", "permute", "combine")
+        # small batches: the prediction and the shuffle's order made inside
+        # the route kernel (srs_predict_route), one launch for both
+        if predict_route_takes(N, P, d, E, K, G):
+            self.STAGES = ("predict_route", "permute", "combine")
 
     def predict(self):
         if self.fallback:
@@ -188,6 +199,16 @@ class RoutePass:
         srs_route_sorted(self.partials, self.row_of_src, self.w, self.K, 1, dest=self.dest,
                          expert_cluster=self.expert_cluster, local=self.local, out=self.x,
                          logits=self.logits, idx=self.idx, weights=self.weights)
+
+    def predict_route(self):
+        fb = dict(conf=self.conf, prev2=self.prev2, prev1=self.prev1, ngram=self.ngram,
+                  conf_thr=self.conf_thr) if self.fallback else {}
+        srs_predict_route(self.tok, self.lut, self.G, self.partials, self.w, self.K, 1,
+                          expert_cluster=self.expert_cluster, local=self.local, dest=self.dest,
+                          offsets=self.cluster_offsets, row_of_src=self.row_of_src,
+                          src_of_row=self.src_of_row, row_cluster=self.row_cluster, out=self.x,
+                          logits=self.logits, idx=self.idx, weights=self.weights, err=self.err,
+                          **fb)
 
     def topk(self):
         route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
