@@ -1110,10 +1110,25 @@ def route_measure(args, name):
     total_bytes = sum(bytes_st.values())
     # the stage holding the router product
     gate_stage = next(g for g in ("gate", "srs_route", "predict_route") if g in st_us)
-    # dominant single-kernel stage: the combine (one launch per pass)
-    dom = "combine"
+    # dominant kernel: the longest stage that is one launch
+    fused_permute = cfg.E <= 16 and N * cfg.K <= 16384 and cfg.d <= 4096 and name != "foe"
+    single = {"predict_route", "srs_route", "combine", "reduce", "gate"}
+    if fused_permute:
+        single.add("permute")
+    dom = max((st for st in stages if st in single), key=lambda st: st_us[st])
     dom_bytes = bytes_st[dom]
     achieved = dom_bytes / (st_us[dom] * 1e-6)
+    small_route = cfg.E <= 64 and name != "foe"
+    kernel_of = {
+        "combine": ("combine_kernel (moe_combine)" if name == "foe"
+                    else "combine_kernel (moe_combine_gather)"),
+        "predict_route": "srs_route_kernel (srs_predict_route)",
+        "srs_route": ("srs_route_kernel (srs_route_sorted)" if small_route
+                      else "srs_gate160_kernel (srs_route_sorted)"),
+        "permute": "permute_fused (moe_permute)",
+        "reduce": "srs_move (srs_shuffle)",
+        "gate": "route_gate",
+    }
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -1138,12 +1153,11 @@ def route_measure(args, name):
         "gate_stage": gate_stage,
         "gate_mfma_frac": 2.0 * N * cfg.d * cfg.E / (st_us[gate_stage] * 1e-6) / MFMA_BF16_PEAK,
         "stage_hbm_frac": {k: round(bytes_st[k] / (st_us[k] * 1e-6) / HBM_PEAK, 4) for k in stages},
-        "roofline": {"bound": "hbm",
-                     "kernel": ("combine_kernel (moe_combine)" if name == "foe"
-                                else "combine_kernel (moe_combine_gather)"),
+        "roofline": {"bound": "hbm", "kernel": kernel_of[dom],
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK,
-                     "traffic": measured_traffic(conf["workload"])},
+                     # the committed counter record is the combine's
+                     "traffic": measured_traffic(conf["workload"]) if dom == "combine" else None},
         "lar": lar_rate(p, N * cfg.K),
         "wall_s_timed": wall,
     }
