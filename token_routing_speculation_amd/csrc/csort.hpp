@@ -277,6 +277,19 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
   const int c = blockIdx.x;
   for (int i = t; i < NW * B; i += THREADS) wrow[i] = 0;
 
+  // this wave's share of the chunk; its keys are read kBatch tiles (of 64)
+  // at a time, and the first batch goes out now, beside the table's loads
+  // below (the first batch stays in registers for pass 2)
+  const int64_t clo = static_cast<int64_t>(c) * chunk;
+  const int64_t chi = clo + chunk < n ? clo + chunk : n;
+  const int64_t share = chunk / NW;
+  const int64_t qlo = clo + w * share;
+  const int64_t qhi = qlo + share < chi ? qlo + share : chi;
+  int* myrow = wrow + w * B;
+  const ArrayKeys<KeyT> src{keys};
+  uint32_t first[kBatch];
+  load_batch(src, first, qlo, qhi);
+
   const int R = THREADS / B < nchunks ? (THREADS / B > 0 ? THREADS / B : 1) : nchunks;
   for (int i = t; i < R * B; i += THREADS) {  // one pass when B <= THREADS
     const int r = i / B, b = i - r * B;
@@ -309,19 +322,6 @@ __global__ __launch_bounds__(THREADS) void csort_rank(const KeyT* __restrict__ k
   }
   if (c == 0 && t == 0) offsets[B] = stotal;
 
-  // this wave's share of the chunk
-  const int64_t clo = static_cast<int64_t>(c) * chunk;
-  const int64_t chi = clo + chunk < n ? clo + chunk : n;
-  const int64_t share = chunk / NW;
-  const int64_t qlo = clo + w * share;
-  const int64_t qhi = qlo + share < chi ? qlo + share : chi;
-  int* myrow = wrow + w * B;
-
-  // keys are read kBatch tiles (of 64) at a time, all loads issued before
-  // any tile is processed; the first batch stays in registers for pass 2
-  const ArrayKeys<KeyT> src{keys};
-  uint32_t first[kBatch];
-  load_batch(src, first, qlo, qhi);
   count_share(src, qlo, qhi, B, nbits, first, myrow);  // csort_hist flagged bad keys
   __syncthreads();
   // counts -> per-wave starting positions
