@@ -63,12 +63,12 @@ def route_bytes(N, d, E, K, P, G, fallback, routed=False, stages=None):
 
 
 def foe_bytes(N, d, E, K, H):
+    """The FoE pass: the group activations reduced, routed, top-K'd and
+    counted in one kernel (the reduced rows are neither written nor read:
+    only the router uses them), then the dispatch and the combine."""
     b = 2
     return {
-        "reduce": H * N * d * b + N * d * b + 8,
-        "gate": N * d * b + E * d * b + 4 * N * E,
-        "topk": 4 * N * E + 8 * N * K,
-        "lar": 4 * N * K + N * H + E,
+        "route": H * N * d * b + E * d * b + 4 * N * E + 8 * N * K + N * H + E,
         "permute": 12 * N * K + 4 * (E + 1) + H * N * d * b + N * K * d * b,
         "combine": N * K * d * b + 8 * N * K + N * d * b,
     }
@@ -1109,10 +1109,10 @@ def route_measure(args, name):
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
     # the stage holding the router product
-    gate_stage = next(g for g in ("gate", "srs_route", "predict_route") if g in st_us)
+    gate_stage = next(g for g in ("gate", "srs_route", "predict_route", "route") if g in st_us)
     # dominant kernel: the longest stage that is one launch
     fused_permute = cfg.E <= 16 and N * cfg.K <= 16384 and cfg.d <= 4096 and name != "foe"
-    single = {"predict_route", "srs_route", "combine", "reduce", "gate"}
+    single = {"predict_route", "srs_route", "combine", "route"}
     if fused_permute:
         single.add("permute")
     dom = max((st for st in stages if st in single), key=lambda st: st_us[st])
@@ -1126,8 +1126,7 @@ def route_measure(args, name):
         "srs_route": ("srs_route_kernel (srs_route_sorted)" if small_route
                       else "srs_gate160_kernel (srs_route_sorted)"),
         "permute": "permute_fused (moe_permute)",
-        "reduce": "srs_move (srs_shuffle)",
-        "gate": "route_gate",
+        "route": "srs_gate160_kernel (srs_route_grouped)",
     }
     out = {
         "metric": METRIC,

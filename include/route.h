@@ -272,6 +272,31 @@ int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut, const u
                       uint32_t* err, hipStream_t s);
 
 /*
+ * srs_route_grouped - the grouped MoE block's routing in one kernel: the
+ * cross-group reduce of the P group activations, the router, the grouped
+ * top-K and the per-group local count. [FOE] grouped MoE block (H groups of
+ * E/H experts, each picking its K/H by the router scores g[i]; the copy of
+ * token i for group h sits on cluster row_cluster[i*H + h]); the reduce is
+ * srs_shuffle's with one cluster ([SMOE] section 3.1). Every output is the
+ * bytes of srs_shuffle (G = 1) + route_gate + route_topk (H) + lar_count
+ * (H) would give, up to route_topk's weights, which are the same function
+ * of the same logits (softmax over each group's picks for renorm = 1, over
+ * all E logits from the row's largest for renorm = 0).
+ *   partials bf16 [P][n][d]; out bf16 [n][d] (nullable: the reduced rows
+ *   are not written); w bf16 [E][d]; logits float [n][E] (nullable);
+ *   idx int32 [n][K] (slots group-major, descending inside a group);
+ *   weights float [n][K] (nullable); row_cluster uint8 [n][H] and
+ *   expert_cluster uint8 [E] with *local += the count (all three nullable
+ *   together; row_cluster required with expert_cluster).
+ * Errors: NULL, SHAPE (E % H, K % H, K/H > E/H, d % 8), ALIGN, UNSUPPORTED
+ * (P not in {1, 2, 4}, d % 128, E > 160, K > 16).
+ */
+int srs_route_grouped(const uint16_t* partials, int32_t P, int64_t n, int32_t d, uint16_t* out,
+                      const uint16_t* w, int32_t E, float* logits, int32_t K, int32_t H,
+                      int32_t renorm, int32_t* idx, float* weights, const uint8_t* row_cluster,
+                      const uint8_t* expert_cluster, unsigned long long* local, hipStream_t s);
+
+/*
  * route_gate - router logits = x . w^T.
  * [FOE] per-layer comparison (router scores g[i]); [SPEC] item 2.A (the
  * next layer's gate applied to q_l). bf16 operands, binary32 accumulation

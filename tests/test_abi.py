@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 43, names
+    assert len(names) == 44, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -217,6 +217,29 @@ def test_predict_route_errors(L):
     assert call(args(idx=None)) == NULL
     assert call(args(ec=A)) == NULL             # the count needs both
     assert call(args(partials=MIS)) == ALIGN
+
+
+def test_route_grouped_errors(L):
+    f = L.srs_route_grouped
+    args = lambda **k: dict(dict(partials=A, P=4, n=1000, d=512, out=None, w=A, E=64, logits=None,
+                                 K=8, H=4, renorm=1, idx=A, weights=None, rc=None, ec=None,
+                                 local=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(n=-1)) == SHAPE
+    assert call(args(H=3)) == SHAPE             # E % H
+    assert call(args(K=6)) == SHAPE             # K % H
+    assert call(args(E=8, H=4, K=12)) == SHAPE  # K/H > E/H
+    assert call(args(d=12)) == SHAPE
+    assert call(args(P=3)) == UNSUP
+    assert call(args(d=520)) == UNSUP           # d % 128
+    assert call(args(E=168, H=4)) == UNSUP      # more than 160 columns
+    assert call(args(K=20, H=4)) == UNSUP       # K > 16
+    assert call(args(idx=None)) == NULL
+    assert call(args(partials=None)) == NULL
+    assert call(args(ec=A)) == NULL             # the count needs local
+    assert call(args(ec=A, local=A)) == NULL    # and row_cluster
+    assert call(args(out=MIS)) == ALIGN
+    assert call(args(n=0)) == OK
 
 
 def test_permute_and_combine_errors(L):

@@ -100,8 +100,9 @@ def test_foe_workload():
     p.step()
     sync()
     assert int(p.err.item()) == 0
-    rs = oracle.srs_shuffle(inp["x"], None, 1)["out"]               # cross-group sum r_full
-    assert np.array_equal(host(p.r_full), rs)
+    # the pass's router reads the cross-group sum r_full on chip (it is not
+    # written: test_gpu_srs_route checks those rows where they are written)
+    rs = oracle.srs_shuffle(inp["x"], None, 1)["out"]
     lg = host(p.logits)
     assert_rel(lg, oracle.route_gate(rs, inp["w"]), LOGIT_TOL, "gate")
     widx, ww = oracle.route_topk(lg, K, H, 1)

@@ -437,7 +437,7 @@ def test_run_twice_bitwise_foe_and_predictor():
     from token_routing_speculation_amd.pipeline import FoEPass, PredictorPass
     inp = make_foe_inputs(3000, 256, 64, 4, 8, 8, 5000, 13)
     f = FoEPass(inp)
-    keys = ("r_full", "logits", "idx", "weights", "slot_of_pair", "disp", "out")
+    keys = ("logits", "idx", "weights", "slot_of_pair", "disp", "out")
     f.step()
     first = {k: host(getattr(f, k)).copy() for k in keys}
     l1 = int(host(f.local)[0])

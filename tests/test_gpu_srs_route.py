@@ -388,3 +388,64 @@ def test_predict_route_flags_like_two_calls(fallback):
     assert torch.equal(sor[:valid], sor2[:valid]) and torch.equal(rc[:valid], rc2[:valid])
     for x, y in ((out, out2), (lg, lg2), (idx, idx2), (wt, wt2)):
         assert torch.equal(x[:valid], y[:valid])
+
+
+# (n, d, P, E, K, H, renorm, with_rows): the FoE grouping (64 experts in 4
+# groups, K = 8) on its partial count; two and eight groups; one group per
+# pick; one row; a ragged last tile; the full softmax (renorm = 0); 160
+# experts; the reduced rows written or not
+GROUPED_CASES = [(3000, 256, 4, 64, 8, 4, 1, False), (1000, 512, 2, 160, 6, 2, 1, True),
+                 (777, 384, 1, 96, 8, 8, 0, True), (65, 128, 4, 64, 4, 4, 0, False),
+                 (1, 128, 2, 16, 4, 4, 1, True), (2049, 1024, 4, 64, 8, 4, 1, True),
+                 (500, 256, 2, 32, 3, 1, 1, False)]
+
+
+@pytest.mark.parametrize("n,d,P,E,K,H,renorm,with_rows", GROUPED_CASES)
+def test_srs_route_grouped_against_oracle(n, d, P, E, K, H, renorm, with_rows):
+    """srs_route_grouped against the oracle's grouped block: the reduced rows
+    (when written) bit-exact, the logits against the oracle's gate on them,
+    the grouped picks bit-exact and their weights within 1e-5 of the oracle's
+    top-K of the kernel's logits, the count exactly lar_count's."""
+    from synth import default_expert_cluster, foe_row_cluster
+    G = 8
+    parts, _, w, _ = _inputs(n, d, P, G, E)
+    rc = foe_row_cluster(n, H, G) if H > 1 else np.random.default_rng(n).integers(0, G, n).astype(np.uint8)
+    ec = default_expert_cluster(E, G)
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda") if with_rows else None
+    _, lg, idx, wt = tr.srs_route_grouped(dev(parts), dev(w), K, H, renorm, row_cluster=dev(rc),
+                                          expert_cluster=dev(ec), local=local, out=out)
+    sync()
+    red = oracle.srs_shuffle(parts, None, 1)["out"]
+    if with_rows:
+        assert np.array_equal(host(out), red)
+    ref = oracle.route_gate(red, w)
+    lgh = host(lg)
+    assert_rel(lgh, ref, LOGIT_TOL, "grouped logits")
+    assert_dot_bound(lgh, ref, oracle.route_gate(red & 0x7FFF, w & 0x7FFF), d,
+                     "grouped logits (binary32 level)")
+    widx, ww = oracle.route_topk(lgh, K, H, renorm)
+    assert np.array_equal(host(idx), widx)
+    np.testing.assert_allclose(host(wt), ww, rtol=1e-5, atol=1e-7)
+    assert int(local.item()) == oracle.lar_count(widx, K, H, rc, ec)
+
+
+def test_srs_route_grouped_equals_separate_calls():
+    """On the FoE grouping, against route_topk (H) and lar_count run on the
+    kernel's own logits: the picks bit-exact, the weights within a few ulp
+    (the same function, another kernel's arithmetic), the count equal."""
+    from synth import default_expert_cluster, foe_row_cluster
+    n, d, P, E, K, H, G = 3000, 512, 4, 64, 8, 4, 8
+    parts, _, w, _ = _inputs(n, d, P, G, E)
+    rc = foe_row_cluster(n, H, G)
+    ec = default_expert_cluster(E, G)
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _, lg, idx, wt = tr.srs_route_grouped(dev(parts), dev(w), K, H, 1, row_cluster=dev(rc),
+                                          expert_cluster=dev(ec), local=local)
+    i2, w2 = tr.route_topk(lg, K, H, 1)
+    loc2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tr.lar_count(i2, H, dev(rc), dev(ec), loc2)
+    sync()
+    assert torch.equal(idx, i2)
+    np.testing.assert_allclose(host(wt), host(w2), rtol=1e-6, atol=1e-8)
+    assert int(local.item()) == int(loc2.item())

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "RouteError", "lib", "library_path",
     "route_predict", "route_predict_sort", "route_predict_sort_workspace_size", "route_lut_build",
-    "srs_shuffle", "srs_route_sorted", "srs_predict_route", "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
+    "srs_shuffle", "srs_route_sorted", "srs_predict_route", "srs_route_grouped",
+    "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "moe_combine_gather", "route_qhidden",
     "route_estimator",
     "hit_count", "srs_shuffle_workspace_size", "moe_permute_workspace_size",
@@ -64,6 +65,8 @@ EXPORTS = {
                                         _p, _p, _p, _p, _p]),
     "srs_predict_route": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _i32,
                                          _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                         _p, _p, _p, _p, _p, _p]),
+    "srs_route_grouped": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _p, _i32, _i32, _i32,
                                          _p, _p, _p, _p, _p, _p]),
     "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
     "route_gate": (ctypes.c_int, [_p, _i64, _i32, _p, _i32, _p, _p]),
@@ -385,6 +388,29 @@ def srs_predict_route(tok, lut, G, partials, w, K, renorm=1, conf=None, prev2=No
           _opt(expert_cluster, torch.uint8, "expert_cluster", E),
           _opt(local, torch.int64, "local", 1), _opt(err, torch.int32, "err", 1), _stream(stream))
     return dest, offsets, row_of_src, src_of_row, row_cluster, out, logits, idx, weights
+
+
+def srs_route_grouped(partials, w, K, H, renorm=1, row_cluster=None, expert_cluster=None,
+                      local=None, out=None, logits=None, idx=None, weights=None,
+                      with_logits=True, stream=None):
+    """The cross-group reduce, router, grouped top-K and per-group count in
+    one kernel: returns (out, logits, idx, weights); out (the reduced rows)
+    is written only when given."""
+    P, n, d = partials.shape
+    E = w.shape[0]
+    bt = _bf16(partials)
+    if with_logits and logits is None:
+        logits = _empty((n, E), torch.float32, partials)
+    idx = _empty((n, K), torch.int32, partials) if idx is None else idx
+    weights = _empty((n, K), torch.float32, partials) if weights is None else weights
+    _call("srs_route_grouped", _dev(partials, bt, "partials"), P, n, d,
+          _opt(out, bt, "out", n * d), _dev(w, _bf16(w), "w", E * d), E,
+          _opt(logits, torch.float32, "logits", n * E), K, H, renorm,
+          _dev(idx, torch.int32, "idx", n * K), _opt(weights, torch.float32, "weights", n * K),
+          _opt(row_cluster, torch.uint8, "row_cluster", n * H),
+          _opt(expert_cluster, torch.uint8, "expert_cluster", E),
+          _opt(local, torch.int64, "local", 1), _stream(stream))
+    return out, logits, idx, weights
 
 
 def route_gate(x, w, logits=None, stream=None):

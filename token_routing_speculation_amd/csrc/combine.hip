@@ -39,7 +39,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t dst, int d, int v, 
                              __float_as_uint(acc[6]), __float_as_uint(acc[7])});
   } else {
     uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(dst) * d + 8 * v;
-    st16_stream(o, pack8(acc));
+    st16_stream(o, pack8_cvt(acc));
   }
 }
 

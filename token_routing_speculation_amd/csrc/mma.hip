@@ -459,11 +459,11 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
   const int64_t ai = row0 + ar;
   const bool alive = ai < n;
   const int adst = alive ? (row_of_src ? row_of_src[ai] : static_cast<int>(ai)) : -1;
-  const bool astore = alive && adst >= 0 && adst < n;
+  const bool astore = alive && adst >= 0 && adst < n && out != nullptr;  // out null: no X
   if (alive && apc == 0) write_identity_row(ident, ai, n);
   const size_t plane = static_cast<size_t>(n) * d;
   const uint16_t* asrc = partials + static_cast<size_t>(alive ? ai : n - 1) * d + 8 * apc;
-  uint16_t* aout = out + static_cast<size_t>(astore ? adst : 0) * d + 8 * apc;
+  uint16_t* aout = astore ? out + static_cast<size_t>(adst) * d + 8 * apc : nullptr;
   const int alds = slab_off(ar, apc);
   char* pwave = pst + w * 1024;  // this wave's 1 KB of each partial slot
   auto load_a = [&](int t) {
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc8[e] += f[e];
     }
-    const u32x4 x = pack8(acc8);
+    const u32x4 x = pack8_cvt(acc8);
     *reinterpret_cast<u32x4*>(lds + (t % kMmaStages) * STAGE + alds) = x;
     if (astore) st16(aout + 64 * t, x);
   };
@@ -640,22 +640,74 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
       val[v] = tile[r * BN + s16 + 16 * v];
       key[v] = s16 + 16 * v < E ? order_key(val[v]) : 0u;
     }
-    int col;
-    float wgt;
-    seg_topk<16, BN / 16>(val, key, tk.K, tk.renorm, &col, &wgt);
     int dst = -1;
     if (row < n) dst = row_of_src ? row_of_src[row] : static_cast<int>(row);
-    const bool pick = dst >= 0 && dst < n && s16 < tk.K;
-    if (pick) {
-      tk.idx[static_cast<int64_t>(dst) * tk.K + s16] = col;
-      if (tk.weights) tk.weights[static_cast<int64_t>(dst) * tk.K + s16] = wgt;
-    }
-    if (tk.expert_cluster) {
-      // (a NaN logit with every bit set has key 0 like the columns past E and
-      // may tie with them: outside the contract, but no read past E)
-      const int cl = tk.dest && row < n ? static_cast<int>(tk.dest[row]) : 0;
-      const int ec = pick && col < E ? static_cast<int>(tk.expert_cluster[col]) : -1;
-      hits += __popcll(__ballot(ec == cl));
+    const bool keep = dst >= 0 && dst < n;
+    if (tk.H <= 1) {
+      int col;
+      float wgt;
+      seg_topk<16, BN / 16>(val, key, tk.K, tk.renorm, &col, &wgt);
+      const bool pick = keep && s16 < tk.K;
+      if (pick) {
+        tk.idx[static_cast<int64_t>(dst) * tk.K + s16] = col;
+        if (tk.weights) tk.weights[static_cast<int64_t>(dst) * tk.K + s16] = wgt;
+      }
+      if (tk.expert_cluster) {
+        // (a NaN logit with every bit set has key 0 like the columns past E
+        // and may tie with them: outside the contract, but no read past E)
+        int cl = 0;
+        if (row < n)
+          cl = tk.lar_cluster ? static_cast<int>(tk.lar_cluster[row])
+                              : (tk.dest ? static_cast<int>(tk.dest[row]) : 0);
+        const int ec = pick && col < E ? static_cast<int>(tk.expert_cluster[col]) : -1;
+        hits += __popcll(__ballot(ec == cl));
+      }
+    } else {
+      // Grouped: group h's columns [h eg, (h + 1) eg) keep their keys, the
+      // others are cleared, and the segment picks the group's kg; lane s < kg
+      // holds group pick s, slot h kg + s. renorm = 1: the softmax over the
+      // group's picks (seg_topk's); renorm = 0: over every column, from the
+      // row's largest logit.
+      const int H = tk.H, kg = tk.K / H, eg = E / H;
+      float mall = 0.f, zall = 0.f;
+      if (!tk.renorm) {
+        uint32_t kmx = 0u;
+#pragma unroll
+        for (int v = 0; v < BN / 16; ++v) kmx = key[v] > kmx ? key[v] : kmx;
+        mall = key_float(seg_max<16>(kmx));
+        float zl = 0.f;
+#pragma unroll
+        for (int v = 0; v < BN / 16; ++v) zl += key[v] ? __expf(val[v] - mall) : 0.f;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) zl += __shfl_xor(zl, o, kWave);
+        zall = zl;
+      }
+#pragma unroll 1
+      for (int h = 0; h < H; ++h) {
+        uint32_t kh[BN / 16];
+#pragma unroll
+        for (int v = 0; v < BN / 16; ++v) {
+          const int c = s16 + 16 * v;
+          kh[v] = c >= h * eg && c < (h + 1) * eg ? key[v] : 0u;
+        }
+        int col;
+        float wgt;
+        seg_topk<16, BN / 16>(val, kh, kg, 1, &col, &wgt);
+        if (!tk.renorm) wgt = __fdividef(__expf(tile[r * BN + (col < BN ? col : 0)] - mall), zall);
+        const bool pick = keep && s16 < kg;
+        if (pick) {
+          tk.idx[static_cast<int64_t>(dst) * tk.K + h * kg + s16] = col;
+          if (tk.weights) tk.weights[static_cast<int64_t>(dst) * tk.K + h * kg + s16] = wgt;
+        }
+        if (tk.expert_cluster) {
+          int cl = 0;
+          if (row < n)
+            cl = tk.lar_cluster ? static_cast<int>(tk.lar_cluster[row * H + h])
+                                : (tk.dest ? static_cast<int>(tk.dest[row]) : 0);
+          const int ec = pick && col < E ? static_cast<int>(tk.expert_cluster[col]) : -1;
+          hits += __popcll(__ballot(ec == cl));
+        }
+      }
     }
   }
   if (tk.expert_cluster) {
@@ -704,7 +756,8 @@ int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int
                     uint16_t* out, const uint16_t* w, int E, float* logits,
                     const SrsIdentity& ident, const GateTopk* topk, hipStream_t s) {
   if (!srs_gate_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
-  const GateTopk tk = topk ? *topk : GateTopk{0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const GateTopk tk =
+      topk ? *topk : GateTopk{0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 1, nullptr};
   const unsigned grid = ceil_div(n, 64);
   if (P == 1)
     srs_gate160_kernel<1><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,

@@ -97,7 +97,7 @@ __device__ __forceinline__ void ln_row(const u32x4 (&raw)[CPL], const float* __r
       y[0] += b0.x; y[1] += b0.y; y[2] += b0.z; y[3] += b0.w;
       y[4] += b1.x; y[5] += b1.y; y[6] += b1.z; y[7] += b1.w;
     }
-    q[c] = pack8(y);
+    q[c] = pack8_cvt(y);
   }
 }
 

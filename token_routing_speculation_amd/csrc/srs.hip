@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kMoveThreads) void srs_move(const uint16_t* __restr
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += f[e];
     }
-    if (v < nv) st16(o + 8 * v, pack8(acc));
+    if (v < nv) st16(o + 8 * v, pack8_cvt(acc));
   }
 }
 
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kMoveThreads) void srs_move_any(const uint16_t* __r
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += f[e];
     }
-    st16(o + 8 * v, pack8(acc));
+    st16(o + 8 * v, pack8_cvt(acc));
   }
 }
 

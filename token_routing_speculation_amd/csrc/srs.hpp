@@ -40,6 +40,12 @@ struct GateTopk {
   const uint8_t* dest;
   const uint8_t* expert_cluster;
   unsigned long long* local;
+  // grouped top-K ("Federation of Experts (FoE)" article): H groups of E / H
+  // experts, each picking its K / H (H <= 1: plain top-K); the local count
+  // then compares group h's picks with lar_cluster[row * H + h] (nullable:
+  // dest[row], as with one group)
+  int H;
+  const uint8_t* lar_cluster;
 };
 
 // mma.hip: the fused shuffle + router kernel for 1 <= E <= 160 columns,

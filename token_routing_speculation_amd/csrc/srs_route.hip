@@ -484,7 +484,7 @@ static int route_rows(const uint16_t* partials, int P, int64_t n, int d, const i
                       const PredSort* ps = nullptr) {
   if (!route_fits(P, d, E)) {
     if (ps) return ROUTE_ERR_UNSUPPORTED;
-    const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local};
+    const GateTopk tk{K, renorm != 0, idx, weights, dest, expert_cluster, local, 1, nullptr};
     return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
   }
   const RouteOut ro{logits, idx, weights, expert_cluster, local};
@@ -607,4 +607,24 @@ ROUTE_API int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lu
   const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
   return route_rows(partials, P, n, d, nullptr, dest, out, w, E, logits, K, renorm, idx, weights,
                     expert_cluster, local, none, s, &ps);
+}
+
+ROUTE_API int srs_route_grouped(const uint16_t* partials, int32_t P, int64_t n, int32_t d,
+                                uint16_t* out, const uint16_t* w, int32_t E, float* logits,
+                                int32_t K, int32_t H, int32_t renorm, int32_t* idx,
+                                float* weights, const uint8_t* row_cluster,
+                                const uint8_t* expert_cluster, unsigned long long* local,
+                                hipStream_t s) {
+  if (n < 0 || P < 1 || d < 8 || d % 8 != 0 || E < 1 || K < 1 || H < 1 || E % H != 0 ||
+      K % H != 0 || K / H > E / H || n >= (int64_t(1) << 31))
+    return ROUTE_ERR_SHAPE;
+  if (K > kMaxK || !srs_gate_fits(P, d, E)) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!partials || !w || !idx) return ROUTE_ERR_NULL;
+  if ((expert_cluster == nullptr) != (local == nullptr)) return ROUTE_ERR_NULL;
+  if (expert_cluster && !row_cluster) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(w) || (out && !aligned16(out))) return ROUTE_ERR_ALIGN;
+  const GateTopk tk{K, renorm != 0, idx, weights, nullptr, expert_cluster, local, H, row_cluster};
+  const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
+  return srs_gate_launch(partials, P, n, d, nullptr, out, w, E, logits, none, &tk, s);
 }

@@ -9,9 +9,9 @@ one kernel after it (``srs_route``); for small batches all of these are one
 kernel (``predict_route``).
 
 ``FoEPass``: cross-group reduce of the H group activations -> gate ->
-grouped top-k/H -> LAR -> permute from the group activations -> combine
-(cross-group sum), the grouped block of the "Federation of Experts (FoE)"
-article.
+grouped top-k/H -> LAR (one kernel, ``route``) -> permute from the group
+activations -> combine (cross-group sum), the grouped block of the
+"Federation of Experts (FoE)" article.
 
 ``ExpertGrouping``: the s-EG expert placement of the "Speculative MoE" notes
 (sections 3.2 and 4.2): a token-expert activation profile, then cross-entropy
@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
-               srs_shuffle_route, srs_route_sorted, srs_predict_route,
+               srs_shuffle_route, srs_route_sorted, srs_predict_route, srs_route_grouped,
                route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
@@ -260,6 +260,14 @@ class FoEPass:
         self.out = e((N, d), out_dtype)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
 
+    def route(self):
+        # the cross-group reduce, router, grouped top-K and per-group count in
+        # one kernel; the reduced rows feed only the router, so they are not
+        # written (r_full stays unwritten)
+        srs_route_grouped(self.xg, self.w, self.K, self.H, 1, row_cluster=self.row_cluster,
+                          expert_cluster=self.expert_cluster, local=self.local,
+                          logits=self.logits, idx=self.idx, weights=self.weights)
+
     def reduce(self):
         srs_shuffle(self.xg, None, 1, out=self.r_full, offsets=self.cluster_offsets, maps=False,
                     ws=self.ws_srs, err=self.err)
@@ -281,7 +289,8 @@ class FoEPass:
     def combine(self):
         moe_combine(self.disp, self.weights, self.slot_of_pair, out=self.out, err=self.err)
 
-    STAGES = ("reduce", "gate", "topk", "lar", "permute", "combine")
+    # the separate calls (reduce, gate, topk, lar) remain for comparison
+    STAGES = ("route", "permute", "combine")
 
     def step(self):
         for s in self.STAGES:
