@@ -277,6 +277,12 @@ def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     b = 2
     if fused and not estimator:
         return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K + 4 * N * K + 16}
+    if fused:
+        # q_l, the hidden layer, then the output layer with its top-K and the
+        # hit count in one kernel (the logits never leave the chip)
+        return {"qhidden": 2 * N * d * b + 4 * d,
+                "hidden": N * d * b + hd * d * b + 4 * hd + N * hd * b,
+                "out_topk_hits": N * hd * b + E * hd * b + 4 * E + 8 * N * K + 8}
     st = {"qhidden": 2 * N * d * b + 4 * d,
           "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
           if estimator else (N * d * b + E * d * b + 4 * N * E),
@@ -575,9 +581,10 @@ def predictor_measure(args):
     byt_gate = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False)
     byt_fused = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, False, fused=True)
     byt_est = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, True)
+    byt_est_fused = predictor_bytes(N, cfg.d, cfg.E, cfg.K, cfg.hd, True, fused=True)
     ne = sum(est)
     total_unfused = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_gate.values())
-    total_bytes = ne * sum(byt_est.values()) + (nl - ne) * sum(byt_fused.values())
+    total_bytes = ne * sum(byt_est_fused.values()) + (nl - ne) * sum(byt_fused.values())
     qg_us = qg_launch_us
     out = {
         "metric": "q_l expert-prediction throughput over all source layers (token-predictions/s)",

@@ -485,6 +485,24 @@ size_t route_gate_packed_size(int32_t E, int32_t d);
 int route_gate_pack(const uint16_t* w, int32_t E, int32_t d, uint16_t* wp, hipStream_t s);
 
 /*
+ * route_est_out_topk_packed - the estimator's output layer with its top-K
+ * and hit count in one kernel: logits = h . w2^T + b2, each row's top K of
+ * them in route_topk's order, and *hits += the picks found among the row's
+ * true picks. [SPEC] items 2.C (the estimator's second layer) and 4 (hit
+ * rate). The logits are binary32 sums of exact bf16 products plus b2.
+ *   h bf16 [n][hd] (the hidden layer, route_est_hidden's output);
+ *   w2p bf16 packed by route_gate_pack(w2, E, hd); b2 float [E] (nullable);
+ *   logits float [n][E] (nullable: not written); idx int32 [n][K];
+ *   truth int32 [n][K] and hits uint64 (nullable together).
+ * Errors: NULL, SHAPE (K > E, hd % 8), ALIGN, UNSUPPORTED (hd not 512,
+ * 1024 or 2048, E > 256, K > 16).
+ */
+int route_est_out_topk_packed(const uint16_t* h, int64_t n, int32_t hd, const uint16_t* w2p,
+                              const float* b2, int32_t E, int32_t K, float* logits,
+                              int32_t* idx, const int32_t* truth, unsigned long long* hits,
+                              hipStream_t s);
+
+/*
  * route_qgate_topk_packed - route_qgate_topk with the router given packed
  * (wp from route_gate_pack for the same E and d). [SPEC] items 2.A and 4.
  * The same results, bit for bit: the matrix products see the same operands

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 44, names
+    assert len(names) == 45, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -239,6 +239,23 @@ def test_route_grouped_errors(L):
     assert call(args(ec=A)) == NULL             # the count needs local
     assert call(args(ec=A, local=A)) == NULL    # and row_cluster
     assert call(args(out=MIS)) == ALIGN
+    assert call(args(n=0)) == OK
+
+
+def test_est_out_topk_errors(L):
+    f = L.route_est_out_topk_packed
+    args = lambda **k: dict(dict(h=A, n=100, hd=512, w2p=A, b2=None, E=128, K=8, logits=None, idx=A,
+                                 truth=None, hits=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(n=-1)) == SHAPE
+    assert call(args(K=129)) == SHAPE
+    assert call(args(hd=12)) == SHAPE
+    assert call(args(hd=640)) == UNSUP
+    assert call(args(E=257, K=8)) == UNSUP
+    assert call(args(K=17)) == UNSUP
+    assert call(args(idx=None)) == NULL
+    assert call(args(truth=A)) == NULL          # truth and hits together
+    assert call(args(h=MIS)) == ALIGN
     assert call(args(n=0)) == OK
 
 

@@ -12,7 +12,7 @@ import token_routing_speculation_amd as tr
 import oracle
 from oracle.bf16 import round_bf16
 
-from gpu_helpers import dev, host
+from gpu_helpers import dev, host, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -207,3 +207,40 @@ def test_qgate_topk_packed_equals_unpacked(n, d, E, K, affine):
     assert int(host(h1)[0]) == int(host(h2)[0])
     assert np.array_equal(host(i2), oracle.route_topk(host(lg2), K, 1, 1)[0])
     assert int(host(h2)[0]) == oracle.hit_count(host(i2), truth)
+
+
+@pytest.mark.parametrize("n,hd,E,K,with_bias,keep", [(8192, 512, 128, 8, True, True),
+                                                     (1, 512, 8, 2, True, False),
+                                                     (1000, 1024, 160, 6, False, True),
+                                                     (37, 2048, 256, 16, True, True),
+                                                     (500, 512, 100, 4, True, False)])
+def test_est_out_topk_packed_against_oracle(n, hd, E, K, with_bias, keep):
+    """The estimator's output layer with its top-K and hit count in one
+    kernel: the logits (when kept) against the oracle's h . w2^T + b2, the
+    picks bit-exact against the oracle's top-K of the kernel's own logits
+    (kept or recomputed by the two-call form), the hit count exactly
+    hit_count's."""
+    rng = np.random.default_rng(n + hd + E)
+    h = round_bf16(rng.standard_normal((n, hd)) * 0.5)
+    w2 = round_bf16(rng.standard_normal((E, hd)) / np.sqrt(hd))
+    b2 = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+    truth = rng.integers(0, E, (n, K)).astype(np.int32)
+    wp = tr.route_gate_pack(dev(w2))
+    lg = torch.empty((n, E), dtype=torch.float32, device="cuda") if keep else None
+    hits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    idx = tr.route_est_out_topk_packed(dev(h), wp, None if b2 is None else dev(b2), E, K, logits=lg,
+                                       truth=dev(truth), hits=hits)
+    sync()
+    ref = oracle.route_gate(h, w2) + (0.0 if b2 is None else b2.astype(np.float64))
+    if keep:
+        lgh = host(lg)
+        assert_rel(lgh, ref, LOGIT_TOL, "estimator output logits")
+    else:
+        # the same products in the kept form (the logits written, nothing else changes)
+        lg2 = torch.empty((n, E), dtype=torch.float32, device="cuda")
+        tr.route_est_out_topk_packed(dev(h), wp, None if b2 is None else dev(b2), E, K, logits=lg2)
+        sync()
+        lgh = host(lg2)
+    widx, _ = oracle.route_topk(lgh, K, 1, 1)
+    assert np.array_equal(host(idx), widx)
+    assert int(hits.item()) == oracle.hit_count(widx, truth)

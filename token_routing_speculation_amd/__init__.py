@@ -31,6 +31,7 @@ __all__ = [
     "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
     "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "route_qgate",
     "route_qgate_topk", "route_gate_packed_size", "route_gate_pack", "route_qgate_topk_packed",
+    "route_est_out_topk_packed",
     "EXPORTS",
 ]
 
@@ -86,6 +87,8 @@ EXPORTS = {
     "route_gate_pack": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
     "route_qgate_topk_packed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _i32, _i32, _p,
                                                _p, _p, _p, _p]),
+    "route_est_out_topk_packed": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p,
+                                                 _p, _p]),
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
@@ -577,6 +580,20 @@ def route_gate_pack(w, wp=None, stream=None):
     _call("route_gate_pack", _dev(w, _bf16(w), "w", E * d), E, d,
           _dev(wp, _bf16(w), "wp", nbytes // 2), _stream(stream))
     return wp
+
+
+def route_est_out_topk_packed(h, w2p, b2, E, K, logits=None, idx=None, truth=None, hits=None,
+                              stream=None):
+    """The estimator's output layer h . w2^T + b2 with its top-K (and the hit
+    count against truth) in one kernel; w2p from route_gate_pack(w2).
+    Returns idx."""
+    n, hd = h.shape
+    idx = _empty((n, K), torch.int32, h) if idx is None else idx
+    _call("route_est_out_topk_packed", _dev(h, _bf16(h), "h"), n, hd, _dev(w2p, _bf16(w2p), "w2p"),
+          _opt(b2, torch.float32, "b2", E), E, K, _opt(logits, torch.float32, "logits", n * E),
+          _dev(idx, torch.int32, "idx", n * K), _opt(truth, torch.int32, "truth", n * K),
+          _opt(hits, torch.int64, "hits", 1), _stream(stream))
+    return idx
 
 
 def route_qgate_topk_packed(r, dvec, wp, E, K, gamma=None, beta=None, eps=1e-5, idx=None,

@@ -173,13 +173,17 @@ __device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ 
 // -0.0 == +0.0), from the logits gathered in LDS; logits may then be NULL.
 // TOPK = 0: the product alone. PW: w is in the packed fragment order of
 // route_gate_pack instead of rows.
-template <int BM, int D, int TOPK, bool PW>
+// LN false: the tile is r's rows themselves (dvec, gamma, beta, eps unused),
+// for a product whose input is already on hand (the estimator's hidden
+// layer). bias (nullable, [E]) is added to every logit before it is stored
+// or ranked.
+template <int BM, int D, int TOPK, bool PW, bool LN = true>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
     const uint16_t* __restrict__ w, int E, float* __restrict__ logits, int K,
     int* __restrict__ idx, const int32_t* __restrict__ truth,
-    unsigned long long* __restrict__ hits) {
+    unsigned long long* __restrict__ hits, const float* __restrict__ bias = nullptr) {
   constexpr int CPL = D / 8 / kWave;
   constexpr int NV = D / 8;
   constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   constexpr int NPAIRS = D / 64;  // pairs of 32-wide K steps
   static_assert(CPL * 8 * kWave == D && RPW >= 1 && BM % 16 == 0, "tile shape");
   static_assert(NPAIRS % (kQgLead + 1) == 0, "the ring cycles whole");
-  __shared__ __attribute__((aligned(16))) float sd[D];
+  __shared__ __attribute__((aligned(16))) float sd[LN ? D : 4];
   __shared__ __attribute__((aligned(16))) char tile[BM * D * 2];
   // the line loads' per-wave staging (16 bytes when W comes packed: the hit
   // count's word only)
@@ -202,9 +206,11 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const int rr = 4 * wv + (lane >> 4);
     if (hits && rr < BM && row0 + rr < n && (lane & 15) < K) tv = truth[(row0 + rr) * K + (lane & 15)];
   }
-  for (int j = threadIdx.x * 4; j < D; j += kQgThreads * 4)
-    *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
-  __syncthreads();
+  if constexpr (LN) {
+    for (int j = threadIdx.x * 4; j < D; j += kQgThreads * 4)
+      *reinterpret_cast<float4*>(sd + j) = *reinterpret_cast<const float4*>(dvec + j);
+    __syncthreads();
+  }
   // q rows: wave wv takes tile rows wv, wv + 8, ...; all their loads are
   // issued before the first is normalised. Rows past n repeat row n - 1
   // (their logits are never stored).
@@ -217,7 +223,12 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     u32x4 y[CPL];
-    ln_row<CPL>(raw[k], sd, gamma, beta, D, eps, lane, y);
+    if constexpr (LN) {
+      ln_row<CPL>(raw[k], sd, gamma, beta, D, eps, lane, y);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) y[c] = raw[k][c];
+    }
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
       *reinterpret_cast<u32x4*>(tile + qg_off<D>(wv + 8 * k, lane + c * kWave)) = y[c];
@@ -312,12 +323,13 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   auto store_logits = [&](int g, const f32x4 (&acc)[MT]) {
     const int colr = 16 * g + r16;
     if (colr < E) {
+      const float b = bias ? bias[colr] : 0.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int64_t row = row0 + 16 * m + 4 * kq + jj;
-          if (row < n) logits[row * E + colr] = acc[m][jj];
+          if (row < n) logits[row * E + colr] = acc[m][jj] + b;
         }
     }
   };
@@ -349,10 +361,12 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
       const int g = wv + NW * gi;
       const int col = 16 * g + r16;
       if (g < ngroups && col < E) {
+        const float b = bias ? bias[col] : 0.f;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) lt[(16 * m + 4 * kq + jj) * E + col] = accs[gi][m][jj];
+          for (int jj = 0; jj < 4; ++jj)
+            lt[(16 * m + 4 * kq + jj) * E + col] = accs[gi][m][jj] + b;
       }
     }
     __syncthreads();
@@ -543,6 +557,32 @@ ROUTE_API int route_qgate_topk(const uint16_t* r, const float* dvec, const float
     qgate_launch<1>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
   else
     qgate_launch<2>(d, n, s, r, dvec, gamma, beta, eps, w, E, logits, K, idx, truth, hits);
+  return launch_status();
+}
+
+ROUTE_API int route_est_out_topk_packed(const uint16_t* h, int64_t n, int32_t hd,
+                                        const uint16_t* w2p, const float* b2, int32_t E,
+                                        int32_t K, float* logits, int32_t* idx,
+                                        const int32_t* truth, unsigned long long* hits,
+                                        hipStream_t s) {
+  if (n < 0 || hd < 8 || hd % 8 != 0 || E < 1 || K < 1 || K > E) return ROUTE_ERR_SHAPE;
+  if (E > 256 || K > kMaxK || (hd != 512 && hd != 1024 && hd != 2048))
+    return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!h || !w2p || !idx || (!truth != !hits)) return ROUTE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w2p)) return ROUTE_ERR_ALIGN;
+  const unsigned grid = ceil_div(n, 32);
+#define ROUTE_EST_OUT(D, T)                                                                   \
+  qgate_kernel<32, D, T, true, false><<<grid, kQgThreads, 0, s>>>(                            \
+      h, nullptr, nullptr, nullptr, n, 0.f, w2p, E, logits, K, idx, truth, hits, b2)
+  if (hd == 512) {
+    if (E <= 128) ROUTE_EST_OUT(512, 1); else ROUTE_EST_OUT(512, 2);
+  } else if (hd == 1024) {
+    if (E <= 128) ROUTE_EST_OUT(1024, 1); else ROUTE_EST_OUT(1024, 2);
+  } else {
+    if (E <= 128) ROUTE_EST_OUT(2048, 1); else ROUTE_EST_OUT(2048, 2);
+  }
+#undef ROUTE_EST_OUT
   return launch_status();
 }
 

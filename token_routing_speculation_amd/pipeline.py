@@ -41,7 +41,8 @@ from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
                eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk,
-               route_gate_pack, route_qgate_topk_packed)
+               route_gate_pack, route_qgate_topk_packed, route_est_hidden,
+               route_est_out_topk_packed)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
@@ -311,6 +312,7 @@ class PredictorPass:
         self.truth = e((N, K), torch.int32)
         self.hits = torch.zeros((1,), dtype=torch.int64, device=dev)
         self.ws = e((max(route_estimator_workspace_size(N, hd), 16),), torch.uint8)
+        self.h = e((N, hd), torch.bfloat16)  # the estimator's hidden layer
         self.device = dev
         self.layer = None
 
@@ -323,6 +325,8 @@ class PredictorPass:
                       for k, v in layer.items()}
         if not self.layer["estimator"] and self.d in QGATE_D and self.E <= 256:
             self.layer["w_next_packed"] = route_gate_pack(self.layer["w_next"])
+        if self.layer["estimator"] and self.hd in (512, 1024, 2048) and self.E <= 256:
+            self.layer["w2_packed"] = route_gate_pack(self.layer["w2"])
         return self
 
     def truth_step(self):
@@ -336,14 +340,25 @@ class PredictorPass:
         in one kernel (route_qgate_topk_packed, q and the logits kept on chip; the
         logits are written only if ``keep_logits``) when ``fused`` and the
         shape allows, else route_qhidden + route_gate + route_topk; on
-        estimator layers q_l, the estimator and top-K. Then the hit count (inside
-        the fused kernel on gate layers)."""
+        estimator layers q_l, the hidden layer, and the output layer with its
+        top-K and hit count in one kernel (route_est_out_topk_packed) when
+        ``fused``, else q_l, the estimator and top-K. Then the hit count
+        (inside the fused kernels)."""
         L = self.layer
         if not L["estimator"] and fused and "w_next_packed" in L:
             route_qgate_topk_packed(L["r"], L["dvec"], L["w_next_packed"], self.E, self.K,
                                     eps=L["eps"], idx=self.pred,
                                     logits=self.logits if keep_logits else None,
                                     truth=self.truth, hits=self.hits)
+            return
+        if L["estimator"] and fused and "w2_packed" in L:
+            # q_l, the hidden layer, then the output layer with its top-K and
+            # the hit count in one kernel
+            route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
+            route_est_hidden(self.q, L["w1"], L["b1"], h=self.h)
+            route_est_out_topk_packed(self.h, L["w2_packed"], L["b2"], self.E, self.K,
+                                      logits=self.logits if keep_logits else None,
+                                      idx=self.pred, truth=self.truth, hits=self.hits)
             return
         else:
             route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
