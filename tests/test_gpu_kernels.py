@@ -461,13 +461,15 @@ def test_run_twice_bitwise_foe_and_predictor():
 
 
 # ------------------------------------------------------------ graph replay
-@pytest.mark.parametrize("E,d,routed", [(160, 512, True), (64, 512, True), (96, 520, False)])
+@pytest.mark.parametrize("E,d,routed", [(160, 512, True), (64, 512, True), (96, 520, False),
+                                        (8, 512, True)])
 def test_graph_replay_matches_eager(E, d, routed):
     """The benchmark replays the pass as a captured graph: every replay, with
     eager work and synchronisations in between, must equal the eager pass
     (the shuffle, router, top-K and count in one kernel: the matrix-core one
-    at 160 columns, the lane-per-expert one at 64; separate calls where
-    neither takes the shape)."""
+    at 160 columns, the lane-per-expert one at 64 and 8, there with the
+    prediction and order inside it and the dispatch in one launch; separate
+    calls where neither takes the shape)."""
     from token_routing_speculation_amd.pipeline import RoutePass, capture_graph
     inp = make_route_inputs(2000, d, E, 6, 2, 8, 5000, 91, ngram=True)
     p = RoutePass(inp, lut=inp["lut"], conf=inp["conf"])
@@ -485,3 +487,30 @@ def test_graph_replay_matches_eager(E, d, routed):
         sync()
         for k in keys:
             assert np.array_equal(host(getattr(p, k)), eager[k]), (rep, k)
+
+
+def test_graph_replay_matches_eager_foe():
+    """The FoE pass (the grouped routing in one kernel, the dispatch, the
+    combine) replayed as a captured graph equals the eager pass, replay after
+    replay."""
+    from synth.gen import make_foe_inputs
+    from token_routing_speculation_amd.pipeline import FoEPass, capture_graph
+    inp = make_foe_inputs(3000, 256, 64, 4, 8, 8, 5000, 17)
+    f = FoEPass(inp)
+    keys = ("logits", "idx", "weights", "slot_of_pair", "pair_of_slot", "disp", "out")
+    f.step()
+    sync()
+    eager = {k: host(getattr(f, k)).copy() for k in keys}
+    l1 = int(host(f.local)[0])
+    g = capture_graph(f.step)
+    for rep in range(4):
+        for k in keys:
+            getattr(f, k).view(torch.uint8).fill_(0xA5)
+        sync()
+        before = int(host(f.local)[0])
+        g.replay()
+        sync()
+        for k in keys:
+            assert np.array_equal(host(getattr(f, k)), eager[k]), (rep, k)
+        assert int(host(f.local)[0]) - before == l1
+
