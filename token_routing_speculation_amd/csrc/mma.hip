@@ -391,8 +391,14 @@ __global__ __launch_bounds__(kM160Threads, 1) void mma_nt160_kernel(
 // (loads and stores alike), so the X stores, which the count leaves out,
 // can only make a wait stricter.
 // ---------------------------------------------------------------------------
-template <int PT>
-constexpr int sg_lead() { return PT <= 2 ? 3 : 1; }  // partial slots: 112 KB of stages + 48 KB at P = 2
+// Steps of partials in flight: what the LDS holds beside the four stages
+// (160 columns: 112 KB of stages, 48 KB of slots at P = 2; 64 columns: 64 KB
+// of stages, the rest for slots, at most six steps).
+template <int PT, int BN>
+constexpr int sg_lead() {
+  if constexpr (BN == 160) return PT <= 2 ? 3 : 1;
+  else return (96 / (8 * PT)) < 6 ? (96 / (8 * PT)) : 6;
+}
 
 // One 16-byte piece per lane into LDS, as lds_load16, with the nontemporal
 // (streaming) policy: the partials are read once.
@@ -403,25 +409,35 @@ __device__ __forceinline__ void lds_load16_nt(const void* g, char* lds_base) {
 #endif
 }
 
-template <int PT>
+// BN = 160 (129..160 columns, DeepSeek-V2's router) or 64 (at most 64: the
+// FoE router), the same pipeline: with 64 columns a step's W stage is 8 KB
+// instead of 20, each wave multiplies 2 tiles of 16 columns instead of 5, and
+// the LDS this frees holds more steps of partials in flight.
+template <int PT, int BN = 160>
 __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
     const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ W, int E, float* __restrict__ logits,
     SrsIdentity ident, GateTopk tk) {
-  constexpr int BM = 64, BN = 160;
-  constexpr int MT = 2, NT = 5;             // 16 x 16 tiles per wave
-  constexpr int STAGE = (BM + BN) * 128;    // 28 KB
-  constexpr int NJW = BN / 8;               // 1 KB W loads per step (20)
+  static_assert(BN == 160 || BN == 64, "the two tile widths");
+  constexpr int BM = 64;
+  constexpr int MT = 2, NT = BN / 32;       // 16 x 16 tiles per wave
+  constexpr int WC = BN / 2;                // each wave's columns
+  constexpr int STAGE = (BM + BN) * 128;    // 28 KB (16 KB at 64 columns)
+  constexpr int NJW = BN / 8;               // 1 KB W loads per step (20, or 8)
   constexpr int NW = kM160Threads / kWave;  // 8
-  constexpr int NIW = (NJW + NW - 1) / NW;  // 3 (waves 0-3), 2 for waves 4-7
-  constexpr int LA = sg_lead<PT>();
+  constexpr int NIW = (NJW + NW - 1) / NW;  // 3 (waves 0-3) and 2 (waves 4-7), or 1
+  constexpr int NIHI = NIW, NILO = BN == 160 ? 2 : 1;
+  constexpr int LA = sg_lead<PT, BN>();
   constexpr int PSLOT = BM * 128;           // one partial's pieces of one step (8 KB)
-  static_assert(NJW == 3 * 4 + 2 * 4, "W loads split 3 / 2 over the waves");
+  static_assert(BN == 64 || NJW == 3 * 4 + 2 * 4, "W loads split 3 / 2 over the waves");
+  static_assert(BN == 160 || NJW == NW, "one W load per wave");
   static_assert(kMmaStages == 4, "the main loop stages two steps per pass");
-  // loads a wave issues after the awaited ones (see above): nw W loads and PT
-  // partial loads per step
-  constexpr int kWaitA3 = (LA - 1) * (3 + PT) + 3, kWaitA2 = (LA - 1) * (2 + PT) + 2;
-  constexpr int kWaitW3 = PT + 2 * (3 + PT), kWaitW2 = PT + 2 * (2 + PT);
+  // loads a wave issues after the awaited ones (see above): its W loads (NIHI
+  // for waves 0-3, NILO for 4-7) and PT partial loads per step
+  constexpr int kWaitA3 = (LA - 1) * (NIHI + PT) + NIHI;
+  constexpr int kWaitA2 = (LA - 1) * (NILO + PT) + NILO;
+  constexpr int kWaitW3 = PT + 2 * (NIHI + PT), kWaitW2 = PT + 2 * (NILO + PT);
+  static_assert(kWaitA3 < 64 && kWaitW3 < 64, "vmcnt range");
   // the four stages, then the partial slots
   __shared__ __attribute__((aligned(1024))) char lds[kMmaStages * STAGE + LA * PT * PSLOT];
   char* const pst = lds + kMmaStages * STAGE;
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
   const int wr = w4 & 1, wc = w4 >> 1;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int nsteps = d / 64;  // even, >= 2
-  const int ni = w < 4 ? 3 : 2;
+  const int ni = w < 4 ? NIHI : NILO;
 
   // W: load j = w + 8 i fills slab rows BM + 8 j .. BM + 8 j + 7; lane l
   // fetches the piece that the swizzle stores at physical piece l % 8.
@@ -517,10 +533,12 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       fb[set][t] = *reinterpret_cast<const u32x4*>(
-          base + BM * 128 + slab_off(wc * 80 + 16 * t + (lane & 15), pc));
+          base + BM * 128 + slab_off(wc * WC + 16 * t + (lane & 15), pc));
   };
   // the MFMAs of one step with the staging of step tl (tl < 0: none): W's
-  // loads after MFMAs 2, 4 and 6, the A piece after MFMA 8
+  // loads after MFMAs 2, 4 and 6, the A piece after MFMA 8 (64 columns: the
+  // W load after MFMA 1, the A piece after MFMA 3)
+  constexpr int QW = BN == 160 ? 2 : 1, QA = BN == 160 ? 8 : 3;
   auto mfma_step = [&](int set, int tl) {
     int q = 0;
 #pragma unroll
@@ -529,15 +547,15 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
       for (int t = 0; t < NT; ++t) {
         acc[m][t] = mfma16x16x32(fa[set][m], fb[set][t], acc[m][t]);
         ++q;
-        if (q == 2 || q == 4 || q == 6) {
+        if (q % QW == 0 && q / QW <= NIW) {
           __builtin_amdgcn_sched_barrier(0);
-          const int i = q / 2 - 1;
+          const int i = q / QW - 1;
           if (tl >= 0 && i < ni) {
             const int ks = tl < nsteps ? tl : nsteps - 1;
             lds_load16(wsrc[i] + ks * 128, lds + (tl % kMmaStages) * STAGE + wdst[i]);
           }
           __builtin_amdgcn_sched_barrier(0);
-        } else if (q == 8) {
+        } else if (q == QA) {
           __builtin_amdgcn_sched_barrier(0);
           if (tl >= 0) stage_a(tl);
           __builtin_amdgcn_sched_barrier(0);
@@ -616,7 +634,7 @@ __global__ __launch_bounds__(kM160Threads, 1) void srs_gate160_kernel(
         const bool ok = dst >= 0 && dst < n;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int col = wc * 80 + 16 * t + (lane & 15);
+          const int col = wc * WC + 16 * t + (lane & 15);
           const float v = acc[m][t][j] + red[((w4 * MT + m) * NT + t) * kWave + lane][j];
           if (logits && ok && col < E) logits[static_cast<int64_t>(dst) * E + col] = v;
           if (tk.idx) tile[r * BN + col] = col < E ? v : -__builtin_inff();
@@ -759,15 +777,16 @@ int srs_gate_launch(const uint16_t* partials, int P, int64_t n, int d, const int
   const GateTopk tk =
       topk ? *topk : GateTopk{0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 1, nullptr};
   const unsigned grid = ceil_div(n, 64);
-  if (P == 1)
-    srs_gate160_kernel<1><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident, tk);
-  else if (P == 2)
-    srs_gate160_kernel<2><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident, tk);
-  else
-    srs_gate160_kernel<4><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, E,
-                                                        logits, ident, tk);
+#define ROUTE_SG(PT, BN)                                                                      \
+  srs_gate160_kernel<PT, BN><<<grid, kM160Threads, 0, s>>>(partials, n, d, row_of_src, out, w, \
+                                                           E, logits, ident, tk)
+  // at most 64 columns: the narrow tile (its LDS holds more partials in flight)
+  if (E <= 64) {
+    if (P == 1) ROUTE_SG(1, 64); else if (P == 2) ROUTE_SG(2, 64); else ROUTE_SG(4, 64);
+  } else {
+    if (P == 1) ROUTE_SG(1, 160); else if (P == 2) ROUTE_SG(2, 160); else ROUTE_SG(4, 160);
+  }
+#undef ROUTE_SG
   return launch_status();
 }
 
