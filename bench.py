@@ -36,7 +36,9 @@ def route_bytes(N, d, E, K, P, G, fallback, routed=False, stages=None):
     shuffle, router, top-K and count in one kernel (srs_shuffle_route) the
     reduced rows are written once and not read back, and neither are the
     logits nor the picks; with the prediction in that kernel too
-    (srs_predict_route) the predicted clusters are not read back either."""
+    (srs_predict_route) the predicted clusters are not read back either; with
+    the dispatch in it as well (srs_predict_route_dispatch) the reduced rows
+    are not written at all."""
     b = 2
     st = {
         "predict": (9 if fallback else 6) * N,
@@ -58,6 +60,13 @@ def route_bytes(N, d, E, K, P, G, fallback, routed=False, stages=None):
             # both in one kernel: the clusters are not read back (N bytes)
             rt = {"predict_route": rt["predict_sort"] + rt["srs_route"] - N,
                   "permute": rt["permute"], "combine": rt["combine"]}
+        if stages is not None and "predict_route_dispatch" in stages:
+            # and the dispatch too: the reduced rows go from registers to
+            # their K slots (neither written as rows nor read back), the
+            # picks are not read back; the two pair maps and the offsets
+            rt = {"predict_route_dispatch": (rt["predict_sort"] + rt["srs_route"] - N - N * d * b
+                                             + 8 * N * K + 4 * (E + 1) + N * K * d * b),
+                  "combine": rt["combine"]}
         return rt
     return st
 
@@ -1116,10 +1125,11 @@ def route_measure(args, name):
     tokens_per_s = N / (ms * 1e-3)
     total_bytes = sum(bytes_st.values())
     # the stage holding the router product
-    gate_stage = next(g for g in ("gate", "srs_route", "predict_route", "route") if g in st_us)
+    gate_stage = next(g for g in ("gate", "srs_route", "predict_route", "predict_route_dispatch",
+                                  "route") if g in st_us)
     # dominant kernel: the longest stage that is one launch
     fused_permute = cfg.E <= 16 and N * cfg.K <= 16384 and cfg.d <= 4096 and name != "foe"
-    single = {"predict_route", "srs_route", "combine", "route"}
+    single = {"predict_route", "predict_route_dispatch", "srs_route", "combine", "route"}
     if fused_permute:
         single.add("permute")
     dom = max((st for st in stages if st in single), key=lambda st: st_us[st])
@@ -1130,6 +1140,7 @@ def route_measure(args, name):
         "combine": ("combine_kernel (moe_combine)" if name == "foe"
                     else "combine_kernel (moe_combine_gather)"),
         "predict_route": "srs_route_kernel (srs_predict_route)",
+        "predict_route_dispatch": "srs_route_kernel (srs_predict_route_dispatch)",
         "srs_route": ("srs_route_kernel (srs_route_sorted)" if small_route
                       else "srs_gate160_kernel (srs_route_sorted)"),
         "permute": "permute_fused (moe_permute)",

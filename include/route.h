@@ -68,7 +68,9 @@ enum {
   ROUTE_EBIT_DEST_RANGE = 2u,    /* cluster id >= G                             */
   ROUTE_EBIT_EXPERT_RANGE = 4u,  /* expert id < 0 or >= E                       */
   ROUTE_EBIT_INDEX_RANGE = 8u,   /* slot / row / pair index out of range        */
-  ROUTE_EBIT_VALUE_RANGE = 16u   /* a count or placement entry out of its range */
+  ROUTE_EBIT_VALUE_RANGE = 16u,  /* a count or placement entry out of its range */
+  ROUTE_EBIT_SYNC = 32u          /* a workgroup gave up waiting at a grid       */
+                                 /* barrier (the grid was not resident at once) */
 };
 
 /* Readable name of a status code (host; static string). */
@@ -270,6 +272,47 @@ int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut, const u
                       uint8_t* row_cluster, uint16_t* out, float* logits, int32_t* idx,
                       float* weights, const uint8_t* expert_cluster, unsigned long long* local,
                       uint32_t* err, hipStream_t s);
+
+/*
+ * srs_predict_route_dispatch - srs_predict_route followed by moe_permute
+ * (one group) in one launch: [SMOE] section 4.1 (prediction), section 3.1
+ * and glossary (shuffled reduce, router, top-K, count), section 1 (dispatch
+ * of each token to its K experts). Each wave keeps its reduced row in
+ * registers; every workgroup publishes its pairs per (cluster, expert) and
+ * meets the others at a grid barrier, then writes its rows straight into
+ * their expert slots, so the shuffled rows are neither written (unless out
+ * is given) nor read back. Every output is the bytes srs_predict_route and
+ * then moe_permute (H = 1, src = the shuffled rows) would write.
+ *   tok .. local: as srs_predict_route, except out bf16 [n][d] nullable
+ *   and weights required; expert_offsets int32 [E+1], slot_of_pair and
+ *   pair_of_slot int32 [n*K] (pairs p = r*K + k over the shuffled rows r),
+ *   disp bf16 [n*K][d]: as moe_permute.
+ *   ws: srs_predict_route_dispatch_workspace_size(n, G, E) bytes, 256-byte
+ *   aligned; its first 4 bytes count the barrier's arrivals and must hold a
+ *   multiple of 256 (zero) before the first call with this ws. Every call
+ *   leaves them so: keep the workspace between calls, and do not overlap
+ *   two calls on one workspace.
+ * Errors: as srs_predict_route, plus NULL (expert_offsets, slot_of_pair,
+ * pair_of_slot, disp, weights), WORKSPACE (size or alignment), UNSUPPORTED
+ * where G*E > 256 or the grid (n/16 workgroups) cannot be resident on the
+ * device at once. Device bits: as srs_predict_route, plus SYNC if a
+ * workgroup gave up at the barrier (its rows are then not dispatched). With
+ * any bit set the dispatch outputs are unspecified.
+ */
+int srs_predict_route_dispatch(const int32_t* tok, int64_t n, const uint8_t* lut,
+                               const uint8_t* conf, int32_t vocab, const uint8_t* prev2,
+                               const uint8_t* prev1, const uint8_t* ngram, int32_t G,
+                               int32_t conf_thr, const uint16_t* partials, int32_t P, int32_t d,
+                               const uint16_t* w, int32_t E, int32_t K, int32_t renorm,
+                               uint8_t* dest, int32_t* cluster_offsets, int32_t* row_of_src,
+                               int32_t* src_of_row, uint8_t* row_cluster, uint16_t* out,
+                               float* logits, int32_t* idx, float* weights,
+                               const uint8_t* expert_cluster, unsigned long long* local,
+                               int32_t* expert_offsets, int32_t* slot_of_pair,
+                               int32_t* pair_of_slot, uint16_t* disp, void* ws, size_t ws_bytes,
+                               uint32_t* err, hipStream_t s);
+/* 0 where the shape is not taken. */
+size_t srs_predict_route_dispatch_workspace_size(int64_t n, int32_t G, int32_t E);
 
 /*
  * srs_route_grouped - the grouped MoE block's routing in one kernel: the

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 45, names
+    assert len(names) == 47, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -217,6 +217,38 @@ def test_predict_route_errors(L):
     assert call(args(idx=None)) == NULL
     assert call(args(ec=A)) == NULL             # the count needs both
     assert call(args(partials=MIS)) == ALIGN
+
+
+def test_predict_route_dispatch_errors(L):
+    f = L.srs_predict_route_dispatch
+    need = L.srs_predict_route_dispatch_workspace_size(1000, 4, 8)
+    assert need == 256 + 4 * 8 * 256 * 4          # the count, then [G*E][256] int32
+    assert L.srs_predict_route_dispatch_workspace_size(1000, 16, 32) == 0   # G*E > 256
+    assert L.srs_predict_route_dispatch_workspace_size(4097, 4, 8) == 0
+    args = lambda **k: dict(dict(tok=A, n=1000, lut=A, conf=None, vocab=5000, p2=None, p1=None,
+                                 ng=None, G=4, thr=128, partials=A, P=2, d=512, w=A, E=8, K=2,
+                                 renorm=1, dest=A, offs=A, ros=A, sor=A, rc=None, out=None,
+                                 logits=None, idx=A, weights=A, ec=None, local=None, eoff=A,
+                                 sop=A, pos=A, disp=A, ws=A, ws_bytes=need, err=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(vocab=0)) == SHAPE
+    assert call(args(K=9)) == SHAPE
+    assert call(args(n=4097)) == UNSUP
+    assert call(args(G=17)) == UNSUP
+    assert call(args(E=65)) == UNSUP
+    assert call(args(G=16, E=32)) == UNSUP      # more than 256 (cluster, expert) entries
+    assert call(args(eoff=None)) == NULL
+    assert call(args(offs=None)) == NULL
+    assert call(args(weights=None)) == NULL     # the combine's weights are part of the dispatch
+    assert call(args(sop=None)) == NULL
+    assert call(args(pos=None)) == NULL
+    assert call(args(disp=None)) == NULL
+    assert call(args(ec=A)) == NULL
+    assert call(args(disp=MIS)) == ALIGN
+    assert call(args(out=MIS)) == ALIGN
+    assert call(args(ws=None)) == WS
+    assert call(args(ws_bytes=need - 1)) == WS
+    assert call(args(ws=A + 16)) == WS          # 256-byte alignment
 
 
 def test_route_grouped_errors(L):

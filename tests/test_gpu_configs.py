@@ -66,7 +66,10 @@ def test_route_workload(name):
     assert np.array_equal(host(p.row_of_src), srs["row_of_src"])
     assert np.array_equal(host(p.cluster_offsets), srs["offsets"])
     assert np.array_equal(host(p.row_cluster), srs["row_cluster"])
-    assert np.array_equal(host(p.x), srs["out"])
+    if p.writes_x:
+        # (with the dispatch in the route kernel the shuffled rows are not
+        # written: every one of them reaches its K slots, checked below)
+        assert np.array_equal(host(p.x), srs["out"])
     x = srs["out"]
     # a3 gate, every row (float64 product of the oracle's rows)
     lg = host(p.logits)

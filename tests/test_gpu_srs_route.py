@@ -390,6 +390,133 @@ def test_predict_route_flags_like_two_calls(fallback):
         assert torch.equal(x[:valid], y[:valid])
 
 
+@pytest.mark.parametrize("V,shift,fallback", [(3000, 0, True), (3000, 5, False), (60000, 0, True),
+                                               (60000, 3, False), (49140, 11, True)])
+def test_predict_route_tables_staged_or_not(V, shift, fallback):
+    """The token table (and the confidence bytes) are read through LDS when
+    they fit (at most 48 KiB from their 16-byte aligned start) and from
+    global memory otherwise; tables at any byte alignment. Both ways, every
+    output equals the two calls' and the dispatch equals moe_permute's."""
+    n, d, P, G, E, K = 2500, 256, 2, 4, 8, 2
+    a = _predict_route_inputs(n, G, V, 11 + V + shift, fallback)
+    parts, _, w, ec = _inputs(n, d, P, G, E)
+    fb = {k: dev(a[k]) for k in ("prev2", "prev1", "ngram") if k in a}
+
+    def shifted(arr):
+        buf = torch.zeros(arr.size + 16, dtype=torch.uint8, device="cuda")
+        buf[shift:shift + arr.size] = dev(arr)
+        return buf[shift:shift + arr.size]
+    lut = shifted(a["lut"])
+    if fallback:
+        fb["conf"] = shifted(a["conf"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    got = tr.srs_predict_route(dev(a["tok"]), lut, G, dev(parts), dev(w), K, 1,
+                               expert_cluster=dev(ec), local=local, err=err, **fb)
+    ws = _dispatch_ws(n, G, E)
+    err3 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    local3 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    got3 = tr.srs_predict_route_dispatch(dev(a["tok"]), lut, G, dev(parts), dev(w), K, 1,
+                                         expert_cluster=dev(ec), local=local3, write_x=True,
+                                         ws=ws, err=err3, **fb)
+    want, local2, err2 = _two_calls(a, G, parts, w, K, ec)
+    perm = tr.moe_permute(want[7], E, want[5], 1)
+    sync()
+    assert int(err.item()) == int(err2.item()) == int(err3.item()) == 0
+    for x, y, z in zip(got, want, got3[:9]):
+        assert torch.equal(x, y) and torch.equal(z, y)
+    for x, y in zip(got3[9:], perm):
+        assert torch.equal(x, y)
+    assert int(local.item()) == int(local2.item()) == int(local3.item())
+
+
+def _dispatch_call(a, G, parts, w, K, ec, ws, renorm=1, write_x=True):
+    fb = {k: dev(a[k]) for k in ("conf", "prev2", "prev1", "ngram") if k in a}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    local = torch.zeros(1, dtype=torch.int64, device="cuda")
+    r = tr.srs_predict_route_dispatch(dev(a["tok"]), dev(a["lut"]), G, dev(parts), dev(w), K,
+                                      renorm, expert_cluster=None if ec is None else dev(ec),
+                                      local=None if ec is None else local, write_x=write_x,
+                                      ws=ws, err=err, **fb)
+    return r, local, err
+
+
+def _dispatch_ws(n, G, E):
+    return torch.zeros(tr.srs_predict_route_dispatch_workspace_size(n, G, E), dtype=torch.uint8,
+                       device="cuda")
+
+
+# (n, d, P, G, E, K, fallback): the predict-route cases within 256 (cluster,
+# expert) entries: one row (one workgroup, no wait at the barrier); a
+# partial workgroup; one and one-and-a-bit workgroups; the Mixtral-8x7B
+# shape (4096 rows: 256 workgroups, the most); 256 entries two ways; one
+# cluster; every P; E from 1 to 64; K up to 8 (streaming slot stores from 4)
+DISP_CASES = [(1, 128, 2, 2, 4, 2, False), (15, 256, 1, 3, 3, 1, True),
+              (16, 512, 2, 4, 8, 2, False), (17, 520, 4, 4, 16, 4, True),
+              (1000, 1024, 2, 8, 32, 8, True), (4096, 4096, 2, 4, 8, 2, False),
+              (3000, 256, 2, 4, 64, 6, True), (777, 384, 4, 1, 12, 3, False),
+              (2049, 128, 1, 8, 1, 1, True)]
+
+
+@pytest.mark.parametrize("n,d,P,G,E,K,fallback", DISP_CASES)
+def test_predict_route_dispatch_against_oracle_and_calls(n, d, P, G, E, K, fallback):
+    """srs_predict_route_dispatch writes the bytes of srs_predict_route and
+    then moe_permute on its rows and picks (every output, the count and the
+    error word), and those are the oracle's prediction, shuffle, gate,
+    top-K, count and dispatch."""
+    a = _predict_route_inputs(n, G, 3000, n + G + E, fallback)
+    parts, _, w, ec = _inputs(n, d, P, G, E)
+    ws = _dispatch_ws(n, G, E)
+    got, local, err = _dispatch_call(a, G, parts, w, K, ec, ws)
+    want, local2, err2 = _one_call(a, G, parts, w, K, ec)
+    perm = tr.moe_permute(want[7], E, want[5], 1)
+    sync()
+    for x, y in zip(got[:9], want):
+        assert torch.equal(x, y)
+    for x, y in zip(got[9:], perm):
+        assert torch.equal(x, y)
+    assert int(local.item()) == int(local2.item())
+    assert int(err.item()) == int(err2.item()) == 0
+    assert int(host(ws[:4].view(torch.int32))[0]) % 256 == 0
+    want_dest = oracle.route_predict(a["tok"], a["lut"], a.get("conf"), a.get("prev2"),
+                                     a.get("prev1"), a.get("ngram"), 128, G=G)
+    assert np.array_equal(host(got[0]), want_dest)
+    dest, offs, ros, sor, rc, out, lg, idx, wt = got[:9]
+    _check(parts, want_dest.astype(np.uint8), G, w, K, ec, 1,
+           (out, offs, ros, sor, rc, lg, idx, wt), local)
+    x = oracle.srs_shuffle(parts, want_dest.astype(np.int64), G)["out"]
+    ref = oracle.moe_permute(oracle.route_topk(host(lg), K, 1, 1)[0], E, 1, src=x[None])
+    eoff, sop, pos, disp = got[9:]
+    assert np.array_equal(host(eoff), ref["expert_offsets"])
+    assert np.array_equal(host(sop), ref["slot_of_pair"])
+    assert np.array_equal(host(pos), ref["pair_of_slot"])
+    assert np.array_equal(host(disp), ref["disp"])
+
+
+def test_predict_route_dispatch_calls_in_a_row():
+    """One workspace across calls of different grids (256, 7 and 1
+    workgroups, then 256 again), with and without the shuffled rows written:
+    every call's dispatch equals the separate calls', the error word stays
+    clear and the barrier count stays a multiple of 256."""
+    G, E, K, d, P = 4, 8, 2, 512, 2
+    ws = _dispatch_ws(4096, G, E)
+    for i, (n, write_x) in enumerate(((4096, True), (100, False), (9, True), (4096, False))):
+        a = _predict_route_inputs(n, G, 3000, 50 + i, i % 2 == 1)
+        parts, _, w, ec = _inputs(n, d, P, G, E)
+        got, local, err = _dispatch_call(a, G, parts, w, K, ec, ws, write_x=write_x)
+        want, local2, err2 = _one_call(a, G, parts, w, K, ec)
+        perm = tr.moe_permute(want[7], E, want[5], 1)
+        sync()
+        assert int(err.item()) == 0 and int(local.item()) == int(local2.item())
+        assert (got[5] is None) == (not write_x)
+        for j, (x, y) in enumerate(zip(got[:9], want)):
+            if x is not None:
+                assert torch.equal(x, y), j
+        for x, y in zip(got[9:], perm):
+            assert torch.equal(x, y)
+        assert int(host(ws[:4].view(torch.int32))[0]) == 256 * (i + 1)
+
+
 # (n, d, P, E, K, H, renorm, with_rows): the FoE grouping (64 experts in 4
 # groups, K = 8) on its partial count; two and eight groups; one group per
 # pick; one row; a ragged last tile; the full softmax (renorm = 0); 160

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "RouteError", "lib", "library_path",
     "route_predict", "route_predict_sort", "route_predict_sort_workspace_size", "route_lut_build",
-    "srs_shuffle", "srs_route_sorted", "srs_predict_route", "srs_route_grouped",
+    "srs_shuffle", "srs_route_sorted", "srs_predict_route", "srs_predict_route_dispatch",
+    "srs_predict_route_dispatch_workspace_size", "srs_route_grouped",
     "srs_shuffle_gate", "srs_shuffle_route", "route_gate", "route_topk",
     "lar_count", "moe_permute", "moe_permute_noalloc", "moe_combine", "moe_combine_gather", "route_qhidden",
     "route_estimator",
@@ -43,7 +44,7 @@ _LIB_PATH = os.environ.get("ROUTE_LIBRARY") or os.path.join(_HERE, "libroute.so"
 # status codes and device error bits (include/route.h)
 ROUTE_OK = 0
 EBIT_TOKEN_RANGE, EBIT_DEST_RANGE, EBIT_EXPERT_RANGE, EBIT_INDEX_RANGE = 1, 2, 4, 8
-EBIT_VALUE_RANGE = 16
+EBIT_VALUE_RANGE, EBIT_SYNC = 16, 32
 
 _p, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 _u64, _f64 = ctypes.c_uint64, ctypes.c_double
@@ -67,6 +68,11 @@ EXPORTS = {
     "srs_predict_route": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _i32,
                                          _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                                          _p, _p, _p, _p, _p, _p]),
+    "srs_predict_route_dispatch": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p, _p, _i32, _i32,
+                                                  _p, _i32, _i32, _p, _i32, _i32, _i32, _p, _p,
+                                                  _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                  _p, _p, _sz, _p, _p]),
+    "srs_predict_route_dispatch_workspace_size": (_sz, [_i64, _i32, _i32]),
     "srs_route_grouped": (ctypes.c_int, [_p, _i32, _i64, _i32, _p, _p, _i32, _p, _i32, _i32, _i32,
                                          _p, _p, _p, _p, _p, _p]),
     "srs_shuffle_workspace_size": (_sz, [_i64, _i32]),
@@ -391,6 +397,68 @@ def srs_predict_route(tok, lut, G, partials, w, K, renorm=1, conf=None, prev2=No
           _opt(expert_cluster, torch.uint8, "expert_cluster", E),
           _opt(local, torch.int64, "local", 1), _opt(err, torch.int32, "err", 1), _stream(stream))
     return dest, offsets, row_of_src, src_of_row, row_cluster, out, logits, idx, weights
+
+
+def srs_predict_route_dispatch_workspace_size(n, G, E):
+    return lib().srs_predict_route_dispatch_workspace_size(n, G, E)
+
+
+def srs_predict_route_dispatch(tok, lut, G, partials, w, K, renorm=1, conf=None, prev2=None,
+                               prev1=None, ngram=None, conf_thr=128, expert_cluster=None,
+                               local=None, dest=None, offsets=None, row_of_src=None,
+                               src_of_row=None, row_cluster=None, out=None, write_x=False,
+                               logits=None, idx=None, weights=None, with_logits=True,
+                               expert_offsets=None, slot_of_pair=None, pair_of_slot=None,
+                               disp=None, ws=None, err=None, stream=None):
+    """srs_predict_route + moe_permute (one group) in one launch: returns
+    (dest, offsets, row_of_src, src_of_row, row_cluster, out, logits, idx,
+    weights, expert_offsets, slot_of_pair, pair_of_slot, disp); out (the
+    shuffled rows) only when given or write_x. ws must start zeroed (a
+    fresh workspace is allocated zeroed) and is reused as it is left."""
+    P, n, d = partials.shape
+    E = w.shape[0]
+    bt = _bf16(partials)
+    e = lambda shape, dt: _empty(shape, dt, partials)
+    dest = e((n,), torch.uint8) if dest is None else dest
+    offsets = e((G + 1,), torch.int32) if offsets is None else offsets
+    row_of_src = e((n,), torch.int32) if row_of_src is None else row_of_src
+    src_of_row = e((n,), torch.int32) if src_of_row is None else src_of_row
+    row_cluster = e((n,), torch.uint8) if row_cluster is None else row_cluster
+    if out is None and write_x:
+        out = e((n, d), bt)
+    if with_logits and logits is None:
+        logits = e((n, E), torch.float32)
+    idx = e((n, K), torch.int32) if idx is None else idx
+    weights = e((n, K), torch.float32) if weights is None else weights
+    expert_offsets = e((E + 1,), torch.int32) if expert_offsets is None else expert_offsets
+    slot_of_pair = e((n * K,), torch.int32) if slot_of_pair is None else slot_of_pair
+    pair_of_slot = e((n * K,), torch.int32) if pair_of_slot is None else pair_of_slot
+    disp = e((n * K, d), bt) if disp is None else disp
+    if ws is None:
+        ws = torch.zeros((max(srs_predict_route_dispatch_workspace_size(n, G, E), 256),),
+                         dtype=torch.uint8, device=partials.device)
+    fb = conf is not None
+    _call("srs_predict_route_dispatch", _dev(tok, torch.int32, "tok", n), n,
+          _dev(lut, torch.uint8, "lut"), _opt(conf, torch.uint8, "conf"), lut.numel(),
+          _opt(prev2, torch.uint8, "prev2", n if fb else None),
+          _opt(prev1, torch.uint8, "prev1", n if fb else None),
+          _opt(ngram, torch.uint8, "ngram", G * G if fb else None), G, conf_thr,
+          _dev(partials, bt, "partials"), P, d, _dev(w, _bf16(w), "w", E * d), E, K, renorm,
+          _dev(dest, torch.uint8, "dest", n), _dev(offsets, torch.int32, "offsets", G + 1),
+          _dev(row_of_src, torch.int32, "row_of_src", n),
+          _dev(src_of_row, torch.int32, "src_of_row", n),
+          _opt(row_cluster, torch.uint8, "row_cluster", n), _opt(out, bt, "out", n * d),
+          _opt(logits, torch.float32, "logits", n * E), _dev(idx, torch.int32, "idx", n * K),
+          _dev(weights, torch.float32, "weights", n * K),
+          _opt(expert_cluster, torch.uint8, "expert_cluster", E),
+          _opt(local, torch.int64, "local", 1),
+          _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+          _dev(slot_of_pair, torch.int32, "slot_of_pair", n * K),
+          _dev(pair_of_slot, torch.int32, "pair_of_slot", n * K), _dev(disp, bt, "disp", n * K * d),
+          _dev(ws, torch.uint8, "ws"), ws.numel(), _opt(err, torch.int32, "err", 1),
+          _stream(stream))
+    return (dest, offsets, row_of_src, src_of_row, row_cluster, out, logits, idx, weights,
+            expert_offsets, slot_of_pair, pair_of_slot, disp)
 
 
 def srs_route_grouped(partials, w, K, H, renorm=1, row_cluster=None, expert_cluster=None,

@@ -25,6 +25,9 @@
 #include "srs.hpp"
 #include "topk.hpp"
 
+#include <mutex>
+#include <vector>
+
 namespace route {
 namespace {
 
@@ -94,6 +97,19 @@ constexpr int kPredOthers = 4;  // other tokens per lane: (4096 - 16) / 16 waves
 static_assert((kPredRouteMax - kRouteWaves + kRouteWaves - 1) / kRouteWaves <= kPredOthers * kWave,
               "one batch of others per wave");
 
+// The dispatch made in the route kernel (srs_predict_route_dispatch): the
+// rows go from registers to their expert slots after a grid barrier at which
+// every workgroup has published its pairs per (cluster, expert).
+struct DispOut {
+  unsigned* arrive;     // the barrier's arrival count (a multiple of 256 between calls),
+                        // then at +256 bytes [grid][G * E] each workgroup's pairs per
+                        // (cluster, expert)
+  int* expert_offsets;  // [E + 1]
+  int* slot_of_pair;    // [n * K]
+  int* pair_of_slot;    // [n * K]
+  uint16_t* disp;       // [n * K][d]
+};
+
 struct PredSort {
   PredictArgs a;          // the prediction's inputs and the error word
   uint8_t* dest;          // [n] predicted clusters (out)
@@ -101,7 +117,30 @@ struct PredSort {
   int* row_of_src;        // [n]
   int* src_of_row;        // [n]
   uint8_t* row_cluster;   // [n]
+  DispOut dp;             // with the dispatch (arrive non-null)
+  int tables;             // the token table (and confidence bytes) staged in LDS
 };
+
+// Tables staged in LDS by the prediction prologue: each at most this many
+// bytes (from its 16-byte aligned start), three 16-byte chunks per thread.
+constexpr int kTabChunks = 3;
+constexpr int kTabMaxBytes = kTabChunks * 1024 * 16;
+// dynamic LDS the router rows and the staged tables may take together
+constexpr int64_t kRouteTabLds = 144 * 1024;
+
+// bytes a table of `len` bytes at `p` takes when staged (whole 16-byte chunks)
+inline int tab_bytes(const void* p, int len) {
+  return static_cast<int>(((reinterpret_cast<uintptr_t>(p) & 15) + len + 15) & ~uintptr_t(15));
+}
+
+// Bounded wait at the grid barrier: this many sleeps of 8 x 64 cycles
+// (about half a second), after which the workgroup flags ROUTE_EBIT_SYNC
+// and skips the dispatch instead of waiting on.
+constexpr unsigned kBarrierSpins = 1u << 21;
+// the dispatch's LDS: per (cluster, expert) entry, the pairs before this
+// workgroup, in all, and the entry's first slot, for up to kDispMaxGE entries
+constexpr int kDispMaxGE = 256;
+constexpr size_t kDispLds = 3 * kDispMaxGE * sizeof(int);
 
 // A key source that never runs (the others' one batch is filled by hand).
 struct NoKeys {
@@ -113,13 +152,22 @@ struct NoKeys {
   }
 };
 
-template <int PT, int CPL, int EB, bool PRED>
+template <int PT, int CPL, int EB, bool PRED, bool DISP = false>
 __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
     const uint16_t* __restrict__ partials, int64_t n, int d, const int* __restrict__ row_of_src,
     const uint8_t* __restrict__ dest, uint16_t* __restrict__ out, const uint16_t* __restrict__ w,
     int E, int K, int renorm, RouteOut ro, SrsIdentity ident, PredSort ps) {
   static_assert(EB * CPL <= 64, "staged router rows fit in 64 KiB");
+  static_assert(PRED || !DISP, "the dispatch needs the workgroup-local order");
+  static_assert(kRouteWaves == 16, "the dispatch's table sums take 16 workgroups per wave");
   extern __shared__ __align__(16) char wl[];
+  __shared__ int ckey[kRouteWaves];  // with the prediction: the rows' clusters
+  // with the dispatch: this workgroup's pairs per (cluster, expert), counted
+  // as the rows are routed (cleared here, ahead of the prologue's barriers)
+  __shared__ int lcnt[DISP ? kDispMaxGE : 1];
+  if constexpr (DISP) {
+    for (int t = threadIdx.x; t < ps.a.G * E; t += kRouteThreads) lcnt[t] = 0;
+  }
   const int wv = wave_id();
   const int lane = lane_id();
   const int nv = d >> 3;  // 16-byte vectors per row
@@ -156,6 +204,43 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
     }
     sm = predict_stage1(ps.a, i_own < n ? i_own : 0);
   }
+  // The token table (and with the fallback the confidence bytes) staged in
+  // LDS after the router rows: each workgroup predicts every token, and as
+  // random byte gathers from global memory every lookup is its own cache
+  // line miss, which the CU serves a few hundred at a time. Staged, the
+  // table is read as whole 16-byte chunks from its aligned start (entry t
+  // at byte (table % 16) + t; a chunk never crosses a page).
+  uint8_t* const ltab = reinterpret_cast<uint8_t*>(wl) + kPieces * 16;
+  __shared__ uint8_t lng[PRED ? kPredRouteMaxG * kPredRouteMaxG : 1];  // the 2-gram table
+  int lpre = 0, cpre = 0, lch = 0, cch = 0;
+  u32x4 tl[kTabChunks], tcf[kTabChunks];
+  int ngv = 0;
+  if constexpr (PRED) {
+    if (ps.tables) {
+      const int gg = ps.a.G * ps.a.G;
+      if (ps.a.conf && static_cast<int>(threadIdx.x) < gg) ngv = ps.a.ngram[threadIdx.x];
+      const uintptr_t la = reinterpret_cast<uintptr_t>(ps.a.lut);
+      lpre = static_cast<int>(la & 15);
+      lch = (lpre + ps.a.vocab + 15) >> 4;
+      const u32x4* lsrc = reinterpret_cast<const u32x4*>(la - lpre);
+#pragma unroll
+      for (int r = 0; r < kTabChunks; ++r) {
+        const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+        tl[r] = lsrc[q < lch ? q : lch - 1];
+      }
+      if (ps.a.conf) {
+        const uintptr_t ca = reinterpret_cast<uintptr_t>(ps.a.conf);
+        cpre = static_cast<int>(ca & 15);
+        cch = (cpre + ps.a.vocab + 15) >> 4;
+        const u32x4* csrc = reinterpret_cast<const u32x4*>(ca - cpre);
+#pragma unroll
+        for (int r = 0; r < kTabChunks; ++r) {
+          const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+          tcf[r] = csrc[q < cch ? q : cch - 1];
+        }
+      }
+    }
+  }
   u32x4 wst[kStage];
 #pragma unroll
   for (int r = 0; r < kStage; ++r) {
@@ -168,6 +253,8 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   // one row, so vectors past the row end read as zeros without a per-vector
   // address. Issued vector by vector (every partial of vector c, then c + 1),
   // so the work on vector c waits only for its own loads.
+  // (with the dispatch, x[0][c] keeps the reduced vector c to the end: the
+  // row stays in the registers its loads landed in)
   u32x4 x[PT][CPL];
   // (valid false: an empty descriptor, every vector reads as zeros and no
   // memory is touched)
@@ -196,23 +283,66 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteWaves + wv;
   int cl = 0;
   if constexpr (PRED) {
+    if (ps.tables) {
+      // Every load so far has landed and the rows are not out yet: the
+      // tables and the router rows into LDS, then, past the barrier, the
+      // lookups from there with no global load at all, so that no wave's
+      // prediction waits in the CU's memory pipeline behind another wave's
+      // rows.
+      compiler_fence();
+      wait_vmcnt<0>();
+      compiler_fence();
 #pragma unroll
-    for (int q = 0; q < kPredOthers; ++q) predict_stage2(quiet, so[q]);
-    predict_stage2(ps.a, sm);
+      for (int r = 0; r < kTabChunks; ++r) {
+        const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+        if (q < lch) *reinterpret_cast<u32x4*>(ltab + 16 * q) = tl[r];
+        if (q < cch) *reinterpret_cast<u32x4*>(ltab + 16 * (lch + q)) = tcf[r];
+      }
+      if (ps.a.conf && static_cast<int>(threadIdx.x) < ps.a.G * ps.a.G)
+        lng[threadIdx.x] = static_cast<uint8_t>(ngv);
+#pragma unroll
+      for (int r = 0; r < kStage; ++r) {
+        const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+        if (q < kPieces) *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = wst[r];
+      }
+      lds_barrier();
+      const int G = ps.a.G;
+      auto stage2_lds = [&](PredictLoads& s) {
+        const bool fb = ps.a.conf != nullptr;
+        const int tc = (s.t >= 0 && s.t < ps.a.vocab) ? s.t : 0;
+        s.c = ltab[lpre + tc];
+        s.cf = fb ? ltab[16 * lch + cpre + tc] : 0;
+        s.g = fb ? lng[(s.p2 < G && s.p1 < G) ? s.p2 * G + s.p1 : 0] : 0;
+      };
+#pragma unroll
+      for (int q = 0; q < kPredOthers; ++q) stage2_lds(so[q]);
+      stage2_lds(sm);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPredOthers; ++q) predict_stage2(quiet, so[q]);
+      predict_stage2(ps.a, sm);
+    }
   } else {
     cl = dest ? static_cast<int>(dest[i < n ? i : n - 1]) : 0;
   }
-  load_row(i, i < n);
+  // With the staged tables the prediction reads only LDS, so the rows go out
+  // after it: a wave's row loads stall at issue until the CU's memory
+  // pipeline takes them (waves issue oldest first), and a prediction behind
+  // them would wait for other waves' rows.
+  bool staged = false;  // the router rows already in LDS (with the staged tables)
+  if constexpr (PRED) staged = ps.tables != 0;
+  if (!staged) load_row(i, i < n);
+  if (!staged) {
 #pragma unroll
-  for (int r = 0; r < kStage; ++r) {
-    const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
-    if (q < kPieces) *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = wst[r];
+    for (int r = 0; r < kStage; ++r) {
+      const int q = static_cast<int>(threadIdx.x) + r * kRouteThreads;
+      if (q < kPieces) *reinterpret_cast<u32x4*>(wl + 16 * static_cast<size_t>(q)) = wst[r];
+    }
   }
   int pdst = -1;  // with the prediction: this wave's row's sorted position
   if constexpr (PRED) {
     __shared__ int orow[kRouteWaves * kPredRouteMaxG];  // others before the rows, per wave
     __shared__ int prow[kRouteWaves * kPredRouteMaxG];  // and after them
-    __shared__ int ckey[kRouteWaves];                   // the rows' clusters
     __shared__ int stot[kPredRouteMaxG];
     __shared__ int sbase[kPredRouteMaxG];
     __shared__ int stotal;
@@ -269,11 +399,19 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
     }
     cl = c_own;
   }
-  lds_barrier();
+  // (staged: the router rows were in LDS before the prediction's barriers,
+  // so each wave goes on to its row as soon as its loads are out)
+  if (staged) load_row(i, i < n);
+  else lds_barrier();
 
   // lane e < E stands for expert e in the top-K and the count
   const int my_ec = (ro.expert_cluster && lane < E) ? static_cast<int>(ro.expert_cluster[lane]) : -1;
   unsigned lar = 0;
+  // with the dispatch: this lane's pick and its rank, and the wave's picks
+  // as a mask over the experts
+  bool dpick = false;
+  int drank = 0, ddst = -1;
+  unsigned long long dpm = 0;
 
   for (; i < n; i += stride) {
     int dst;
@@ -285,9 +423,10 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
     // The row's store through a descriptor spanning the destination row
     // (vectors past its end are dropped; for a row without a destination the
     // descriptor is empty and drops them all).
+    const bool xst = keep && out != nullptr;  // out null (dispatch only): X is not written
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-        out + (keep ? static_cast<size_t>(dst) * d : 0), static_cast<short>(0), keep ? d * 2 : 0,
-        0x00020000);
+        xst ? out + static_cast<size_t>(dst) * d : const_cast<uint16_t*>(partials),
+        static_cast<short>(0), xst ? d * 2 : 0, 0x00020000);
     // Vector by vector, as its loads land: reduce, round, store, and add its
     // products with every staged router row (binary32 dot products of exact
     // bf16 pairs) into one accumulator per expert. The work runs in steps of
@@ -331,6 +470,7 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
         }
         xb = pack8_cvt(f);
         __builtin_amdgcn_raw_buffer_store_b128(xb, ors, lane * 16, c * kWave * 16, 0);
+        if constexpr (DISP) x[0][c] = xb;
       }
       if (st + 1 < kSteps) read_step(st + 1, wr[(st + 1) & 1]);
 #pragma unroll
@@ -370,10 +510,180 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
       }
       if (ro.expert_cluster) lar += __popcll(__ballot(pick && my_ec == cl));
     }
-    if (lane == 0) write_identity_row(ident, i, n);
+    if constexpr (DISP) {
+      dpick = pick;
+      drank = rank;
+      ddst = dst;
+      dpm = __ballot(pick);
+      if (pick) atomicAdd(&lcnt[lane * ps.a.G + cl], 1);  // entry (expert, cluster)
+    }
+    if constexpr (!PRED) {
+      if (lane == 0) write_identity_row(ident, i, n);
+    }
     if (!PRED && i + stride < n) {
       cl = dest ? static_cast<int>(dest[i + stride]) : 0;
       load_row(i + stride, true);
+    }
+  }
+
+  if constexpr (DISP) {
+    // The dispatch ("Speculative MoE" section 1; the pair order of
+    // moe_permute). Pair (X row r, rank k) with expert e goes to slot: the
+    // pairs of experts before e, plus those of expert e in X rows before r.
+    // X holds the clusters in order, each cluster's rows in source order, and
+    // workgroup b's rows are sources 16 b .. 16 b + 15, so over the entries
+    // u = e G + c (expert-major) the slot is: the pairs of all entries before
+    // u, those of entry u in workgroups before b, and those of entry u in
+    // this workgroup's earlier waves. Each workgroup publishes its pairs per
+    // entry, meets every other at a grid barrier, then sums the table itself.
+    __shared__ unsigned long long pmask[kRouteWaves];
+    __shared__ int sflag;
+    const int G = ps.a.G, GE = G * E;
+    const int nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    if (lane == 0) pmask[wv] = dpm;
+    __syncthreads();  // (also: every wave is done with the router rows)
+    // The table is entry-major (entry u of workgroup b' at u * 256 + b'),
+    // written and read with agent-scope atomic accesses, which are coherent
+    // across the XCDs' L2s without a cache write-back or invalidation.
+    int* const table = reinterpret_cast<int*>(ps.dp.arrive) + 64;
+    // The grid barrier. Wave 0 publishes the workgroup's counts and waits
+    // until they have completed; its lane 0 then adds one arrival (workgroup
+    // 0 adds 257 - grid, so one call adds 256 in all and the count, a
+    // multiple of 256 before the call, moves from base to base + 256) and
+    // waits for the last one. The host launches this kernel only where the
+    // whole grid is resident at once.
+    if (wv == 0) {
+      for (int u = lane; u < GE; u += kWave)
+        __hip_atomic_store(&table[u * kRouteMaxGrid + b], lcnt[u], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      compiler_fence();
+      wait_vmcnt<0>();
+      compiler_fence();
+      if (lane == 0) {
+        const unsigned inc = b == 0 ? 257u - static_cast<unsigned>(nb) : 1u;
+        const unsigned old = __hip_atomic_fetch_add(ps.dp.arrive, inc, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned base = old & ~255u;
+        int ok = 1;
+        for (unsigned it = 0;; ++it) {
+          const unsigned now =
+              __hip_atomic_load(ps.dp.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (now - base >= 256u) break;
+          if (it >= kBarrierSpins) {
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        sflag = ok;
+      }
+    }
+    __syncthreads();
+    if (!sflag) {
+      if (threadIdx.x == 0) set_err(ps.a.err, ROUTE_EBIT_SYNC);
+    } else {
+      int* const spre = reinterpret_cast<int*>(wl);  // [GE] pairs in earlier workgroups
+      int* const stot = spre + GE;                   // [GE] pairs in all
+      int* const sbase = stot + GE;                  // [GE] first slot of the entry here
+      // wave w sums entries w, w + 16, ... (four at a time); lane l reads
+      // workgroups l, l + 64, l + 128, l + 192
+      for (int u0 = wv; u0 < GE; u0 += 4 * kRouteWaves) {
+        int v[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = u0 + q * kRouteWaves;
+          const int uc = u < GE ? u : GE - 1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[q][j] = __hip_atomic_load(&table[uc * kRouteMaxGrid + lane + kWave * j],
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = u0 + q * kRouteWaves;
+          int pre = 0, tot = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int bb = lane + kWave * j;
+            tot += bb < nb ? v[q][j] : 0;
+            pre += bb < b ? v[q][j] : 0;
+          }
+          tot = wave_sum_dpp(tot);
+          pre = wave_sum_dpp(pre);
+          if (u < GE && lane == 0) {
+            spre[u] = pre;
+            stot[u] = tot;
+          }
+        }
+      }
+      __syncthreads();
+      // wave 0: exclusive scan of the entry totals (lane l holds entries
+      // 4 l .. 4 l + 3); expert e's offset is the scan at entry e G
+      if (wv == 0) {
+        int s[4], run = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int u = 4 * lane + j;
+          s[j] = run;
+          run += u < GE ? stot[u] : 0;
+        }
+        int incl = run;  // inclusive scan of the lane sums
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_up(incl, o, kWave);
+          incl += lane >= o ? y : 0;
+        }
+        const int before = incl - run;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int u = 4 * lane + j;
+          if (u < GE) {
+            sbase[u] = before + s[j] + spre[u];
+            if (b == 0 && u % G == 0) ps.dp.expert_offsets[u / G] = before + s[j];
+          }
+        }
+        if (b == 0 && lane == kWave - 1) ps.dp.expert_offsets[E] = incl;
+      }
+      __syncthreads();
+      if (ddst >= 0) {
+        // this lane's pair: its slot, the maps, then the row into each slot
+        // (a slot past the pairs, possible only with a broken table, is
+        // flagged and not written)
+        const int64_t npairs = n * K;
+        int slot = 0;
+        bool sok = false;
+        if (dpick) {
+          int before = 0;
+          for (int v2 = 0; v2 < wv; ++v2)
+            before += (ckey[v2] == cl && ((pmask[v2] >> lane) & 1ull)) ? 1 : 0;
+          slot = sbase[lane * G + cl] + before;
+          sok = slot >= 0 && slot < npairs;
+          const int pair = ddst * K + drank;
+          if (sok) {
+            ps.dp.slot_of_pair[pair] = slot;
+            ps.dp.pair_of_slot[slot] = pair;
+          } else {
+            set_err(ps.a.err, ROUTE_EBIT_INDEX_RANGE);
+          }
+        }
+        for (int k = 0; k < K; ++k) {
+          const unsigned long long m = __ballot(dpick && sok && drank == k);
+          if (!m) continue;
+          const int sl = __builtin_amdgcn_readlane(slot, __builtin_ctzll(m));
+          const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+              ps.dp.disp + static_cast<size_t>(sl) * d, static_cast<short>(0), d * 2, 0x00020000);
+          // streaming stores from four copies per row up (moe_permute's policy)
+          if (K >= 4) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              __builtin_amdgcn_raw_buffer_store_b128(x[0][c], drs, lane * 16, c * kWave * 16, 2);
+          } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              __builtin_amdgcn_raw_buffer_store_b128(x[0][c], drs, lane * 16, c * kWave * 16, 0);
+          }
+        }
+      }
     }
   }
 
@@ -397,6 +707,31 @@ int route_cpl(int nv) {
   return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
 }
 
+// Whether `grid` workgroups of kRouteThreads with `lds` bytes of dynamic LDS
+// are resident on the current device at once (workgroups per CU from the
+// occupancy query times the CUs), cached per kernel, LDS size and device.
+bool grid_resident(const void* kern, unsigned grid, size_t lds) {
+  struct Entry {
+    const void* kern;
+    size_t lds;
+    int dev;
+    int64_t fits;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.kern == kern && e.lds == lds && e.dev == dev) return grid <= e.fits;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kRouteThreads, lds) != hipSuccess)
+    return false;
+  cache.push_back(Entry{kern, lds, dev, static_cast<int64_t>(cus) * per});
+  return grid <= static_cast<int64_t>(cus) * per;
+}
+
 // the smallest expert bound (8, 16, 32, 64) holding E
 int route_eb(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
 
@@ -408,10 +743,17 @@ bool launch_one(unsigned grid, size_t lds, hipStream_t s, const uint16_t* partia
   if constexpr (EB * CPL > 64 || (PT == 4 && CPL == 8)) {
     return false;  // beyond the staged rows' 64 KiB, or the registers
   } else {
-    if (ps)
+    if (ps && ps->dp.arrive) {
+      // the grid barrier needs every workgroup resident at once
+      auto* kern = &srs_route_kernel<PT, CPL, EB, true, true>;
+      const size_t dl = lds > kDispLds ? lds : kDispLds;
+      if (!grid_resident(reinterpret_cast<const void*>(kern), grid, dl)) return false;
+      kern<<<grid, kRouteThreads, dl, s>>>(partials, n, d, fwd, dest, out, w, E, K, renorm, ro,
+                                           ident, *ps);
+    } else if (ps) {
       srs_route_kernel<PT, CPL, EB, true><<<grid, kRouteThreads, lds, s>>>(
           partials, n, d, fwd, dest, out, w, E, K, renorm, ro, ident, *ps);
-    else
+    } else
       srs_route_kernel<PT, CPL, EB, false><<<grid, kRouteThreads, lds, s>>>(
           partials, n, d, fwd, dest, out, w, E, K, renorm, ro, ident, PredSort{});
     return true;
@@ -488,10 +830,24 @@ static int route_rows(const uint16_t* partials, int P, int64_t n, int d, const i
     return srs_gate_launch(partials, P, n, d, fwd, out, w, E, logits, ident, &tk, s);
   }
   const RouteOut ro{logits, idx, weights, expert_cluster, local};
+  PredSort pst{};
+  if (ps) {
+    // with the prediction: stage the token table (and the confidence bytes)
+    // in LDS where they fit beside the router rows
+    pst = *ps;
+    const int tb = tab_bytes(ps->a.lut, ps->a.vocab);
+    const int cb = ps->a.conf ? tab_bytes(ps->a.conf, ps->a.vocab) : 0;
+    pst.tables = tb <= kTabMaxBytes && cb <= kTabMaxBytes &&
+                 route_lds(d, E) + tb + cb <= kRouteTabLds;
+    ps = &pst;
+  }
   const int64_t need = (n + kRouteWaves - 1) / kRouteWaves;
   const unsigned grid = static_cast<unsigned>(need < kRouteMaxGrid ? need : kRouteMaxGrid);
   // the padded router rows (room for the per-wave counts at the end too)
   size_t lds = static_cast<size_t>(route_lds(d, E));
+  if (ps && ps->tables)
+    lds += tab_bytes(ps->a.lut, ps->a.vocab) +
+           (ps->a.conf ? tab_bytes(ps->a.conf, ps->a.vocab) : 0);
   if (lds < kRouteWaves * sizeof(unsigned)) lds = kRouteWaves * sizeof(unsigned);
   const int cpl = route_cpl(d / 8);
   const int eb = route_eb(E);
@@ -607,6 +963,56 @@ ROUTE_API int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lu
   const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
   return route_rows(partials, P, n, d, nullptr, dest, out, w, E, logits, K, renorm, idx, weights,
                     expert_cluster, local, none, s, &ps);
+}
+
+// the dispatch's workspace: the barrier count, then the count table
+static size_t disp_ws(int G, int E) {
+  return 256 + static_cast<size_t>(G) * E * kRouteMaxGrid * sizeof(int);
+}
+
+ROUTE_API int srs_predict_route_dispatch(
+    const int32_t* tok, int64_t n, const uint8_t* lut, const uint8_t* conf, int32_t vocab,
+    const uint8_t* prev2, const uint8_t* prev1, const uint8_t* ngram, int32_t G,
+    int32_t conf_thr, const uint16_t* partials, int32_t P, int32_t d, const uint16_t* w,
+    int32_t E, int32_t K, int32_t renorm, uint8_t* dest, int32_t* cluster_offsets,
+    int32_t* row_of_src, int32_t* src_of_row, uint8_t* row_cluster, uint16_t* out,
+    float* logits, int32_t* idx, float* weights, const uint8_t* expert_cluster,
+    unsigned long long* local, int32_t* expert_offsets, int32_t* slot_of_pair,
+    int32_t* pair_of_slot, uint16_t* disp, void* ws, size_t ws_bytes, uint32_t* err,
+    hipStream_t s) {
+  if (vocab < 1 || G < 1) return ROUTE_ERR_SHAPE;
+  const int chk = route_shape(P, n, d, E, K);
+  if (chk != ROUTE_OK) return chk;
+  if (n > kPredRouteMax || G > kPredRouteMaxG || !route_fits(P, d, E) || G * E > kDispMaxGE)
+    return ROUTE_ERR_UNSUPPORTED;
+  if (!cluster_offsets || !expert_offsets) return ROUTE_ERR_NULL;
+  if (n == 0) {
+    fill_i32<<<ceil_div(G + 1, 256), 256, 0, s>>>(cluster_offsets, G + 1, 0);
+    fill_i32<<<ceil_div(E + 1, 256), 256, 0, s>>>(expert_offsets, E + 1, 0);
+    return launch_status();
+  }
+  if (!tok || !lut || !dest || !row_of_src || !src_of_row) return ROUTE_ERR_NULL;
+  if (conf && (!prev2 || !prev1 || !ngram)) return ROUTE_ERR_NULL;
+  if (!partials || !w || !idx || !weights || !slot_of_pair || !pair_of_slot || !disp)
+    return ROUTE_ERR_NULL;
+  if ((expert_cluster == nullptr) != (local == nullptr)) return ROUTE_ERR_NULL;
+  if (!aligned16(partials) || !aligned16(w) || !aligned16(disp) || (out && !aligned16(out)))
+    return ROUTE_ERR_ALIGN;
+  if (!ws || ws_bytes < disp_ws(G, E) || reinterpret_cast<uintptr_t>(ws) % 256)
+    return ROUTE_ERR_WORKSPACE;
+  char* wsp = static_cast<char*>(ws);
+  const DispOut dp{reinterpret_cast<unsigned*>(wsp), expert_offsets, slot_of_pair, pair_of_slot,
+                   disp};
+  const PredSort ps{PredictArgs{tok, lut, conf, vocab, prev2, prev1, ngram, G, conf_thr, err},
+                    dest, cluster_offsets, row_of_src, src_of_row, row_cluster, dp};
+  const SrsIdentity none{nullptr, nullptr, nullptr, nullptr};
+  return route_rows(partials, P, n, d, nullptr, dest, out, w, E, logits, K, renorm, idx, weights,
+                    expert_cluster, local, none, s, &ps);
+}
+
+ROUTE_API size_t srs_predict_route_dispatch_workspace_size(int64_t n, int32_t G, int32_t E) {
+  if (n < 0 || n > kPredRouteMax || G < 1 || E < 1 || G * E > kDispMaxGE) return 0;
+  return disp_ws(G, E);
 }
 
 ROUTE_API int srs_route_grouped(const uint16_t* partials, int32_t P, int64_t n, int32_t d,

@@ -6,7 +6,10 @@ s-MoE layer of the "Speculative MoE" notes (section 3.1 and Figure 3's online
 path) on one GPU. Where the shapes allow, prediction is folded into the
 cluster sort (``predict_sort``) and the SRS, gate, top-K and LAR stages are
 one kernel after it (``srs_route``); for small batches all of these are one
-kernel (``predict_route``).
+kernel (``predict_route``), which can also dispatch the rows to their
+expert slots where the (cluster, expert) table is small
+(``dispatch_in_route=True``: ``predict_route_dispatch``, the shuffled rows
+are then not written).
 
 ``FoEPass``: cross-group reduce of the H group activations -> gate ->
 grouped top-k/H -> LAR (one kernel, ``route``) -> permute from the group
@@ -36,6 +39,7 @@ import torch
 
 from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
                srs_shuffle_route, srs_route_sorted, srs_predict_route, srs_route_grouped,
+               srs_predict_route_dispatch, srs_predict_route_dispatch_workspace_size,
                route_gate, route_topk, lar_count,
                moe_permute, moe_combine, route_qhidden, route_estimator, hit_count,
                srs_shuffle_workspace_size, moe_permute_workspace_size,
@@ -74,6 +78,13 @@ def predict_route_takes(n: int, P: int, d: int, E: int, K: int, G: int) -> bool:
     """The shapes srs_predict_route takes: at most 4096 tokens and 16
     clusters, on the small-set route kernel (srs_route_fits)."""
     return 0 < n <= 4096 and 1 <= G <= 16 and srs_route_fits(P, d, E, K)
+
+
+def predict_route_dispatch_takes(n: int, P: int, d: int, E: int, K: int, G: int) -> bool:
+    """The shapes srs_predict_route_dispatch takes on the host's checks:
+    those of srs_predict_route with at most 256 (cluster, expert) entries
+    (the launch also needs its n/16 workgroups resident at once)."""
+    return predict_route_takes(n, P, d, E, K, G) and G * E <= 256
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -123,7 +134,8 @@ def build_tables_device(inp: dict, device="cuda"):
 
 
 class RoutePass:
-    def __init__(self, inp: dict, lut=None, conf=None, device="cuda", out_dtype=torch.bfloat16):
+    def __init__(self, inp: dict, lut=None, conf=None, device="cuda", out_dtype=torch.bfloat16,
+                 dispatch_in_route=False):
         self.N, self.d, self.E, self.K = inp["N"], inp["d"], inp["E"], inp["K"]
         self.P, self.G = inp["P"], inp["G"]
         N, d, E, K, P, G = self.N, self.d, self.E, self.K, self.P, self.G
@@ -172,6 +184,17 @@ class RoutePass:
         # the route kernel (srs_predict_route), one launch for both
         if predict_route_takes(N, P, d, E, K, G):
             self.STAGES = ("predict_route", "permute", "combine")
+        # optionally the dispatch in the same kernel too
+        # (srs_predict_route_dispatch): the shuffled rows go from registers
+        # to their expert slots across a grid barrier, so x is not written.
+        # Not the default: on MI355X the barrier's cross-XCD round trips cost
+        # about what the rows' write and re-read save at these sizes.
+        self.writes_x = True
+        if dispatch_in_route and predict_route_dispatch_takes(N, P, d, E, K, G):
+            self.STAGES = ("predict_route_dispatch", "combine")
+            self.writes_x = False
+            self.ws_disp = torch.zeros((srs_predict_route_dispatch_workspace_size(N, G, E),),
+                                       dtype=torch.uint8, device=dev)
 
     def predict(self):
         if self.fallback:
@@ -210,6 +233,17 @@ class RoutePass:
                           src_of_row=self.src_of_row, row_cluster=self.row_cluster, out=self.x,
                           logits=self.logits, idx=self.idx, weights=self.weights, err=self.err,
                           **fb)
+
+    def predict_route_dispatch(self):
+        fb = dict(conf=self.conf, prev2=self.prev2, prev1=self.prev1, ngram=self.ngram,
+                  conf_thr=self.conf_thr) if self.fallback else {}
+        srs_predict_route_dispatch(
+            self.tok, self.lut, self.G, self.partials, self.w, self.K, 1,
+            expert_cluster=self.expert_cluster, local=self.local, dest=self.dest,
+            offsets=self.cluster_offsets, row_of_src=self.row_of_src, src_of_row=self.src_of_row,
+            row_cluster=self.row_cluster, logits=self.logits, idx=self.idx, weights=self.weights,
+            expert_offsets=self.expert_offsets, slot_of_pair=self.slot_of_pair,
+            pair_of_slot=self.pair_of_slot, disp=self.disp, ws=self.ws_disp, err=self.err, **fb)
 
     def topk(self):
         route_topk(self.logits, self.K, 1, 1, idx=self.idx, weights=self.weights)
