@@ -18,6 +18,18 @@
 // by each staged router row with v_dot2_f32_bf16 (binary32 accumulation of
 // exact bf16 products) and summed over the wave; lane e keeps expert e's
 // logit, so the top-K ranks one expert per lane on wave-uniform values.
+//
+// Two further modes of the same kernel, for at most 4096 tokens (one row per
+// wave, sixteen consecutive tokens per workgroup):
+//  - PRED (srs_predict_route): the route prediction ("Speculative MoE"
+//    section 4.1) and the shuffle's order are made inside the kernel. Each
+//    workgroup predicts and counts every token itself, from the token table
+//    staged in its LDS where it fits, and places its own rows without a
+//    separate sort.
+//  - DISP (srs_predict_route_dispatch): each reduced row also goes straight
+//    into its K expert slots (the dispatch, section 1), after a bounded grid
+//    barrier at which every workgroup has published its pairs per (expert,
+//    cluster).
 #include "common.hpp"
 #include "csort.hpp"
 #include "mfma.hpp"
@@ -178,14 +190,17 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   // value without a guard: piece q (16 bytes) at byte 16 q. The pieces are
   // loaded into registers here and written to LDS once the first row's loads
   // are out too; only these older loads are waited for before the barrier.
+  // (With the prediction's staged tables they go to LDS with the tables,
+  // before the rows are issued.)
   constexpr int kRowV = CPL * kWave;  // vectors per staged router row
   constexpr int kPieces = EB * kRowV;
   constexpr int kStage = (kPieces + kRouteThreads - 1) / kRouteThreads;
 
   // With the prediction: the first loads of every token this wave predicts
   // (its own row's, and its share of the tokens outside the workgroup's
-  // sixteen), then the router staging, then the tables' entries; the rows
-  // go out after those, so waiting for the predictions never waits for them.
+  // sixteen), then the router staging, then the tables' entries (or the
+  // whole tables, staged); the rows go out after those, so waiting for the
+  // predictions never waits for them.
   const int64_t clo = static_cast<int64_t>(blockIdx.x) * kRouteWaves;
   const int64_t chi = clo + kRouteWaves < n ? clo + kRouteWaves : n;
   const int64_t i_own = clo + wv;
@@ -274,7 +289,8 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
   };
   // The first row's loads go out behind the staging loads, which retire
   // first (loads count down in issue order): the row's first vectors can be
-  // reduced and stored while its later ones are in flight.
+  // reduced and stored while its later ones are in flight. (With the staged
+  // tables the rows go out after the whole prediction; see below.)
   // A row's predicted cluster is loaded just before the row itself, so no
   // later load stands between the row and its first use. Both loads are
   // issued by every wave (a wave without a row reads zeros and a valid
