@@ -291,7 +291,9 @@ int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut, const u
  *   aligned; its first 4 bytes count the barrier's arrivals and must hold a
  *   multiple of 256 (zero) before the first call with this ws. Every call
  *   leaves them so: keep the workspace between calls, and do not overlap
- *   two calls on one workspace.
+ *   two calls on one workspace. Its next 4 bytes bound each workgroup's wait
+ *   at the barrier in polls (0, as zero-filled: the default, about half a
+ *   second); a workgroup that waits that long flags SYNC.
  * Errors: as srs_predict_route, plus NULL (expert_offsets, slot_of_pair,
  * pair_of_slot, disp, weights), WORKSPACE (size or alignment), UNSUPPORTED
  * where G*E > 256 or the grid (n/16 workgroups) cannot be resident on the

@@ -517,6 +517,35 @@ def test_predict_route_dispatch_calls_in_a_row():
         assert int(host(ws[:4].view(torch.int32))[0]) == 256 * (i + 1)
 
 
+def test_predict_route_dispatch_barrier_timeout_flags_sync():
+    """The barrier's bounded wait, forced from the host through the
+    workspace's bound word. With a bound of one poll, the workgroups that
+    arrive first give up, flag SYNC and skip their dispatch, and every
+    kernel still ends. The routing outputs, made before the barrier, are
+    whole. The arrival count stays a multiple of 256, and the next call
+    with the default bound is whole again."""
+    n, d, P, G, E, K = 4096, 512, 2, 4, 8, 2
+    a = _predict_route_inputs(n, G, 3000, 5, False)
+    parts, _, w, ec = _inputs(n, d, P, G, E)
+    ws = _dispatch_ws(n, G, E)
+    ws[4:8].view(torch.int32).fill_(1)
+    got, local, err = _dispatch_call(a, G, parts, w, K, ec, ws)
+    want, local2, err2 = _one_call(a, G, parts, w, K, ec)
+    sync()
+    assert int(err.item()) == tr.EBIT_SYNC and int(err2.item()) == 0
+    assert int(host(ws[:4].view(torch.int32))[0]) % 256 == 0
+    for x, y in zip(got[:9], want):
+        assert torch.equal(x, y)
+    assert int(local.item()) == int(local2.item())
+    ws[4:8].view(torch.int32).fill_(0)
+    got2, _, err3 = _dispatch_call(a, G, parts, w, K, ec, ws)
+    perm = tr.moe_permute(want[7], E, want[5], 1)
+    sync()
+    assert int(err3.item()) == 0
+    for x, y in zip(got2[9:], perm):
+        assert torch.equal(x, y)
+
+
 # (n, d, P, E, K, H, renorm, with_rows): the FoE grouping (64 experts in 4
 # groups, K = 8) on its partial count; two and eight groups; one group per
 # pick; one row; a ragged last tile; the full softmax (renorm = 0); 160

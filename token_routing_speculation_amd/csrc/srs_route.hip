@@ -145,10 +145,12 @@ inline int tab_bytes(const void* p, int len) {
   return static_cast<int>(((reinterpret_cast<uintptr_t>(p) & 15) + len + 15) & ~uintptr_t(15));
 }
 
-// Bounded wait at the grid barrier: this many sleeps of 8 x 64 cycles
-// (about half a second), after which the workgroup flags ROUTE_EBIT_SYNC
-// and skips the dispatch instead of waiting on.
-constexpr unsigned kBarrierSpins = 1u << 21;
+// Bounded wait at the grid barrier: this many polls (each after a sleep of
+// 2 x 64 cycles; a poll is a coherent load, about a microsecond), after which
+// the workgroup flags ROUTE_EBIT_SYNC and skips the dispatch instead of
+// waiting on. The workspace's second word, when not zero, replaces it (a
+// caller's way to force the time-out).
+constexpr unsigned kBarrierSpins = 1u << 19;
 // the dispatch's LDS: per (cluster, expert) entry, the pairs before this
 // workgroup, in all, and the entry's first slot, for up to kDispMaxGE entries
 constexpr int kDispMaxGE = 256;
@@ -580,12 +582,15 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
         const unsigned old = __hip_atomic_fetch_add(ps.dp.arrive, inc, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         const unsigned base = old & ~255u;
+        const unsigned cap_set = __hip_atomic_load(ps.dp.arrive + 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned cap = cap_set ? cap_set : kBarrierSpins;
         int ok = 1;
         for (unsigned it = 0;; ++it) {
           const unsigned now =
               __hip_atomic_load(ps.dp.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (now - base >= 256u) break;
-          if (it >= kBarrierSpins) {
+          if (it >= cap) {
             ok = 0;
             break;
           }
