@@ -178,6 +178,24 @@ def test_srs_route_empty():
     assert host(r[1]).tolist() == [0] * 5 and r[6].shape == (0, 2)
 
 
+def test_predict_route_and_dispatch_empty():
+    """No tokens: the one-launch calls only clear the cluster offsets (and
+    the dispatch the expert offsets) and return empty outputs."""
+    parts = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    tok = torch.empty((0,), dtype=torch.int32, device="cuda")
+    lut = dev(np.zeros(100, np.uint8))
+    w = dev(_bf16((8, 128), 0))
+    offs = torch.full((5,), 7, dtype=torch.int32, device="cuda")
+    r = tr.srs_predict_route(tok, lut, 4, parts, w, 2, offsets=offs)
+    eoff = torch.full((9,), 7, dtype=torch.int32, device="cuda")
+    offs2 = torch.full((5,), 7, dtype=torch.int32, device="cuda")
+    q = tr.srs_predict_route_dispatch(tok, lut, 4, parts, w, 2, offsets=offs2, expert_offsets=eoff)
+    sync()
+    assert host(r[1]).tolist() == [0] * 5 and r[7].shape == (0, 2)
+    assert host(q[1]).tolist() == [0] * 5 and host(q[9]).tolist() == [0] * 9
+    assert q[12].shape == (0, 128) and q[10].numel() == 0
+
+
 @pytest.mark.parametrize("E,K", [(8, 2), (160, 6)])
 def test_srs_route_flags_bad_cluster_and_skips_its_row(E, K):
     """A key past G is flagged; its row gets no outputs and adds nothing to
