@@ -287,10 +287,10 @@ def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     if fused and not estimator:
         return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K + 4 * N * K + 16}
     if fused:
-        # q_l, the hidden layer, then the output layer with its top-K and the
-        # hit count in one kernel (the logits never leave the chip)
-        return {"qhidden": 2 * N * d * b + 4 * d,
-                "hidden": N * d * b + hd * d * b + 4 * hd + N * hd * b,
+        # q_l and the hidden layer in one kernel (q never leaves the chip),
+        # then the output layer with its top-K and the hit count in one
+        # kernel (the logits never leave the chip)
+        return {"q_hidden": N * d * b + 4 * d + hd * d * b + 4 * hd + N * hd * b,
                 "out_topk_hits": N * hd * b + E * hd * b + 4 * E + 8 * N * K + 8}
     st = {"qhidden": 2 * N * d * b + 4 * d,
           "logits": (N * d * b + hd * d * b + 4 * hd + N * hd * b + E * hd * b + 4 * E + 4 * N * E)
@@ -568,6 +568,11 @@ def predictor_measure(args):
     q_bf = p.q.view(torch.bfloat16)
     est_first_us = back_to_back_us(lambda: route_est_hidden(p.q, Le["w1"], Le["b1"], h=h_est))
     vendor_first_us = back_to_back_us(lambda: torch.matmul(q_bf, w1_t, out=h_est))
+    # q_l with the hidden layer in one kernel, as the fused sweep runs it
+    from token_routing_speculation_amd import route_qest_hidden_packed
+    q_hidden_us = (back_to_back_us(lambda: route_qest_hidden_packed(
+        Le["r"], Le["dvec"], Le["w1_packed"], Le["b1"], cfg.hd, eps=Le["eps"], h=p.h))
+        if "w1_packed" in Le else None)
     del h_est, w1_t
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
@@ -625,6 +630,7 @@ def predictor_measure(args):
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
         "estimator_first_product_us": {"route_est_hidden": est_first_us,
                                        "vendor_gemm_no_epilogue": vendor_first_us,
+                                       "route_qest_hidden_packed_with_q_l": q_hidden_us,
                                        "mfma_frac": 2.0 * N * cfg.d * cfg.hd
                                        / (est_first_us * 1e-6) / MFMA_BF16_PEAK},
         "hit_rate_estimator_layers": float(np.mean([r for r, e_ in zip(rates, est) if e_])),

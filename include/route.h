@@ -548,6 +548,24 @@ int route_est_out_topk_packed(const uint16_t* h, int64_t n, int32_t hd, const ui
                               hipStream_t s);
 
 /*
+ * route_qest_hidden_packed - q_l and the estimator's hidden layer in one
+ * kernel: h = GELU(q W1^T + b1), q = LN_{l+1}(d_l + r_l) kept on chip.
+ * [SPEC] items 2.A (q_l) and 2.C (the estimator's first layer). q is
+ * rounded to bf16 exactly as route_qhidden stores it, so h equals
+ * route_qhidden followed by route_est_hidden up to the order of the
+ * binary32 sums (each element bf16, nearest even, of GELU in binary32).
+ *   r bf16 [n][d], dvec float [d], gamma, beta float [d] (nullable), eps:
+ *   as route_qhidden; w1p bf16 W1 [hd][d] packed by route_gate_pack(w1,
+ *   hd, d); b1 float [hd]; h bf16 [n][hd].
+ * Errors: NULL, SHAPE (d % 8, hd % 8 or hd < 8 as route_est_hidden, eps < 0),
+ * ALIGN, UNSUPPORTED (d not 1024, 2048 or 4096; hd > 1024).
+ */
+int route_qest_hidden_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                             const float* beta, int64_t n, int32_t d, float eps,
+                             const uint16_t* w1p, const float* b1, int32_t hd, uint16_t* h,
+                             hipStream_t s);
+
+/*
  * route_qgate_topk_packed - route_qgate_topk with the router given packed
  * (wp from route_gate_pack for the same E and d). [SPEC] items 2.A and 4.
  * The same results, bit for bit: the matrix products see the same operands

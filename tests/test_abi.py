@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 47, names
+    assert len(names) == 48, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -217,6 +217,24 @@ def test_predict_route_errors(L):
     assert call(args(idx=None)) == NULL
     assert call(args(ec=A)) == NULL             # the count needs both
     assert call(args(partials=MIS)) == ALIGN
+
+
+def test_qest_hidden_errors(L):
+    f = L.route_qest_hidden_packed
+    args = lambda **k: dict(dict(r=A, dvec=A, g=None, b=None, n=100, d=2048, eps=1e-5, w1p=A,
+                                 b1=A, hd=512, h=A, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(d=12)) == SHAPE
+    assert call(args(hd=0)) == SHAPE
+    assert call(args(hd=12)) == SHAPE           # rows of whole 16-byte vectors
+    assert call(args(eps=-1.0)) == SHAPE
+    assert call(args(d=512)) == UNSUP          # q_l's tile sizes: 1024, 2048, 4096
+    assert call(args(hd=1032)) == UNSUP
+    assert call(args(b1=None)) == NULL
+    assert call(args(w1p=None)) == NULL
+    assert call(args(h=None)) == NULL
+    assert call(args(r=MIS)) == ALIGN
+    assert call(args(n=0)) == OK                # nothing to do
 
 
 def test_predict_route_dispatch_errors(L):

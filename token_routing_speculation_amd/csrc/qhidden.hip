@@ -7,6 +7,7 @@
 // row's own bytes); the row loads are unconditional (vectors past the row
 // end reload vector 0 and are masked out), so they issue back to back.
 #include "common.hpp"
+#include "gemm.hpp"
 #include "mfma.hpp"
 #include "topk.hpp"
 
@@ -176,14 +177,17 @@ __device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ 
 // LN false: the tile is r's rows themselves (dvec, gamma, beta, eps unused),
 // for a product whose input is already on hand (the estimator's hidden
 // layer). bias (nullable, [E]) is added to every logit before it is stored
-// or ranked.
+// or ranked. hout (TOPK = 0, nullable): instead of the logits, each value
+// goes out as bf16(GELU(logit + bias)) into hout [n][E] (the estimator's
+// hidden layer, with the arithmetic of the matrix-core kernel's epilogue).
 template <int BM, int D, int TOPK, bool PW, bool LN = true>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
     const uint16_t* __restrict__ w, int E, float* __restrict__ logits, int K,
     int* __restrict__ idx, const int32_t* __restrict__ truth,
-    unsigned long long* __restrict__ hits, const float* __restrict__ bias = nullptr) {
+    unsigned long long* __restrict__ hits, const float* __restrict__ bias = nullptr,
+    uint16_t* __restrict__ hout = nullptr) {
   constexpr int CPL = D / 8 / kWave;
   constexpr int NV = D / 8;
   constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
@@ -333,11 +337,29 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
         }
     }
   };
+  auto store_hidden = [&](int g, const f32x4 (&acc)[MT]) {
+    const int colr = 16 * g + r16;
+    if (colr < E) {
+      const float b = bias ? bias[colr] : 0.f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int64_t row = row0 + 16 * m + 4 * kq + jj;
+          if (row < n)
+            hout[row * E + colr] =
+                static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(acc[m][jj] + b)));
+        }
+    }
+  };
   if constexpr (TOPK == 0) {
     for (int g = wv; g < ngroups; g += kQgThreads / kWave) {
       f32x4 acc[MT];
       gemm_group(g, acc);
-      store_logits(g, acc);
+      if (hout)
+        store_hidden(g, acc);
+      else
+        store_logits(g, acc);
     }
   } else {
     // at most two column groups per wave (E <= 256)
@@ -583,6 +605,29 @@ ROUTE_API int route_est_out_topk_packed(const uint16_t* h, int64_t n, int32_t hd
     if (E <= 128) ROUTE_EST_OUT(2048, 1); else ROUTE_EST_OUT(2048, 2);
   }
 #undef ROUTE_EST_OUT
+  return launch_status();
+}
+
+ROUTE_API int route_qest_hidden_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                                       const float* beta, int64_t n, int32_t d, float eps,
+                                       const uint16_t* w1p, const float* b1, int32_t hd,
+                                       uint16_t* h, hipStream_t s) {
+  if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || hd < 8 || hd % 8 != 0)
+    return ROUTE_ERR_SHAPE;
+  if (hd > kMaxExperts || (d != 1024 && d != 2048 && d != 4096)) return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!r || !dvec || !w1p || !b1 || !h) return ROUTE_ERR_NULL;
+  if (!aligned16(r) || !aligned16(dvec) || !aligned16(w1p)) return ROUTE_ERR_ALIGN;
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
+  if (d == 1024)
+    qgate_kernel<32, 1024, 0, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w1p, hd, nullptr, 0, nullptr, nullptr, nullptr, b1, h);
+  else if (d == 2048)
+    qgate_kernel<32, 2048, 0, true><<<ceil_div(n, 32), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w1p, hd, nullptr, 0, nullptr, nullptr, nullptr, b1, h);
+  else
+    qgate_kernel<16, 4096, 0, true><<<ceil_div(n, 16), kQgThreads, 0, s>>>(
+        r, dvec, gamma, beta, n, eps, w1p, hd, nullptr, 0, nullptr, nullptr, nullptr, b1, h);
   return launch_status();
 }
 

@@ -46,7 +46,7 @@ from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
                eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk,
                route_gate_pack, route_qgate_topk_packed, route_est_hidden,
-               route_est_out_topk_packed)
+               route_est_out_topk_packed, route_qest_hidden_packed)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
@@ -361,6 +361,8 @@ class PredictorPass:
             self.layer["w_next_packed"] = route_gate_pack(self.layer["w_next"])
         if self.layer["estimator"] and self.hd in (512, 1024, 2048) and self.E <= 256:
             self.layer["w2_packed"] = route_gate_pack(self.layer["w2"])
+            if self.d in QGATE_D and self.hd <= 1024:
+                self.layer["w1_packed"] = route_gate_pack(self.layer["w1"])
         return self
 
     def truth_step(self):
@@ -374,8 +376,9 @@ class PredictorPass:
         in one kernel (route_qgate_topk_packed, q and the logits kept on chip; the
         logits are written only if ``keep_logits``) when ``fused`` and the
         shape allows, else route_qhidden + route_gate + route_topk; on
-        estimator layers q_l, the hidden layer, and the output layer with its
-        top-K and hit count in one kernel (route_est_out_topk_packed) when
+        estimator layers q_l with the hidden layer in one kernel
+        (route_qest_hidden_packed, q kept on chip) and the output layer with
+        its top-K and hit count in one kernel (route_est_out_topk_packed) when
         ``fused``, else q_l, the estimator and top-K. Then the hit count
         (inside the fused kernels)."""
         L = self.layer
@@ -386,10 +389,15 @@ class PredictorPass:
                                     truth=self.truth, hits=self.hits)
             return
         if L["estimator"] and fused and "w2_packed" in L:
-            # q_l, the hidden layer, then the output layer with its top-K and
-            # the hit count in one kernel
-            route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
-            route_est_hidden(self.q, L["w1"], L["b1"], h=self.h)
+            # q_l and the hidden layer in one kernel (q kept on chip) where
+            # the shape allows, then the output layer with its top-K and the
+            # hit count in one kernel
+            if "w1_packed" in L:
+                route_qest_hidden_packed(L["r"], L["dvec"], L["w1_packed"], L["b1"], self.hd,
+                                         eps=L["eps"], h=self.h)
+            else:
+                route_qhidden(L["r"], L["dvec"], eps=L["eps"], q=self.q)
+                route_est_hidden(self.q, L["w1"], L["b1"], h=self.h)
             route_est_out_topk_packed(self.h, L["w2_packed"], L["b2"], self.E, self.K,
                                       logits=self.logits if keep_logits else None,
                                       idx=self.pred, truth=self.truth, hits=self.hits)
