@@ -286,6 +286,11 @@ def predictor_bytes(N, d, E, K, hd, estimator, fused=False):
     b = 2
     if fused and not estimator:
         return {"qgate_topk": N * d * b + 4 * d + E * d * b + 4 * N * K + 4 * N * K + 16}
+    if fused and hd in (512, 1024) and hd <= d:
+        # the whole estimator predictor in one kernel (q, h and the logits
+        # never leave the chip)
+        return {"qest_topk_hits": N * d * b + 4 * d + hd * d * b + 4 * hd + E * hd * b + 4 * E
+                + 8 * N * K + 8}
     if fused:
         # q_l and the hidden layer in one kernel (q never leaves the chip),
         # then the output layer with its top-K and the hit count in one
@@ -573,6 +578,19 @@ def predictor_measure(args):
     q_hidden_us = (back_to_back_us(lambda: route_qest_hidden_packed(
         Le["r"], Le["dvec"], Le["w1_packed"], Le["b1"], cfg.hd, eps=Le["eps"], h=p.h))
         if "w1_packed" in Le else None)
+    # one estimator layer's prediction: the one-kernel form the sweep runs
+    # beside q_l + hidden layer, then output layer + top-K + hits
+    from token_routing_speculation_amd import route_qest_topk_packed, route_est_out_topk_packed
+    p.layer, p.truth = Le, truths[0]
+    est_one_us = (back_to_back_us(lambda: route_qest_topk_packed(
+        Le["r"], Le["dvec"], Le["w1_packed"], Le["b1"], cfg.hd, Le["w2_packed"], Le["b2"], p.E,
+        p.K, eps=Le["eps"], idx=p.pred, truth=p.truth, hits=p.hits))
+        if "w1_packed" in Le and cfg.hd in (512, 1024) and cfg.hd <= cfg.d else None)
+    est_two_us = (back_to_back_us(lambda: (route_qest_hidden_packed(
+        Le["r"], Le["dvec"], Le["w1_packed"], Le["b1"], cfg.hd, eps=Le["eps"], h=p.h),
+        route_est_out_topk_packed(p.h, Le["w2_packed"], Le["b2"], p.E, p.K, idx=p.pred,
+                                  truth=p.truth, hits=p.hits)))
+        if "w1_packed" in Le and "w2_packed" in Le else None)
     del h_est, w1_t
     # hit rates per layer (one sweep from zeroed counters)
     p.hits.zero_()
@@ -628,6 +646,7 @@ def predictor_measure(args):
                                                  QGATE_TRAFFIC_SOURCES)},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
+        "estimator_layer_us": {"one_kernel": est_one_us, "two_kernels": est_two_us},
         "estimator_first_product_us": {"route_est_hidden": est_first_us,
                                        "vendor_gemm_no_epilogue": vendor_first_us,
                                        "route_qest_hidden_packed_with_q_l": q_hidden_us,

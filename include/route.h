@@ -573,6 +573,30 @@ int route_qest_hidden_packed(const uint16_t* r, const float* dvec, const float* 
  * per-wave transpose in on-chip memory.
  * Errors: as route_qgate_topk.
  */
+/*
+ * route_qest_topk_packed - the whole estimator predictor of one layer in one
+ * kernel: q = LN_{l+1}(d_l + r_l), h = GELU(q W1^T + b1), logits = h W2^T +
+ * b2, their top-K and the hit count against truth. [SPEC] items 2.A, 2.C
+ * and 4. q and h stay on chip (h as bf16, nearest even, as the estimator
+ * keeps it); the two products see the same operands in the same order as
+ * route_qest_hidden_packed followed by route_est_out_topk_packed, so
+ * logits, idx and hits equal that pair's, bit for bit.
+ *   r, dvec, gamma, beta, eps: as route_qhidden; w1p: W1 [hd][d] packed by
+ *   route_gate_pack(w1, hd, d); b1 float [hd]; w2p: W2 [E][hd] packed by
+ *   route_gate_pack(w2, E, hd); b2 float [E] (nullable); logits float
+ *   [n][E] (nullable), idx int32 [n][K], truth int32 [n][K] and hits (one
+ *   uint64, added to): as route_qgate_topk.
+ * Errors: NULL, SHAPE (as route_qest_hidden_packed and route_topk), ALIGN,
+ * UNSUPPORTED (d not 1024, 2048 or 4096; hd not 512 or 1024, or hd > d;
+ * E > 256; K > 16).
+ */
+int route_qest_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                           const float* beta, int64_t n, int32_t d, float eps,
+                           const uint16_t* w1p, const float* b1, int32_t hd,
+                           const uint16_t* w2p, const float* b2, int32_t E, int32_t K,
+                           float* logits, int32_t* idx, const int32_t* truth,
+                           unsigned long long* hits, hipStream_t s);
+
 int route_qgate_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
                             const float* beta, int64_t n, int32_t d, float eps,
                             const uint16_t* wp, int32_t E, int32_t K, float* logits,

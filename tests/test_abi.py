@@ -33,7 +33,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 48, names
+    assert len(names) == 49, names
     for n in names:
         assert hasattr(L, n), n
     assert names == set(tr.EXPORTS)
@@ -234,6 +234,29 @@ def test_qest_hidden_errors(L):
     assert call(args(w1p=None)) == NULL
     assert call(args(h=None)) == NULL
     assert call(args(r=MIS)) == ALIGN
+    assert call(args(n=0)) == OK                # nothing to do
+
+
+def test_qest_topk_errors(L):
+    f = L.route_qest_topk_packed
+    args = lambda **k: dict(dict(r=A, dvec=A, g=None, b=None, n=100, d=2048, eps=1e-5, w1p=A,
+                                 b1=A, hd=512, w2p=A, b2=None, E=128, K=8, logits=None, idx=A,
+                                 truth=None, hits=None, s=None), **k)
+    call = lambda a: f(*a.values())
+    assert call(args(d=12)) == SHAPE
+    assert call(args(hd=12)) == SHAPE
+    assert call(args(eps=-1.0)) == SHAPE
+    assert call(args(K=0)) == SHAPE
+    assert call(args(K=129)) == SHAPE          # K > E
+    assert call(args(d=512)) == UNSUP          # q_l's tile sizes: 1024, 2048, 4096
+    assert call(args(hd=768)) == UNSUP         # the hidden tile: 512 or 1024 wide
+    assert call(args(E=257, K=8)) == UNSUP
+    assert call(args(K=17)) == UNSUP
+    assert call(args(b1=None)) == NULL
+    assert call(args(w2p=None)) == NULL
+    assert call(args(idx=None)) == NULL
+    assert call(args(truth=A)) == NULL         # truth without hits
+    assert call(args(w2p=MIS)) == ALIGN
     assert call(args(n=0)) == OK                # nothing to do
 
 

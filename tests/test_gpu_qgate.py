@@ -275,3 +275,46 @@ def test_qest_hidden_packed(n, d, hd, affine):
     assert np.abs(a - c).max() <= 1
     assert (a != c).mean() <= 1e-3
     assert (oracle.bf16_to_f64(qg) != oracle.bf16_to_f64(qb)).mean() < 1e-3
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,d,hd,E,K,affine", [(1, 2048, 512, 128, 8, False),
+                                               (8192, 2048, 512, 128, 8, False),
+                                               (1000, 2048, 1024, 256, 16, True),
+                                               (300, 4096, 512, 200, 8, True),
+                                               (77, 1024, 1024, 8, 2, False),
+                                               (4097, 1024, 512, 64, 6, True)])
+def test_qest_topk_packed(n, d, hd, E, K, affine):
+    """The whole estimator predictor in one kernel against
+    route_qest_hidden_packed + route_est_out_topk_packed (the same products
+    on the same operands in the same order: logits, idx and hits bit for
+    bit), and its logits against the oracle's h W2^T + b2 in binary64 on
+    that bf16 h, within the bound of a binary32 sum of hd products in any
+    order (2 hd 2^-24 sum |h||w|)."""
+    r, dv, g, b, w1 = _case(n, d, hd, affine, 5 * n + d + hd + E)
+    rng = np.random.default_rng(hd + E)
+    b1 = (rng.standard_normal(hd) * 0.1).astype(np.float32)
+    w2 = round_bf16(rng.standard_normal((E, hd)) * hd ** -0.5)
+    b2 = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    truth = rng.integers(0, E, size=(n, K)).astype(np.int32)
+    opt = lambda a: None if a is None else dev(a)
+    w1p = tr.route_gate_pack(dev(w1))
+    w2p = tr.route_gate_pack(dev(w2))
+    hits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    idx = tr.route_qest_topk_packed(dev(r), dev(dv), w1p, dev(b1), hd, w2p, dev(b2), E, K,
+                                    opt(g), opt(b), 1e-5, logits=lg, truth=dev(truth), hits=hits)
+    h = tr.route_qest_hidden_packed(dev(r), dev(dv), w1p, dev(b1), hd, opt(g), opt(b), 1e-5)
+    hits2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    lg2 = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    idx2 = tr.route_est_out_topk_packed(h, w2p, dev(b2), E, K, logits=lg2, truth=dev(truth),
+                                        hits=hits2)
+    sync()
+    assert np.array_equal(host(lg).view(np.uint32), host(lg2).view(np.uint32))
+    assert np.array_equal(host(idx), host(idx2))
+    assert int(hits.item()) == int(hits2.item())
+    hf = oracle.bf16_to_f64(host(h))
+    wf = oracle.bf16_to_f64(w2)
+    ref = hf @ wf.T + b2.astype(np.float64)[None, :]
+    bound = 2.0 * hd * 2.0 ** -24 * (np.abs(hf) @ np.abs(wf).T) + np.abs(ref) * 2.0 ** -23
+    assert np.all(np.abs(host(lg).astype(np.float64) - ref) <= bound)

@@ -32,7 +32,7 @@ __all__ = [
     "est_fit_gram_workspace_size", "est_fit_gram", "est_fit_solve", "est_fit_weights",
     "prefetch_plan", "prefetch_copy", "prefetch_coverage", "prefetch_issue", "route_qgate",
     "route_qgate_topk", "route_gate_packed_size", "route_gate_pack", "route_qgate_topk_packed",
-    "route_est_out_topk_packed", "route_qest_hidden_packed",
+    "route_est_out_topk_packed", "route_qest_hidden_packed", "route_qest_topk_packed",
     "EXPORTS",
 ]
 
@@ -97,6 +97,8 @@ EXPORTS = {
                                                  _p, _p]),
     "route_qest_hidden_packed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p, _i32,
                                                 _p, _p]),
+    "route_qest_topk_packed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i32, _f32, _p, _p, _i32, _p,
+                                              _p, _i32, _i32, _p, _p, _p, _p, _p]),
     "route_estimator": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _sz, _p]),
     "route_estimator_workspace_size": (_sz, [_i64, _i32]),
     "hit_count": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
@@ -678,6 +680,27 @@ def route_qest_hidden_packed(r, dvec, w1p, b1, hd, gamma=None, beta=None, eps=1e
           _dev(w1p, _bf16(w1p), "w1p", route_gate_packed_size(hd, d) // 2),
           _dev(b1, torch.float32, "b1", hd), hd, _dev(h, bt, "h", n * hd), _stream(stream))
     return h
+
+
+def route_qest_topk_packed(r, dvec, w1p, b1, hd, w2p, b2, E, K, gamma=None, beta=None, eps=1e-5,
+                           idx=None, logits=None, truth=None, hits=None, stream=None):
+    """The estimator predictor of one layer in one kernel: q_l, h = GELU(q_l
+    W1^T + b1) (bf16), h . W2^T + b2, its top-K and the hit count, with W1
+    and W2 packed by route_gate_pack. Returns idx."""
+    n, d = r.shape
+    bt = _bf16(r)
+    idx = _empty((n, K), torch.int32, r) if idx is None else idx
+    if (truth is None) != (hits is None):
+        raise ValueError("truth and hits go together")
+    _call("route_qest_topk_packed", _dev(r, bt, "r"), _dev(dvec, torch.float32, "dvec", d),
+          _opt(gamma, torch.float32, "gamma", d), _opt(beta, torch.float32, "beta", d), n, d, eps,
+          _dev(w1p, _bf16(w1p), "w1p", route_gate_packed_size(hd, d) // 2),
+          _dev(b1, torch.float32, "b1", hd), hd,
+          _dev(w2p, _bf16(w2p), "w2p", route_gate_packed_size(E, hd) // 2),
+          _opt(b2, torch.float32, "b2", E), E, K, _opt(logits, torch.float32, "logits", n * E),
+          _dev(idx, torch.int32, "idx", n * K), _opt(truth, torch.int32, "truth", n * K),
+          _opt(hits, torch.int64, "hits", 1), _stream(stream))
+    return idx
 
 
 def route_qgate_topk_packed(r, dvec, wp, E, K, gamma=None, beta=None, eps=1e-5, idx=None,

@@ -180,14 +180,22 @@ __device__ __forceinline__ int wst_off(int rr, int p) { return rr * 128 + ((p ^ 
 // or ranked. hout (TOPK = 0, nullable): instead of the logits, each value
 // goes out as bf16(GELU(logit + bias)) into hout [n][E] (the estimator's
 // hidden layer, with the arithmetic of the matrix-core kernel's epilogue).
-template <int BM, int D, int TOPK, bool PW, bool LN = true>
+// H2 > 0 (TOPK > 0, PW): the estimator on q_l in one kernel. w (packed) is
+// W1 with H2 rows and bias its b1: each value becomes bf16(GELU(. + b1)) as
+// above, into the tile (q is done with by then) as an H2-wide bf16 tile; the
+// product, top-K and hit count then run on that tile with w2 (packed, E
+// rows) and bias2.
+template <int BM, int D, int TOPK, bool PW, bool LN = true, int H2 = 0>
 __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     const uint16_t* __restrict__ r, const float* __restrict__ dvec,
     const float* __restrict__ gamma, const float* __restrict__ beta, int64_t n, float eps,
     const uint16_t* __restrict__ w, int E, float* __restrict__ logits, int K,
     int* __restrict__ idx, const int32_t* __restrict__ truth,
     unsigned long long* __restrict__ hits, const float* __restrict__ bias = nullptr,
-    uint16_t* __restrict__ hout = nullptr) {
+    uint16_t* __restrict__ hout = nullptr, const uint16_t* __restrict__ w2 = nullptr,
+    const float* __restrict__ bias2 = nullptr) {
+  static_assert(H2 == 0 || (TOPK > 0 && PW && H2 % 256 == 0 && BM * H2 <= BM * D),
+                "the estimator's hidden layer is a packed product into the q tile");
   constexpr int CPL = D / 8 / kWave;
   constexpr int NV = D / 8;
   constexpr int RPW = BM / (kQgThreads / kWave);  // rows per wave
@@ -246,33 +254,39 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   const int r16 = lane & 15, kq = lane >> 4;
   const int ngroups = (E + 15) / 16;
   // packed W: group g, K step st (32 k), lane l's fragment at
-  // (g * NSTEPS + st) * 64 + l in 16-byte units
+  // (g * NSTEPS + st) * 64 + l in 16-byte units; the tile's rows are RL
+  // values long (D for q, H2 for the estimator's hidden layer)
   constexpr int NSTEPS = D / 32;
-  auto gemm_group_packed = [&](int g, f32x4 (&acc)[MT]) {
-    const u32x4* wp = reinterpret_cast<const u32x4*>(w) + static_cast<size_t>(g) * NSTEPS * kWave + lane;
+  auto gemm_packed = [&](auto rl, const uint16_t* wsrc, int g, f32x4 (&acc)[MT]) {
+    constexpr int RL = decltype(rl)::value;
+    constexpr int NS = RL / 32;
+    const u32x4* wp = reinterpret_cast<const u32x4*>(wsrc) + static_cast<size_t>(g) * NS * kWave + lane;
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    static_assert(NSTEPS % kQgPackLead == 0, "the ring cycles whole");
+    static_assert(NS % kQgPackLead == 0, "the ring cycles whole");
     u32x4 ring[kQgPackLead];
 #pragma unroll
     for (int j = 0; j < kQgPackLead; ++j) ring[j] = wp[j * kWave];
 #pragma unroll 1
-    for (int st0 = 0; st0 < NSTEPS; st0 += kQgPackLead) {
+    for (int st0 = 0; st0 < NS; st0 += kQgPackLead) {
 #pragma unroll
       for (int j = 0; j < kQgPackLead; ++j) {
         const int st = st0 + j;
         const u32x4 bf = ring[j];
         // past the last step: reload the last one (in bounds, never used)
-        const int nx = st + kQgPackLead < NSTEPS ? st + kQgPackLead : NSTEPS - 1;
+        const int nx = st + kQgPackLead < NS ? st + kQgPackLead : NS - 1;
         ring[j] = wp[nx * kWave];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const u32x4 af =
-              *reinterpret_cast<const u32x4*>(tile + qg_off<D>(16 * m + r16, 4 * st + kq));
+              *reinterpret_cast<const u32x4*>(tile + qg_off<RL>(16 * m + r16, 4 * st + kq));
           acc[m] = mfma16x16x32(af, bf, acc[m]);
         }
       }
     }
+  };
+  auto gemm_group_packed = [&](int g, f32x4 (&acc)[MT]) {
+    gemm_packed(std::integral_constant<int, D>{}, w, g, acc);
   };
   char* wst = wstage + (PW ? 0 : wv * 2048);
   const int lrow = lane >> 3, lchunk = lane & 7;  // line-load mapping: row, 16-byte chunk
@@ -324,10 +338,12 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
     else
       gemm_group_lines(g, acc);
   };
+  // the bias of the logits the kernel ranks (b2 in the two-layer form)
+  const float* const bfin = H2 > 0 ? bias2 : bias;
   auto store_logits = [&](int g, const f32x4 (&acc)[MT]) {
     const int colr = 16 * g + r16;
     if (colr < E) {
-      const float b = bias ? bias[colr] : 0.f;
+      const float b = bfin ? bfin[colr] : 0.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -364,12 +380,39 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
   } else {
     // at most two column groups per wave (E <= 256)
     constexpr int NW = kQgThreads / kWave;
+    if constexpr (H2 > 0) {
+      // the hidden layer: wave wv takes W1's 16-column groups wv, wv + 8, ...
+      // into registers; once every wave is done with q, the tile takes them
+      // as bf16(GELU(. + b1)), H2 values a row, laid out as a q tile of
+      // that width
+      constexpr int GPW = H2 / 16 / NW;
+      f32x4 hacc[GPW][MT];
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) gemm_group(wv + NW * gi, hacc[gi]);
+      __syncthreads();
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int col = 16 * (wv + NW * gi) + r16;
+        const float b = bias[col];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<uint16_t*>(tile + qg_off<H2>(16 * m + 4 * kq + jj, col >> 3) +
+                                         2 * (col & 7)) =
+                static_cast<uint16_t>(f32_to_bf16_bits(gelu_erf(hacc[gi][m][jj] + b)));
+      }
+      __syncthreads();
+    }
     f32x4 accs[2][MT];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int g = wv + NW * gi;
       if (g < ngroups) {
-        gemm_group(g, accs[gi]);
+        if constexpr (H2 > 0)
+          gemm_packed(std::integral_constant<int, (H2 > 0 ? H2 : D)>{}, w2, g, accs[gi]);
+        else
+          gemm_group(g, accs[gi]);
         if (logits) store_logits(g, accs[gi]);
       }
     }
@@ -383,7 +426,7 @@ __global__ __launch_bounds__(kQgThreads, 1) void qgate_kernel(
       const int g = wv + NW * gi;
       const int col = 16 * g + r16;
       if (g < ngroups && col < E) {
-        const float b = bias ? bias[col] : 0.f;
+        const float b = bfin ? bfin[col] : 0.f;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -631,6 +674,44 @@ ROUTE_API int route_qest_hidden_packed(const uint16_t* r, const float* dvec, con
   return launch_status();
 }
 
+ROUTE_API int route_qest_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
+                                     const float* beta, int64_t n, int32_t d, float eps,
+                                     const uint16_t* w1p, const float* b1, int32_t hd,
+                                     const uint16_t* w2p, const float* b2, int32_t E, int32_t K,
+                                     float* logits, int32_t* idx, const int32_t* truth,
+                                     unsigned long long* hits, hipStream_t s) {
+  if (n < 0 || d < 8 || d % 8 != 0 || !(eps >= 0.f) || hd < 8 || hd % 8 != 0 || E < 1 ||
+      K < 1 || K > E)
+    return ROUTE_ERR_SHAPE;
+  if ((d != 1024 && d != 2048 && d != 4096) || (hd != 512 && hd != 1024) || hd > d ||
+      E > 256 || K > kMaxK)
+    return ROUTE_ERR_UNSUPPORTED;
+  if (n == 0) return ROUTE_OK;
+  if (!r || !dvec || !w1p || !b1 || !w2p || !idx || (!truth != !hits)) return ROUTE_ERR_NULL;
+  if (!aligned16(r) || !aligned16(dvec) || !aligned16(w1p) || !aligned16(w2p))
+    return ROUTE_ERR_ALIGN;
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return ROUTE_ERR_ALIGN;
+#define ROUTE_QEST(BM, D, T, H)                                                               \
+  qgate_kernel<BM, D, T, true, true, H><<<ceil_div(n, BM), kQgThreads, 0, s>>>(              \
+      r, dvec, gamma, beta, n, eps, w1p, E, logits, K, idx, truth, hits, b1, nullptr, w2p, b2)
+#define ROUTE_QEST_T(BM, D, H)                    \
+  do {                                            \
+    if (E <= 128) ROUTE_QEST(BM, D, 1, H);        \
+    else ROUTE_QEST(BM, D, 2, H);                 \
+  } while (0)
+  if (hd == 512) {
+    if (d == 1024) ROUTE_QEST_T(32, 1024, 512);
+    else if (d == 2048) ROUTE_QEST_T(32, 2048, 512);
+    else ROUTE_QEST_T(16, 4096, 512);
+  } else {
+    if (d == 1024) ROUTE_QEST_T(32, 1024, 1024);
+    else if (d == 2048) ROUTE_QEST_T(32, 2048, 1024);
+    else ROUTE_QEST_T(16, 4096, 1024);
+  }
+#undef ROUTE_QEST_T
+#undef ROUTE_QEST
+  return launch_status();
+}
 ROUTE_API int route_qgate_topk_packed(const uint16_t* r, const float* dvec, const float* gamma,
                                       const float* beta, int64_t n, int32_t d, float eps,
                                       const uint16_t* wp, int32_t E, int32_t K, float* logits,

@@ -46,7 +46,7 @@ from . import (route_predict, route_predict_sort, route_lut_build, srs_shuffle,
                route_estimator_workspace_size, eg_profile, eg_init, eg_sample, eg_score,
                eg_update, eg_score_workspace_size, route_qgate, route_qgate_topk,
                route_gate_pack, route_qgate_topk_packed, route_est_hidden,
-               route_est_out_topk_packed, route_qest_hidden_packed)
+               route_est_out_topk_packed, route_qest_hidden_packed, route_qest_topk_packed)
 
 QGATE_D = (1024, 2048, 4096)  # hidden sizes route_qgate supports
 
@@ -335,6 +335,10 @@ class FoEPass:
 class PredictorPass:
     """One source layer of the q_l predictor; ``load(layer)`` swaps inputs."""
 
+    # estimator layers: q_l, both layers, top-K and the hit count in one
+    # kernel where the shape allows (else q_l + hidden, then output + top-K)
+    one_kernel_estimator = True
+
     def __init__(self, N, d, E, K, hd, device="cuda"):
         self.N, self.d, self.E, self.K, self.hd = N, d, E, K, hd
         dev = device
@@ -392,6 +396,15 @@ class PredictorPass:
             # q_l and the hidden layer in one kernel (q kept on chip) where
             # the shape allows, then the output layer with its top-K and the
             # hit count in one kernel
+            if "w1_packed" in L and self.one_kernel_estimator and self.hd in (512, 1024) \
+                    and self.hd <= self.d:
+                # the whole predictor in one kernel (h kept on chip as well)
+                route_qest_topk_packed(L["r"], L["dvec"], L["w1_packed"], L["b1"], self.hd,
+                                       L["w2_packed"], L["b2"], self.E, self.K, eps=L["eps"],
+                                       idx=self.pred,
+                                       logits=self.logits if keep_logits else None,
+                                       truth=self.truth, hits=self.hits)
+                return
             if "w1_packed" in L:
                 route_qest_hidden_packed(L["r"], L["dvec"], L["w1_packed"], L["b1"], self.hd,
                                          eps=L["eps"], h=self.h)
