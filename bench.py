@@ -638,7 +638,7 @@ def predictor_measure(args):
         "stages_us_gate_layer": st_fused, "stages_us_estimator_layer": st_est,
         "qgate_topk_us_per_launch": qg_launch_us,
         "qgate_topk_unpacked_us_per_launch": qg_unpacked_us,
-        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, 1, true> (route_qgate_topk_packed)",
+        "roofline": {"bound": "hbm", "kernel": "qgate_kernel<32, 2048, 1, true, true, 0> (route_qgate_topk_packed)",
                      "achieved": byt_fused["qgate_topk"] / (qg_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": byt_fused["qgate_topk"] / (qg_us * 1e-6) / HBM_PEAK,
@@ -646,7 +646,10 @@ def predictor_measure(args):
                                                  QGATE_TRAFFIC_SOURCES)},
         "estimator_mfma_frac": (2.0 * N * cfg.d * cfg.hd + 2.0 * N * cfg.hd * cfg.E)
         / (st_est["logits"] * 1e-6) / MFMA_BF16_PEAK,
-        "estimator_layer_us": {"one_kernel": est_one_us, "two_kernels": est_two_us},
+        "estimator_layer_us": {"one_kernel": est_one_us, "two_kernels": est_two_us,
+                               "mfma_frac_one_kernel": (2.0 * N * cfg.d * cfg.hd
+                                                        + 2.0 * N * cfg.hd * cfg.E)
+                               / (est_one_us * 1e-6) / MFMA_BF16_PEAK if est_one_us else None},
         "estimator_first_product_us": {"route_est_hidden": est_first_us,
                                        "vendor_gemm_no_epilogue": vendor_first_us,
                                        "route_qest_hidden_packed_with_q_l": q_hidden_us,
@@ -1063,6 +1066,7 @@ def predictor_summary(o: dict) -> dict:
             "alg_bytes_sweep": o["alg_bytes_sweep"], "hbm_frac_sweep": o["hbm_frac_sweep"],
             "dominant_kernel": {k: o["roofline"][k] for k in ("kernel", "achieved", "unit", "frac")},
             "estimator_mfma_frac": o["estimator_mfma_frac"],
+            "estimator_layer_us": o["estimator_layer_us"],
             "hit_rate_gate_layers": o["hit_rate_gate_layers"],
             "hit_rate_estimator_layers": o["hit_rate_estimator_layers"]}
 

@@ -313,6 +313,10 @@ def test_qest_topk_packed(n, d, hd, E, K, affine):
     assert np.array_equal(host(lg).view(np.uint32), host(lg2).view(np.uint32))
     assert np.array_equal(host(idx), host(idx2))
     assert int(hits.item()) == int(hits2.item())
+    # the picks against the oracle's top-K of the kernel's logits, and the
+    # hit count against a count of the picks found among the true ones
+    assert np.array_equal(host(idx), oracle.route_topk(host(lg), K, 1, 1)[0])
+    assert int(hits.item()) == oracle.hit_count(host(idx), truth)
     hf = oracle.bf16_to_f64(host(h))
     wf = oracle.bf16_to_f64(w2)
     ref = hf @ wf.T + b2.astype(np.float64)[None, :]
