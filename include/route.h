@@ -292,8 +292,10 @@ int srs_predict_route(const int32_t* tok, int64_t n, const uint8_t* lut, const u
  *   multiple of 256 (zero) before the first call with this ws. Every call
  *   leaves them so: keep the workspace between calls, and do not overlap
  *   two calls on one workspace. Its next 4 bytes bound each workgroup's wait
- *   at the barrier in polls (0, as zero-filled: the default, about half a
- *   second); a workgroup that waits that long flags SYNC.
+ *   at the barrier: 0 (as zero-filled) is the default, about half a second;
+ *   p > 0 allows p - 1 polls after the workgroup's own arrival, so 1 lets
+ *   only the last workgroup to arrive through. A workgroup that waits past
+ *   the bound flags SYNC.
  * Errors: as srs_predict_route, plus NULL (expert_offsets, slot_of_pair,
  * pair_of_slot, disp, weights), WORKSPACE (size or alignment), UNSUPPORTED
  * where G*E > 256 or the grid (n/16 workgroups) cannot be resident on the

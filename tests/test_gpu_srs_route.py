@@ -537,9 +537,10 @@ def test_predict_route_dispatch_calls_in_a_row():
 
 def test_predict_route_dispatch_barrier_timeout_flags_sync():
     """The barrier's bounded wait, forced from the host through the
-    workspace's bound word. With a bound of one poll, the workgroups that
-    arrive first give up, flag SYNC and skip their dispatch, and every
-    kernel still ends. The routing outputs, made before the barrier, are
+    workspace's bound word. With a bound word of 1 (no poll after a
+    workgroup's own arrival), every workgroup but the last to arrive gives
+    up, flags SYNC and skips its dispatch, whatever the arrival timing, and
+    every kernel still ends. The routing outputs, made before the barrier, are
     whole. The arrival count stays a multiple of 256, and the next call
     with the default bound is whole again."""
     n, d, P, G, E, K = 4096, 512, 2, 4, 8, 2

@@ -584,11 +584,15 @@ __global__ __launch_bounds__(kRouteThreads) void srs_route_kernel(
         const unsigned base = old & ~255u;
         const unsigned cap_set = __hip_atomic_load(ps.dp.arrive + 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned cap = cap_set ? cap_set : kBarrierSpins;
+        // the bound word holds the polls allowed plus one (0: the default);
+        // the first check is this workgroup's own arrival, so a word of 1
+        // lets only the last workgroup to arrive through
+        const unsigned cap = cap_set ? cap_set - 1 : kBarrierSpins;
         int ok = 1;
         for (unsigned it = 0;; ++it) {
           const unsigned now =
-              __hip_atomic_load(ps.dp.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              it == 0 ? old + inc
+                      : __hip_atomic_load(ps.dp.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (now - base >= 256u) break;
           if (it >= cap) {
             ok = 0;
