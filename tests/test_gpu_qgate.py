@@ -304,6 +304,9 @@ def test_qest_topk_packed(n, d, hd, E, K, affine):
     lg = torch.empty((n, E), dtype=torch.float32, device="cuda")
     idx = tr.route_qest_topk_packed(dev(r), dev(dv), w1p, dev(b1), hd, w2p, dev(b2), E, K,
                                     opt(g), opt(b), 1e-5, logits=lg, truth=dev(truth), hits=hits)
+    # the optional outputs left out (no logits, no hit count): the same picks
+    idx0 = tr.route_qest_topk_packed(dev(r), dev(dv), w1p, dev(b1), hd, w2p, None if n % 2 else
+                                     dev(b2), E, K, opt(g), opt(b), 1e-5)
     h = tr.route_qest_hidden_packed(dev(r), dev(dv), w1p, dev(b1), hd, opt(g), opt(b), 1e-5)
     hits2 = torch.zeros(1, dtype=torch.int64, device="cuda")
     lg2 = torch.empty((n, E), dtype=torch.float32, device="cuda")
@@ -313,6 +316,13 @@ def test_qest_topk_packed(n, d, hd, E, K, affine):
     assert np.array_equal(host(lg).view(np.uint32), host(lg2).view(np.uint32))
     assert np.array_equal(host(idx), host(idx2))
     assert int(hits.item()) == int(hits2.item())
+    if n % 2 == 0:
+        assert np.array_equal(host(idx0), host(idx))
+    else:
+        # without b2: the picks of the logits less b2, i.e. of h W2^T alone
+        idx0b = tr.route_est_out_topk_packed(h, w2p, None, E, K)
+        sync()
+        assert np.array_equal(host(idx0), host(idx0b))
     # the picks against the oracle's top-K of the kernel's logits, and the
     # hit count against a count of the picks found among the true ones
     assert np.array_equal(host(idx), oracle.route_topk(host(lg), K, 1, 1)[0])
