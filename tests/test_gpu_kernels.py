@@ -547,3 +547,33 @@ def test_graph_replay_matches_eager_foe():
             assert np.array_equal(host(getattr(f, k)), eager[k]), (rep, k)
         assert int(host(f.local)[0]) - before == l1
 
+
+
+def test_graph_replay_matches_eager_predictor():
+    """The q_l predictor on an estimator layer (the whole estimator in one
+    kernel) and on a gate layer, captured as a graph: every replay's picks
+    and logits equal the eager step's, and the hit count grows by the same
+    amount each replay (the kernels add to it; nothing clears it)."""
+    from synth import get_config
+    from synth.gen import make_predictor_layer
+    from token_routing_speculation_amd.pipeline import PredictorPass, capture_graph
+    cfg = get_config("qwen3")
+    for layer in (1, 20):
+        lay = make_predictor_layer(cfg, layer, N=777)
+        p = PredictorPass(777, cfg.d, cfg.E, cfg.K, cfg.hd).load(lay)
+        p.truth_step()
+        p.hits.zero_()
+        p.step(keep_logits=True)
+        sync()
+        eager = {k: host(getattr(p, k)).copy() for k in ("logits", "pred")}
+        h1 = int(p.hits.item())
+        g = capture_graph(lambda: p.step(keep_logits=True))
+        for rep in range(3):
+            p.logits.fill_(-1.0)
+            p.pred.fill_(-1)
+            before = int(p.hits.item())
+            g.replay()
+            sync()
+            for k, v in eager.items():
+                assert np.array_equal(host(getattr(p, k)), v), (layer, rep, k)
+            assert int(p.hits.item()) - before == h1, (layer, rep)
